@@ -1,0 +1,173 @@
+/*
+ * fwt.h - batched in-place Walsh-Hadamard transform on MI355X (gfx950).
+ *
+ * Operation.  For every vector b < batch and each of the two planar
+ * components (real part re, imaginary part im) independently:
+ *
+ *     y_k = c * sum_{i=0}^{2^n - 1} (-1)^{popcount(k AND i)} * x_i
+ *
+ * in natural (Sylvester) order, with c = 1, or c = 2^(-n/2) when
+ * `normalize` is non-zero.  The matrix entry is the on-the-fly Walsh
+ * coefficient of the Apache Mahout pull request "[QDP] [feature] Pr4
+ * kronecker fwt" (section "How"); the transform is the butterfly network
+ * of n add/subtract stages at strides 1, 2, 4, ... described in the iThome
+ * "Day 18" native-FWT article (section "Tensor Core wants matrix
+ * multiplication").  Because the matrix is real, a complex state stored as
+ * separate real and imaginary buffers (the planar layout of the pull
+ * request's section "How") is two independent real transforms.
+ *
+ * Execution.  A plan splits the n index bits into passes (the Kronecker
+ * factorisation H_n = H_{n1} (x) H_{n2} of the pull request's sections
+ * "Why" and "Why submit PR4"; the iThome article's "Kronecker block GEMM
+ * idea").  Each pass streams the state through HBM once, in place, with no
+ * transpose and no temporary buffer.  n <= 14 (fp32) / 13 (fp64) runs as a
+ * single pass whose tiles hold a whole vector on chip.
+ *
+ * Conventions common to every entry point:
+ *  - Status codes are the FWT_* values below; no C++ exception crosses
+ *    this interface.
+ *  - Nothing here allocates device memory; fwt_execute never synchronises.
+ *  - Plans hold host metadata only, are immutable after creation, and may
+ *    be used concurrently from several host threads and streams.
+ */
+#ifndef QSE_FWT_H
+#define QSE_FWT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fwt_plan_s* fwt_plan_t;
+
+/* Element type of both planar buffers. */
+typedef enum { FWT_F32 = 0, FWT_F64 = 1 } fwt_dtype;
+
+/* Execution path chosen at plan creation.
+ *  AUTO          single pass while a vector fits one tile (n <= 14 for
+ *                fp32, n <= 13 for fp64), otherwise multi-pass.
+ *  SINGLE_BLOCK  one pass, one vector per tile; FWT_EUNSUPPORTED above the
+ *                single-pass limit.
+ *  MULTIPASS     Kronecker split into >= 2 passes whenever n allows it
+ *                (n >= 2 for fp32, n >= 2 for fp64; below that one pass).
+ *  MFMA_ABLATION reserved for a matrix-core variant; FWT_EUNSUPPORTED. */
+typedef enum {
+    FWT_PATH_AUTO = 0,
+    FWT_PATH_SINGLE_BLOCK = 1,
+    FWT_PATH_MULTIPASS = 2,
+    FWT_PATH_MFMA_ABLATION = 3
+} fwt_path;
+
+enum {
+    FWT_OK = 0,
+    FWT_EINVAL = -1,       /* bad argument: null, range, n mismatch, overlap */
+    FWT_EALIGN = -2,       /* a buffer is not 16-byte aligned */
+    FWT_EUNSUPPORTED = -3, /* valid request this build does not implement */
+    FWT_EHIP = -4,         /* the HIP runtime reported an error */
+    FWT_ENOMEM = -5        /* host allocation of the plan failed */
+};
+
+/* Largest supported n (2^30 amplitudes per vector). */
+#define FWT_MAX_N 30   /* fp64 plans support n <= 29 (FWT_EUNSUPPORTED above) */
+
+/* Create a plan for vectors of 2^n amplitudes of `dtype`.
+ *  out    receives the plan (set to NULL on failure); must not be NULL.
+ *  n      0 <= n <= FWT_MAX_N; n = 0 is the identity.
+ * Returns FWT_OK, FWT_EINVAL (null out, n out of range, unknown dtype or
+ * path), FWT_EUNSUPPORTED (SINGLE_BLOCK above its limit, MFMA_ABLATION),
+ * FWT_ENOMEM, or FWT_EHIP (the kernels' launch attributes could not be
+ * set on the current device). */
+int fwt_plan_create(fwt_plan_t* out, int n, fwt_dtype dtype, fwt_path path);
+
+/* Create a plan with an explicit Kronecker split: npasses factors whose
+ * bit counts bits[0..npasses-1] sum to n.  bits[0] is the factor on the
+ * lowest (contiguous) index bits, bits[1] the next, and so on; so the
+ * two-factor split n = n1 + n2 of the pull request's section "How" is
+ * {n2, n1}.  Each factor must be within the per-pass limit (14 bits fp32 /
+ * 13 bits fp64 for bits[0], 12 bits for the others) and every factor after
+ * the first needs at least 2 (fp32) / 1 (fp64) bits below it.
+ * Returns FWT_OK, FWT_EINVAL (null pointers, npasses < 1, sum != n, a
+ * factor < 1 or out of its limit), FWT_ENOMEM or FWT_EHIP. */
+int fwt_plan_create_split(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
+                          const int* bits);
+
+/* As fwt_plan_create_split, with the on-chip tiling of each pass forced
+ * (tuning and testing of kernel variants; the result is the same).
+ *  eb     per pass, log2 of the 16-byte vectors a thread holds per register
+ *         round (0..5), or -1 for the default; NULL = all defaults.
+ *  gbits  per pass, log2 of the 16-byte column groups per tile of a column
+ *         pass (0..4; must be 0 or -1 for the first pass), or -1 for the
+ *         default; NULL = all defaults.
+ * Returns as fwt_plan_create_split, plus FWT_EINVAL for a value out of
+ * range or a tile that exceeds the LDS or workgroup limits, and
+ * FWT_EUNSUPPORTED for a variant that is not compiled in. */
+int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
+                          const int* bits, const int* eb, const int* gbits);
+
+/* Transform in place, asynchronously on `stream` (0 = the null stream).
+ *  re, im   device buffers of batch * 2^n elements of the plan's dtype,
+ *           vector b at offset b * 2^n; 16-byte aligned; must not overlap.
+ *           im may be NULL (real-only transform).  The caller owns them.
+ *  batch    >= 0; 0 is a no-op.
+ *  n        must equal the plan's n.
+ *  normalize  non-zero multiplies the result by 2^(-n/2) (applied once,
+ *           in the last pass; an exact power of two for even n).
+ * Validation happens on the host before anything is enqueued: FWT_EINVAL
+ * for a NULL plan or re, batch < 0, n mismatch, re == im, overlapping
+ * buffers, or a buffer that is not device memory or too small for
+ * batch * 2^n elements; FWT_EALIGN for misalignment.  A launch failure
+ * returns FWT_EHIP (earlier passes may already be enqueued; the buffers
+ * are then undefined).  Faults during execution surface at the caller's
+ * next synchronisation of the stream. */
+int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im,
+                int normalize, hipStream_t stream);
+
+/* Enqueue only pass `pass` (0 <= pass < fwt_plan_num_passes; 0 for an
+ * n = 0 plan, which has none and does nothing) of the plan, with the
+ * arguments and validation of fwt_execute.  Running passes 0, 1, ..., P-1
+ * in order on the same buffers and stream is exactly fwt_execute; the
+ * factors commute, so any order gives the same transform up to rounding.
+ * `normalize` takes effect only in the last pass.  Meant for per-kernel
+ * timing and for interleaving passes with other work.  Returns as
+ * fwt_execute, plus FWT_EINVAL for a pass index out of range. */
+int fwt_execute_pass(fwt_plan_t plan, int pass, int64_t batch, int n, void* re,
+                     void* im, int normalize, hipStream_t stream);
+
+/* Run exactly the host-side validation of fwt_execute (same arguments,
+ * same status codes, including the device-memory and size checks) without
+ * enqueuing anything.  Returns FWT_OK when fwt_execute would launch. */
+int fwt_execute_check(fwt_plan_t plan, int64_t batch, int n, const void* re,
+                      const void* im);
+
+/* Number of HBM passes one fwt_execute of this plan makes (each reads and
+ * writes the state once).  Returns FWT_OK or FWT_EINVAL (null argument). */
+int fwt_plan_num_passes(fwt_plan_t plan, int* out_passes);
+
+/* Bit count of pass i (the pass on the lowest bits is i = 0).  Returns
+ * FWT_OK or FWT_EINVAL (null argument, i out of range). */
+int fwt_plan_pass_bits(fwt_plan_t plan, int i, int* out_bits);
+
+/* Release a plan; NULL is a no-op.  Returns FWT_OK. */
+int fwt_plan_destroy(fwt_plan_t plan);
+
+/* Static description of a status code (never NULL). */
+const char* fwt_strerror(int status);
+
+/* HIP error code recorded by the most recent FWT_EHIP on the calling
+ * thread (hipSuccess if none). */
+int fwt_last_hip_error(void);
+
+/* Measurement aid, not part of the transform: copies `bytes` (a multiple
+ * of 16) from src to dst with the same 16-byte streaming access the passes
+ * use, so a benchmark can price one read plus one write of the state.
+ * Both device buffers 16-byte aligned and non-overlapping.  Returns
+ * FWT_OK, FWT_EINVAL, FWT_EALIGN or FWT_EHIP. */
+int fwt_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSE_FWT_H */

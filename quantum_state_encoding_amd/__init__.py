@@ -1,0 +1,263 @@
+"""Batched in-place Walsh-Hadamard transform on MI355X (gfx950).
+
+A thin ctypes binding over ``libfwt.so`` (the C ABI declared in
+``include/fwt.h``).  This module only marshals arguments: every step of the
+transform runs in the library's HIP kernels.  PyTorch is used for device
+memory and streams only.  If the library has not been built the import
+still succeeds, but every call raises: there is no fallback.
+
+Example::
+
+    import torch, quantum_state_encoding_amd as qse
+    re = torch.randn(64, 4096, device="cuda"); im = torch.randn_like(re)
+    plan = qse.Plan(12, "f32")
+    plan.execute(re, im, normalize=True)   # in place, on the current stream
+"""
+import ctypes
+import os
+
+__all__ = ["Plan", "FwtError", "execute", "stream_copy", "library_path", "load_library",
+           "PATH_AUTO", "PATH_SINGLE_BLOCK", "PATH_MULTIPASS", "PATH_MFMA_ABLATION",
+           "FWT_OK", "FWT_EINVAL", "FWT_EALIGN", "FWT_EUNSUPPORTED", "FWT_EHIP",
+           "FWT_ENOMEM", "EXPORTED_SYMBOLS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfwt.so")
+
+FWT_OK, FWT_EINVAL, FWT_EALIGN, FWT_EUNSUPPORTED, FWT_EHIP, FWT_ENOMEM = 0, -1, -2, -3, -4, -5
+PATH_AUTO, PATH_SINGLE_BLOCK, PATH_MULTIPASS, PATH_MFMA_ABLATION = 0, 1, 2, 3
+_DTYPES = {"f32": 0, "f64": 1}
+
+# Every symbol include/fwt.h declares.
+EXPORTED_SYMBOLS = ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create_tuned",
+                    "fwt_execute", "fwt_execute_pass", "fwt_execute_check",
+                    "fwt_plan_num_passes", "fwt_plan_pass_bits",
+                    "fwt_plan_destroy", "fwt_strerror", "fwt_last_hip_error",
+                    "fwt_stream_copy")
+
+_lib = None
+
+
+class FwtError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status, what):
+        self.status = status
+        msg = "%s failed: %s (status %d)" % (what, _strerror(status), status)
+        if status == FWT_EHIP:
+            msg += ", HIP error %d" % load_library().fwt_last_hip_error()
+        super().__init__(msg)
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libfwt.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libfwt.so not found at %s: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'` or "
+                          "`python quantum_state_encoding_amd/build.py`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    pi = ctypes.POINTER(ctypes.c_int)
+    lib.fwt_plan_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32]
+    lib.fwt_plan_create_split.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi]
+    lib.fwt_plan_create_tuned.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi, pi, pi]
+    lib.fwt_execute.argtypes = [vp, i64, i32, vp, vp, i32, vp]
+    lib.fwt_execute_pass.argtypes = [vp, i32, i64, i32, vp, vp, i32, vp]
+    lib.fwt_execute_check.argtypes = [vp, i64, i32, vp, vp]
+    lib.fwt_plan_num_passes.argtypes = [vp, pi]
+    lib.fwt_plan_pass_bits.argtypes = [vp, i32, pi]
+    lib.fwt_plan_destroy.argtypes = [vp]
+    lib.fwt_strerror.argtypes = [i32]
+    lib.fwt_strerror.restype = ctypes.c_char_p
+    lib.fwt_last_hip_error.argtypes = []
+    lib.fwt_stream_copy.argtypes = [vp, vp, i64, vp]
+    for name in ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create_tuned",
+                 "fwt_execute", "fwt_execute_pass", "fwt_execute_check",
+                 "fwt_plan_num_passes", "fwt_plan_pass_bits", "fwt_plan_destroy", "fwt_last_hip_error",
+                 "fwt_stream_copy"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def _strerror(status):
+    return load_library().fwt_strerror(status).decode()
+
+
+def _int_array(vals):
+    if vals is None:
+        return None
+    return (ctypes.c_int * len(vals))(*[int(v) for v in vals])
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """A plan for 2^n-amplitude vectors of dtype "f32" or "f64".
+
+    ``split`` (bit counts, lowest index bits first) forces a Kronecker
+    split; ``eb``/``gbits`` (one entry per pass, -1 = default) force the
+    register-round width and column-group count of each pass (tuning).
+    """
+
+    def __init__(self, n, dtype="f32", path=PATH_AUTO, split=None, eb=None, gbits=None):
+        lib = load_library()
+        if dtype not in _DTYPES:
+            raise ValueError("dtype must be 'f32' or 'f64'")
+        self.n, self.dtype = int(n), dtype
+        h = ctypes.c_void_p()
+        if split is None and eb is None and gbits is None:
+            st = lib.fwt_plan_create(ctypes.byref(h), self.n, _DTYPES[dtype], int(path))
+        elif eb is None and gbits is None:
+            st = lib.fwt_plan_create_split(ctypes.byref(h), self.n, _DTYPES[dtype],
+                                           len(split), _int_array(split))
+        else:
+            if split is None:
+                raise ValueError("eb/gbits need an explicit split")
+            st = lib.fwt_plan_create_tuned(ctypes.byref(h), self.n, _DTYPES[dtype],
+                                           len(split), _int_array(split), _int_array(eb),
+                                           _int_array(gbits))
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_plan_create(n=%d, %s)" % (self.n, dtype))
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def num_passes(self):
+        out = ctypes.c_int()
+        st = load_library().fwt_plan_num_passes(self._h, ctypes.byref(out))
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_plan_num_passes")
+        return out.value
+
+    @property
+    def pass_bits(self):
+        out, lib, bits = ctypes.c_int(), load_library(), []
+        for i in range(self.num_passes):
+            st = lib.fwt_plan_pass_bits(self._h, i, ctypes.byref(out))
+            if st != FWT_OK:
+                raise FwtError(st, "fwt_plan_pass_bits")
+            bits.append(out.value)
+        return bits
+
+    def execute(self, re, im=None, normalize=True, stream=None):
+        """Transform torch device tensors re (and im) in place.
+
+        Both must be contiguous, of the plan's dtype, on the current device,
+        with numel a multiple of 2^n.  Runs asynchronously on ``stream``
+        (default: torch's current stream).
+        """
+        import torch
+        want = torch.float32 if self.dtype == "f32" else torch.float64
+        N = 1 << self.n
+        for name, t in (("re", re), ("im", im)):
+            if t is None:
+                continue
+            if not t.is_cuda:
+                raise ValueError("%s must be a device tensor" % name)
+            if t.dtype != want:
+                raise ValueError("%s must be %s" % (name, want))
+            if not t.is_contiguous():
+                raise ValueError("%s must be contiguous" % name)
+            if t.numel() % N:
+                raise ValueError("%s.numel() is not a multiple of 2^%d" % (name, self.n))
+        if im is not None and im.numel() != re.numel():
+            raise ValueError("re and im must have the same number of elements")
+        batch = re.numel() // N
+        st = load_library().fwt_execute(self._h, batch, self.n, ctypes.c_void_p(re.data_ptr()),
+                                        ctypes.c_void_p(im.data_ptr() if im is not None else None),
+                                        1 if normalize else 0, _stream_handle(stream))
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_execute")
+        return re, im
+
+    def bind(self, re, im=None, normalize=True, stream=None):
+        """A zero-argument callable that enqueues fwt_execute on these
+        tensors with the arguments marshalled once (for tight loops)."""
+        self.execute(re, im, normalize, stream)      # validates the tensors once
+        fn = load_library().fwt_execute
+        args = (self._h, re.numel() >> self.n, self.n, ctypes.c_void_p(re.data_ptr()),
+                ctypes.c_void_p(im.data_ptr() if im is not None else None),
+                1 if normalize else 0, _stream_handle(stream))
+
+        def call():
+            st = fn(*args)
+            if st != FWT_OK:
+                raise FwtError(st, "fwt_execute")
+        return call
+
+    def execute_pass(self, i, re, im=None, normalize=True, stream=None):
+        """Enqueue only pass i (see fwt_execute_pass) on torch tensors."""
+        N = 1 << self.n
+        batch = re.numel() // N
+        st = load_library().fwt_execute_pass(
+            self._h, int(i), batch, self.n, ctypes.c_void_p(re.data_ptr()),
+            ctypes.c_void_p(im.data_ptr() if im is not None else None),
+            1 if normalize else 0, _stream_handle(stream))
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_execute_pass")
+        return re, im
+
+    def execute_raw(self, batch, re_ptr, im_ptr, normalize, stream_ptr=0):
+        """Call fwt_execute on raw device addresses; returns the status."""
+        return load_library().fwt_execute(self._h, int(batch), self.n, ctypes.c_void_p(re_ptr),
+                                          ctypes.c_void_p(im_ptr), int(normalize),
+                                          ctypes.c_void_p(stream_ptr))
+
+    def check_raw(self, batch, re_ptr, im_ptr):
+        """Call fwt_execute_check on raw addresses; returns the status."""
+        return load_library().fwt_execute_check(self._h, int(batch), self.n,
+                                                ctypes.c_void_p(re_ptr), ctypes.c_void_p(im_ptr))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            load_library().fwt_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def execute(re, im=None, n=None, normalize=True, stream=None, path=PATH_AUTO):
+    """One-shot transform of the last dimension (2^n) of re/im in place."""
+    if n is None:
+        N = re.shape[-1]
+        n = N.bit_length() - 1
+        if (1 << n) != N:
+            raise ValueError("last dimension %d is not a power of two" % N)
+    dtype = {"torch.float32": "f32", "torch.float64": "f64"}.get(str(re.dtype))
+    if dtype is None:
+        raise ValueError("re must be float32 or float64")
+    return Plan(n, dtype, path).execute(re, im, normalize, stream)
+
+
+def stream_copy(dst, src, stream=None):
+    """Copy src to dst (device tensors of equal byte size) with the
+    library's streaming copy kernel (measurement aid)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("size mismatch")
+    st = load_library().fwt_stream_copy(ctypes.c_void_p(dst.data_ptr()),
+                                        ctypes.c_void_p(src.data_ptr()), nbytes,
+                                        _stream_handle(stream))
+    if st != FWT_OK:
+        raise FwtError(st, "fwt_stream_copy")
+    return dst

@@ -1,0 +1,81 @@
+// Internal interface between the planner (fwt_api.cpp) and the gfx950
+// kernels (fwt_kernels.hip).  Not installed; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace qse {
+
+// Runtime description of one tile pass.  A pass transforms the index bits
+// [lo, lo + k) of every real vector.  It views the vector as
+// [outer][2^k rows][2^lo columns] and processes tiles of all 2^k rows by
+// G = 2^gbits 16-byte column groups.  A row pass (lo = 0) instead views its
+// 2^k contiguous elements as 2^(k - vb) rows of one 16-byte vector
+// (vb = log2 of elements per vector) and also transforms the vb bits
+// inside each vector.
+struct TileArgs {
+    int64_t tiles;       // tiles per component (real or imaginary buffer)
+    int64_t wg_count;    // workgroups needed: ceil(tiles / tiles per workgroup)
+    int64_t tile0;       // first tile of this launch (set by the launcher)
+    int lo;              // log2 of the element stride between rows (col passes)
+    int nblk_bits;       // log2 of column blocks per outer index (col passes)
+    int tpw_bits;        // log2 of tiles per workgroup
+    int tt_bits;         // log2 of threads per tile
+    int do_scale;        // multiply by `scale` before the final store
+    double scale;        // 2^(-n/2) rounded to the element type
+};
+
+// Kernel variant: element type, row bits KR, register-round bits EB,
+// column-group bits GB, and whether it is a row (contiguous) pass.
+struct KernelKey {
+    int f64;   // 0: float, 1: double
+    int kr;    // log2 rows per tile
+    int eb;    // log2 16-byte vectors per thread per round
+    int gb;    // log2 16-byte column groups per tile (0 for row passes)
+    int row;   // 1: contiguous row pass
+};
+
+// Number of register rounds of a (kr, eb) kernel: ceil(kr / eb), at least 1.
+__host__ __device__ constexpr int rounds_of(int kr, int eb)
+{
+    return kr <= eb ? 1 : 1 + (kr - eb + eb - 1) / eb;
+}
+
+// Whether a (kr, eb, gb) tile kernel stores from its load layout after one
+// more LDS exchange: when the last round's layout gives runs of consecutive
+// lanes shorter than 128 bytes and the load layout gives longer ones.  The
+// run of the layout whose register bits start at row bit a is 16 * 2^(gb+a)
+// bytes.
+__host__ __device__ constexpr bool store_back(int kr, int eb, int gb)
+{
+    return rounds_of(kr, eb) > 1 &&
+           (16 << (gb + (kr - eb * rounds_of(kr, eb) > 0 ? kr - eb * rounds_of(kr, eb) : 0))) <
+               128 &&
+           (16 << (gb + kr - eb)) >
+               (16 << (gb + (kr - eb * rounds_of(kr, eb) > 0 ? kr - eb * rounds_of(kr, eb) : 0)));
+}
+
+// True if the variant is compiled into this library.
+bool kernel_available(const KernelKey& key);
+
+// Sets the dynamic-LDS limit of every compiled variant on the current
+// device.  Returns hipSuccess or the first error.
+hipError_t kernels_init_device();
+
+// Enqueue one tile pass.  `re` and `im` (im may be null) are device
+// pointers; ncomp = 1 or 2.
+hipError_t launch_tile_pass(const KernelKey& key, void* re, void* im, int ncomp,
+                            const TileArgs& args, unsigned block, size_t lds_bytes,
+                            hipStream_t stream);
+
+// Enqueue the two-element transform used for fp32 vectors of 2 elements
+// (n = 1): pairs (a, b) -> (a + b, a - b) * scale.
+hipError_t launch_pair_f32(float* re, float* im, int64_t pairs, int do_scale,
+                           float scale, hipStream_t stream);
+
+// Enqueue a 16-byte streaming copy of `bytes` (a multiple of 16).
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes,
+                              hipStream_t stream);
+
+}  // namespace qse

@@ -1,0 +1,453 @@
+// gfx950 kernels for the batched in-place Walsh-Hadamard transform.
+//
+// Every pass is one launch of tile_kernel.  A pass owns the index bits
+// [lo, lo + k) of each real vector (the Kronecker factor H_{2^k} acting on
+// those bits, Apache Mahout pull request "[QDP] [feature] Pr4 kronecker
+// fwt", sections "Why" and "How"; iThome "Day 18" native-FWT article,
+// section "Kronecker block GEMM idea").  Its work is cut into tiles: all
+// 2^k "rows" (the values of the pass's bits) times G 16-byte column
+// groups.  A tile is read from HBM once, transformed on chip, and written
+// back to the same place, so a pass costs exactly one read and one write of
+// the state, and tiles are disjoint, so in-place passes are race-free.
+//
+// On chip, each thread holds E = 2^EB 16-byte vectors (rows of one column
+// group).  The add/subtract stages (one per index bit, iThome article,
+// section "Tensor Core wants matrix multiplication") whose bits are
+// currently "register bits" run as butterflies on those registers; then
+// the tile is exchanged through LDS so that the next EB row bits become
+// register bits (the shared-memory swizzle of the article's introduction,
+// done here by padding the 16-byte slots, see LdsLayout).  Column groups never
+// mix, so an exchange moves whole 16-byte vectors.  Row passes (lo = 0) see
+// the 2^k contiguous elements as 2^(k - vb) rows of a single vector and do
+// the vb in-vector bits in registers as well.
+//
+// Global accesses are 16-byte vector loads and stores in which consecutive
+// lanes touch consecutive 16-byte chunks (consecutive rows of a row pass,
+// or the G column groups of a row of a column pass).
+#include <hip/hip_runtime.h>
+
+#include <vector>
+
+#include "fwt_internal.h"
+
+namespace qse {
+namespace {
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<float> {
+    typedef float type __attribute__((ext_vector_type(4)));
+    static constexpr int WB = 2;  // log2 elements per 16-byte vector
+};
+template <>
+struct Vec<double> {
+    typedef double type __attribute__((ext_vector_type(2)));
+    static constexpr int WB = 1;
+};
+
+template <typename V>
+__device__ __forceinline__ void butterfly(V& a, V& b)
+{
+    const V s = a + b;
+    const V d = a - b;
+    a = s;
+    b = d;
+}
+
+// Stages on the vb index bits inside one vector (row passes only).
+__device__ __forceinline__ void in_vector(Vec<float>::type& v)
+{
+    const float s0 = v.x + v.y, d0 = v.x - v.y;   // bit 0: (0,1), (2,3)
+    const float s1 = v.z + v.w, d1 = v.z - v.w;
+    v.x = s0 + s1;                                // bit 1: (0,2), (1,3)
+    v.z = s0 - s1;
+    v.y = d0 + d1;
+    v.w = d0 - d1;
+}
+__device__ __forceinline__ void in_vector(Vec<double>::type& v)
+{
+    const double s = v.x + v.y, d = v.x - v.y;
+    v.x = s;
+    v.y = d;
+}
+
+// Butterflies on register bits [0, NB) of x[0..E).
+template <int NB, int E, typename V>
+__device__ __forceinline__ void register_stages(V* x)
+{
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            if (!(j & (1 << b)))
+                butterfly(x[j], x[j | (1 << b)]);
+        }
+    }
+}
+
+// Row held by thread tau in register j when the register bits are the EB
+// row bits starting at A: the low A row bits come from tau's low bits, the
+// row bits above A + EB from tau's high bits.  Split into the part that
+// depends on the thread and the part that depends on the register.
+template <int A, int EB>
+__device__ __forceinline__ int row_thread_part(int tau)
+{
+    return (tau & ((1 << A) - 1)) | ((tau >> A) << (A + EB));
+}
+
+// First row bit held in registers in round r.
+__host__ __device__ constexpr int round_lo(int kr, int eb, int r)
+{
+    return kr - eb * (r + 1) > 0 ? kr - eb * (r + 1) : 0;
+}
+
+// LDS layout of a tile: 16-byte slot s = (row << GB) | g, stored at
+// s + (s >> P) with P = EB + GB, i.e. one pad slot after every 2^P
+// slots.  For every layout of the kernel, the 8 (or 16) lanes that the LDS
+// serves together then fall on distinct bank groups: lanes holding
+// consecutive slots stay consecutive, and lanes whose slots are 2^P apart
+// are shifted by one slot each.  Because the thread part and the register
+// part of a slot are disjoint bit fields, s + (s >> P) splits into a
+// per-thread base plus a per-register constant, so each access is one
+// address register plus an immediate offset.
+template <int A, int EB, int GB>
+struct LdsLayout {
+    static constexpr int P = EB + GB;
+    int base;  // padded slot of register 0 for this thread
+    __device__ __forceinline__ LdsLayout(int tau, int g)
+    {
+        const int s = (row_thread_part<A, EB>(tau) << GB) | g;
+        base = s + (s >> P);
+    }
+    // Padded offset of register j from register 0 (a compile-time constant
+    // once j is unrolled).
+    __device__ __forceinline__ static constexpr int offset(int j)
+    {
+        return ((j << A) << GB) + (((j << A) << GB) >> P);
+    }
+};
+
+template <typename V, int AF, int AT, int EB, int GB>
+__device__ __forceinline__ void exchange(V* x, V* L, int tau, int g)
+{
+    constexpr int E = 1 << EB;
+    const LdsLayout<AF, EB, GB> from(tau, g);
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        L[from.base + LdsLayout<AF, EB, GB>::offset(j)] = x[j];
+    __syncthreads();
+    const LdsLayout<AT, EB, GB> to(tau, g);
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        x[j] = L[to.base + LdsLayout<AT, EB, GB>::offset(j)];
+    __syncthreads();
+}
+
+// Rounds 1 .. NR-1: exchange into round R's layout, then the stages on the
+// row bits [round_lo(R), round_lo(R-1)) that no earlier round did.
+template <typename V, int KR, int EB, int GB, int R, int NR>
+struct Rounds {
+    __device__ __forceinline__ static void run(V* x, V* L, int tau, int g)
+    {
+        constexpr int AP = round_lo(KR, EB, R - 1);
+        constexpr int AC = round_lo(KR, EB, R);
+        exchange<V, AP, AC, EB, GB>(x, L, tau, g);
+        register_stages<AP - AC, (1 << EB)>(x);
+        Rounds<V, KR, EB, GB, R + 1, NR>::run(x, L, tau, g);
+    }
+};
+template <typename V, int KR, int EB, int GB, int NR>
+struct Rounds<V, KR, EB, GB, NR, NR> {
+    __device__ __forceinline__ static void run(V*, V*, int, int) {}
+};
+
+// Global element offset (relative to the workgroup's base) of register j
+// in the layout whose register bits start at row bit A.
+template <int A, int EB>
+struct GlobalLayout {
+    uint32_t base;     // bytes, thread part
+    uint32_t jstride;  // bytes between consecutive registers
+    __device__ __forceinline__ GlobalLayout(uint32_t lane_bytes, int tau, uint32_t row_bytes)
+        : base(lane_bytes + (uint32_t)row_thread_part<A, EB>(tau) * row_bytes),
+          jstride(row_bytes << A)
+    {
+    }
+};
+
+template <typename V>
+__device__ __forceinline__ V load16(const unsigned char* p, uint32_t off)
+{
+    return *reinterpret_cast<const V*>(p + off);
+}
+template <typename V>
+__device__ __forceinline__ void store16(unsigned char* p, uint32_t off, const V& v)
+{
+    *reinterpret_cast<V*>(p + off) = v;
+}
+
+template <typename T, int KR, int EB, int GB, bool ROW>
+__global__ void __launch_bounds__(EB >= 5 ? 512 : 1024)
+    tile_kernel(T* __restrict__ re, T* __restrict__ im, TileArgs a)
+{
+    using V = typename Vec<T>::type;
+    constexpr int WB = Vec<T>::WB;
+    constexpr int E = 1 << EB;
+    constexpr int NR = KR <= EB ? 1 : 1 + (KR - EB + EB - 1) / EB;
+    constexpr int A0 = round_lo(KR, EB, 0);
+    constexpr int AL = round_lo(KR, EB, NR - 1);
+    static_assert(EB <= KR || (KR == 0 && EB == 0), "EB must not exceed KR");
+    static_assert(!ROW || GB == 0, "row passes have one column group");
+    // Store from the load layout (one more exchange) when the last round's
+    // layout would give consecutive lanes runs shorter than 128 bytes.
+    constexpr bool STORE_BACK = store_back(KR, EB, GB);
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+
+    const int tid = threadIdx.x;
+    const int tl = tid >> a.tt_bits;                  // tile within the workgroup
+    const int tt = tid & ((1 << a.tt_bits) - 1);      // thread within the tile
+    const int g = tt & ((1 << GB) - 1);               // column group
+    const int tau = tt >> GB;                         // row-thread index
+    constexpr int tile_slots = 1 << (KR + GB);
+    V* const L = reinterpret_cast<V*>(lds_raw) + tl * (tile_slots + (tile_slots >> (EB + GB)));
+
+    // Workgroup-uniform base of its first tile; lanes address from it with
+    // 32-bit byte offsets (a pass's tile span is below 4 GiB).
+    const int64_t t0 = a.tile0 + ((int64_t)blockIdx.x << a.tpw_bits);
+    int64_t base;
+    uint32_t lane_bytes;
+    uint32_t row_bytes;
+    if (ROW) {
+        base = t0 << (KR + WB);
+        lane_bytes = (uint32_t)tl << (KR + WB + (sizeof(T) == 8 ? 3 : 2));
+        row_bytes = 16;
+    } else {
+        const int64_t blk_mask = ((int64_t)1 << a.nblk_bits) - 1;
+        base = ((t0 >> a.nblk_bits) << (a.lo + KR)) + ((t0 & blk_mask) << (GB + WB));
+        const uint32_t tlo = (uint32_t)tl >> a.nblk_bits;
+        const uint32_t tlb = (uint32_t)tl & (uint32_t)blk_mask;
+        lane_bytes = ((tlo << (a.lo + KR)) + (tlb << (GB + WB))) * (uint32_t)sizeof(T) +
+                     ((uint32_t)g << 4);
+        row_bytes = (uint32_t)sizeof(T) << a.lo;
+    }
+    unsigned char* const p =
+        reinterpret_cast<unsigned char*>((blockIdx.y ? im : re) + base);
+    const bool active = t0 + tl < a.tiles;
+
+    V x[E];
+    const GlobalLayout<A0, EB> gl0(lane_bytes, tau, row_bytes);
+    if (active) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] = load16<V>(p, gl0.base + (uint32_t)j * gl0.jstride);
+    } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] = V{};
+    }
+
+    if (ROW) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            in_vector(x[j]);
+    }
+    register_stages<EB, E>(x);
+    Rounds<V, KR, EB, GB, 1, NR>::run(x, L, tau, g);
+
+    if (a.do_scale) {
+        const T scale = (T)a.scale;
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] *= scale;
+    }
+
+    if constexpr (STORE_BACK) {
+        exchange<V, AL, A0, EB, GB>(x, L, tau, g);
+        if (active) {
+#pragma unroll
+            for (int j = 0; j < E; ++j)
+                store16<V>(p, gl0.base + (uint32_t)j * gl0.jstride, x[j]);
+        }
+    } else if (active) {
+        const GlobalLayout<AL, EB> gll(lane_bytes, tau, row_bytes);
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            store16<V>(p, gll.base + (uint32_t)j * gll.jstride, x[j]);
+    }
+}
+
+__global__ void __launch_bounds__(256)
+    pair_f32_kernel(float* __restrict__ re, float* __restrict__ im, int64_t pairs, int do_scale,
+                    float scale)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    f2* const buf = reinterpret_cast<f2*>(blockIdx.y ? im : re);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pairs; i += stride) {
+        const f2 v = buf[i];
+        f2 r;
+        r.x = v.x + v.y;
+        r.y = v.x - v.y;
+        if (do_scale)
+            r *= scale;
+        buf[i] = r;
+    }
+}
+
+// Streaming copy: each workgroup moves 256 threads x 8 vectors of 16 bytes,
+// all loads issued before the stores, like a pass's tile.
+__global__ void __launch_bounds__(256)
+    stream_copy_kernel(int4* __restrict__ dst, const int4* __restrict__ src, int64_t nvec)
+{
+    constexpr int U = 8;
+    const int64_t chunk = (int64_t)blockDim.x * U;
+    for (int64_t b = (int64_t)blockIdx.x * chunk; b < nvec; b += (int64_t)gridDim.x * chunk) {
+        const int64_t i0 = b + threadIdx.x;
+        if (b + chunk <= nvec) {
+            int4 v0 = src[i0], v1 = src[i0 + 256], v2 = src[i0 + 512], v3 = src[i0 + 768];
+            int4 v4 = src[i0 + 1024], v5 = src[i0 + 1280], v6 = src[i0 + 1536];
+            int4 v7 = src[i0 + 1792];
+            dst[i0] = v0;
+            dst[i0 + 256] = v1;
+            dst[i0 + 512] = v2;
+            dst[i0 + 768] = v3;
+            dst[i0 + 1024] = v4;
+            dst[i0 + 1280] = v5;
+            dst[i0 + 1536] = v6;
+            dst[i0 + 1792] = v7;
+        } else {
+            for (int64_t i = i0; i < nvec; i += blockDim.x)
+                dst[i] = src[i];
+        }
+    }
+}
+
+struct Entry {
+    KernelKey key;
+    const void* fn;
+};
+
+template <typename T, bool ROW, int KR, int EB, int GB>
+void add_variant(std::vector<Entry>& v)
+{
+    v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, ROW ? 1 : 0},
+                 reinterpret_cast<const void*>(&tile_kernel<T, KR, EB, GB, ROW>)});
+}
+
+// Column groups 2^GB for GB in [0, GBMAX] whose tile fits 160 KiB of LDS
+// and 1024 (EB <= 4) or 512 (EB = 5) threads.
+template <typename T, bool ROW, int KR, int EB, int GB>
+void add_groups(std::vector<Entry>& v)
+{
+    constexpr long slots = 1L << (KR + GB);
+    constexpr long lds = 16 * (slots + (slots >> (EB + GB)));
+    constexpr int max_tt_bits = EB >= 5 ? 9 : 10;
+    if constexpr ((KR <= EB || lds <= 160 * 1024) && (KR - EB + GB) <= max_tt_bits)
+        add_variant<T, ROW, KR, EB, GB>(v);
+    if constexpr (!ROW && GB < 4)
+        add_groups<T, ROW, KR, EB, GB + 1>(v);
+}
+
+// Variants for every KR in [KRMIN, KR]: EB = min(KR, 4), plus EB = 3 and
+// (row passes) EB = 5 where they fit.
+template <typename T, bool ROW, int KR, int KRMIN>
+struct Register {
+    static void add(std::vector<Entry>& v)
+    {
+        add_groups<T, ROW, KR, (KR < 4 ? KR : 4), 0>(v);
+        if constexpr (ROW && KR >= 5)
+            add_groups<T, ROW, KR, 5, 0>(v);
+        if constexpr (KR >= 4)
+            add_groups<T, ROW, KR, 3, 0>(v);
+        if constexpr (KR > KRMIN)
+            Register<T, ROW, KR - 1, KRMIN>::add(v);
+    }
+};
+
+const std::vector<Entry>& table()
+{
+    static const std::vector<Entry> t = [] {
+        std::vector<Entry> v;
+        Register<float, true, 13, 0>::add(v);
+        Register<double, true, 13, 0>::add(v);
+        Register<float, false, 12, 1>::add(v);
+        Register<double, false, 12, 1>::add(v);
+        return v;
+    }();
+    return t;
+}
+
+const void* find(const KernelKey& k)
+{
+    for (const Entry& e : table())
+        if (e.key.f64 == k.f64 && e.key.kr == k.kr && e.key.eb == k.eb && e.key.gb == k.gb &&
+            e.key.row == k.row)
+            return e.fn;
+    return nullptr;
+}
+
+}  // namespace
+
+bool kernel_available(const KernelKey& key) { return find(key) != nullptr; }
+
+hipError_t kernels_init_device()
+{
+    for (const Entry& e : table()) {
+        hipError_t err = hipFuncSetAttribute(e.fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             160 * 1024);
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_tile_pass(const KernelKey& key, void* re, void* im, int ncomp,
+                            const TileArgs& args, unsigned block, size_t lds_bytes,
+                            hipStream_t stream)
+{
+    const void* fn = find(key);
+    if (!fn)
+        return hipErrorInvalidDeviceFunction;
+    // One workgroup per group of 2^tpw_bits tiles; grids beyond 2^30
+    // workgroups are split into several launches.
+    constexpr int64_t kMaxGrid = (int64_t)1 << 30;
+    TileArgs a = args;
+    for (int64_t w0 = 0; w0 < args.wg_count; w0 += kMaxGrid) {
+        const int64_t nw = args.wg_count - w0 < kMaxGrid ? args.wg_count - w0 : kMaxGrid;
+        a.tile0 = w0 << args.tpw_bits;
+        void* kargs[] = {&re, &im, &a};
+        const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nw, (unsigned)ncomp, 1),
+                                             dim3(block, 1, 1), kargs, lds_bytes, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_pair_f32(float* re, float* im, int64_t pairs, int do_scale, float scale,
+                           hipStream_t stream)
+{
+    const int64_t blocks64 = (pairs + 255) / 256;
+    const unsigned blocks = (unsigned)(blocks64 < 65536 ? (blocks64 > 0 ? blocks64 : 1) : 65536);
+    hipLaunchKernelGGL(pair_f32_kernel, dim3(blocks, im ? 2 : 1, 1), dim3(256, 1, 1), 0, stream,
+                       re, im, pairs, do_scale, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream)
+{
+    const int64_t nvec = bytes / 16;
+    const int64_t chunk = 256 * 8;
+    int64_t blocks64 = (nvec + chunk - 1) / chunk;
+    if (blocks64 < 1)
+        blocks64 = 1;
+    if (blocks64 > (1 << 30))
+        blocks64 = 1 << 30;
+    hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks64, 1, 1), dim3(256, 1, 1), 0,
+                       stream, reinterpret_cast<int4*>(dst), reinterpret_cast<const int4*>(src),
+                       nvec);
+    return hipGetLastError();
+}
+
+}  // namespace qse

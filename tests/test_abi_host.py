@@ -1,0 +1,175 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+declared symbol, plans split n as documented, and fwt_execute rejects bad
+arguments before it makes any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantum_state_encoding_amd as qse
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fwt.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fwt_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(qse.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_every_status(lib):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.fwt_strerror(st).decode() != "unknown status"
+    assert lib.fwt_strerror(7).decode() == "unknown status"
+
+
+def _create(lib, n, dtype=0, path=0):
+    h = ctypes.c_void_p()
+    st = lib.fwt_plan_create(ctypes.byref(h), n, dtype, path)
+    return st, h
+
+
+def _split(lib, n, dtype, bits, eb=None, gbits=None):
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_int * len(bits))(*bits)
+    if eb is None and gbits is None:
+        st = lib.fwt_plan_create_split(ctypes.byref(h), n, dtype, len(bits), arr)
+    else:
+        e = (ctypes.c_int * len(bits))(*eb) if eb is not None else None
+        g = (ctypes.c_int * len(bits))(*gbits) if gbits is not None else None
+        st = lib.fwt_plan_create_tuned(ctypes.byref(h), n, dtype, len(bits), arr, e, g)
+    if st == 0:
+        lib.fwt_plan_destroy(h)
+    return st
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_default_plans_cover_all_bits(dtype, lib):
+    nmax = 30 if dtype == "f32" else 29
+    for n in range(0, nmax + 1):
+        p = qse.Plan(n, dtype)
+        bits = p.pass_bits
+        assert sum(bits) == n
+        assert p.num_passes == len(bits)
+        if n <= 24:
+            assert p.num_passes <= 2, (n, bits)
+        p.close()
+
+
+def test_plan_shapes_of_the_workloads(lib):
+    assert qse.Plan(10, "f32").pass_bits == [10]
+    assert qse.Plan(12, "f32").pass_bits == [12]
+    assert qse.Plan(14, "f32").pass_bits == [14]
+    assert qse.Plan(14, "f32", split=(7, 7)).pass_bits == [7, 7]
+    assert qse.Plan(20, "f32").num_passes == 2
+    assert qse.Plan(24, "f64").num_passes == 2
+    assert qse.Plan(14, "f32", path=qse.PATH_MULTIPASS).pass_bits == [7, 7]
+    assert qse.Plan(15, "f32", path=qse.PATH_SINGLE_BLOCK).pass_bits == [15]
+
+
+def test_plan_create_errors(lib):
+    assert _create(lib, -1)[0] == qse.FWT_EINVAL
+    assert _create(lib, 31)[0] == qse.FWT_EINVAL
+    assert _create(lib, 10, dtype=2)[0] == qse.FWT_EINVAL
+    assert _create(lib, 10, path=9)[0] == qse.FWT_EINVAL
+    assert _create(lib, 10, path=qse.PATH_MFMA_ABLATION)[0] == qse.FWT_EUNSUPPORTED
+    assert _create(lib, 16, 0, qse.PATH_SINGLE_BLOCK)[0] == qse.FWT_EUNSUPPORTED
+    assert _create(lib, 15, 1, qse.PATH_SINGLE_BLOCK)[0] == qse.FWT_EUNSUPPORTED
+    assert _create(lib, 30, 1)[0] == qse.FWT_EUNSUPPORTED
+    assert lib.fwt_plan_create(None, 10, 0, 0) == qse.FWT_EINVAL
+
+
+def test_split_validation(lib):
+    assert _split(lib, 10, 0, [5, 5]) == 0
+    assert _split(lib, 10, 0, [2, 8]) == 0
+    assert _split(lib, 10, 0, [3, 3, 4]) == 0
+    assert _split(lib, 10, 0, [4, 4]) == qse.FWT_EINVAL        # sum != n
+    assert _split(lib, 10, 0, [1, 9]) == qse.FWT_EINVAL        # fp32 row pass needs 2 bits
+    assert _split(lib, 10, 1, [1, 9]) == 0                     # fp64 needs 1
+    assert _split(lib, 20, 0, [7, 13]) == qse.FWT_EINVAL       # column pass > 12 bits
+    assert _split(lib, 20, 0, [16, 4]) == qse.FWT_EINVAL       # row pass > 15 bits
+    assert _split(lib, 10, 0, [5, 0, 5]) == qse.FWT_EINVAL     # empty factor
+    assert _split(lib, 10, 0, [2, 2, 2, 2, 2]) == qse.FWT_EINVAL  # > 4 passes
+    h = ctypes.c_void_p()
+    assert lib.fwt_plan_create_split(ctypes.byref(h), 10, 0, 0, None) == qse.FWT_EINVAL
+    assert lib.fwt_plan_create_split(ctypes.byref(h), 10, 0, 2, None) == qse.FWT_EINVAL
+
+
+def test_tuned_validation(lib):
+    assert _split(lib, 16, 0, [8, 8], eb=[3, 4], gbits=[-1, 2]) == 0
+    assert _split(lib, 16, 0, [8, 8], eb=[5, 3], gbits=[0, 4]) == 0
+    assert _split(lib, 16, 0, [8, 8], eb=[9, 4]) == qse.FWT_EINVAL      # eb > kr
+    assert _split(lib, 16, 0, [8, 8], gbits=[1, 2]) == qse.FWT_EINVAL   # row pass G = 1
+    assert _split(lib, 16, 0, [8, 8], gbits=[0, 7]) == qse.FWT_EINVAL   # too many groups
+    assert _split(lib, 12, 0, [2, 10], gbits=[0, 1]) == qse.FWT_EINVAL  # only 1 group in a row
+    assert _split(lib, 24, 1, [12, 12], gbits=[0, 3]) == qse.FWT_EINVAL  # tile > 160 KiB
+
+
+def test_destroy(lib):
+    assert lib.fwt_plan_destroy(None) == 0
+    st, h = _create(lib, 8)
+    assert st == 0
+    assert lib.fwt_plan_destroy(h) == 0
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every case fails before any HIP call
+
+
+@pytest.fixture
+def plan10(lib):
+    p = qse.Plan(10, "f32")
+    yield p
+    p.close()
+
+
+def test_execute_rejects_before_any_hip_call(lib, plan10):
+    N = 1 << 10
+    ex = lambda *a: lib.fwt_execute(*a)
+    h = plan10.handle
+    assert ex(None, 1, 10, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_EINVAL
+    assert ex(h, 1, 10, None, FAKE, 1, None) == qse.FWT_EINVAL
+    assert ex(h, -1, 10, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_EINVAL
+    assert ex(h, 1, 11, FAKE, FAKE + 8 * N, 1, None) == qse.FWT_EINVAL
+    assert ex(h, 1, 10, FAKE + 4, FAKE + 4 * N, 1, None) == qse.FWT_EALIGN
+    assert ex(h, 1, 10, FAKE, FAKE + 4 * N + 8, 1, None) == qse.FWT_EALIGN
+    assert ex(h, 1, 10, FAKE, FAKE, 1, None) == qse.FWT_EINVAL
+    assert ex(h, 2, 10, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_EINVAL   # overlap
+    assert ex(h, 2, 10, FAKE + 4 * N, FAKE, 1, None) == qse.FWT_EINVAL   # overlap
+    assert ex(h, 1 << 62, 10, FAKE, FAKE + 16, 1, None) == qse.FWT_EINVAL  # size overflow
+    # batch 0 is a no-op that touches nothing
+    assert ex(h, 0, 10, FAKE, FAKE + 16, 1, None) == qse.FWT_OK
+    assert lib.fwt_execute_check(h, 1, 10, FAKE + 4, None) == qse.FWT_EALIGN
+
+
+def test_n0_plan_is_a_noop(lib):
+    p = qse.Plan(0, "f64")
+    assert p.num_passes == 0
+    assert lib.fwt_execute(p.handle, 5, 0, FAKE, FAKE + 64, 1, None) == qse.FWT_OK
+
+
+def test_stream_copy_rejects_before_any_hip_call(lib):
+    assert lib.fwt_stream_copy(FAKE, FAKE + 4096, 100, None) == qse.FWT_EINVAL   # not x16
+    assert lib.fwt_stream_copy(FAKE + 8, FAKE + 4096, 64, None) == qse.FWT_EALIGN
+    assert lib.fwt_stream_copy(FAKE, FAKE + 32, 64, None) == qse.FWT_EINVAL      # overlap
+    assert lib.fwt_stream_copy(None, FAKE, 64, None) == qse.FWT_EINVAL
+    assert lib.fwt_stream_copy(FAKE, FAKE + 4096, 0, None) == qse.FWT_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib
+    monkeypatch.setattr(qse, "_lib", None)
+    monkeypatch.setattr(qse, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        qse.Plan(4, "f32")
+    importlib.reload(qse)

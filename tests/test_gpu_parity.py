@@ -1,0 +1,322 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars:
+* integer inputs (U{-8..8}) unnormalised, and normalised at even n:
+  bit-exact (every partial sum is an integer below 2^24, so every order of
+  evaluation is exact, and 2^(-n/2) is a power of two);
+* Gaussian unit-norm inputs, normalised: max |err| <= 1e-5 * ||x||_2
+  (fp32) or 1e-12 * ||x||_2 (fp64) per vector, ||x||_2 the complex 2-norm
+  of the input after the cast, the error measured against the fp64
+  oracle.
+The full-size workloads are checked on sampled vectors that the oracle
+transforms one by one, plus norm preservation (Parseval) of every vector.
+"""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import quantum_state_encoding_amd as qse
+import workloads
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+TOL = {"f32": 1e-5, "f64": 1e-12}
+
+
+def say(msg):
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def run(plan, re, im, normalize, stream=None):
+    tre, tim = to_dev(re), (to_dev(im) if im is not None else None)
+    plan.execute(tre, tim, normalize=normalize, stream=stream)
+    torch.cuda.synchronize()
+    return tre.cpu().numpy(), (tim.cpu().numpy() if tim is not None else None)
+
+
+def ints(shape, seed, dtype):
+    return np.random.default_rng(seed).integers(-8, 9, size=shape).astype(dtype)
+
+
+def assert_exact(got, re, n, normalize):
+    want = oracle.fwt(re, n, normalize)
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def assert_close(w_dtype, n, re, im, gre, gim, normalize=True):
+    ore, oim = oracle.fwt_complex(re, im, n, normalize)
+    re2, im2 = re.reshape(-1, 1 << n), im.reshape(-1, 1 << n)
+    for b in range(re2.shape[0]):
+        nx = np.sqrt(np.sum(re2[b].astype(np.float64) ** 2) + np.sum(im2[b].astype(np.float64) ** 2))
+        bound = TOL[w_dtype] * nx * (1.0 if normalize else 2.0 ** (n / 2))
+        err = max(np.abs(gre.reshape(re2.shape)[b] - ore.reshape(re2.shape)[b]).max(),
+                  np.abs(gim.reshape(re2.shape)[b] - oim.reshape(re2.shape)[b]).max())
+        assert err <= bound, "vector %d: max|err| %.3g > %.3g" % (b, err, bound)
+
+
+# ---- the small workloads, as configured ------------------------------------
+
+def test_n10_b8_integer_bit_exact():
+    w = workloads.WORKLOADS["n10_b8_f32_int"]
+    say(w.name)
+    re, im = workloads.gen(w)
+    gre, gim = run(qse.Plan(w.n, w.dtype), re, im, w.normalize)
+    assert_exact(gre, re, w.n, False)
+    assert_exact(gim, im, w.n, False)
+
+
+@pytest.mark.parametrize("name,split", [("n12_b64_f32", None), ("n14_b64_f32", (7, 7)),
+                                        ("n14_b64_f32", None)])
+def test_gaussian_workloads(name, split):
+    w = workloads.WORKLOADS[name]
+    say("%s split=%s" % (name, split))
+    re, im = workloads.gen(w)
+    plan = qse.Plan(w.n, w.dtype, split=split)
+    gre, gim = run(plan, re, im, True)
+    assert_close(w.dtype, w.n, re, im, gre, gim)
+
+
+# ---- exact sweeps over n, dtype and batch ------------------------------------
+
+@pytest.mark.parametrize("dtype,n", [("f32", n) for n in range(0, 21)] +
+                         [("f64", n) for n in range(0, 25)])
+def test_integer_sweep_auto_plan(dtype, n):
+    say("sweep %s n=%d" % (dtype, n))
+    batch = 3 if n <= 18 else 1
+    npd = np.float32 if dtype == "f32" else np.float64
+    re = ints((batch, 1 << n), 10_000 + n, npd)
+    im = ints((batch, 1 << n), 20_000 + n, npd)
+    plan = qse.Plan(n, dtype)
+    gre, gim = run(plan, re, im, False)
+    assert_exact(gre, re, n, False)
+    assert_exact(gim, im, n, False)
+    if n % 2 == 0:   # normalised by an exact power of two
+        gre, gim = run(plan, re, im, True)
+        assert_exact(gre, re, n, True)
+        assert_exact(gim, im, n, True)
+
+
+@pytest.mark.parametrize("dtype,n,split", [
+    ("f32", 10, (5, 5)), ("f32", 10, (2, 8)), ("f32", 10, (8, 2)), ("f32", 10, (3, 3, 4)),
+    ("f32", 10, (2, 2, 2, 4)), ("f32", 14, (7, 7)), ("f32", 14, (12, 2)), ("f32", 16, (4, 12)),
+    ("f32", 18, (15, 3)), ("f32", 20, (10, 10)), ("f32", 20, (8, 12)), ("f32", 20, (10, 5, 5)),
+    ("f64", 10, (1, 9)), ("f64", 10, (5, 5)), ("f64", 13, (13,)), ("f64", 14, (14,)),
+    ("f64", 18, (9, 9)), ("f64", 20, (8, 12)), ("f64", 22, (10, 12)), ("f64", 21, (7, 7, 7)),
+])
+def test_integer_forced_splits(dtype, n, split):
+    say("split %s n=%d %s" % (dtype, n, split))
+    npd = np.float32 if dtype == "f32" else np.float64
+    re = ints((2, 1 << n), 30_000 + n, npd)
+    im = ints((2, 1 << n), 40_000 + n, npd)
+    plan = qse.Plan(n, dtype, split=split)
+    assert plan.pass_bits == list(split)
+    gre, gim = run(plan, re, im, False)
+    assert_exact(gre, re, n, False)
+    assert_exact(gim, im, n, False)
+
+
+def _variants():
+    out = []
+    for dtype in ("f32", "f64"):
+        vb = 2 if dtype == "f32" else 1
+        for row_eb in (3, 4, 5):
+            out.append((dtype, 8 + vb + 8, (8 + vb, 8), (row_eb, 4), (-1, -1)))
+        for col_eb in (3, 4):
+            for gb in range(0, 5):
+                out.append((dtype, 8 + vb + 8, (8 + vb, 8), (4, col_eb), (-1, gb)))
+        out.append((dtype, 3 + vb + 10, (3 + vb, 10), (3, 4), (-1, 0)))
+        out.append((dtype, 12 + vb, (12 + vb,), (5,), (-1,)))
+        out.append((dtype, 12 + vb, (12 + vb,), (3,), (-1,)))
+    return out
+
+
+@pytest.mark.parametrize("dtype,n,split,eb,gbits", _variants())
+def test_integer_kernel_variants(dtype, n, split, eb, gbits):
+    say("variant %s n=%d split=%s eb=%s gbits=%s" % (dtype, n, split, eb, gbits))
+    npd = np.float32 if dtype == "f32" else np.float64
+    re = ints((2, 1 << n), 50_000 + n, npd)
+    im = ints((2, 1 << n), 60_000 + n, npd)
+    plan = qse.Plan(n, dtype, split=split, eb=eb, gbits=gbits)
+    gre, gim = run(plan, re, im, False)
+    assert_exact(gre, re, n, False)
+    assert_exact(gim, im, n, False)
+
+
+@pytest.mark.parametrize("dtype,n,batch", [("f32", 12, 1), ("f32", 12, 3), ("f32", 12, 257),
+                                           ("f32", 8, 1001), ("f32", 16, 5), ("f64", 16, 3),
+                                           ("f64", 6, 77), ("f32", 3, 9), ("f32", 1, 7),
+                                           ("f64", 1, 5), ("f32", 2, 33)])
+def test_ragged_batches(dtype, n, batch):
+    say("batch %s n=%d batch=%d" % (dtype, n, batch))
+    npd = np.float32 if dtype == "f32" else np.float64
+    re = ints((batch, 1 << n), 70_000 + batch, npd)
+    im = ints((batch, 1 << n), 80_000 + batch, npd)
+    gre, gim = run(qse.Plan(n, dtype), re, im, False)
+    assert_exact(gre, re, n, False)
+    assert_exact(gim, im, n, False)
+
+
+# ---- floating point, odd n and the normalisation -----------------------------
+
+@pytest.mark.parametrize("dtype,n", [("f32", n) for n in (3, 5, 11, 13, 15, 17, 19, 21, 23)] +
+                         [("f64", n) for n in (3, 7, 13, 15, 19, 23)])
+def test_gaussian_normalised_odd_and_large_n(dtype, n):
+    say("gauss %s n=%d" % (dtype, n))
+    w = workloads.custom(n, 2, dtype, "gauss", True, seed=90_000 + n)
+    re, im = workloads.gen(w)
+    gre, gim = run(qse.Plan(n, dtype), re, im, True)
+    assert_close(dtype, n, re, im, gre, gim)
+
+
+def test_unnormalised_gaussian_f32():
+    n = 16
+    say("gauss unnormalised n=16")
+    w = workloads.custom(n, 3, "f32", "gauss", False, seed=5)
+    re, im = workloads.gen(w)
+    gre, gim = run(qse.Plan(n, "f32"), re, im, False)
+    assert_close("f32", n, re, im, gre, gim, normalize=False)
+
+
+# ---- the full-size workloads, in the benchmark's launch configuration --------
+
+def _full_size(name, samples):
+    w = workloads.WORKLOADS[name]
+    say("full size %s" % name)
+    re, im = workloads.gen(w)
+    plan = qse.Plan(w.n, w.dtype)          # the plan the benchmark times
+    tre, tim = to_dev(re), to_dev(im)
+    plan.execute(tre, tim, normalize=True)
+    torch.cuda.synchronize()
+    # Parseval for every vector: the normalised transform keeps the norm.
+    ny = torch.sqrt((tre.double() ** 2).sum(1) + (tim.double() ** 2).sum(1)).cpu().numpy()
+    nx = np.sqrt((re.astype(np.float64) ** 2).sum(1) + (im.astype(np.float64) ** 2).sum(1))
+    assert np.abs(ny - nx).max() <= TOL[w.dtype] * nx.max()
+    for b in samples:
+        gre, gim = tre[b].cpu().numpy(), tim[b].cpu().numpy()
+        assert_close(w.dtype, w.n, re[b:b + 1], im[b:b + 1], gre, gim)
+        # the sampled input regenerates on its own from the recipe
+        r2, i2 = workloads.gen_vector(w, b)
+        assert np.array_equal(r2, re[b]) and np.array_equal(i2, im[b])
+    del tre, tim
+    torch.cuda.empty_cache()
+
+
+def test_full_size_n20_b256_f32():
+    _full_size("n20_b256_f32", samples=(0, 1, 137, 255))
+
+
+def test_full_size_n24_b16_f64():
+    _full_size("n24_b16_f64", samples=(0, 9, 15))
+
+
+# ---- API behaviour on the device ----------------------------------------------
+
+def test_real_only_transform():
+    say("real only")
+    n = 12
+    re = ints((4, 1 << n), 7, np.float32)
+    tre = to_dev(re)
+    qse.Plan(n, "f32").execute(tre, None, normalize=False)
+    torch.cuda.synchronize()
+    assert_exact(tre.cpu().numpy(), re, n, False)
+
+
+def test_non_default_stream_and_determinism():
+    say("stream + determinism")
+    n = 20
+    w = workloads.custom(n, 4, "f32", "gauss", True, seed=11)
+    re, im = workloads.gen(w)
+    s = torch.cuda.Stream()
+    plan = qse.Plan(n, "f32")
+    a_re, a_im = to_dev(re), to_dev(im)
+    b_re, b_im = to_dev(re), to_dev(im)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        plan.execute(a_re, a_im, normalize=True)
+    plan.execute(b_re, b_im, normalize=True, stream=s)
+    s.synchronize()
+    assert torch.equal(a_re, b_re) and torch.equal(a_im, b_im)
+    assert_close("f32", n, re, im, a_re.cpu().numpy(), a_im.cpu().numpy())
+
+
+def test_involution_normalised():
+    say("involution")
+    for n, dtype in ((13, "f32"), (20, "f32"), (17, "f64")):
+        w = workloads.custom(n, 2, dtype, "gauss", True, seed=n)
+        re, im = workloads.gen(w)
+        tre, tim = to_dev(re), to_dev(im)
+        plan = qse.Plan(n, dtype)
+        plan.execute(tre, tim, True)
+        plan.execute(tre, tim, True)
+        torch.cuda.synchronize()
+        tol = 2 * TOL[dtype]
+        assert np.abs(tre.cpu().numpy() - re).max() <= tol
+        assert np.abs(tim.cpu().numpy() - im).max() <= tol
+
+
+def test_guard_regions_untouched():
+    say("guard regions")
+    pad = 1024
+    for n, dtype, batch in ((12, "f32", 3), (20, "f32", 2), (14, "f64", 3), (22, "f64", 1)):
+        npd = np.float32 if dtype == "f32" else np.float64
+        N = 1 << n
+        sentinel = 12345.0
+        bufs = [torch.full((pad + batch * N + pad,), sentinel, dtype=torch.float32
+                           if dtype == "f32" else torch.float64, device="cuda") for _ in range(2)]
+        re = ints((batch, N), n, npd)
+        im = ints((batch, N), n + 1, npd)
+        bufs[0][pad:pad + batch * N] = to_dev(re.ravel())
+        bufs[1][pad:pad + batch * N] = to_dev(im.ravel())
+        qse.Plan(n, dtype).execute(bufs[0][pad:pad + batch * N], bufs[1][pad:pad + batch * N],
+                                   normalize=False)
+        torch.cuda.synchronize()
+        for t, x in zip(bufs, (re, im)):
+            h = t.cpu().numpy()
+            assert (h[:pad] == sentinel).all() and (h[pad + batch * N:] == sentinel).all()
+            assert_exact(h[pad:pad + batch * N].reshape(batch, N), x, n, False)
+
+
+def _alloc_range(ptr):
+    hip = ctypes.CDLL("libamdhip64.so")
+    base, size = ctypes.c_void_p(), ctypes.c_size_t()
+    st = hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size), ctypes.c_void_p(ptr))
+    assert st == 0
+    return base.value, size.value
+
+
+def test_validation_on_device_memory():
+    say("validation")
+    n = 10
+    N = 1 << n
+    plan = qse.Plan(n, "f32")
+    re = torch.zeros(4 * N, device="cuda")
+    im = torch.zeros(4 * N, device="cuda")
+    assert plan.check_raw(4, re.data_ptr(), im.data_ptr()) == qse.FWT_OK
+    host = np.zeros(4 * N, np.float32)
+    assert plan.check_raw(4, host.ctypes.data, im.data_ptr()) == qse.FWT_EINVAL
+    base, size = _alloc_range(re.data_ptr())
+    too_many = (base + size - re.data_ptr()) // (4 * N) + 1
+    assert plan.check_raw(too_many, re.data_ptr(), None) == qse.FWT_EINVAL
+    # fwt_execute runs the same validation first, so it rejects before launching
+    assert plan.execute_raw(too_many, re.data_ptr(), 0, 1) == qse.FWT_EINVAL
+    with pytest.raises(qse.FwtError):
+        plan.execute(re, re)   # same buffer twice
+    assert plan.execute_raw(0, re.data_ptr(), im.data_ptr(), 1) == qse.FWT_OK
+
+
+def test_stream_copy():
+    say("stream copy")
+    src = torch.randn(3 * 2**20 + 12, device="cuda")
+    dst = torch.empty_like(src)
+    qse.stream_copy(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
