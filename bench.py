@@ -112,13 +112,29 @@ def bench_workload(torch, w, steps, warmup, with_passes=True):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ms = ms_events
-    # Per-kernel durations: the same passes, one event pair per launch.
+    # Per-kernel durations: the schedule fwt_execute runs (all passes of one
+    # chunk of vectors, chunk after chunk), each kernel timed by HIP events
+    # that its own dispatch records at its start and end; averaged per pass
+    # over `steps` steps.
     per_pass = []
+    chunk = plan.chunk_vectors(w.batch, True) or w.batch
     if with_passes:
-        for i in range(passes):
-            per_pass.append(time_events(
-                torch, stream, lambda: plan.execute_pass(i, re, im, normalize=w.normalize),
-                max(10, steps // 2)))
+        evs = []
+        for _ in range(steps):
+            for c0 in range(0, w.batch, chunk):
+                sl = slice(c0, min(w.batch, c0 + chunk))
+                for i in range(passes):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    plan.execute_pass_timed(i, re[sl], im[sl], a, b, normalize=w.normalize)
+                    evs.append((i, a, b))
+        torch.cuda.synchronize()
+        tot = [0.0] * passes
+        cnt = [0] * passes
+        for i, a, b in evs:
+            tot[i] += a.elapsed_time(b)
+            cnt[i] += 1
+        per_pass = [tot[i] / cnt[i] for i in range(passes)]
     # Stream-copy ceiling: one read and one write of the whole state.
     copy_ms = None
     if with_passes:
@@ -133,7 +149,103 @@ def bench_workload(torch, w, steps, warmup, with_passes=True):
     torch.cuda.empty_cache()
     S = w.state_bytes
     return {"ms": ms, "wall_ms": wall_ms, "passes": passes, "pass_bits": plan.pass_bits,
-            "per_pass_ms": per_pass, "copy_ms": copy_ms, "S": S}
+            "per_pass_ms": per_pass, "copy_ms": copy_ms, "S": S, "chunk": chunk}
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    for root, _, files in os.walk(dirpath):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError("no *%s under %s" % (suffix, dirpath))
+
+
+def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command):
+    """Turn rocprofv3 CSV output of this benchmark into the text summaries
+    under profiles/ and profiles/traffic.json (HBM bytes per launch)."""
+    import quantum_state_encoding_amd as qse
+    w = workloads.WORKLOADS[workload]
+    plan = qse.Plan(w.n, w.dtype, split=w.split or None)
+    trace = _read_csv(_find(kt_dir, "kernel_trace.csv"))
+    groups = {}
+    for r in trace:
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+
+    def counters(d):
+        out = {}
+        for r in _read_csv(_find(d, "counter_collection.csv")):
+            key = (r["Kernel_Name"], int(r["Grid_Size"]))
+            out.setdefault(key, []).append(float(r["Counter_Value"]))
+        return out
+    fetch, write = counters(fetch_dir), counters(write_dir)
+
+    def short(name):
+        return name.replace("qse::(anonymous namespace)::", "").split("(float*")[0].split(
+            "(double*")[0]
+
+    # Calibration: the streaming copy of one component moves S/2 bytes each way.
+    half_kib = w.state_bytes / 2 / 1024
+    cf = [v for (k, g), v in fetch.items() if "stream_copy_kernel" in k]
+    cw = [v for (k, g), v in write.items() if "stream_copy_kernel" in k]
+    f_scale = half_kib / float(np.mean(cf[0])) if cf else None
+    w_scale = half_kib / float(np.mean(cw[0])) if cw else None
+    chunk = plan.chunk_vectors(w.batch, True) or w.batch
+    chunk_bytes = w.state_bytes * chunk // w.batch
+    lines = ["# rocprofv3 kernel trace: %s" % workload,
+             "# command: " + command,
+             "# kernel | grid (threads x, y) | dispatches | avg us | min us | max us"]
+    for (name, gx, gy), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append("%s | %d x %d | %d | %.2f | %.2f | %.2f" % (
+            short(name), gx, gy, len(d), np.mean(d) / 1e3, np.min(d) / 1e3, np.max(d) / 1e3))
+    passes = {}
+    tl = ["# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (separate runs): %s" % workload,
+          "# command: " + command.replace("--kernel-trace --stats", "--pmc FETCH_SIZE|WRITE_SIZE"),
+          "# calibration on fwt_stream_copy of %.0f KiB each way: FETCH_SIZE x %.4f, "
+          "WRITE_SIZE x %.4f" % (half_kib, f_scale or float("nan"), w_scale or float("nan")),
+          "# pass | kernel | launches | FETCH KiB | WRITE KiB | scaled HBM bytes/launch | "
+          "algorithmic bytes/launch | ratio | avg us (trace)"]
+    for i in range(plan.num_passes):
+        kname = plan.kernel_name(i)
+        cand = [(k, v) for k, v in groups.items() if kname in k[0]]
+        if not cand:
+            continue
+        (name, gx, gy), d = max(cand, key=lambda kv: kv[0][1] * kv[0][2])
+        fv = fetch.get((name, gx * gy)) or fetch.get((name, gx))
+        wv = write.get((name, gx * gy)) or write.get((name, gx))
+        rec = {"kernel": short(name), "grid": [gx, gy], "dispatches": len(d),
+               "avg_us": float(np.mean(d) / 1e3), "algorithmic_bytes_per_launch": 2 * chunk_bytes}
+        if fv and wv and f_scale and w_scale:
+            b = (float(np.mean(fv)) * f_scale + float(np.mean(wv)) * w_scale) * 1024
+            rec.update({"fetch_kib": float(np.mean(fv)), "write_kib": float(np.mean(wv)),
+                        "bytes_per_launch": b})
+            tl.append("%d | %s | %d | %.1f | %.1f | %.4g | %.4g | %.4f | %.2f" % (
+                i, short(name), len(fv), np.mean(fv), np.mean(wv), b, 2 * chunk_bytes,
+                b / (2 * chunk_bytes), rec["avg_us"]))
+        passes[str(i)] = rec
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "%s_kernel_trace.txt" % workload), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(ROOT, "profiles", "%s_traffic.txt" % workload), "w") as f:
+        f.write("\n".join(tl) + "\n")
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allt = json.load(f)
+    except (OSError, ValueError):
+        allt = {"workloads": {}}
+    allt["workloads"][workload] = {"kernel_source_sha256_16": kernel_source_hash(),
+                                   "fetch_scale": f_scale, "write_scale": w_scale,
+                                   "chunk_vectors": chunk, "passes": passes}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allt, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print("\n".join(lines + [""] + tl))
 
 
 def main():
@@ -143,7 +255,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="n20_b256_f32", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 CSV output of this benchmark")
+    ap.add_argument("--profile-command", default="",
+                    help="the rocprofv3 command line recorded in the summaries")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.workload, *args.summarize_profile, args.profile_command)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(batches shard across GPUs with no communication); run with --gpus 1",
@@ -163,7 +282,8 @@ def main():
     gbps_alg = 2 * S / (r["ms"] * 1e-3) / 1e9
     dom = int(np.argmax(r["per_pass_ms"])) if r["per_pass_ms"] else 0
     dom_ms = r["per_pass_ms"][dom] if r["per_pass_ms"] else r["ms"]
-    achieved = 2 * S / (dom_ms * 1e-3) / 1e9
+    launch_bytes = 2 * S * r["chunk"] // w.batch     # read + write of one chunk's state
+    achieved = launch_bytes / (dom_ms * 1e-3) / 1e9
     traffic = measured_traffic(w.name, dom)
 
     also = {}
@@ -192,7 +312,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic: seeded Gaussian states, L2-normalised per vector",
         "config": {"workload": w.name, "n": w.n, "batch": w.batch, "normalize": w.normalize,
-                   "layout": "planar re/im", "passes": r["passes"], "pass_bits": r["pass_bits"]},
+                   "layout": "planar re/im", "passes": r["passes"], "pass_bits": r["pass_bits"],
+                   "chunk_vectors": r["chunk"]},
         "gbps_accounted": gbps_accounted,
         "pct_peak_accounted": 100 * gbps_accounted / HBM_PEAK_GBS,
         "gbps_algorithmic": gbps_alg,
@@ -205,7 +326,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "pass %d (%d bits, %s)" % (dom, r["pass_bits"][dom] if r["pass_bits"] else 0,
                                                            "row" if dom == 0 else "column"),
-                     "bytes_per_launch": 2 * S},
+                     "bytes_per_launch": launch_bytes,
+                     "launches_per_step": r["passes"] * (-(-w.batch // r["chunk"]))},
         "cpu_baseline": cpu,
         "also": also,
     }

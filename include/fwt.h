@@ -19,9 +19,11 @@
  * Execution.  A plan splits the n index bits into passes (the Kronecker
  * factorisation H_n = H_{n1} (x) H_{n2} of the pull request's sections
  * "Why" and "Why submit PR4"; the iThome article's "Kronecker block GEMM
- * idea").  Each pass streams the state through HBM once, in place, with no
- * transpose and no temporary buffer.  n <= 14 (fp32) / 13 (fp64) runs as a
- * single pass whose tiles hold a whole vector on chip.
+ * idea").  Each pass streams the state through memory once, in place, with
+ * no transpose and no temporary buffer.  n <= 14 (fp32) / 13 (fp64) runs
+ * as a single pass whose tiles hold a whole vector on chip; up to n = 24,
+ * two passes; above, three.  Large multi-pass calls run in chunks of
+ * vectors sized to the Infinity Cache (fwt_plan_chunk_vectors).
  *
  * Conventions common to every entry point:
  *  - Status codes are the FWT_* values below; no C++ exception crosses
@@ -100,11 +102,15 @@ int fwt_plan_create_split(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
  *  gbits  per pass, log2 of the 16-byte column groups per tile of a column
  *         pass (0..4; must be 0 or -1 for the first pass), or -1 for the
  *         default; NULL = all defaults.
+ *  phases per pass, log2 of the phases a column pass splits each LDS
+ *         exchange into (0..2, at most gbits; column passes of >= 9 bits and
+ *         >= 8 groups only), or -1 for the default; NULL = all defaults.
  * Returns as fwt_plan_create_split, plus FWT_EINVAL for a value out of
  * range or a tile that exceeds the LDS or workgroup limits, and
  * FWT_EUNSUPPORTED for a variant that is not compiled in. */
 int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
-                          const int* bits, const int* eb, const int* gbits);
+                          const int* bits, const int* eb, const int* gbits,
+                          const int* phases);
 
 /* Transform in place, asynchronously on `stream` (0 = the null stream).
  *  re, im   device buffers of batch * 2^n elements of the plan's dtype,
@@ -124,6 +130,15 @@ int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
 int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im,
                 int normalize, hipStream_t stream);
 
+/* Vectors per chunk that fwt_execute uses for a call on `batch` vectors
+ * (with_im != 0: both components): a multi-pass call whose state exceeds
+ * the 256 MiB Infinity Cache runs every pass on one chunk of vectors before
+ * the next chunk, so later passes re-read what earlier passes left in the
+ * cache.  *out = 0 means no chunking.  fwt_execute is then exactly, for
+ * each chunk in order, fwt_execute_pass for passes 0..P-1 on that chunk.
+ * Returns FWT_OK or FWT_EINVAL (null argument, batch < 0). */
+int fwt_plan_chunk_vectors(fwt_plan_t plan, int64_t batch, int with_im, int64_t* out);
+
 /* Enqueue only pass `pass` (0 <= pass < fwt_plan_num_passes; 0 for an
  * n = 0 plan, which has none and does nothing) of the plan, with the
  * arguments and validation of fwt_execute.  Running passes 0, 1, ..., P-1
@@ -134,6 +149,16 @@ int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im,
  * fwt_execute, plus FWT_EINVAL for a pass index out of range. */
 int fwt_execute_pass(fwt_plan_t plan, int pass, int64_t batch, int n, void* re,
                      void* im, int normalize, hipStream_t stream);
+
+/* fwt_execute_pass with the pass's kernel timed by the dispatch itself:
+ * `start` and `stop` (timing-enabled events the caller owns) are recorded
+ * when the kernel starts and ends, so their elapsed time is the kernel's
+ * duration without launch gaps.  Returns as fwt_execute_pass, plus
+ * FWT_EINVAL for a null event or a call with nothing to launch (batch 0,
+ * n = 0). */
+int fwt_execute_pass_timed(fwt_plan_t plan, int pass, int64_t batch, int n, void* re,
+                           void* im, int normalize, hipStream_t stream,
+                           hipEvent_t start, hipEvent_t stop);
 
 /* Run exactly the host-side validation of fwt_execute (same arguments,
  * same status codes, including the device-memory and size checks) without
@@ -148,6 +173,13 @@ int fwt_plan_num_passes(fwt_plan_t plan, int* out_passes);
 /* Bit count of pass i (the pass on the lowest bits is i = 0).  Returns
  * FWT_OK or FWT_EINVAL (null argument, i out of range). */
 int fwt_plan_pass_bits(fwt_plan_t plan, int i, int* out_bits);
+
+/* Tiling of pass i, for logging and profiling: out[0..9] = first index
+ * bit, bit count, kind (0 row pass, 1 column pass, 2 two-element kernel),
+ * row bits KR of the tile, register-round bits EB, column-group bits,
+ * exchange-phase bits, workgroup size, dynamic LDS bytes, log2 tiles per
+ * workgroup.  `out` must hold 10 ints.  Returns FWT_OK or FWT_EINVAL. */
+int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out);
 
 /* Release a plan; NULL is a no-op.  Returns FWT_OK. */
 int fwt_plan_destroy(fwt_plan_t plan);

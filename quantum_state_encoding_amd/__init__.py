@@ -30,10 +30,11 @@ _DTYPES = {"f32": 0, "f64": 1}
 
 # Every symbol include/fwt.h declares.
 EXPORTED_SYMBOLS = ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create_tuned",
-                    "fwt_execute", "fwt_execute_pass", "fwt_execute_check",
-                    "fwt_plan_num_passes", "fwt_plan_pass_bits",
+                    "fwt_execute", "fwt_execute_pass", "fwt_execute_pass_timed",
+                    "fwt_execute_check",
+                    "fwt_plan_num_passes", "fwt_plan_pass_config", "fwt_plan_pass_bits",
                     "fwt_plan_destroy", "fwt_strerror", "fwt_last_hip_error",
-                    "fwt_stream_copy")
+                    "fwt_stream_copy", "fwt_plan_chunk_vectors")
 
 _lib = None
 
@@ -67,20 +68,24 @@ def load_library():
     pi = ctypes.POINTER(ctypes.c_int)
     lib.fwt_plan_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32]
     lib.fwt_plan_create_split.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi]
-    lib.fwt_plan_create_tuned.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi, pi, pi]
+    lib.fwt_plan_create_tuned.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi, pi, pi, pi]
+    lib.fwt_plan_chunk_vectors.argtypes = [vp, i64, i32, ctypes.POINTER(i64)]
     lib.fwt_execute.argtypes = [vp, i64, i32, vp, vp, i32, vp]
     lib.fwt_execute_pass.argtypes = [vp, i32, i64, i32, vp, vp, i32, vp]
+    lib.fwt_execute_pass_timed.argtypes = [vp, i32, i64, i32, vp, vp, i32, vp, vp, vp]
     lib.fwt_execute_check.argtypes = [vp, i64, i32, vp, vp]
     lib.fwt_plan_num_passes.argtypes = [vp, pi]
     lib.fwt_plan_pass_bits.argtypes = [vp, i32, pi]
+    lib.fwt_plan_pass_config.argtypes = [vp, i32, pi]
     lib.fwt_plan_destroy.argtypes = [vp]
     lib.fwt_strerror.argtypes = [i32]
     lib.fwt_strerror.restype = ctypes.c_char_p
     lib.fwt_last_hip_error.argtypes = []
     lib.fwt_stream_copy.argtypes = [vp, vp, i64, vp]
     for name in ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create_tuned",
-                 "fwt_execute", "fwt_execute_pass", "fwt_execute_check",
-                 "fwt_plan_num_passes", "fwt_plan_pass_bits", "fwt_plan_destroy", "fwt_last_hip_error",
+                 "fwt_execute", "fwt_execute_pass", "fwt_execute_pass_timed",
+                 "fwt_execute_check", "fwt_plan_num_passes", "fwt_plan_pass_bits",
+                 "fwt_plan_pass_config", "fwt_plan_destroy", "fwt_last_hip_error",
                  "fwt_stream_copy"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -108,27 +113,30 @@ class Plan:
     """A plan for 2^n-amplitude vectors of dtype "f32" or "f64".
 
     ``split`` (bit counts, lowest index bits first) forces a Kronecker
-    split; ``eb``/``gbits`` (one entry per pass, -1 = default) force the
-    register-round width and column-group count of each pass (tuning).
+    split; ``eb``/``gbits``/``phases`` (one entry per pass, -1 = default)
+    force the register-round width, column-group count and exchange phases
+    of each pass (tuning).
     """
 
-    def __init__(self, n, dtype="f32", path=PATH_AUTO, split=None, eb=None, gbits=None):
+    def __init__(self, n, dtype="f32", path=PATH_AUTO, split=None, eb=None, gbits=None,
+                 phases=None):
         lib = load_library()
         if dtype not in _DTYPES:
             raise ValueError("dtype must be 'f32' or 'f64'")
         self.n, self.dtype = int(n), dtype
         h = ctypes.c_void_p()
-        if split is None and eb is None and gbits is None:
+        tuned = eb is not None or gbits is not None or phases is not None
+        if split is None and not tuned:
             st = lib.fwt_plan_create(ctypes.byref(h), self.n, _DTYPES[dtype], int(path))
-        elif eb is None and gbits is None:
+        elif not tuned:
             st = lib.fwt_plan_create_split(ctypes.byref(h), self.n, _DTYPES[dtype],
                                            len(split), _int_array(split))
         else:
             if split is None:
-                raise ValueError("eb/gbits need an explicit split")
+                raise ValueError("eb/gbits/phases need an explicit split")
             st = lib.fwt_plan_create_tuned(ctypes.byref(h), self.n, _DTYPES[dtype],
                                            len(split), _int_array(split), _int_array(eb),
-                                           _int_array(gbits))
+                                           _int_array(gbits), _int_array(phases))
         if st != FWT_OK:
             raise FwtError(st, "fwt_plan_create(n=%d, %s)" % (self.n, dtype))
         self._h = h
@@ -154,6 +162,28 @@ class Plan:
                 raise FwtError(st, "fwt_plan_pass_bits")
             bits.append(out.value)
         return bits
+
+    def pass_config(self, i):
+        """Tiling of pass i as a dict (see fwt_plan_pass_config)."""
+        out = (ctypes.c_int * 10)()
+        st = load_library().fwt_plan_pass_config(self._h, int(i), out)
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_plan_pass_config")
+        keys = ("lo", "bits", "kind", "kr", "eb", "gbits", "phase_bits", "block", "lds",
+                "tpw_bits")
+        d = dict(zip(keys, list(out)))
+        d["kind"] = ("row", "column", "pair")[d["kind"]]
+        return d
+
+    def kernel_name(self, i):
+        """Demangled name of pass i's kernel as profilers print it."""
+        c = self.pass_config(i)
+        if c["kind"] == "pair":
+            return "pair_f32_kernel"
+        t = "float" if self.dtype == "f32" else "double"
+        return "tile_kernel<%s, %d, %d, %d, %d, %s>" % (
+            t, c["kr"], c["eb"], c["gbits"], c["phase_bits"],
+            "true" if c["kind"] == "row" else "false")
 
     def execute(self, re, im=None, normalize=True, stream=None):
         """Transform torch device tensors re (and im) in place.
@@ -186,6 +216,15 @@ class Plan:
             raise FwtError(st, "fwt_execute")
         return re, im
 
+    def chunk_vectors(self, batch, with_im=True):
+        """Vectors per chunk fwt_execute uses for `batch` vectors (0 = none)."""
+        out = ctypes.c_int64()
+        st = load_library().fwt_plan_chunk_vectors(self._h, int(batch), 1 if with_im else 0,
+                                                   ctypes.byref(out))
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_plan_chunk_vectors")
+        return out.value
+
     def bind(self, re, im=None, normalize=True, stream=None):
         """A zero-argument callable that enqueues fwt_execute on these
         tensors with the arguments marshalled once (for tight loops)."""
@@ -212,6 +251,23 @@ class Plan:
         if st != FWT_OK:
             raise FwtError(st, "fwt_execute_pass")
         return re, im
+
+    def execute_pass_timed(self, i, re, im, start, stop, normalize=True, stream=None):
+        """Enqueue pass i with torch timing events `start`/`stop` recorded
+        by the kernel dispatch itself (see fwt_execute_pass_timed)."""
+        import torch
+        s = torch.cuda.current_stream() if stream is None else stream
+        for ev in (start, stop):
+            if not ev.cuda_event:          # torch creates events lazily
+                ev.record(s)
+        N = 1 << self.n
+        st = load_library().fwt_execute_pass_timed(
+            self._h, int(i), re.numel() // N, self.n, ctypes.c_void_p(re.data_ptr()),
+            ctypes.c_void_p(im.data_ptr() if im is not None else None), 1 if normalize else 0,
+            ctypes.c_void_p(s.cuda_stream), ctypes.c_void_p(start.cuda_event),
+            ctypes.c_void_p(stop.cuda_event))
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_execute_pass_timed")
 
     def execute_raw(self, batch, re_ptr, im_ptr, normalize, stream_ptr=0):
         """Call fwt_execute on raw device addresses; returns the status."""

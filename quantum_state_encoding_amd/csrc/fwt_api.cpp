@@ -34,7 +34,8 @@ constexpr int kMaxPasses = 4;
 constexpr int kRowKrMax = 13;          // rows bits of a row pass (vectors)
 constexpr int kColKrMax = 12;          // rows bits of a column pass
 constexpr size_t kLdsMax = 160 * 1024; // per workgroup on gfx950
-constexpr size_t kColLdsBudget = 128 * 1024;
+constexpr size_t kPhaseLdsTarget = 68 * 1024;  // two tiles per CU
+constexpr size_t kChunkBytes = (size_t)256 << 20;  // Infinity Cache capacity
 constexpr int kTargetThreads = 256;    // workgroup size aimed for when packing tiles
 
 struct Pass {
@@ -47,6 +48,7 @@ struct Pass {
     int tt_bits = 0;     // log2 threads per tile
     int tpw_bits = 0;    // log2 tiles per workgroup
     int store_back = 0;
+    int phb = 0;         // log2 exchange phases
     unsigned block = 0;
     size_t lds = 0;
     int tiles_bits = 0;  // log2 tiles per vector (per component)
@@ -93,9 +95,26 @@ bool log_enabled()
     return s && s[0] && s[0] != '0';
 }
 
+// LDS bytes of one exchange phase of a tile: 2^(kr + gbits - phb) 16-byte
+// slots plus one pad slot per 2^(eb + gbits - phb) slots.
+size_t phase_lds(int kr, int eb, int gbits, int phb)
+{
+    const size_t slots = (size_t)1 << (kr + gbits - phb);
+    return 16 * (slots + (slots >> (eb + gbits - phb)));
+}
+
+// Whether a column-pass variant with phased exchange exists (mirrors the
+// instantiation rule in fwt_kernels.hip).
+bool phases_allowed(int kr, int eb, int gbits, int phb)
+{
+    return phb == 0 || (kr >= 9 && gbits >= 3 && kr > eb && phb <= 2);
+}
+
 // Fill in the tiling of a pass over bits [lo, lo + k) of a 2^n vector.
-// eb_req / gbits_req < 0 select defaults.  Returns FWT_OK or an error.
-int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int gbits_req)
+// eb_req / gbits_req / phb_req < 0 select defaults.  Returns FWT_OK or an
+// error.
+int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int gbits_req,
+               int phb_req)
 {
     const int vb = vec_bits(dtype);
     p = Pass{};
@@ -106,15 +125,12 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int g
         return FWT_OK;
     }
     const bool row = (lo == 0);
-    int kr, gbits;
+    int kr;
     if (row) {
         if (k < vb)
             return FWT_EINVAL;
         kr = k - vb;
-        if (kr > kRowKrMax)
-            return FWT_EINVAL;
-        gbits = 0;
-        if (gbits_req > 0)
+        if (kr > kRowKrMax || gbits_req > 0 || phb_req > 0)
             return FWT_EINVAL;
     } else {
         if (lo < vb)
@@ -123,51 +139,65 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int g
         if (kr < 1 || kr > kColKrMax)
             return FWT_EINVAL;
     }
-    int eb = eb_req < 0 ? default_eb(kr) : eb_req;
-    if (eb > kr || eb < 0)
+    const int eb = eb_req < 0 ? default_eb(kr) : eb_req;
+    if (eb > kr || eb < 0 || eb > 5)
         return FWT_EINVAL;
+    const int tt_max = ilog2(max_threads(eb));
+    const int nr = qse::rounds_of(kr, eb);
+    const bool needs_lds = nr > 1;
+    int gbits = 0, phb = 0;
     if (!row) {
         const int gmax_cols = lo - vb;  // log2 16-byte groups in a row
-        if (gbits_req >= 0) {
-            gbits = gbits_req;
-            if (gbits > gmax_cols)
-                return FWT_EINVAL;
-        } else {
-            gbits = 0;
-            while (gbits < 4 && gbits < gmax_cols &&
-                   ((size_t)16 << (kr + gbits + 1)) <= kColLdsBudget &&
-                   (kr - eb) + gbits + 1 <= ilog2(max_threads(eb)))
-                ++gbits;
+        if (gbits_req > 4 || gbits_req > gmax_cols || phb_req > 2)
+            return FWT_EINVAL;
+        // Defaults: row segments of at least 128 bytes (8 groups) where the
+        // rows allow it, then the fewest exchange phases, then the most
+        // groups (up to 256-byte segments), such that one phase's LDS stays
+        // near 64 KiB (two tiles per CU); failing that, up to the 160 KiB
+        // limit; failing that, shorter segments.
+        const int gb_top = gbits_req >= 0 ? gbits_req : (gmax_cols < 4 ? gmax_cols : 4);
+        const int gb_min = gmax_cols < 3 ? gmax_cols : 3;
+        const int ph_lo = phb_req >= 0 ? phb_req : 0;
+        const int ph_hi = phb_req >= 0 ? phb_req : 2;
+        bool found = false;
+        for (int attempt = 0; attempt < 3 && !found; ++attempt) {
+            const size_t limit = attempt == 0 ? kPhaseLdsTarget : kLdsMax;
+            const int gb_lo = gbits_req >= 0 ? gbits_req : (attempt < 2 ? gb_min : 0);
+            for (int ph = ph_lo; ph <= ph_hi && !found; ++ph) {
+                for (int gb = gb_top; gb >= gb_lo && !found; --gb) {
+                    if ((kr - eb) + gb > tt_max)
+                        continue;
+                    if (ph > gb || !phases_allowed(kr, eb, gb, ph))
+                        continue;
+                    if (needs_lds && phase_lds(kr, eb, gb, ph) > limit)
+                        continue;
+                    gbits = gb;
+                    phb = needs_lds ? ph : 0;
+                    found = true;
+                }
+            }
         }
+        if (!found)
+            return FWT_EINVAL;
         p.nblk_bits = gmax_cols - gbits;
     }
-    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, gbits, row ? 1 : 0};
+    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, gbits, phb, row ? 1 : 0};
     p.gbits = gbits;
+    p.phb = phb;
     p.tt_bits = (kr - eb) + gbits;
-    if (p.tt_bits > ilog2(max_threads(eb)))
+    if (p.tt_bits > tt_max)
         return FWT_EINVAL;
-    const int nr = qse::rounds_of(kr, eb);
-    // LDS of one tile: 2^(kr + gbits) 16-byte slots plus one pad slot per
-    // 2^(eb + gbits) slots.
-    const size_t slots = (size_t)1 << (kr + gbits);
-    const size_t tile_lds = 16 * (slots + (slots >> (eb + gbits)));
+    const size_t tile_lds = phase_lds(kr, eb, gbits, phb);
     // Pack tiles into a workgroup of about kTargetThreads threads.
     int tpw_bits = 0;
     while (p.tt_bits + tpw_bits < ilog2(kTargetThreads))
         ++tpw_bits;
     p.store_back = qse::store_back(kr, eb, gbits) ? 1 : 0;
-    const bool needs_lds = nr > 1;
     if (needs_lds) {
         if (tile_lds > kLdsMax)
             return FWT_EINVAL;
         while (tpw_bits > 0 && (tile_lds << tpw_bits) > kLdsMax)
             --tpw_bits;
-    }
-    if (!row) {
-        // Tiles of one workgroup stay inside one outer index unless there
-        // are fewer column blocks than tiles per workgroup.
-        if (tpw_bits > p.nblk_bits && p.nblk_bits < 0)
-            return FWT_EINVAL;
     }
     // Lanes address from the workgroup's first tile with 32-bit byte
     // offsets; the largest one must fit.
@@ -195,12 +225,17 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int g
 }
 
 // Default Kronecker split (bit counts, lowest bits first).
+//  - one pass while a vector fits one 64 KiB tile: n <= 14 (fp32), 13 (fp64);
+//  - two passes up to n = 24: the row pass takes 13 (fp32) / 14 (fp64)
+//    contiguous bits, the column pass the rest (at most 11 / 10 bits, so
+//    its tile keeps 128-byte row segments);
+//  - three passes above: 10 row bits, the rest split evenly.
 int default_split(int n, fwt_dtype dtype, fwt_path path, int* bits)
 {
     const int vb = vec_bits(dtype);
-    const int single_max = kRowKrMax - 1 + vb;   // 64 KiB tiles: 14 fp32, 13 fp64
+    const int single_max = 12 + vb;
     if (path == FWT_PATH_SINGLE_BLOCK) {
-        if (n > single_max + 1)
+        if (n > kRowKrMax + vb)
             return -1;
         bits[0] = n;
         return 1;
@@ -215,14 +250,12 @@ int default_split(int n, fwt_dtype dtype, fwt_path path, int* bits)
         bits[0] = n - bits[1];
         return 2;
     }
-    if (n <= 12 + kColKrMax) {
-        // Two passes: a 12-bit row pass on the contiguous low bits, then
-        // one column pass on the rest.
-        bits[0] = 12;
-        bits[1] = n - 12;
+    const int row2 = dtype == FWT_F64 ? 14 : 13;
+    if (n <= 24) {
+        bits[0] = row2 < n - 1 ? row2 : n - 1;
+        bits[1] = n - bits[0];
         return 2;
     }
-    // Three passes: 10 row bits, the rest split evenly (n <= 30).
     const int rest = n - 10;
     bits[0] = 10;
     bits[1] = rest - rest / 2;
@@ -231,7 +264,7 @@ int default_split(int n, fwt_dtype dtype, fwt_path path, int* bits)
 }
 
 int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* bits,
-              const int* ebs, const int* gbits)
+              const int* ebs, const int* gbits, const int* phbs)
 {
     if (!out)
         return FWT_EINVAL;
@@ -258,7 +291,7 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
     int lo = 0;
     for (int i = 0; i < p->npasses; ++i) {
         const int rc = build_pass(p->passes[i], n, dtype, lo, bits[i], ebs ? ebs[i] : -1,
-                                  gbits ? gbits[i] : -1);
+                                  gbits ? gbits[i] : -1, phbs ? phbs[i] : -1);
         if (rc != FWT_OK) {
             delete p;
             return rc;
@@ -271,11 +304,11 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
         for (int i = 0; i < p->npasses; ++i) {
             const Pass& q = p->passes[i];
             std::fprintf(stderr,
-                         "[fwt]   pass %d: bits [%d,%d) %s kr=%d eb=%d G=%d threads/tile=%d "
-                         "block=%u lds=%zu store_back=%d tiles/vec=2^%d\n",
+                         "[fwt]   pass %d: bits [%d,%d) %s kr=%d eb=%d G=%d phases=%d "
+                         "threads/tile=%d block=%u lds=%zu store_back=%d tiles/vec=2^%d\n",
                          i, q.lo, q.lo + q.k, q.pair ? "pair" : (q.key.row ? "row" : "col"),
-                         q.key.kr, q.key.eb, 1 << q.gbits, 1 << q.tt_bits, q.block, q.lds,
-                         q.store_back, q.tiles_bits);
+                         q.key.kr, q.key.eb, 1 << q.gbits, 1 << q.phb, 1 << q.tt_bits, q.block,
+                         q.lds, q.store_back, q.tiles_bits);
         }
     }
     *out = p;
@@ -367,6 +400,67 @@ int validate(fwt_plan_t plan, int64_t batch, int n, const void* re, const void* 
     return rc;
 }
 
+// Vectors per chunk of a call: multi-pass calls whose state exceeds the
+// Infinity Cache run all passes on one chunk of about kChunkBytes before
+// the next chunk starts, so the later passes re-read data the earlier
+// passes left in the cache.  0 = one chunk (the whole batch).
+int64_t chunk_vectors(const fwt_plan_s* plan, int64_t batch, int ncomp)
+{
+    if (plan->npasses < 2)
+        return 0;
+    const size_t esize = plan->dtype == FWT_F64 ? 8 : 4;
+    const size_t vec_bytes = ((size_t)1 << plan->n) * esize * (size_t)ncomp;
+    if ((size_t)batch * vec_bytes <= kChunkBytes)
+        return 0;
+    const int64_t v = (int64_t)(kChunkBytes / vec_bytes);
+    return v > 0 ? v : 1;
+}
+
+// Enqueue passes [first, last) over `batch` vectors starting at re/im.  In
+// a multi-pass plan the first pass reads and the last pass writes with
+// nontemporal hints: their data is not reused by this call, while the
+// intermediate data between passes should stay in the caches.
+int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, void* re, void* im,
+                  int normalize, hipStream_t stream, hipEvent_t start = nullptr,
+                  hipEvent_t stop = nullptr)
+{
+    int rc = ensure_device_init();
+    if (rc != FWT_OK)
+        return rc;
+    const int ncomp = im ? 2 : 1;
+    const double c = norm_constant(n);
+    const bool multi = plan->npasses >= 2;
+    for (int i = first; i < last; ++i) {
+        const Pass& p = plan->passes[i];
+        const bool final_pass = (i == plan->npasses - 1);
+        const int do_scale = (normalize && final_pass) ? 1 : 0;
+        hipError_t e;
+        if (p.pair) {
+            e = qse::launch_pair_f32((float*)re, (float*)im, batch, do_scale, (float)c, stream,
+                                     i == first ? start : nullptr,
+                                     i == last - 1 ? stop : nullptr);
+        } else {
+            TileArgs a{};
+            a.tiles = batch << p.tiles_bits;
+            a.wg_count = (a.tiles + ((int64_t)1 << p.tpw_bits) - 1) >> p.tpw_bits;
+            a.lo = p.lo;
+            a.nblk_bits = p.nblk_bits;
+            a.tpw_bits = p.tpw_bits;
+            a.tt_bits = p.tt_bits;
+            a.do_scale = do_scale;
+            a.ld_nt = (multi && i == 0) ? 1 : 0;
+            a.st_nt = (multi && final_pass) ? 1 : 0;
+            a.scale = plan->dtype == FWT_F64 ? c : (double)(float)c;
+            e = qse::launch_tile_pass(p.key, re, im, ncomp, a, p.block, p.lds, stream,
+                                      i == first ? start : nullptr,
+                                      i == last - 1 ? stop : nullptr);
+        }
+        if (e != hipSuccess)
+            return hip_fail(e);
+    }
+    return FWT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -386,18 +480,18 @@ int fwt_plan_create(fwt_plan_t* out, int n, fwt_dtype dtype, fwt_path path)
     const int np = default_split(n, dtype, path, bits);
     if (np < 0)
         return FWT_EUNSUPPORTED;
-    return make_plan(out, n, dtype, np, bits, nullptr, nullptr);
+    return make_plan(out, n, dtype, np, bits, nullptr, nullptr, nullptr);
 }
 
 int fwt_plan_create_split(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* bits)
 {
-    return make_plan(out, n, dtype, npasses, bits, nullptr, nullptr);
+    return make_plan(out, n, dtype, npasses, bits, nullptr, nullptr, nullptr);
 }
 
 int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* bits,
-                          const int* eb, const int* gbits)
+                          const int* eb, const int* gbits, const int* phases)
 {
-    return make_plan(out, n, dtype, npasses, bits, eb, gbits);
+    return make_plan(out, n, dtype, npasses, bits, eb, gbits, phases);
 }
 
 int fwt_execute_check(fwt_plan_t plan, int64_t batch, int n, const void* re, const void* im)
@@ -406,44 +500,6 @@ int fwt_execute_check(fwt_plan_t plan, int64_t batch, int n, const void* re, con
     return validate(plan, batch, n, re, im, &nothing);
 }
 
-namespace {
-
-// Enqueue passes [first, last) of a validated call.
-int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, void* re, void* im,
-                  int normalize, hipStream_t stream)
-{
-    int rc = ensure_device_init();
-    if (rc != FWT_OK)
-        return rc;
-    const int ncomp = im ? 2 : 1;
-    const double c = norm_constant(n);
-    for (int i = first; i < last; ++i) {
-        const Pass& p = plan->passes[i];
-        const bool final_pass = (i == plan->npasses - 1);
-        const int do_scale = (normalize && final_pass) ? 1 : 0;
-        hipError_t e;
-        if (p.pair) {
-            e = qse::launch_pair_f32((float*)re, (float*)im, batch, do_scale, (float)c, stream);
-        } else {
-            TileArgs a{};
-            a.tiles = batch << p.tiles_bits;
-            a.wg_count = (a.tiles + ((int64_t)1 << p.tpw_bits) - 1) >> p.tpw_bits;
-            a.lo = p.lo;
-            a.nblk_bits = p.nblk_bits;
-            a.tpw_bits = p.tpw_bits;
-            a.tt_bits = p.tt_bits;
-            a.do_scale = do_scale;
-            a.scale = plan->dtype == FWT_F64 ? c : (double)(float)c;
-            e = qse::launch_tile_pass(p.key, re, im, ncomp, a, p.block, p.lds, stream);
-        }
-        if (e != hipSuccess)
-            return hip_fail(e);
-    }
-    return FWT_OK;
-}
-
-}  // namespace
-
 int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im, int normalize,
                 hipStream_t stream)
 {
@@ -451,7 +507,19 @@ int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im, int n
     const int rc = validate(plan, batch, n, re, im, &nothing);
     if (rc != FWT_OK || nothing)
         return rc;
-    return launch_passes(plan, 0, plan->npasses, batch, n, re, im, normalize, stream);
+    const int64_t cv = chunk_vectors(plan, batch, im ? 2 : 1);
+    if (cv == 0)
+        return launch_passes(plan, 0, plan->npasses, batch, n, re, im, normalize, stream);
+    const size_t vec_bytes = ((size_t)1 << n) * (plan->dtype == FWT_F64 ? 8 : 4);
+    for (int64_t b0 = 0; b0 < batch; b0 += cv) {
+        const int64_t nb = batch - b0 < cv ? batch - b0 : cv;
+        void* cre = (char*)re + (size_t)b0 * vec_bytes;
+        void* cim = im ? (char*)im + (size_t)b0 * vec_bytes : nullptr;
+        const int r = launch_passes(plan, 0, plan->npasses, nb, n, cre, cim, normalize, stream);
+        if (r != FWT_OK)
+            return r;
+    }
+    return FWT_OK;
 }
 
 int fwt_execute_pass(fwt_plan_t plan, int pass, int64_t batch, int n, void* re, void* im,
@@ -464,6 +532,26 @@ int fwt_execute_pass(fwt_plan_t plan, int pass, int64_t batch, int n, void* re, 
     if (rc != FWT_OK || nothing)
         return rc;
     return launch_passes(plan, pass, pass + 1, batch, n, re, im, normalize, stream);
+}
+
+int fwt_execute_pass_timed(fwt_plan_t plan, int pass, int64_t batch, int n, void* re, void* im,
+                           int normalize, hipStream_t stream, hipEvent_t start, hipEvent_t stop)
+{
+    if (!valid_plan(plan) || pass < 0 || pass >= plan->npasses || !start || !stop)
+        return FWT_EINVAL;
+    bool nothing = false;
+    const int rc = validate(plan, batch, n, re, im, &nothing);
+    if (rc != FWT_OK || nothing)
+        return rc == FWT_OK ? FWT_EINVAL : rc;   // nothing to time
+    return launch_passes(plan, pass, pass + 1, batch, n, re, im, normalize, stream, start, stop);
+}
+
+int fwt_plan_chunk_vectors(fwt_plan_t plan, int64_t batch, int with_im, int64_t* out)
+{
+    if (!valid_plan(plan) || !out || batch < 0)
+        return FWT_EINVAL;
+    *out = chunk_vectors(plan, batch, with_im ? 2 : 1);
+    return FWT_OK;
 }
 
 int fwt_plan_num_passes(fwt_plan_t plan, int* out_passes)
@@ -479,6 +567,24 @@ int fwt_plan_pass_bits(fwt_plan_t plan, int i, int* out_bits)
     if (!valid_plan(plan) || !out_bits || i < 0 || i >= plan->npasses)
         return FWT_EINVAL;
     *out_bits = plan->passes[i].k;
+    return FWT_OK;
+}
+
+int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out)
+{
+    if (!valid_plan(plan) || !out || i < 0 || i >= plan->npasses)
+        return FWT_EINVAL;
+    const Pass& p = plan->passes[i];
+    out[0] = p.lo;
+    out[1] = p.k;
+    out[2] = p.pair ? 2 : (p.key.row ? 0 : 1);
+    out[3] = p.key.kr;
+    out[4] = p.key.eb;
+    out[5] = p.gbits;
+    out[6] = p.phb;
+    out[7] = (int)p.block;
+    out[8] = (int)p.lds;
+    out[9] = p.tpw_bits;
     return FWT_OK;
 }
 

@@ -23,16 +23,20 @@ struct TileArgs {
     int tpw_bits;        // log2 of tiles per workgroup
     int tt_bits;         // log2 of threads per tile
     int do_scale;        // multiply by `scale` before the final store
+    int ld_nt;           // nontemporal loads (input not reused by this call)
+    int st_nt;           // nontemporal stores (output not reused by this call)
     double scale;        // 2^(-n/2) rounded to the element type
 };
 
 // Kernel variant: element type, row bits KR, register-round bits EB,
-// column-group bits GB, and whether it is a row (contiguous) pass.
+// column-group bits GB, exchange-phase bits PHB, and whether it is a row
+// (contiguous) pass.
 struct KernelKey {
     int f64;   // 0: float, 1: double
     int kr;    // log2 rows per tile
     int eb;    // log2 16-byte vectors per thread per round
     int gb;    // log2 16-byte column groups per tile (0 for row passes)
+    int phb;   // log2 of the phases an LDS exchange is split into
     int row;   // 1: contiguous row pass
 };
 
@@ -64,15 +68,16 @@ bool kernel_available(const KernelKey& key);
 hipError_t kernels_init_device();
 
 // Enqueue one tile pass.  `re` and `im` (im may be null) are device
-// pointers; ncomp = 1 or 2.
+// pointers; ncomp = 1 or 2.  start/stop (may be null) are recorded by the
+// dispatch itself at the kernel's start and end.
 hipError_t launch_tile_pass(const KernelKey& key, void* re, void* im, int ncomp,
                             const TileArgs& args, unsigned block, size_t lds_bytes,
-                            hipStream_t stream);
+                            hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 // Enqueue the two-element transform used for fp32 vectors of 2 elements
 // (n = 1): pairs (a, b) -> (a + b, a - b) * scale.
 hipError_t launch_pair_f32(float* re, float* im, int64_t pairs, int do_scale,
-                           float scale, hipStream_t stream);
+                           float scale, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 // Enqueue a 16-byte streaming copy of `bytes` (a multiple of 16).
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes,

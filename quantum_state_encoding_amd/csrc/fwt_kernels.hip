@@ -24,6 +24,7 @@
 // Global accesses are 16-byte vector loads and stores in which consecutive
 // lanes touch consecutive 16-byte chunks (consecutive rows of a row pass,
 // or the G column groups of a row of a column pass).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <vector>
@@ -102,63 +103,78 @@ __host__ __device__ constexpr int round_lo(int kr, int eb, int r)
     return kr - eb * (r + 1) > 0 ? kr - eb * (r + 1) : 0;
 }
 
-// LDS layout of a tile: 16-byte slot s = (row << GB) | g, stored at
-// s + (s >> P) with P = EB + GB, i.e. one pad slot after every 2^P
-// slots.  For every layout of the kernel, the 8 (or 16) lanes that the LDS
-// serves together then fall on distinct bank groups: lanes holding
-// consecutive slots stay consecutive, and lanes whose slots are 2^P apart
-// are shifted by one slot each.  Because the thread part and the register
-// part of a slot are disjoint bit fields, s + (s >> P) splits into a
-// per-thread base plus a per-register constant, so each access is one
-// address register plus an immediate offset.
-template <int A, int EB, int GB>
+// LDS layout of one exchange phase of a tile.  A tile's 2^GB column
+// groups never mix, so an exchange may run in 2^PHB phases, each moving the
+// 2^GL (GL = GB - PHB) column groups of one phase through an LDS region
+// 2^PHB times smaller than the tile; threads of the other groups wait at
+// the phase's barriers.  Within a phase, 16-byte slot s = (row << GL) | gl
+// (gl = the group within the phase) is stored at s + (s >> P) with
+// P = EB + GL, i.e. one pad slot after every 2^P slots.  For every layout
+// of the kernel, the 8 (or 16) lanes that the LDS serves together then
+// fall on distinct bank groups: lanes holding consecutive slots stay
+// consecutive, and lanes whose slots are 2^P apart are shifted by one slot
+// each.  Because the thread part and the register part of a slot are
+// disjoint bit fields, s + (s >> P) splits into a per-thread base plus a
+// per-register constant, so each access is one address register plus an
+// immediate offset.
+template <int A, int EB, int GL>
 struct LdsLayout {
-    static constexpr int P = EB + GB;
+    static constexpr int P = EB + GL;
     int base;  // padded slot of register 0 for this thread
-    __device__ __forceinline__ LdsLayout(int tau, int g)
+    __device__ __forceinline__ LdsLayout(int tau, int gl)
     {
-        const int s = (row_thread_part<A, EB>(tau) << GB) | g;
+        const int s = (row_thread_part<A, EB>(tau) << GL) | gl;
         base = s + (s >> P);
     }
     // Padded offset of register j from register 0 (a compile-time constant
     // once j is unrolled).
     __device__ __forceinline__ static constexpr int offset(int j)
     {
-        return ((j << A) << GB) + (((j << A) << GB) >> P);
+        return ((j << A) << GL) + (((j << A) << GL) >> P);
     }
 };
 
-template <typename V, int AF, int AT, int EB, int GB>
+template <typename V, int AF, int AT, int EB, int GB, int PHB>
 __device__ __forceinline__ void exchange(V* x, V* L, int tau, int g)
 {
     constexpr int E = 1 << EB;
-    const LdsLayout<AF, EB, GB> from(tau, g);
+    constexpr int GL = GB - PHB;
+    const int gl = g & ((1 << GL) - 1);
+    const int my_phase = g >> GL;
+    const LdsLayout<AF, EB, GL> from(tau, gl);
+    const LdsLayout<AT, EB, GL> to(tau, gl);
 #pragma unroll
-    for (int j = 0; j < E; ++j)
-        L[from.base + LdsLayout<AF, EB, GB>::offset(j)] = x[j];
-    __syncthreads();
-    const LdsLayout<AT, EB, GB> to(tau, g);
+    for (int ph = 0; ph < (1 << PHB); ++ph) {
+        if (PHB == 0 || my_phase == ph) {
 #pragma unroll
-    for (int j = 0; j < E; ++j)
-        x[j] = L[to.base + LdsLayout<AT, EB, GB>::offset(j)];
-    __syncthreads();
+            for (int j = 0; j < E; ++j)
+                L[from.base + LdsLayout<AF, EB, GL>::offset(j)] = x[j];
+        }
+        __syncthreads();
+        if (PHB == 0 || my_phase == ph) {
+#pragma unroll
+            for (int j = 0; j < E; ++j)
+                x[j] = L[to.base + LdsLayout<AT, EB, GL>::offset(j)];
+        }
+        __syncthreads();
+    }
 }
 
 // Rounds 1 .. NR-1: exchange into round R's layout, then the stages on the
 // row bits [round_lo(R), round_lo(R-1)) that no earlier round did.
-template <typename V, int KR, int EB, int GB, int R, int NR>
+template <typename V, int KR, int EB, int GB, int PHB, int R, int NR>
 struct Rounds {
     __device__ __forceinline__ static void run(V* x, V* L, int tau, int g)
     {
         constexpr int AP = round_lo(KR, EB, R - 1);
         constexpr int AC = round_lo(KR, EB, R);
-        exchange<V, AP, AC, EB, GB>(x, L, tau, g);
+        exchange<V, AP, AC, EB, GB, PHB>(x, L, tau, g);
         register_stages<AP - AC, (1 << EB)>(x);
-        Rounds<V, KR, EB, GB, R + 1, NR>::run(x, L, tau, g);
+        Rounds<V, KR, EB, GB, PHB, R + 1, NR>::run(x, L, tau, g);
     }
 };
-template <typename V, int KR, int EB, int GB, int NR>
-struct Rounds<V, KR, EB, GB, NR, NR> {
+template <typename V, int KR, int EB, int GB, int PHB, int NR>
+struct Rounds<V, KR, EB, GB, PHB, NR, NR> {
     __device__ __forceinline__ static void run(V*, V*, int, int) {}
 };
 
@@ -175,18 +191,31 @@ struct GlobalLayout {
     }
 };
 
+// 16-byte global accesses; the nontemporal forms mark data that this
+// pass will not touch again (a first pass's input, a last pass's output),
+// so that the caches keep the intermediate data between passes.
 template <typename V>
 __device__ __forceinline__ V load16(const unsigned char* p, uint32_t off)
 {
     return *reinterpret_cast<const V*>(p + off);
 }
 template <typename V>
+__device__ __forceinline__ V load16_nt(const unsigned char* p, uint32_t off)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const V*>(p + off));
+}
+template <typename V>
 __device__ __forceinline__ void store16(unsigned char* p, uint32_t off, const V& v)
 {
     *reinterpret_cast<V*>(p + off) = v;
 }
+template <typename V>
+__device__ __forceinline__ void store16_nt(unsigned char* p, uint32_t off, const V& v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<V*>(p + off));
+}
 
-template <typename T, int KR, int EB, int GB, bool ROW>
+template <typename T, int KR, int EB, int GB, int PHB, bool ROW>
 __global__ void __launch_bounds__(EB >= 5 ? 512 : 1024)
     tile_kernel(T* __restrict__ re, T* __restrict__ im, TileArgs a)
 {
@@ -198,6 +227,7 @@ __global__ void __launch_bounds__(EB >= 5 ? 512 : 1024)
     constexpr int AL = round_lo(KR, EB, NR - 1);
     static_assert(EB <= KR || (KR == 0 && EB == 0), "EB must not exceed KR");
     static_assert(!ROW || GB == 0, "row passes have one column group");
+    static_assert(PHB <= GB, "at most one phase per column group");
     // Store from the load layout (one more exchange) when the last round's
     // layout would give consecutive lanes runs shorter than 128 bytes.
     constexpr bool STORE_BACK = store_back(KR, EB, GB);
@@ -209,8 +239,8 @@ __global__ void __launch_bounds__(EB >= 5 ? 512 : 1024)
     const int tt = tid & ((1 << a.tt_bits) - 1);      // thread within the tile
     const int g = tt & ((1 << GB) - 1);               // column group
     const int tau = tt >> GB;                         // row-thread index
-    constexpr int tile_slots = 1 << (KR + GB);
-    V* const L = reinterpret_cast<V*>(lds_raw) + tl * (tile_slots + (tile_slots >> (EB + GB)));
+    constexpr int phase_slots = 1 << (KR + GB - PHB);
+    V* const L = reinterpret_cast<V*>(lds_raw) + tl * (phase_slots + (phase_slots >> (EB + GB - PHB)));
 
     // Workgroup-uniform base of its first tile; lanes address from it with
     // 32-bit byte offsets (a pass's tile span is below 4 GiB).
@@ -237,7 +267,11 @@ __global__ void __launch_bounds__(EB >= 5 ? 512 : 1024)
 
     V x[E];
     const GlobalLayout<A0, EB> gl0(lane_bytes, tau, row_bytes);
-    if (active) {
+    if (active && a.ld_nt) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] = load16_nt<V>(p, gl0.base + (uint32_t)j * gl0.jstride);
+    } else if (active) {
 #pragma unroll
         for (int j = 0; j < E; ++j)
             x[j] = load16<V>(p, gl0.base + (uint32_t)j * gl0.jstride);
@@ -253,7 +287,7 @@ __global__ void __launch_bounds__(EB >= 5 ? 512 : 1024)
             in_vector(x[j]);
     }
     register_stages<EB, E>(x);
-    Rounds<V, KR, EB, GB, 1, NR>::run(x, L, tau, g);
+    Rounds<V, KR, EB, GB, PHB, 1, NR>::run(x, L, tau, g);
 
     if (a.do_scale) {
         const T scale = (T)a.scale;
@@ -262,18 +296,20 @@ __global__ void __launch_bounds__(EB >= 5 ? 512 : 1024)
             x[j] *= scale;
     }
 
-    if constexpr (STORE_BACK) {
-        exchange<V, AL, A0, EB, GB>(x, L, tau, g);
-        if (active) {
-#pragma unroll
-            for (int j = 0; j < E; ++j)
-                store16<V>(p, gl0.base + (uint32_t)j * gl0.jstride, x[j]);
-        }
-    } else if (active) {
-        const GlobalLayout<AL, EB> gll(lane_bytes, tau, row_bytes);
+    // Final layout: the load layout after one more exchange, or the last
+    // round's layout.
+    constexpr int AF = STORE_BACK ? A0 : AL;
+    if constexpr (STORE_BACK)
+        exchange<V, AL, A0, EB, GB, PHB>(x, L, tau, g);
+    const GlobalLayout<AF, EB> glf(lane_bytes, tau, row_bytes);
+    if (active && a.st_nt) {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            store16<V>(p, gll.base + (uint32_t)j * gll.jstride, x[j]);
+            store16_nt<V>(p, glf.base + (uint32_t)j * glf.jstride, x[j]);
+    } else if (active) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            store16<V>(p, glf.base + (uint32_t)j * glf.jstride, x[j]);
     }
 }
 
@@ -328,23 +364,31 @@ struct Entry {
     const void* fn;
 };
 
-template <typename T, bool ROW, int KR, int EB, int GB>
+template <typename T, bool ROW, int KR, int EB, int GB, int PHB>
 void add_variant(std::vector<Entry>& v)
 {
-    v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, ROW ? 1 : 0},
-                 reinterpret_cast<const void*>(&tile_kernel<T, KR, EB, GB, ROW>)});
+    v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, PHB, ROW ? 1 : 0},
+                 reinterpret_cast<const void*>(&tile_kernel<T, KR, EB, GB, PHB, ROW>)});
 }
 
-// Column groups 2^GB for GB in [0, GBMAX] whose tile fits 160 KiB of LDS
-// and 1024 (EB <= 4) or 512 (EB = 5) threads.
+// Column groups 2^GB for GB in [0, 4] (row passes: GB = 0) whose tile fits
+// 160 KiB of LDS and 1024 (EB <= 4) or 512 (EB = 5) threads; column passes
+// of at least 9 row bits and 8 groups also get the phased exchange
+// (PHB = 1, 2).
 template <typename T, bool ROW, int KR, int EB, int GB>
 void add_groups(std::vector<Entry>& v)
 {
-    constexpr long slots = 1L << (KR + GB);
-    constexpr long lds = 16 * (slots + (slots >> (EB + GB)));
     constexpr int max_tt_bits = EB >= 5 ? 9 : 10;
-    if constexpr ((KR <= EB || lds <= 160 * 1024) && (KR - EB + GB) <= max_tt_bits)
-        add_variant<T, ROW, KR, EB, GB>(v);
+    if constexpr ((KR - EB + GB) <= max_tt_bits) {
+        constexpr long slots = 1L << (KR + GB);
+        constexpr long lds = 16 * (slots + (slots >> (EB + GB)));
+        if constexpr (KR <= EB || lds <= 160 * 1024)
+            add_variant<T, ROW, KR, EB, GB, 0>(v);
+        if constexpr (!ROW && KR >= 9 && GB >= 3 && KR > EB) {
+            add_variant<T, ROW, KR, EB, GB, 1>(v);
+            add_variant<T, ROW, KR, EB, GB, 2>(v);
+        }
+    }
     if constexpr (!ROW && GB < 4)
         add_groups<T, ROW, KR, EB, GB + 1>(v);
 }
@@ -382,7 +426,7 @@ const void* find(const KernelKey& k)
 {
     for (const Entry& e : table())
         if (e.key.f64 == k.f64 && e.key.kr == k.kr && e.key.eb == k.eb && e.key.gb == k.gb &&
-            e.key.row == k.row)
+            e.key.phb == k.phb && e.key.row == k.row)
             return e.fn;
     return nullptr;
 }
@@ -404,21 +448,29 @@ hipError_t kernels_init_device()
 
 hipError_t launch_tile_pass(const KernelKey& key, void* re, void* im, int ncomp,
                             const TileArgs& args, unsigned block, size_t lds_bytes,
-                            hipStream_t stream)
+                            hipStream_t stream, hipEvent_t start, hipEvent_t stop)
 {
     const void* fn = find(key);
     if (!fn)
         return hipErrorInvalidDeviceFunction;
     // One workgroup per group of 2^tpw_bits tiles; grids beyond 2^30
-    // workgroups are split into several launches.
+    // workgroups are split into several launches.  Timing events, when
+    // given, are recorded at the first launch's start and the last launch's
+    // end by the dispatch itself.
     constexpr int64_t kMaxGrid = (int64_t)1 << 30;
     TileArgs a = args;
     for (int64_t w0 = 0; w0 < args.wg_count; w0 += kMaxGrid) {
         const int64_t nw = args.wg_count - w0 < kMaxGrid ? args.wg_count - w0 : kMaxGrid;
+        const bool first = (w0 == 0), last = (w0 + nw >= args.wg_count);
         a.tile0 = w0 << args.tpw_bits;
         void* kargs[] = {&re, &im, &a};
-        const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nw, (unsigned)ncomp, 1),
-                                             dim3(block, 1, 1), kargs, lds_bytes, stream);
+        const dim3 grid((unsigned)nw, (unsigned)ncomp, 1);
+        hipError_t e;
+        if (start || stop)
+            e = hipExtLaunchKernel(fn, grid, dim3(block, 1, 1), kargs, lds_bytes, stream,
+                                   first ? start : nullptr, last ? stop : nullptr, 0);
+        else
+            e = hipLaunchKernel(fn, grid, dim3(block, 1, 1), kargs, lds_bytes, stream);
         if (e != hipSuccess)
             return e;
     }
@@ -426,13 +478,16 @@ hipError_t launch_tile_pass(const KernelKey& key, void* re, void* im, int ncomp,
 }
 
 hipError_t launch_pair_f32(float* re, float* im, int64_t pairs, int do_scale, float scale,
-                           hipStream_t stream)
+                           hipStream_t stream, hipEvent_t start, hipEvent_t stop)
 {
     const int64_t blocks64 = (pairs + 255) / 256;
     const unsigned blocks = (unsigned)(blocks64 < 65536 ? (blocks64 > 0 ? blocks64 : 1) : 65536);
-    hipLaunchKernelGGL(pair_f32_kernel, dim3(blocks, im ? 2 : 1, 1), dim3(256, 1, 1), 0, stream,
-                       re, im, pairs, do_scale, scale);
-    return hipGetLastError();
+    void* kargs[] = {&re, &im, &pairs, &do_scale, &scale};
+    const void* fn = reinterpret_cast<const void*>(&pair_f32_kernel);
+    const dim3 grid(blocks, im ? 2 : 1, 1);
+    if (start || stop)
+        return hipExtLaunchKernel(fn, grid, dim3(256, 1, 1), kargs, 0, stream, start, stop, 0);
+    return hipLaunchKernel(fn, grid, dim3(256, 1, 1), kargs, 0, stream);
 }
 
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream)

@@ -40,15 +40,15 @@ def _create(lib, n, dtype=0, path=0):
     return st, h
 
 
-def _split(lib, n, dtype, bits, eb=None, gbits=None):
+def _split(lib, n, dtype, bits, eb=None, gbits=None, phases=None):
     h = ctypes.c_void_p()
     arr = (ctypes.c_int * len(bits))(*bits)
-    if eb is None and gbits is None:
+    if eb is None and gbits is None and phases is None:
         st = lib.fwt_plan_create_split(ctypes.byref(h), n, dtype, len(bits), arr)
     else:
-        e = (ctypes.c_int * len(bits))(*eb) if eb is not None else None
-        g = (ctypes.c_int * len(bits))(*gbits) if gbits is not None else None
-        st = lib.fwt_plan_create_tuned(ctypes.byref(h), n, dtype, len(bits), arr, e, g)
+        mk = lambda v: (ctypes.c_int * len(bits))(*v) if v is not None else None
+        st = lib.fwt_plan_create_tuned(ctypes.byref(h), n, dtype, len(bits), arr, mk(eb),
+                                       mk(gbits), mk(phases))
     if st == 0:
         lib.fwt_plan_destroy(h)
     return st
@@ -72,8 +72,19 @@ def test_plan_shapes_of_the_workloads(lib):
     assert qse.Plan(12, "f32").pass_bits == [12]
     assert qse.Plan(14, "f32").pass_bits == [14]
     assert qse.Plan(14, "f32", split=(7, 7)).pass_bits == [7, 7]
-    assert qse.Plan(20, "f32").num_passes == 2
-    assert qse.Plan(24, "f64").num_passes == 2
+    assert qse.Plan(20, "f32").pass_bits == [13, 7]
+    assert qse.Plan(24, "f64").pass_bits == [14, 10]
+    assert qse.Plan(24, "f32").pass_bits == [13, 11]
+    assert qse.Plan(25, "f32").pass_bits == [10, 8, 7]
+
+
+def test_chunk_schedule(lib):
+    p20 = qse.Plan(20, "f32")
+    assert p20.chunk_vectors(256, True) == 32       # 8 MiB per complex vector, 256 MiB chunks
+    assert p20.chunk_vectors(256, False) == 64
+    assert p20.chunk_vectors(32, True) == 0         # fits: one chunk
+    assert qse.Plan(24, "f64").chunk_vectors(16, True) == 1
+    assert qse.Plan(12, "f32").chunk_vectors(10**6, True) == 0   # single pass: never chunked
     assert qse.Plan(14, "f32", path=qse.PATH_MULTIPASS).pass_bits == [7, 7]
     assert qse.Plan(15, "f32", path=qse.PATH_SINGLE_BLOCK).pass_bits == [15]
 
@@ -114,6 +125,14 @@ def test_tuned_validation(lib):
     assert _split(lib, 16, 0, [8, 8], gbits=[0, 7]) == qse.FWT_EINVAL   # too many groups
     assert _split(lib, 12, 0, [2, 10], gbits=[0, 1]) == qse.FWT_EINVAL  # only 1 group in a row
     assert _split(lib, 24, 1, [12, 12], gbits=[0, 3]) == qse.FWT_EINVAL  # tile > 160 KiB
+    assert _split(lib, 24, 1, [14, 10], gbits=[-1, 3], phases=[-1, 1]) == 0
+    assert _split(lib, 24, 1, [14, 10], gbits=[-1, 3], phases=[-1, 2]) == 0
+    assert _split(lib, 24, 1, [14, 10], gbits=[-1, 3], phases=[-1, 0]) == 0   # 128 KiB, 1 tile/CU
+    assert _split(lib, 24, 1, [14, 10], gbits=[-1, 2], phases=[-1, 3]) == qse.FWT_EINVAL
+    assert _split(lib, 20, 0, [13, 7], phases=[-1, 1]) == qse.FWT_EINVAL    # < 9 column bits
+    assert _split(lib, 20, 0, [13, 7], phases=[1, -1]) == qse.FWT_EINVAL    # row pass
+    # a forced group count that breaks the thread limit is rejected, not replaced
+    assert _split(lib, 16, 0, [6, 10], eb=[-1, 3], gbits=[-1, 4]) == qse.FWT_EINVAL
 
 
 def test_destroy(lib):

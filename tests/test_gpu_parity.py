@@ -125,27 +125,33 @@ def test_integer_forced_splits(dtype, n, split):
 
 
 def _variants():
-    out = []
+    out = [("f64", 14, (4, 10), (-1, 4), (-1, 3), (-1, 1)),
+           ("f64", 14, (4, 10), (-1, 4), (-1, 3), (-1, 2)),
+           ("f64", 15, (4, 11), (-1, 4), (-1, 3), (-1, 2)),
+           ("f32", 16, (5, 11), (-1, 4), (-1, 3), (-1, 2)),
+           ("f32", 16, (6, 10), (-1, 3), (-1, 3), (-1, 1)),
+           ("f32", 16, (6, 10), (-1, 4), (-1, 4), (-1, 2)),
+           ("f32", 21, (12, 9), (-1, 4), (-1, 4), (-1, 1))]
     for dtype in ("f32", "f64"):
         vb = 2 if dtype == "f32" else 1
         for row_eb in (3, 4, 5):
-            out.append((dtype, 8 + vb + 8, (8 + vb, 8), (row_eb, 4), (-1, -1)))
+            out.append((dtype, 8 + vb + 8, (8 + vb, 8), (row_eb, 4), (-1, -1), None))
         for col_eb in (3, 4):
             for gb in range(0, 5):
-                out.append((dtype, 8 + vb + 8, (8 + vb, 8), (4, col_eb), (-1, gb)))
-        out.append((dtype, 3 + vb + 10, (3 + vb, 10), (3, 4), (-1, 0)))
-        out.append((dtype, 12 + vb, (12 + vb,), (5,), (-1,)))
-        out.append((dtype, 12 + vb, (12 + vb,), (3,), (-1,)))
+                out.append((dtype, 8 + vb + 8, (8 + vb, 8), (4, col_eb), (-1, gb), None))
+        out.append((dtype, 3 + vb + 10, (3 + vb, 10), (3, 4), (-1, 0), None))
+        out.append((dtype, 12 + vb, (12 + vb,), (5,), (-1,), None))
+        out.append((dtype, 12 + vb, (12 + vb,), (3,), (-1,), None))
     return out
 
 
-@pytest.mark.parametrize("dtype,n,split,eb,gbits", _variants())
-def test_integer_kernel_variants(dtype, n, split, eb, gbits):
-    say("variant %s n=%d split=%s eb=%s gbits=%s" % (dtype, n, split, eb, gbits))
+@pytest.mark.parametrize("dtype,n,split,eb,gbits,phases", _variants())
+def test_integer_kernel_variants(dtype, n, split, eb, gbits, phases):
+    say("variant %s n=%d split=%s eb=%s gbits=%s phases=%s" % (dtype, n, split, eb, gbits, phases))
     npd = np.float32 if dtype == "f32" else np.float64
     re = ints((2, 1 << n), 50_000 + n, npd)
     im = ints((2, 1 << n), 60_000 + n, npd)
-    plan = qse.Plan(n, dtype, split=split, eb=eb, gbits=gbits)
+    plan = qse.Plan(n, dtype, split=split, eb=eb, gbits=gbits, phases=phases)
     gre, gim = run(plan, re, im, False)
     assert_exact(gre, re, n, False)
     assert_exact(gim, im, n, False)
@@ -163,6 +169,24 @@ def test_ragged_batches(dtype, n, batch):
     gre, gim = run(qse.Plan(n, dtype), re, im, False)
     assert_exact(gre, re, n, False)
     assert_exact(gim, im, n, False)
+
+
+@pytest.mark.parametrize("dtype,n,batch", [("f32", 20, 37), ("f32", 21, 20), ("f64", 22, 5),
+                                           ("f32", 20, 33)])
+def test_integer_chunked_schedule(dtype, n, batch):
+    """Calls larger than the Infinity Cache run in chunks of vectors
+    (including a ragged last chunk); every vector must still be exact."""
+    say("chunked %s n=%d batch=%d" % (dtype, n, batch))
+    npd = np.float32 if dtype == "f32" else np.float64
+    plan = qse.Plan(n, dtype)
+    cv = plan.chunk_vectors(batch, True)
+    assert 0 < cv < batch
+    re = ints((batch, 1 << n), 85_000 + n, npd)
+    im = ints((batch, 1 << n), 86_000 + n, npd)
+    gre, gim = run(plan, re, im, False)
+    for b in range(batch):
+        assert_exact(gre[b], re[b], n, False)
+        assert_exact(gim[b], im[b], n, False)
 
 
 # ---- floating point, odd n and the normalisation -----------------------------
@@ -311,6 +335,32 @@ def test_validation_on_device_memory():
     with pytest.raises(qse.FwtError):
         plan.execute(re, re)   # same buffer twice
     assert plan.execute_raw(0, re.data_ptr(), im.data_ptr(), 1) == qse.FWT_OK
+
+
+def test_timed_passes_follow_the_chunk_schedule():
+    """Running every pass of every chunk with fwt_execute_pass_timed (the
+    benchmark's per-kernel timing) is exactly fwt_execute."""
+    say("timed passes")
+    n, batch = 20, 40
+    plan = qse.Plan(n, "f32")
+    cv = plan.chunk_vectors(batch, True)
+    assert 0 < cv < batch
+    re = ints((batch, 1 << n), 91, np.float32)
+    im = ints((batch, 1 << n), 92, np.float32)
+    tre, tim = to_dev(re), to_dev(im)
+    times = []
+    for c0 in range(0, batch, cv):
+        sl = slice(c0, min(batch, c0 + cv))
+        for i in range(plan.num_passes):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            plan.execute_pass_timed(i, tre[sl], tim[sl], a, b, normalize=False)
+            times.append((a, b))
+    torch.cuda.synchronize()
+    assert all(a.elapsed_time(b) > 0 for a, b in times)
+    gre, gim = run(plan, re, im, False)
+    assert np.array_equal(tre.cpu().numpy(), gre) and np.array_equal(tim.cpu().numpy(), gim)
+    assert_exact(gre[: 3], re[: 3], n, False)
 
 
 def test_stream_copy():
