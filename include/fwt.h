@@ -105,12 +105,16 @@ int fwt_plan_create_split(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
  *  phases per pass, log2 of the phases a column pass splits each LDS
  *         exchange into (0..2, at most gbits; column passes of >= 9 bits and
  *         >= 8 groups only), or -1 for the default; NULL = all defaults.
+ *  pipe   per pass, 1 for the persistent software-pipelined kernel (tiles
+ *         of >= 2^11 16-byte vectors in workgroups of <= 512 threads), 0
+ *         for one workgroup per tile group, -1 for the default (pipelined
+ *         when one workgroup fills a CU's LDS); NULL = all defaults.
  * Returns as fwt_plan_create_split, plus FWT_EINVAL for a value out of
  * range or a tile that exceeds the LDS or workgroup limits, and
  * FWT_EUNSUPPORTED for a variant that is not compiled in. */
 int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
                           const int* bits, const int* eb, const int* gbits,
-                          const int* phases);
+                          const int* phases, const int* pipe);
 
 /* Transform in place, asynchronously on `stream` (0 = the null stream).
  *  re, im   device buffers of batch * 2^n elements of the plan's dtype,
@@ -178,7 +182,8 @@ int fwt_plan_pass_bits(fwt_plan_t plan, int i, int* out_bits);
  * bit, bit count, kind (0 row pass, 1 column pass, 2 two-element kernel),
  * row bits KR of the tile, register-round bits EB, column-group bits,
  * exchange-phase bits, workgroup size, dynamic LDS bytes, log2 tiles per
- * workgroup.  `out` must hold 10 ints.  Returns FWT_OK or FWT_EINVAL. */
+ * workgroup, pipelined (1) or not (0).  `out` must hold 11 ints.  Returns
+ * FWT_OK or FWT_EINVAL. */
 int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out);
 
 /* Release a plan; NULL is a no-op.  Returns FWT_OK. */

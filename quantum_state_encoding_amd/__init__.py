@@ -68,7 +68,7 @@ def load_library():
     pi = ctypes.POINTER(ctypes.c_int)
     lib.fwt_plan_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32]
     lib.fwt_plan_create_split.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi]
-    lib.fwt_plan_create_tuned.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi, pi, pi, pi]
+    lib.fwt_plan_create_tuned.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi, pi, pi, pi, pi]
     lib.fwt_plan_chunk_vectors.argtypes = [vp, i64, i32, ctypes.POINTER(i64)]
     lib.fwt_execute.argtypes = [vp, i64, i32, vp, vp, i32, vp]
     lib.fwt_execute_pass.argtypes = [vp, i32, i64, i32, vp, vp, i32, vp]
@@ -113,19 +113,19 @@ class Plan:
     """A plan for 2^n-amplitude vectors of dtype "f32" or "f64".
 
     ``split`` (bit counts, lowest index bits first) forces a Kronecker
-    split; ``eb``/``gbits``/``phases`` (one entry per pass, -1 = default)
-    force the register-round width, column-group count and exchange phases
-    of each pass (tuning).
+    split; ``eb``/``gbits``/``phases``/``pipe`` (one entry per pass, -1 =
+    default) force the register-round width, column-group count, exchange
+    phases and pipelined kernel of each pass (tuning).
     """
 
     def __init__(self, n, dtype="f32", path=PATH_AUTO, split=None, eb=None, gbits=None,
-                 phases=None):
+                 phases=None, pipe=None):
         lib = load_library()
         if dtype not in _DTYPES:
             raise ValueError("dtype must be 'f32' or 'f64'")
         self.n, self.dtype = int(n), dtype
         h = ctypes.c_void_p()
-        tuned = eb is not None or gbits is not None or phases is not None
+        tuned = eb is not None or gbits is not None or phases is not None or pipe is not None
         if split is None and not tuned:
             st = lib.fwt_plan_create(ctypes.byref(h), self.n, _DTYPES[dtype], int(path))
         elif not tuned:
@@ -133,10 +133,11 @@ class Plan:
                                            len(split), _int_array(split))
         else:
             if split is None:
-                raise ValueError("eb/gbits/phases need an explicit split")
+                raise ValueError("eb/gbits/phases/pipe need an explicit split")
             st = lib.fwt_plan_create_tuned(ctypes.byref(h), self.n, _DTYPES[dtype],
                                            len(split), _int_array(split), _int_array(eb),
-                                           _int_array(gbits), _int_array(phases))
+                                           _int_array(gbits), _int_array(phases),
+                                           _int_array(pipe))
         if st != FWT_OK:
             raise FwtError(st, "fwt_plan_create(n=%d, %s)" % (self.n, dtype))
         self._h = h
@@ -165,12 +166,12 @@ class Plan:
 
     def pass_config(self, i):
         """Tiling of pass i as a dict (see fwt_plan_pass_config)."""
-        out = (ctypes.c_int * 10)()
+        out = (ctypes.c_int * 11)()
         st = load_library().fwt_plan_pass_config(self._h, int(i), out)
         if st != FWT_OK:
             raise FwtError(st, "fwt_plan_pass_config")
         keys = ("lo", "bits", "kind", "kr", "eb", "gbits", "phase_bits", "block", "lds",
-                "tpw_bits")
+                "tpw_bits", "pipe")
         d = dict(zip(keys, list(out)))
         d["kind"] = ("row", "column", "pair")[d["kind"]]
         return d
@@ -181,7 +182,8 @@ class Plan:
         if c["kind"] == "pair":
             return "pair_f32_kernel"
         t = "float" if self.dtype == "f32" else "double"
-        return "tile_kernel<%s, %d, %d, %d, %d, %s>" % (
+        return "%s<%s, %d, %d, %d, %d, %s>" % (
+            "tile_kernel_pipe" if c["pipe"] else "tile_kernel",
             t, c["kr"], c["eb"], c["gbits"], c["phase_bits"],
             "true" if c["kind"] == "row" else "false")
 

@@ -114,7 +114,7 @@ bool phases_allowed(int kr, int eb, int gbits, int phb)
 // eb_req / gbits_req / phb_req < 0 select defaults.  Returns FWT_OK or an
 // error.
 int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int gbits_req,
-               int phb_req)
+               int phb_req, int pipe_req)
 {
     const int vb = vec_bits(dtype);
     p = Pass{};
@@ -181,7 +181,9 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int g
             return FWT_EINVAL;
         p.nblk_bits = gmax_cols - gbits;
     }
-    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, gbits, phb, row ? 1 : 0};
+    if (pipe_req > 1)
+        return FWT_EINVAL;
+    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, gbits, phb, row ? 1 : 0, 0};
     p.gbits = gbits;
     p.phb = phb;
     p.tt_bits = (kr - eb) + gbits;
@@ -217,6 +219,20 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int g
     }
     if (!qse::kernel_available(p.key))
         return FWT_EUNSUPPORTED;
+    // Tiles so large that a CU holds one workgroup run in the persistent
+    // software-pipelined kernel, which streams the next tile group in while
+    // the current one is exchanged.
+    {
+        KernelKey pk = p.key;
+        pk.pipe = 1;
+        const bool one_per_cu = needs_lds && (tile_lds << tpw_bits) > kLdsMax / 2;
+        const bool want = pipe_req >= 0 ? pipe_req == 1 : one_per_cu;
+        const bool can = (1 << (p.tt_bits + tpw_bits)) <= 512 && qse::kernel_available(pk);
+        if (want && can)
+            p.key = pk;
+        else if (want && pipe_req == 1)
+            return FWT_EUNSUPPORTED;
+    }
     p.tpw_bits = tpw_bits;
     p.block = 1u << (p.tt_bits + tpw_bits);
     p.lds = needs_lds ? (tile_lds << tpw_bits) : 0;
@@ -264,7 +280,7 @@ int default_split(int n, fwt_dtype dtype, fwt_path path, int* bits)
 }
 
 int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* bits,
-              const int* ebs, const int* gbits, const int* phbs)
+              const int* ebs, const int* gbits, const int* phbs, const int* pipes)
 {
     if (!out)
         return FWT_EINVAL;
@@ -291,7 +307,8 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
     int lo = 0;
     for (int i = 0; i < p->npasses; ++i) {
         const int rc = build_pass(p->passes[i], n, dtype, lo, bits[i], ebs ? ebs[i] : -1,
-                                  gbits ? gbits[i] : -1, phbs ? phbs[i] : -1);
+                                  gbits ? gbits[i] : -1, phbs ? phbs[i] : -1,
+                                  pipes ? pipes[i] : -1);
         if (rc != FWT_OK) {
             delete p;
             return rc;
@@ -304,11 +321,11 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
         for (int i = 0; i < p->npasses; ++i) {
             const Pass& q = p->passes[i];
             std::fprintf(stderr,
-                         "[fwt]   pass %d: bits [%d,%d) %s kr=%d eb=%d G=%d phases=%d "
+                         "[fwt]   pass %d: bits [%d,%d) %s kr=%d eb=%d G=%d phases=%d pipe=%d "
                          "threads/tile=%d block=%u lds=%zu store_back=%d tiles/vec=2^%d\n",
                          i, q.lo, q.lo + q.k, q.pair ? "pair" : (q.key.row ? "row" : "col"),
-                         q.key.kr, q.key.eb, 1 << q.gbits, 1 << q.phb, 1 << q.tt_bits, q.block,
-                         q.lds, q.store_back, q.tiles_bits);
+                         q.key.kr, q.key.eb, 1 << q.gbits, 1 << q.phb, q.key.pipe,
+                         1 << q.tt_bits, q.block, q.lds, q.store_back, q.tiles_bits);
         }
     }
     *out = p;
@@ -317,25 +334,36 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
 
 bool valid_plan(fwt_plan_t p) { return p && p->magic == kPlanMagic; }
 
+constexpr int kMaxDevices = 64;
 std::mutex g_init_mutex;
 std::atomic<uint64_t> g_init_devices{0};
+int g_cu_count[kMaxDevices];
 
-int ensure_device_init()
+// Once per device: kernel attributes and the compute-unit count.  Returns
+// the CU count of the current device in *cus.
+int ensure_device_init(int* cus)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return hip_fail(e);
-    if (dev < 64 && (g_init_devices.load(std::memory_order_acquire) >> dev) & 1)
-        return FWT_OK;
-    std::lock_guard<std::mutex> lock(g_init_mutex);
-    if (dev < 64 && (g_init_devices.load() >> dev) & 1)
-        return FWT_OK;
-    e = qse::kernels_init_device();
-    if (e != hipSuccess)
-        return hip_fail(e);
-    if (dev < 64)
-        g_init_devices.fetch_or((uint64_t)1 << dev);
+    if (dev < 0 || dev >= kMaxDevices)
+        return FWT_EUNSUPPORTED;
+    if (!((g_init_devices.load(std::memory_order_acquire) >> dev) & 1)) {
+        std::lock_guard<std::mutex> lock(g_init_mutex);
+        if (!((g_init_devices.load() >> dev) & 1)) {
+            e = qse::kernels_init_device();
+            if (e != hipSuccess)
+                return hip_fail(e);
+            int n = 0;
+            e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess)
+                return hip_fail(e);
+            g_cu_count[dev] = n > 0 ? n : 1;
+            g_init_devices.fetch_or((uint64_t)1 << dev, std::memory_order_release);
+        }
+    }
+    *cus = g_cu_count[dev];
     return FWT_OK;
 }
 
@@ -424,7 +452,8 @@ int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, vo
                   int normalize, hipStream_t stream, hipEvent_t start = nullptr,
                   hipEvent_t stop = nullptr)
 {
-    int rc = ensure_device_init();
+    int cus = 1;
+    int rc = ensure_device_init(&cus);
     if (rc != FWT_OK)
         return rc;
     const int ncomp = im ? 2 : 1;
@@ -451,6 +480,10 @@ int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, vo
             a.ld_nt = (multi && i == 0) ? 1 : 0;
             a.st_nt = (multi && final_pass) ? 1 : 0;
             a.scale = plan->dtype == FWT_F64 ? c : (double)(float)c;
+            // Persistent kernels: as many workgroups as the CUs hold at once.
+            const int64_t per_cu = p.lds ? (int64_t)(kLdsMax / p.lds) : 1;
+            const int64_t total = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+            a.grid = total / ncomp > 0 ? total / ncomp : 1;
             e = qse::launch_tile_pass(p.key, re, im, ncomp, a, p.block, p.lds, stream,
                                       i == first ? start : nullptr,
                                       i == last - 1 ? stop : nullptr);
@@ -480,18 +513,18 @@ int fwt_plan_create(fwt_plan_t* out, int n, fwt_dtype dtype, fwt_path path)
     const int np = default_split(n, dtype, path, bits);
     if (np < 0)
         return FWT_EUNSUPPORTED;
-    return make_plan(out, n, dtype, np, bits, nullptr, nullptr, nullptr);
+    return make_plan(out, n, dtype, np, bits, nullptr, nullptr, nullptr, nullptr);
 }
 
 int fwt_plan_create_split(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* bits)
 {
-    return make_plan(out, n, dtype, npasses, bits, nullptr, nullptr, nullptr);
+    return make_plan(out, n, dtype, npasses, bits, nullptr, nullptr, nullptr, nullptr);
 }
 
 int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* bits,
-                          const int* eb, const int* gbits, const int* phases)
+                          const int* eb, const int* gbits, const int* phases, const int* pipe)
 {
-    return make_plan(out, n, dtype, npasses, bits, eb, gbits, phases);
+    return make_plan(out, n, dtype, npasses, bits, eb, gbits, phases, pipe);
 }
 
 int fwt_execute_check(fwt_plan_t plan, int64_t batch, int n, const void* re, const void* im)
@@ -585,6 +618,7 @@ int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out)
     out[7] = (int)p.block;
     out[8] = (int)p.lds;
     out[9] = p.tpw_bits;
+    out[10] = p.key.pipe;
     return FWT_OK;
 }
 

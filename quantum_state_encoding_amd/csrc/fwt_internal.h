@@ -18,6 +18,7 @@ struct TileArgs {
     int64_t tiles;       // tiles per component (real or imaginary buffer)
     int64_t wg_count;    // workgroups needed: ceil(tiles / tiles per workgroup)
     int64_t tile0;       // first tile of this launch (set by the launcher)
+    int64_t grid;        // persistent kernels: workgroups per component
     int lo;              // log2 of the element stride between rows (col passes)
     int nblk_bits;       // log2 of column blocks per outer index (col passes)
     int tpw_bits;        // log2 of tiles per workgroup
@@ -38,6 +39,7 @@ struct KernelKey {
     int gb;    // log2 16-byte column groups per tile (0 for row passes)
     int phb;   // log2 of the phases an LDS exchange is split into
     int row;   // 1: contiguous row pass
+    int pipe;  // 1: persistent software-pipelined kernel
 };
 
 // Number of register rounds of a (kr, eb) kernel: ceil(kr / eb), at least 1.

@@ -215,101 +215,192 @@ __device__ __forceinline__ void store16_nt(unsigned char* p, uint32_t off, const
     __builtin_nontemporal_store(v, reinterpret_cast<V*>(p + off));
 }
 
+// Compile-time shape of a tile kernel.
+template <typename T, int KR_, int EB_, int GB_, int PHB_, bool ROW_>
+struct Shape {
+    using Elem = T;
+    using V = typename Vec<T>::type;
+    static constexpr int KR = KR_, EB = EB_, GB = GB_, PHB = PHB_;
+    static constexpr bool ROW = ROW_;
+    static constexpr int WB = Vec<T>::WB;
+    static constexpr int E = 1 << EB;
+    static constexpr int NR = rounds_of(KR, EB);
+    static constexpr int A0 = round_lo(KR, EB, 0);
+    static constexpr int AL = round_lo(KR, EB, NR - 1);
+    // Store from the load layout (one more exchange) when the last round's
+    // layout would give consecutive lanes runs shorter than 128 bytes.
+    static constexpr bool STORE_BACK = store_back(KR, EB, GB);
+    static constexpr int AF = STORE_BACK ? A0 : AL;   // layout of the final store
+    static constexpr int PHASE_SLOTS = 1 << (KR + GB - PHB);
+    static constexpr int TILE_LDS = PHASE_SLOTS + (PHASE_SLOTS >> (EB + GB - PHB));
+    static_assert(EB <= KR || (KR == 0 && EB == 0), "EB must not exceed KR");
+    static_assert(!ROW || GB == 0, "row passes have one column group");
+    static_assert(PHB <= GB, "at most one phase per column group");
+};
+
+// Where the lanes of one tile group (2^tpw_bits tiles) read and write:
+// a workgroup-uniform base pointer plus 32-bit lane offsets (a pass's tile
+// span is below 4 GiB).
+struct TileAddr {
+    unsigned char* p;
+    uint32_t lane_bytes;
+    uint32_t row_bytes;
+    bool active;
+};
+
+template <typename S, typename T>
+__device__ __forceinline__ TileAddr tile_addr(T* buf, const TileArgs& a, int64_t w, int tl, int g)
+{
+    const int64_t t0 = a.tile0 + (w << a.tpw_bits);
+    int64_t base;
+    TileAddr r;
+    if (S::ROW) {
+        base = t0 << (S::KR + S::WB);
+        r.lane_bytes = (uint32_t)tl << (S::KR + S::WB + (sizeof(T) == 8 ? 3 : 2));
+        r.row_bytes = 16;
+    } else {
+        const int64_t blk_mask = ((int64_t)1 << a.nblk_bits) - 1;
+        base = ((t0 >> a.nblk_bits) << (a.lo + S::KR)) + ((t0 & blk_mask) << (S::GB + S::WB));
+        const uint32_t tlo = (uint32_t)tl >> a.nblk_bits;
+        const uint32_t tlb = (uint32_t)tl & (uint32_t)blk_mask;
+        r.lane_bytes = ((tlo << (a.lo + S::KR)) + (tlb << (S::GB + S::WB))) * (uint32_t)sizeof(T) +
+                       ((uint32_t)g << 4);
+        r.row_bytes = (uint32_t)sizeof(T) << a.lo;
+    }
+    r.p = reinterpret_cast<unsigned char*>(buf + base);
+    r.active = t0 + tl < a.tiles;
+    return r;
+}
+
+template <typename S>
+__device__ __forceinline__ void load_tile(typename S::V* x, const TileAddr& ta, int tau, int nt)
+{
+    using V = typename S::V;
+    const GlobalLayout<S::A0, S::EB> gl(ta.lane_bytes, tau, ta.row_bytes);
+    if (ta.active && nt) {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            x[j] = load16_nt<V>(ta.p, gl.base + (uint32_t)j * gl.jstride);
+    } else if (ta.active) {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            x[j] = load16<V>(ta.p, gl.base + (uint32_t)j * gl.jstride);
+    } else {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            x[j] = V{};
+    }
+}
+
+// All stages of the tile: in-vector bits (row passes), the register bits of
+// the load layout, then the remaining rounds through LDS; then the scale
+// and, where the final layout differs from the last round's, one more
+// exchange.  Every exchange ends with a barrier, so LDS is free again when
+// this returns.
+template <typename S>
+__device__ __forceinline__ void process_tile(typename S::V* x, typename S::V* L, int tau, int g,
+                                             int do_scale, double scale)
+{
+    using V = typename S::V;
+    if (S::ROW) {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            in_vector(x[j]);
+    }
+    register_stages<S::EB, S::E>(x);
+    Rounds<V, S::KR, S::EB, S::GB, S::PHB, 1, S::NR>::run(x, L, tau, g);
+    if (do_scale) {
+        const typename S::Elem c = (typename S::Elem)scale;
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            x[j] *= c;
+    }
+    if constexpr (S::STORE_BACK)
+        exchange<V, S::AL, S::A0, S::EB, S::GB, S::PHB>(x, L, tau, g);
+}
+
+template <typename S>
+__device__ __forceinline__ void store_tile(const typename S::V* x, const TileAddr& ta, int tau,
+                                           int nt)
+{
+    using V = typename S::V;
+    const GlobalLayout<S::AF, S::EB> gl(ta.lane_bytes, tau, ta.row_bytes);
+    if (ta.active && nt) {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            store16_nt<V>(ta.p, gl.base + (uint32_t)j * gl.jstride, x[j]);
+    } else if (ta.active) {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            store16<V>(ta.p, gl.base + (uint32_t)j * gl.jstride, x[j]);
+    }
+}
+
+// One workgroup per tile group: load, transform, store.
 template <typename T, int KR, int EB, int GB, int PHB, bool ROW>
 __global__ void __launch_bounds__(EB >= 5 ? 512 : 1024)
     tile_kernel(T* __restrict__ re, T* __restrict__ im, TileArgs a)
 {
-    using V = typename Vec<T>::type;
-    constexpr int WB = Vec<T>::WB;
-    constexpr int E = 1 << EB;
-    constexpr int NR = KR <= EB ? 1 : 1 + (KR - EB + EB - 1) / EB;
-    constexpr int A0 = round_lo(KR, EB, 0);
-    constexpr int AL = round_lo(KR, EB, NR - 1);
-    static_assert(EB <= KR || (KR == 0 && EB == 0), "EB must not exceed KR");
-    static_assert(!ROW || GB == 0, "row passes have one column group");
-    static_assert(PHB <= GB, "at most one phase per column group");
-    // Store from the load layout (one more exchange) when the last round's
-    // layout would give consecutive lanes runs shorter than 128 bytes.
-    constexpr bool STORE_BACK = store_back(KR, EB, GB);
-
+    using S = Shape<T, KR, EB, GB, PHB, ROW>;
+    using V = typename S::V;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-
     const int tid = threadIdx.x;
     const int tl = tid >> a.tt_bits;                  // tile within the workgroup
     const int tt = tid & ((1 << a.tt_bits) - 1);      // thread within the tile
     const int g = tt & ((1 << GB) - 1);               // column group
     const int tau = tt >> GB;                         // row-thread index
-    constexpr int phase_slots = 1 << (KR + GB - PHB);
-    V* const L = reinterpret_cast<V*>(lds_raw) + tl * (phase_slots + (phase_slots >> (EB + GB - PHB)));
+    V* const L = reinterpret_cast<V*>(lds_raw) + tl * S::TILE_LDS;
 
-    // Workgroup-uniform base of its first tile; lanes address from it with
-    // 32-bit byte offsets (a pass's tile span is below 4 GiB).
-    const int64_t t0 = a.tile0 + ((int64_t)blockIdx.x << a.tpw_bits);
-    int64_t base;
-    uint32_t lane_bytes;
-    uint32_t row_bytes;
-    if (ROW) {
-        base = t0 << (KR + WB);
-        lane_bytes = (uint32_t)tl << (KR + WB + (sizeof(T) == 8 ? 3 : 2));
-        row_bytes = 16;
-    } else {
-        const int64_t blk_mask = ((int64_t)1 << a.nblk_bits) - 1;
-        base = ((t0 >> a.nblk_bits) << (a.lo + KR)) + ((t0 & blk_mask) << (GB + WB));
-        const uint32_t tlo = (uint32_t)tl >> a.nblk_bits;
-        const uint32_t tlb = (uint32_t)tl & (uint32_t)blk_mask;
-        lane_bytes = ((tlo << (a.lo + KR)) + (tlb << (GB + WB))) * (uint32_t)sizeof(T) +
-                     ((uint32_t)g << 4);
-        row_bytes = (uint32_t)sizeof(T) << a.lo;
-    }
-    unsigned char* const p =
-        reinterpret_cast<unsigned char*>((blockIdx.y ? im : re) + base);
-    const bool active = t0 + tl < a.tiles;
+    const TileAddr ta = tile_addr<S>(blockIdx.y ? im : re, a, blockIdx.x, tl, g);
+    V x[S::E];
+    load_tile<S>(x, ta, tau, a.ld_nt);
+    process_tile<S>(x, L, tau, g, a.do_scale, a.scale);
+    store_tile<S>(x, ta, tau, a.st_nt);
+}
 
-    V x[E];
-    const GlobalLayout<A0, EB> gl0(lane_bytes, tau, row_bytes);
-    if (active && a.ld_nt) {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            x[j] = load16_nt<V>(p, gl0.base + (uint32_t)j * gl0.jstride);
-    } else if (active) {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            x[j] = load16<V>(p, gl0.base + (uint32_t)j * gl0.jstride);
-    } else {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            x[j] = V{};
-    }
+// Persistent, software-pipelined form for tiles so large that a CU holds
+// only one: each workgroup walks tile groups blockIdx.x, blockIdx.x +
+// gridDim.x, ... and issues the next group's loads into a second register
+// set before transforming the current one, so the CU keeps HBM busy while
+// its tile goes through the LDS exchanges (barriers wait on LDS only).
+template <typename T, int KR, int EB, int GB, int PHB, bool ROW>
+__global__ void __launch_bounds__(512)
+    tile_kernel_pipe(T* __restrict__ re, T* __restrict__ im, TileArgs a)
+{
+    using S = Shape<T, KR, EB, GB, PHB, ROW>;
+    using V = typename S::V;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    const int tid = threadIdx.x;
+    const int tl = tid >> a.tt_bits;
+    const int tt = tid & ((1 << a.tt_bits) - 1);
+    const int g = tt & ((1 << GB) - 1);
+    const int tau = tt >> GB;
+    V* const L = reinterpret_cast<V*>(lds_raw) + tl * S::TILE_LDS;
+    T* const buf = blockIdx.y ? im : re;
 
-    if (ROW) {
+    int64_t w = blockIdx.x;
+    if (w >= a.wg_count)
+        return;   // uniform across the workgroup
+    V nx[S::E];
+    TileAddr na = tile_addr<S>(buf, a, w, tl, g);
+    load_tile<S>(nx, na, tau, a.ld_nt);
+    while (true) {
+        V x[S::E];
 #pragma unroll
-        for (int j = 0; j < E; ++j)
-            in_vector(x[j]);
-    }
-    register_stages<EB, E>(x);
-    Rounds<V, KR, EB, GB, PHB, 1, NR>::run(x, L, tau, g);
-
-    if (a.do_scale) {
-        const T scale = (T)a.scale;
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            x[j] *= scale;
-    }
-
-    // Final layout: the load layout after one more exchange, or the last
-    // round's layout.
-    constexpr int AF = STORE_BACK ? A0 : AL;
-    if constexpr (STORE_BACK)
-        exchange<V, AL, A0, EB, GB, PHB>(x, L, tau, g);
-    const GlobalLayout<AF, EB> glf(lane_bytes, tau, row_bytes);
-    if (active && a.st_nt) {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            store16_nt<V>(p, glf.base + (uint32_t)j * glf.jstride, x[j]);
-    } else if (active) {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            store16<V>(p, glf.base + (uint32_t)j * glf.jstride, x[j]);
+        for (int j = 0; j < S::E; ++j)
+            x[j] = nx[j];
+        const TileAddr ca = na;
+        const int64_t wn = w + gridDim.x;
+        const bool more = wn < a.wg_count;   // uniform across the workgroup
+        if (more) {
+            na = tile_addr<S>(buf, a, wn, tl, g);
+            load_tile<S>(nx, na, tau, a.ld_nt);
+        }
+        process_tile<S>(x, L, tau, g, a.do_scale, a.scale);
+        store_tile<S>(x, ca, tau, a.st_nt);
+        if (!more)
+            break;
+        w = wn;
     }
 }
 
@@ -367,8 +458,13 @@ struct Entry {
 template <typename T, bool ROW, int KR, int EB, int GB, int PHB>
 void add_variant(std::vector<Entry>& v)
 {
-    v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, PHB, ROW ? 1 : 0},
+    v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, PHB, ROW ? 1 : 0, 0},
                  reinterpret_cast<const void*>(&tile_kernel<T, KR, EB, GB, PHB, ROW>)});
+    // The pipelined form, for tiles of at least 32 KiB whose workgroup fits
+    // 512 threads (it holds two register sets).
+    if constexpr (KR + GB >= 11 && KR - EB + GB <= 9 && EB <= 4)
+        v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, PHB, ROW ? 1 : 0, 1},
+                     reinterpret_cast<const void*>(&tile_kernel_pipe<T, KR, EB, GB, PHB, ROW>)});
 }
 
 // Column groups 2^GB for GB in [0, 4] (row passes: GB = 0) whose tile fits
@@ -426,7 +522,7 @@ const void* find(const KernelKey& k)
 {
     for (const Entry& e : table())
         if (e.key.f64 == k.f64 && e.key.kr == k.kr && e.key.eb == k.eb && e.key.gb == k.gb &&
-            e.key.phb == k.phb && e.key.row == k.row)
+            e.key.phb == k.phb && e.key.row == k.row && e.key.pipe == k.pipe)
             return e.fn;
     return nullptr;
 }
@@ -459,6 +555,18 @@ hipError_t launch_tile_pass(const KernelKey& key, void* re, void* im, int ncomp,
     // end by the dispatch itself.
     constexpr int64_t kMaxGrid = (int64_t)1 << 30;
     TileArgs a = args;
+    if (key.pipe) {
+        // Persistent: `args.grid` workgroups (per component) walk all tile
+        // groups.
+        a.tile0 = 0;
+        void* kargs[] = {&re, &im, &a};
+        const int64_t nw = args.grid < args.wg_count ? args.grid : args.wg_count;
+        const dim3 grid((unsigned)(nw > 0 ? nw : 1), (unsigned)ncomp, 1);
+        if (start || stop)
+            return hipExtLaunchKernel(fn, grid, dim3(block, 1, 1), kargs, lds_bytes, stream,
+                                      start, stop, 0);
+        return hipLaunchKernel(fn, grid, dim3(block, 1, 1), kargs, lds_bytes, stream);
+    }
     for (int64_t w0 = 0; w0 < args.wg_count; w0 += kMaxGrid) {
         const int64_t nw = args.wg_count - w0 < kMaxGrid ? args.wg_count - w0 : kMaxGrid;
         const bool first = (w0 == 0), last = (w0 + nw >= args.wg_count);

@@ -40,15 +40,15 @@ def _create(lib, n, dtype=0, path=0):
     return st, h
 
 
-def _split(lib, n, dtype, bits, eb=None, gbits=None, phases=None):
+def _split(lib, n, dtype, bits, eb=None, gbits=None, phases=None, pipe=None):
     h = ctypes.c_void_p()
     arr = (ctypes.c_int * len(bits))(*bits)
-    if eb is None and gbits is None and phases is None:
+    if eb is None and gbits is None and phases is None and pipe is None:
         st = lib.fwt_plan_create_split(ctypes.byref(h), n, dtype, len(bits), arr)
     else:
         mk = lambda v: (ctypes.c_int * len(bits))(*v) if v is not None else None
         st = lib.fwt_plan_create_tuned(ctypes.byref(h), n, dtype, len(bits), arr, mk(eb),
-                                       mk(gbits), mk(phases))
+                                       mk(gbits), mk(phases), mk(pipe))
     if st == 0:
         lib.fwt_plan_destroy(h)
     return st
@@ -131,6 +131,10 @@ def test_tuned_validation(lib):
     assert _split(lib, 24, 1, [14, 10], gbits=[-1, 2], phases=[-1, 3]) == qse.FWT_EINVAL
     assert _split(lib, 20, 0, [13, 7], phases=[-1, 1]) == qse.FWT_EINVAL    # < 9 column bits
     assert _split(lib, 20, 0, [13, 7], phases=[1, -1]) == qse.FWT_EINVAL    # row pass
+    assert _split(lib, 24, 1, [14, 10], pipe=[1, 0]) == 0
+    assert _split(lib, 24, 1, [14, 10], pipe=[0, 1]) == 0
+    assert _split(lib, 24, 1, [14, 10], pipe=[2, 0]) == qse.FWT_EINVAL
+    assert _split(lib, 12, 0, [2, 10], pipe=[1, -1]) == qse.FWT_EUNSUPPORTED  # tiny tile
     # a forced group count that breaks the thread limit is rejected, not replaced
     assert _split(lib, 16, 0, [6, 10], eb=[-1, 3], gbits=[-1, 4]) == qse.FWT_EINVAL
 

@@ -157,6 +157,26 @@ def test_integer_kernel_variants(dtype, n, split, eb, gbits, phases):
     assert_exact(gim, im, n, False)
 
 
+@pytest.mark.parametrize("dtype,n,split,pipe,batch", [
+    ("f64", 18, (14, 4), (1, 0), 3), ("f64", 18, (14, 4), (0, 0), 3), ("f32", 17, (15, 2), (1, 0), 2),
+    ("f32", 16, (13, 3), (1, 0), 5), ("f64", 16, (13, 3), (1, 0), 3), ("f64", 20, (10, 10), (0, 1), 2),
+    ("f32", 19, (9, 10), (-1, 1), 1), ("f64", 24, (14, 10), (1, 0), 1), ("f32", 14, (14,), (1,), 7)])
+def test_integer_pipelined_kernels(dtype, n, split, pipe, batch):
+    """The persistent software-pipelined kernel (each workgroup walks several
+    tile groups and prefetches the next) against the oracle, exactly."""
+    say("pipe %s n=%d split=%s pipe=%s batch=%d" % (dtype, n, split, pipe, batch))
+    npd = np.float32 if dtype == "f32" else np.float64
+    plan = qse.Plan(n, dtype, split=split, pipe=pipe)
+    for i, pv in enumerate(pipe):
+        if pv >= 0:
+            assert plan.pass_config(i)["pipe"] == pv
+    re = ints((batch, 1 << n), 95_000 + n, npd)
+    im = ints((batch, 1 << n), 96_000 + n, npd)
+    gre, gim = run(plan, re, im, False)
+    assert_exact(gre, re, n, False)
+    assert_exact(gim, im, n, False)
+
+
 @pytest.mark.parametrize("dtype,n,batch", [("f32", 12, 1), ("f32", 12, 3), ("f32", 12, 257),
                                            ("f32", 8, 1001), ("f32", 16, 5), ("f64", 16, 3),
                                            ("f64", 6, 77), ("f32", 3, 9), ("f32", 1, 7),
