@@ -1,0 +1,41 @@
+"""Plan parameters of the GPU parity tests, shared with the CPU tests that
+check every one of them is a valid plan (so a planner change cannot break
+the GPU suite unnoticed)."""
+
+# (dtype, n, split): explicit Kronecker splits, lowest bits first
+FORCED_SPLITS = [("f32", 10, (5, 5)), ("f32", 10, (2, 8)), ("f32", 10, (8, 2)), ("f32", 10, (3, 3, 4)),
+    ("f32", 10, (2, 2, 2, 4)), ("f32", 14, (7, 7)), ("f32", 14, (12, 2)), ("f32", 16, (4, 12)),
+    ("f32", 18, (15, 3)), ("f32", 20, (10, 10)), ("f32", 20, (8, 12)), ("f32", 20, (10, 5, 5)),
+    ("f64", 10, (1, 9)), ("f64", 10, (5, 5)), ("f64", 13, (13,)), ("f64", 14, (14,)),
+    ("f64", 18, (9, 9)), ("f64", 20, (8, 12)), ("f64", 22, (10, 12)), ("f64", 21, (7, 7, 7))]
+
+
+def _variants():
+    out = [("f64", 14, (4, 10), (-1, 4), (-1, 3), (-1, 1)),
+           ("f64", 14, (4, 10), (-1, 4), (-1, 3), (-1, 2)),
+           ("f64", 15, (4, 11), (-1, 4), (-1, 3), (-1, 2)),
+           ("f32", 16, (5, 11), (-1, 4), (-1, 3), (-1, 2)),
+           ("f32", 16, (6, 10), (-1, 3), (-1, 3), (-1, 1)),
+           ("f32", 16, (6, 10), (-1, 4), (-1, 4), (-1, 2)),
+           ("f32", 21, (12, 9), (-1, 4), (-1, 4), (-1, 1))]
+    for dtype in ("f32", "f64"):
+        vb = 2 if dtype == "f32" else 1
+        for row_eb in (3, 4, 5):
+            out.append((dtype, 8 + vb + 8, (8 + vb, 8), (row_eb, 4), (-1, -1), None))
+        for col_eb in (3, 4):
+            for gb in range(0, 5):
+                out.append((dtype, 8 + vb + 8, (8 + vb, 8), (4, col_eb), (-1, gb), None))
+        out.append((dtype, 3 + vb + 10, (3 + vb, 10), (3, 4), (-1, 0), None))
+        out.append((dtype, 12 + vb, (12 + vb,), (5,), (-1,), None))
+        out.append((dtype, 12 + vb, (12 + vb,), (3,), (-1,), None))
+    return out
+VARIANTS = _variants()
+
+# (dtype, n, split, eb, pipe, batch): the persistent pipelined kernel forced
+# on (1) or off (0) per pass
+PIPE_CASES = [
+    ("f64", 18, (14, 4), (4, -1), (1, 0), 3), ("f64", 18, (14, 4), (4, -1), (0, 0), 3),
+    ("f32", 17, (15, 2), (4, -1), (1, 0), 2), ("f32", 16, (13, 3), (4, -1), (1, 0), 5),
+    ("f64", 16, (13, 3), (4, -1), (1, 0), 3), ("f64", 20, (10, 10), (-1, 4), (0, 1), 2),
+    ("f32", 19, (9, 10), (-1, 4), (-1, 1), 1), ("f64", 24, (14, 10), (4, -1), (1, 0), 1),
+    ("f32", 14, (14,), (4,), (1,), 7), ("f32", 20, (13, 7), (4, 3), (1, 1), 2)]

@@ -139,6 +139,21 @@ def test_tuned_validation(lib):
     assert _split(lib, 16, 0, [6, 10], eb=[-1, 3], gbits=[-1, 4]) == qse.FWT_EINVAL
 
 
+def test_every_gpu_test_plan_is_valid(lib):
+    """Each plan the GPU parity suite builds is accepted by the planner and
+    has the forced properties (caught here, on the CPU)."""
+    from plan_cases import FORCED_SPLITS, PIPE_CASES, VARIANTS
+    for dtype, n, split in FORCED_SPLITS:
+        assert qse.Plan(n, dtype, split=split).pass_bits == list(split)
+    for dtype, n, split, eb, gbits, phases in VARIANTS:
+        qse.Plan(n, dtype, split=split, eb=eb, gbits=gbits, phases=phases)
+    for dtype, n, split, eb, pipe, batch in PIPE_CASES:
+        p = qse.Plan(n, dtype, split=split, eb=eb, pipe=pipe)
+        for i, pv in enumerate(pipe):
+            if pv >= 0:
+                assert p.pass_config(i)["pipe"] == pv
+
+
 def test_destroy(lib):
     assert lib.fwt_plan_destroy(None) == 0
     st, h = _create(lib, 8)

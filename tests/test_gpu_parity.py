@@ -20,6 +20,7 @@ import pytest
 import oracle
 import quantum_state_encoding_amd as qse
 import workloads
+from plan_cases import FORCED_SPLITS, PIPE_CASES, VARIANTS
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -105,13 +106,7 @@ def test_integer_sweep_auto_plan(dtype, n):
         assert_exact(gim, im, n, True)
 
 
-@pytest.mark.parametrize("dtype,n,split", [
-    ("f32", 10, (5, 5)), ("f32", 10, (2, 8)), ("f32", 10, (8, 2)), ("f32", 10, (3, 3, 4)),
-    ("f32", 10, (2, 2, 2, 4)), ("f32", 14, (7, 7)), ("f32", 14, (12, 2)), ("f32", 16, (4, 12)),
-    ("f32", 18, (15, 3)), ("f32", 20, (10, 10)), ("f32", 20, (8, 12)), ("f32", 20, (10, 5, 5)),
-    ("f64", 10, (1, 9)), ("f64", 10, (5, 5)), ("f64", 13, (13,)), ("f64", 14, (14,)),
-    ("f64", 18, (9, 9)), ("f64", 20, (8, 12)), ("f64", 22, (10, 12)), ("f64", 21, (7, 7, 7)),
-])
+@pytest.mark.parametrize("dtype,n,split", FORCED_SPLITS)
 def test_integer_forced_splits(dtype, n, split):
     say("split %s n=%d %s" % (dtype, n, split))
     npd = np.float32 if dtype == "f32" else np.float64
@@ -124,28 +119,7 @@ def test_integer_forced_splits(dtype, n, split):
     assert_exact(gim, im, n, False)
 
 
-def _variants():
-    out = [("f64", 14, (4, 10), (-1, 4), (-1, 3), (-1, 1)),
-           ("f64", 14, (4, 10), (-1, 4), (-1, 3), (-1, 2)),
-           ("f64", 15, (4, 11), (-1, 4), (-1, 3), (-1, 2)),
-           ("f32", 16, (5, 11), (-1, 4), (-1, 3), (-1, 2)),
-           ("f32", 16, (6, 10), (-1, 3), (-1, 3), (-1, 1)),
-           ("f32", 16, (6, 10), (-1, 4), (-1, 4), (-1, 2)),
-           ("f32", 21, (12, 9), (-1, 4), (-1, 4), (-1, 1))]
-    for dtype in ("f32", "f64"):
-        vb = 2 if dtype == "f32" else 1
-        for row_eb in (3, 4, 5):
-            out.append((dtype, 8 + vb + 8, (8 + vb, 8), (row_eb, 4), (-1, -1), None))
-        for col_eb in (3, 4):
-            for gb in range(0, 5):
-                out.append((dtype, 8 + vb + 8, (8 + vb, 8), (4, col_eb), (-1, gb), None))
-        out.append((dtype, 3 + vb + 10, (3 + vb, 10), (3, 4), (-1, 0), None))
-        out.append((dtype, 12 + vb, (12 + vb,), (5,), (-1,), None))
-        out.append((dtype, 12 + vb, (12 + vb,), (3,), (-1,), None))
-    return out
-
-
-@pytest.mark.parametrize("dtype,n,split,eb,gbits,phases", _variants())
+@pytest.mark.parametrize("dtype,n,split,eb,gbits,phases", VARIANTS)
 def test_integer_kernel_variants(dtype, n, split, eb, gbits, phases):
     say("variant %s n=%d split=%s eb=%s gbits=%s phases=%s" % (dtype, n, split, eb, gbits, phases))
     npd = np.float32 if dtype == "f32" else np.float64
@@ -157,16 +131,13 @@ def test_integer_kernel_variants(dtype, n, split, eb, gbits, phases):
     assert_exact(gim, im, n, False)
 
 
-@pytest.mark.parametrize("dtype,n,split,pipe,batch", [
-    ("f64", 18, (14, 4), (1, 0), 3), ("f64", 18, (14, 4), (0, 0), 3), ("f32", 17, (15, 2), (1, 0), 2),
-    ("f32", 16, (13, 3), (1, 0), 5), ("f64", 16, (13, 3), (1, 0), 3), ("f64", 20, (10, 10), (0, 1), 2),
-    ("f32", 19, (9, 10), (-1, 1), 1), ("f64", 24, (14, 10), (1, 0), 1), ("f32", 14, (14,), (1,), 7)])
-def test_integer_pipelined_kernels(dtype, n, split, pipe, batch):
+@pytest.mark.parametrize("dtype,n,split,eb,pipe,batch", PIPE_CASES)
+def test_integer_pipelined_kernels(dtype, n, split, eb, pipe, batch):
     """The persistent software-pipelined kernel (each workgroup walks several
     tile groups and prefetches the next) against the oracle, exactly."""
-    say("pipe %s n=%d split=%s pipe=%s batch=%d" % (dtype, n, split, pipe, batch))
+    say("pipe %s n=%d split=%s eb=%s pipe=%s batch=%d" % (dtype, n, split, eb, pipe, batch))
     npd = np.float32 if dtype == "f32" else np.float64
-    plan = qse.Plan(n, dtype, split=split, pipe=pipe)
+    plan = qse.Plan(n, dtype, split=split, eb=eb, pipe=pipe)
     for i, pv in enumerate(pipe):
         if pv >= 0:
             assert plan.pass_config(i)["pipe"] == pv
