@@ -20,7 +20,7 @@
  * factorisation H_n = H_{n1} (x) H_{n2} of the pull request's sections
  * "Why" and "Why submit PR4"; the iThome article's "Kronecker block GEMM
  * idea").  Each pass streams the state through memory once, in place, with
- * no transpose and no temporary buffer.  n <= 14 (fp32) / 13 (fp64) runs
+ * no transpose and no temporary buffer.  n <= 15 (fp32) / 14 (fp64) runs
  * as a single pass whose tiles hold a whole vector on chip; up to n = 24,
  * two passes; above, three.  Large multi-pass calls run in chunks of
  * vectors sized to the Infinity Cache (fwt_plan_chunk_vectors).
@@ -48,8 +48,8 @@ typedef struct fwt_plan_s* fwt_plan_t;
 typedef enum { FWT_F32 = 0, FWT_F64 = 1 } fwt_dtype;
 
 /* Execution path chosen at plan creation.
- *  AUTO          single pass while a vector fits one tile (n <= 14 for
- *                fp32, n <= 13 for fp64), otherwise multi-pass.
+ *  AUTO          single pass while a vector fits one tile (n <= 15 for
+ *                fp32, n <= 14 for fp64), otherwise multi-pass.
  *  SINGLE_BLOCK  one pass, one vector per tile; FWT_EUNSUPPORTED above the
  *                single-pass limit.
  *  MULTIPASS     Kronecker split into >= 2 passes whenever n allows it
@@ -95,26 +95,33 @@ int fwt_plan_create(fwt_plan_t* out, int n, fwt_dtype dtype, fwt_path path);
 int fwt_plan_create_split(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
                           const int* bits);
 
+/* Per-pass tiling overrides for fwt_plan_create_tuned; -1 in a field
+ * selects the default. */
+typedef struct {
+    int eb;      /* log2 of the 16-byte vectors a thread holds per register
+                    round (0..5) */
+    int gbits;   /* log2 of the 16-byte column groups per tile of a column
+                    pass (0..4; 0 or -1 for the first pass) */
+    int phases;  /* log2 of the phases a column pass splits each LDS exchange
+                    into (0..2, at most gbits; column passes of >= 9 bits and
+                    >= 8 groups only) */
+    int pipe;    /* 1: persistent software-pipelined kernel (tiles of >= 2^11
+                    16-byte vectors in workgroups of <= 512 threads); 0: one
+                    workgroup per tile group; default: pipelined when one
+                    workgroup fills a CU's LDS */
+    int wave;    /* 1: wave-tile kernel (a whole tile in one wave, lane bits
+                    crossed with DPP / ds_swizzle / permlane swaps, no LDS;
+                    row bits - eb <= 6 - gbits); 0 or default: LDS tiles */
+} fwt_pass_tuning;
+
 /* As fwt_plan_create_split, with the on-chip tiling of each pass forced
- * (tuning and testing of kernel variants; the result is the same).
- *  eb     per pass, log2 of the 16-byte vectors a thread holds per register
- *         round (0..5), or -1 for the default; NULL = all defaults.
- *  gbits  per pass, log2 of the 16-byte column groups per tile of a column
- *         pass (0..4; must be 0 or -1 for the first pass), or -1 for the
- *         default; NULL = all defaults.
- *  phases per pass, log2 of the phases a column pass splits each LDS
- *         exchange into (0..2, at most gbits; column passes of >= 9 bits and
- *         >= 8 groups only), or -1 for the default; NULL = all defaults.
- *  pipe   per pass, 1 for the persistent software-pipelined kernel (tiles
- *         of >= 2^11 16-byte vectors in workgroups of <= 512 threads), 0
- *         for one workgroup per tile group, -1 for the default (pipelined
- *         when one workgroup fills a CU's LDS); NULL = all defaults.
- * Returns as fwt_plan_create_split, plus FWT_EINVAL for a value out of
- * range or a tile that exceeds the LDS or workgroup limits, and
- * FWT_EUNSUPPORTED for a variant that is not compiled in. */
+ * (tuning and testing of kernel variants; the result is the same up to
+ * rounding order).  `tuning` holds npasses entries, or is NULL (all
+ * defaults).  Returns as fwt_plan_create_split, plus FWT_EINVAL for a value
+ * out of range or a tile that exceeds the LDS, lane or workgroup limits,
+ * and FWT_EUNSUPPORTED for a variant that is not compiled in. */
 int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
-                          const int* bits, const int* eb, const int* gbits,
-                          const int* phases, const int* pipe);
+                          const int* bits, const fwt_pass_tuning* tuning);
 
 /* Transform in place, asynchronously on `stream` (0 = the null stream).
  *  re, im   device buffers of batch * 2^n elements of the plan's dtype,
@@ -182,8 +189,8 @@ int fwt_plan_pass_bits(fwt_plan_t plan, int i, int* out_bits);
  * bit, bit count, kind (0 row pass, 1 column pass, 2 two-element kernel),
  * row bits KR of the tile, register-round bits EB, column-group bits,
  * exchange-phase bits, workgroup size, dynamic LDS bytes, log2 tiles per
- * workgroup, pipelined (1) or not (0).  `out` must hold 11 ints.  Returns
- * FWT_OK or FWT_EINVAL. */
+ * workgroup, pipelined (1) or not (0), wave-tile kernel (1) or not (0).
+ * `out` must hold 12 ints.  Returns FWT_OK or FWT_EINVAL. */
 int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out);
 
 /* Release a plan; NULL is a no-op.  Returns FWT_OK. */

@@ -39,6 +39,12 @@ EXPORTED_SYMBOLS = ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create
 _lib = None
 
 
+class PassTuning(ctypes.Structure):
+    """fwt_pass_tuning: per-pass tiling overrides (-1 = default)."""
+    _fields_ = [("eb", ctypes.c_int), ("gbits", ctypes.c_int), ("phases", ctypes.c_int),
+                ("pipe", ctypes.c_int), ("wave", ctypes.c_int)]
+
+
 class FwtError(RuntimeError):
     """A non-zero status returned by the library."""
 
@@ -68,7 +74,8 @@ def load_library():
     pi = ctypes.POINTER(ctypes.c_int)
     lib.fwt_plan_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32]
     lib.fwt_plan_create_split.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi]
-    lib.fwt_plan_create_tuned.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi, pi, pi, pi, pi]
+    lib.fwt_plan_create_tuned.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi,
+                                          ctypes.POINTER(PassTuning)]
     lib.fwt_plan_chunk_vectors.argtypes = [vp, i64, i32, ctypes.POINTER(i64)]
     lib.fwt_execute.argtypes = [vp, i64, i32, vp, vp, i32, vp]
     lib.fwt_execute_pass.argtypes = [vp, i32, i64, i32, vp, vp, i32, vp]
@@ -113,19 +120,21 @@ class Plan:
     """A plan for 2^n-amplitude vectors of dtype "f32" or "f64".
 
     ``split`` (bit counts, lowest index bits first) forces a Kronecker
-    split; ``eb``/``gbits``/``phases``/``pipe`` (one entry per pass, -1 =
-    default) force the register-round width, column-group count, exchange
-    phases and pipelined kernel of each pass (tuning).
+    split; ``eb``/``gbits``/``phases``/``pipe``/``wave`` (one entry per
+    pass, -1 = default) force the register-round width, column-group count,
+    exchange phases, pipelined kernel and wave-tile kernel of each pass
+    (tuning; see fwt_pass_tuning).
     """
 
     def __init__(self, n, dtype="f32", path=PATH_AUTO, split=None, eb=None, gbits=None,
-                 phases=None, pipe=None):
+                 phases=None, pipe=None, wave=None):
         lib = load_library()
         if dtype not in _DTYPES:
             raise ValueError("dtype must be 'f32' or 'f64'")
         self.n, self.dtype = int(n), dtype
         h = ctypes.c_void_p()
-        tuned = eb is not None or gbits is not None or phases is not None or pipe is not None
+        knobs = {"eb": eb, "gbits": gbits, "phases": phases, "pipe": pipe, "wave": wave}
+        tuned = any(v is not None for v in knobs.values())
         if split is None and not tuned:
             st = lib.fwt_plan_create(ctypes.byref(h), self.n, _DTYPES[dtype], int(path))
         elif not tuned:
@@ -133,11 +142,13 @@ class Plan:
                                            len(split), _int_array(split))
         else:
             if split is None:
-                raise ValueError("eb/gbits/phases/pipe need an explicit split")
+                raise ValueError("tuning needs an explicit split")
+            tun = (PassTuning * len(split))()
+            for i in range(len(split)):
+                for name, vals in knobs.items():
+                    setattr(tun[i], name, -1 if vals is None else int(vals[i]))
             st = lib.fwt_plan_create_tuned(ctypes.byref(h), self.n, _DTYPES[dtype],
-                                           len(split), _int_array(split), _int_array(eb),
-                                           _int_array(gbits), _int_array(phases),
-                                           _int_array(pipe))
+                                           len(split), _int_array(split), tun)
         if st != FWT_OK:
             raise FwtError(st, "fwt_plan_create(n=%d, %s)" % (self.n, dtype))
         self._h = h
@@ -166,12 +177,12 @@ class Plan:
 
     def pass_config(self, i):
         """Tiling of pass i as a dict (see fwt_plan_pass_config)."""
-        out = (ctypes.c_int * 11)()
+        out = (ctypes.c_int * 12)()
         st = load_library().fwt_plan_pass_config(self._h, int(i), out)
         if st != FWT_OK:
             raise FwtError(st, "fwt_plan_pass_config")
         keys = ("lo", "bits", "kind", "kr", "eb", "gbits", "phase_bits", "block", "lds",
-                "tpw_bits", "pipe")
+                "tpw_bits", "pipe", "wave")
         d = dict(zip(keys, list(out)))
         d["kind"] = ("row", "column", "pair")[d["kind"]]
         return d
@@ -182,18 +193,16 @@ class Plan:
         if c["kind"] == "pair":
             return "pair_f32_kernel"
         t = "float" if self.dtype == "f32" else "double"
+        if c["wave"]:
+            return "wave_kernel<%s, %d, %d, %d, %s>" % (
+                t, c["kr"], c["eb"], c["gbits"], "true" if c["kind"] == "row" else "false")
         return "%s<%s, %d, %d, %d, %d, %s>" % (
             "tile_kernel_pipe" if c["pipe"] else "tile_kernel",
             t, c["kr"], c["eb"], c["gbits"], c["phase_bits"],
             "true" if c["kind"] == "row" else "false")
 
-    def execute(self, re, im=None, normalize=True, stream=None):
-        """Transform torch device tensors re (and im) in place.
-
-        Both must be contiguous, of the plan's dtype, on the current device,
-        with numel a multiple of 2^n.  Runs asynchronously on ``stream``
-        (default: torch's current stream).
-        """
+    def _check_tensors(self, re, im):
+        """Validate torch tensors for this plan; returns the batch size."""
         import torch
         want = torch.float32 if self.dtype == "f32" else torch.float64
         N = 1 << self.n
@@ -210,7 +219,16 @@ class Plan:
                 raise ValueError("%s.numel() is not a multiple of 2^%d" % (name, self.n))
         if im is not None and im.numel() != re.numel():
             raise ValueError("re and im must have the same number of elements")
-        batch = re.numel() // N
+        return re.numel() // N
+
+    def execute(self, re, im=None, normalize=True, stream=None):
+        """Transform torch device tensors re (and im) in place.
+
+        Both must be contiguous, of the plan's dtype, on the current device,
+        with numel a multiple of 2^n.  Runs asynchronously on ``stream``
+        (default: torch's current stream).
+        """
+        batch = self._check_tensors(re, im)
         st = load_library().fwt_execute(self._h, batch, self.n, ctypes.c_void_p(re.data_ptr()),
                                         ctypes.c_void_p(im.data_ptr() if im is not None else None),
                                         1 if normalize else 0, _stream_handle(stream))
@@ -229,17 +247,25 @@ class Plan:
 
     def bind(self, re, im=None, normalize=True, stream=None):
         """A zero-argument callable that enqueues fwt_execute on these
-        tensors with the arguments marshalled once (for tight loops)."""
-        self.execute(re, im, normalize, stream)      # validates the tensors once
-        fn = load_library().fwt_execute
-        args = (self._h, re.numel() >> self.n, self.n, ctypes.c_void_p(re.data_ptr()),
-                ctypes.c_void_p(im.data_ptr() if im is not None else None),
-                1 if normalize else 0, _stream_handle(stream))
+        tensors with the arguments marshalled once (for tight loops).
+        Binding validates the arguments (fwt_execute_check) but runs
+        nothing; the callable keeps the plan alive."""
+        batch = self._check_tensors(re, im)
+        lib = load_library()
+        rp = ctypes.c_void_p(re.data_ptr())
+        ip = ctypes.c_void_p(im.data_ptr() if im is not None else None)
+        st = lib.fwt_execute_check(self._h, batch, self.n, rp, ip)
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_execute_check")
+        fn = lib.fwt_execute
+        args = (self._h, batch, self.n, rp, ip, 1 if normalize else 0, _stream_handle(stream))
+        plan = self
 
         def call():
             st = fn(*args)
             if st != FWT_OK:
                 raise FwtError(st, "fwt_execute")
+        call.plan = plan
         return call
 
     def execute_pass(self, i, re, im=None, normalize=True, stream=None):

@@ -86,14 +86,27 @@ int vec_bits(fwt_dtype d) { return d == FWT_F64 ? 1 : 2; }
 
 int max_threads(int eb) { return eb >= 5 ? 512 : 1024; }
 
-// Default register-round width for a pass of kr row bits: 16 vectors per
-// thread, except 8 in the fp32 passes of multi-pass plans (more threads per
-// tile; measured about 2% faster at n = 20).
-int default_eb(int kr, fwt_dtype dtype, bool multipass)
+// Default register-round width for a pass of kr row bits (measured on
+// MI355X): 8 vectors per thread (more threads per tile: lower latency for
+// single passes, more memory parallelism for streaming passes); 16 for
+// fp64 rows of 12+ bits (32 in a single pass of 13) and fp64 column tiles
+// of 9+ bits, and for any column tile of 11+ bits, where 8 per thread
+// would exceed the thread limits of the pipelined or phased kernels.
+int default_eb(int kr, fwt_dtype dtype, bool multipass, bool row)
 {
-    if (dtype == FWT_F32 && multipass && kr >= 6)
-        return 3;
-    return kr < 4 ? kr : 4;
+    if (kr < 3)
+        return kr;
+    if (dtype == FWT_F64) {
+        if (row && kr >= 13)
+            return multipass ? 4 : 5;
+        if (row && kr == 12)
+            return 4;
+        if (!row && kr >= 9)
+            return 4;
+    }
+    if (!row && kr >= 11)
+        return 4;   // keeps 8 column groups (128-byte segments) within 1024 threads
+    return 3;
 }
 
 bool log_enabled()
@@ -120,9 +133,13 @@ bool phases_allowed(int kr, int eb, int gbits, int phb)
 // Fill in the tiling of a pass over bits [lo, lo + k) of a 2^n vector.
 // eb_req / gbits_req / phb_req < 0 select defaults.  Returns FWT_OK or an
 // error.
-int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int gbits_req,
-               int phb_req, int pipe_req, bool multipass)
+int build_wave_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool row,
+                    const fwt_pass_tuning& t);
+
+int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tuning& t,
+               bool multipass)
 {
+    const int eb_req = t.eb, gbits_req = t.gbits, phb_req = t.phases, pipe_req = t.pipe;
     const int vb = vec_bits(dtype);
     p = Pass{};
     p.lo = lo;
@@ -146,7 +163,11 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int g
         if (kr < 1 || kr > kColKrMax)
             return FWT_EINVAL;
     }
-    const int eb = eb_req < 0 ? default_eb(kr, dtype, multipass) : eb_req;
+    if (t.wave > 1 || t.pipe > 1)
+        return FWT_EINVAL;
+    if (t.wave == 1)
+        return build_wave_pass(p, n, dtype, lo, k, kr, row, t);
+    const int eb = eb_req < 0 ? default_eb(kr, dtype, multipass, row) : eb_req;
     if (eb > kr || eb < 0 || eb > 5)
         return FWT_EINVAL;
     const int tt_max = ilog2(max_threads(eb));
@@ -190,7 +211,7 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int g
     }
     if (pipe_req > 1)
         return FWT_EINVAL;
-    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, gbits, phb, row ? 1 : 0, 0};
+    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, gbits, phb, row ? 1 : 0, 0, 0};
     p.gbits = gbits;
     p.phb = phb;
     p.tt_bits = (kr - eb) + gbits;
@@ -247,18 +268,80 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int eb_req, int g
     return FWT_OK;
 }
 
-// Default Kronecker split (bit counts, lowest bits first).
-//  - one pass while a vector fits one 64 KiB tile: n <= 14 (fp32), 13 (fp64);
-//  - two passes up to n = 24: the row pass takes 13 (fp32) / 14 (fp64)
-//    contiguous bits, the column pass the rest (at most 11 / 10 bits, so
-//    its tile keeps 128-byte row segments);
+// Largest 32-bit lane offset of a pass's tile group must fit (lanes address
+// from the workgroup's first tile).  Returns FWT_OK or FWT_EUNSUPPORTED.
+int check_offsets(const Pass& p, fwt_dtype dtype, bool row, int kr, int vb)
+{
+    const int esize_bits = dtype == FWT_F64 ? 3 : 2;
+    const uint64_t tmax = ((uint64_t)1 << p.tpw_bits) - 1;
+    uint64_t max_el;
+    if (row) {
+        max_el = ((tmax + 1) << p.k) - 1;
+    } else {
+        const uint64_t mask = ((uint64_t)1 << p.nblk_bits) - 1;
+        max_el = ((tmax >> p.nblk_bits) << (p.lo + kr)) + ((tmax & mask) << (p.gbits + vb)) +
+                 ((((uint64_t)1 << kr) - 1) << p.lo) + ((uint64_t)1 << (p.gbits + vb)) - 1;
+    }
+    if ((max_el << esize_bits) + ((uint64_t)1 << esize_bits) - 1 > 0xFFFFFFFFull)
+        return FWT_EUNSUPPORTED;
+    return FWT_OK;
+}
+
+// A pass in the wave-tile kernel: each wave holds whole tiles, register bits
+// [LB, kr) in registers and row bits [0, LB) in lanes (above the column-group
+// lane bits), with lane stages instead of LDS exchanges; LB <= 6 - gbits.
+int build_wave_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool row,
+                    const fwt_pass_tuning& t)
+{
+    const int vb = vec_bits(dtype);
+    if (t.phases > 0 || t.pipe > 0)
+        return FWT_EINVAL;
+    int gbits = 0;
+    if (!row) {
+        const int gmax_cols = lo - vb;
+        if (t.gbits > 4 || t.gbits > gmax_cols)
+            return FWT_EINVAL;
+        // Default: 8 groups (128-byte segments) where the rows allow, else
+        // as many as there are.
+        gbits = t.gbits >= 0 ? t.gbits : (gmax_cols < 3 ? gmax_cols : 3);
+        p.nblk_bits = gmax_cols - gbits;
+    } else if (t.gbits > 0) {
+        return FWT_EINVAL;
+    }
+    const int lane_room = 6 - gbits;
+    int eb = t.eb >= 0 ? t.eb : (kr - lane_room > 0 ? kr - lane_room : 0);
+    if (t.eb < 0 && eb == 0 && kr + gbits >= 5)
+        eb = 1;   // lane bits 4 and 5 are swapped through register pairs
+    const int lb = kr - eb;
+    if (eb < 0 || eb > 5 || eb > kr || lb < 0 || lb > lane_room)
+        return FWT_EINVAL;
+    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, gbits, 0, row ? 1 : 0, 0, 1};
+    if (!qse::kernel_available(p.key))
+        return FWT_EUNSUPPORTED;
+    p.gbits = gbits;
+    p.phb = 0;
+    p.tt_bits = gbits + lb;
+    p.tpw_bits = 2 + (lane_room - lb);   // 4 waves of 2^(6 - gbits - lb) tiles
+    p.block = 256;
+    p.lds = 0;
+    p.store_back = 0;
+    p.tiles_bits = row ? (n - k) : (n - lo - k) + p.nblk_bits;
+    return check_offsets(p, dtype, row, kr, vb);
+}
+
+// Default Kronecker split (bit counts, lowest bits first), from sweeps on
+// MI355X:
+//  - one pass while a vector fits one tile: n <= 15 (fp32), 14 (fp64);
+//  - two passes up to n = 24: a column factor of 7 (fp32) / 8 (fp64) bits
+//    (col tiles of 128 rows x 256 B / 256 rows x 128 B), the rest in the
+//    contiguous row pass, which takes at most 13 (fp32) / 14 (fp64) bits;
 //  - three passes above: 10 row bits, the rest split evenly.
 int default_split(int n, fwt_dtype dtype, fwt_path path, int* bits)
 {
     const int vb = vec_bits(dtype);
-    const int single_max = 12 + vb;
+    const int single_max = kRowKrMax + vb;   // 15 fp32, 14 fp64
     if (path == FWT_PATH_SINGLE_BLOCK) {
-        if (n > kRowKrMax + vb)
+        if (n > single_max)
             return -1;
         bits[0] = n;
         return 1;
@@ -273,10 +356,11 @@ int default_split(int n, fwt_dtype dtype, fwt_path path, int* bits)
         bits[0] = n - bits[1];
         return 2;
     }
-    const int row2 = dtype == FWT_F64 ? 14 : 13;
     if (n <= 24) {
-        bits[0] = row2 < n - 1 ? row2 : n - 1;
-        bits[1] = n - bits[0];
+        const int row_max = dtype == FWT_F64 ? 14 : 13;
+        const int col_pref = dtype == FWT_F64 ? 8 : 7;
+        bits[1] = n - row_max > col_pref ? n - row_max : col_pref;
+        bits[0] = n - bits[1];
         return 2;
     }
     const int rest = n - 10;
@@ -287,7 +371,7 @@ int default_split(int n, fwt_dtype dtype, fwt_path path, int* bits)
 }
 
 int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* bits,
-              const int* ebs, const int* gbits, const int* phbs, const int* pipes)
+              const fwt_pass_tuning* tuning)
 {
     if (!out)
         return FWT_EINVAL;
@@ -313,9 +397,9 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
     p->npasses = n == 0 ? 0 : npasses;
     int lo = 0;
     for (int i = 0; i < p->npasses; ++i) {
-        const int rc = build_pass(p->passes[i], n, dtype, lo, bits[i], ebs ? ebs[i] : -1,
-                                  gbits ? gbits[i] : -1, phbs ? phbs[i] : -1,
-                                  pipes ? pipes[i] : -1, p->npasses > 1);
+        const fwt_pass_tuning dflt{-1, -1, -1, -1, -1};
+        const int rc = build_pass(p->passes[i], n, dtype, lo, bits[i], tuning ? tuning[i] : dflt,
+                                  p->npasses > 1);
         if (rc != FWT_OK) {
             delete p;
             return rc;
@@ -329,9 +413,9 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
             const Pass& q = p->passes[i];
             std::fprintf(stderr,
                          "[fwt]   pass %d: bits [%d,%d) %s kr=%d eb=%d G=%d phases=%d pipe=%d "
-                         "threads/tile=%d block=%u lds=%zu store_back=%d tiles/vec=2^%d\n",
+                         "wave=%d threads/tile=%d block=%u lds=%zu store_back=%d tiles/vec=2^%d\n",
                          i, q.lo, q.lo + q.k, q.pair ? "pair" : (q.key.row ? "row" : "col"),
-                         q.key.kr, q.key.eb, 1 << q.gbits, 1 << q.phb, q.key.pipe,
+                         q.key.kr, q.key.eb, 1 << q.gbits, 1 << q.phb, q.key.pipe, q.key.wave,
                          1 << q.tt_bits, q.block, q.lds, q.store_back, q.tiles_bits);
         }
     }
@@ -520,18 +604,18 @@ int fwt_plan_create(fwt_plan_t* out, int n, fwt_dtype dtype, fwt_path path)
     const int np = default_split(n, dtype, path, bits);
     if (np < 0)
         return FWT_EUNSUPPORTED;
-    return make_plan(out, n, dtype, np, bits, nullptr, nullptr, nullptr, nullptr);
+    return make_plan(out, n, dtype, np, bits, nullptr);
 }
 
 int fwt_plan_create_split(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* bits)
 {
-    return make_plan(out, n, dtype, npasses, bits, nullptr, nullptr, nullptr, nullptr);
+    return make_plan(out, n, dtype, npasses, bits, nullptr);
 }
 
 int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* bits,
-                          const int* eb, const int* gbits, const int* phases, const int* pipe)
+                          const fwt_pass_tuning* tuning)
 {
-    return make_plan(out, n, dtype, npasses, bits, eb, gbits, phases, pipe);
+    return make_plan(out, n, dtype, npasses, bits, tuning);
 }
 
 int fwt_execute_check(fwt_plan_t plan, int64_t batch, int n, const void* re, const void* im)
@@ -626,6 +710,7 @@ int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out)
     out[8] = (int)p.lds;
     out[9] = p.tpw_bits;
     out[10] = p.key.pipe;
+    out[11] = p.key.wave;
     return FWT_OK;
 }
 

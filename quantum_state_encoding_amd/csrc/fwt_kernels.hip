@@ -404,6 +404,188 @@ __global__ void __launch_bounds__(512)
     }
 }
 
+// ---- wave tiles: a whole tile in one wave, lane stages, no LDS ----------
+//
+// A wave holds 2^(6 - GB - LB) tiles of 2^KR rows x 2^GB column groups: lane
+// l holds column group l mod 2^GB and row bits [0, LB) = the next LB lane
+// bits; its E = 2^EB registers hold row bits [LB, KR).  Register bits are
+// butterflied in registers; lane bits cross lanes (the single-block design
+// of the iThome article's introduction, registers plus warp shuffle, on
+// wave64): lane bits 0 and 1 with DPP quad permutes, 2 and 3 with
+// ds_swizzle, and 4 and 5 with v_permlane16/32_swap, which exchange a lane
+// bit with a register bit so the stage becomes a register butterfly (and
+// a second swap restores the layout).  Lanes keep their own half of each
+// pair with y = partner + s * x, s = +1 for the lower index and -1 for the
+// upper: one rounding, exactly the sum or difference.
+
+template <int LBIT>
+__device__ __forceinline__ unsigned lane_partner_u32(unsigned v)
+{
+    if constexpr (LBIT == 0)
+        return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // quad [1,0,3,2]
+    else if constexpr (LBIT == 1)
+        return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad [2,3,0,1]
+    else if constexpr (LBIT == 2)
+        return (unsigned)__builtin_amdgcn_ds_swizzle((int)v, (4 << 10) | 0x1F);   // xor 4
+    else
+        return (unsigned)__builtin_amdgcn_ds_swizzle((int)v, (8 << 10) | 0x1F);   // xor 8
+}
+
+template <int LBIT>
+__device__ __forceinline__ float lane_partner(float v)
+{
+    return __uint_as_float(lane_partner_u32<LBIT>(__float_as_uint(v)));
+}
+template <int LBIT>
+__device__ __forceinline__ double lane_partner(double v)
+{
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const unsigned lo = lane_partner_u32<LBIT>((unsigned)u);
+    const unsigned hi = lane_partner_u32<LBIT>((unsigned)(u >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+__device__ __forceinline__ float fma_sign(float x, float s, float p) { return __builtin_fmaf(x, s, p); }
+__device__ __forceinline__ double fma_sign(double x, double s, double p) { return __builtin_fma(x, s, p); }
+
+// Swap lane bit 4 (LBIT = 4) or 5 with the register pair (a, b).
+template <int LBIT>
+__device__ __forceinline__ void permlane_swap_u32(unsigned& a, unsigned& b)
+{
+    if constexpr (LBIT == 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    }
+}
+template <int LBIT>
+__device__ __forceinline__ void permlane_swap(float& a, float& b)
+{
+    unsigned ua = __float_as_uint(a), ub = __float_as_uint(b);
+    permlane_swap_u32<LBIT>(ua, ub);
+    a = __uint_as_float(ua);
+    b = __uint_as_float(ub);
+}
+template <int LBIT>
+__device__ __forceinline__ void permlane_swap(double& a, double& b)
+{
+    const unsigned long long ua = (unsigned long long)__double_as_longlong(a);
+    const unsigned long long ub = (unsigned long long)__double_as_longlong(b);
+    unsigned alo = (unsigned)ua, ahi = (unsigned)(ua >> 32);
+    unsigned blo = (unsigned)ub, bhi = (unsigned)(ub >> 32);
+    permlane_swap_u32<LBIT>(alo, blo);
+    permlane_swap_u32<LBIT>(ahi, bhi);
+    a = __longlong_as_double((long long)(((unsigned long long)ahi << 32) | alo));
+    b = __longlong_as_double((long long)(((unsigned long long)bhi << 32) | blo));
+}
+
+// Stage on lane bit LBIT for all E registers.
+template <int LBIT, int E, typename V, typename T>
+__device__ __forceinline__ void lane_stage(V* x, int lane)
+{
+    constexpr int W = sizeof(V) / sizeof(T);
+    if constexpr (LBIT < 4) {
+        const T s = ((lane >> LBIT) & 1) ? T(-1) : T(1);
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+#pragma unroll
+            for (int c = 0; c < W; ++c) {
+                const T v = x[j][c];
+                x[j][c] = fma_sign(v, s, lane_partner<LBIT>(v));
+            }
+        }
+    } else {
+        static_assert(E >= 2, "lane bits 4 and 5 pair registers");
+#pragma unroll
+        for (int j = 0; j < E; j += 2) {
+#pragma unroll
+            for (int c = 0; c < W; ++c) {
+                T a = x[j][c], b = x[j + 1][c];
+                permlane_swap<LBIT>(a, b);
+                const T sum = a + b, dif = a - b;
+                a = sum;
+                b = dif;
+                permlane_swap<LBIT>(a, b);
+                x[j][c] = a;
+                x[j + 1][c] = b;
+            }
+        }
+    }
+}
+
+template <int B, int LB, int GB, int E, typename V, typename T>
+struct LaneStages {
+    __device__ __forceinline__ static void run(V* x, int lane)
+    {
+        lane_stage<GB + B, E, V, T>(x, lane);
+        LaneStages<B + 1, LB, GB, E, V, T>::run(x, lane);
+    }
+};
+template <int LB, int GB, int E, typename V, typename T>
+struct LaneStages<LB, LB, GB, E, V, T> {
+    __device__ __forceinline__ static void run(V*, int) {}
+};
+
+template <typename T, int KR, int EB, int GB, bool ROW>
+__global__ void __launch_bounds__(256)
+    wave_kernel(T* __restrict__ re, T* __restrict__ im, TileArgs a)
+{
+    using S = Shape<T, KR, EB, GB, 0, ROW>;
+    using V = typename S::V;
+    constexpr int LB = KR - EB;           // row bits held by lanes
+    constexpr int E = 1 << EB;
+    constexpr int SUB = 6 - GB - LB;      // log2 tiles per wave
+    static_assert(LB >= 0 && SUB >= 0, "a wave tile spans at most 64 lanes");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane & ((1 << GB) - 1);
+    const int rl = (lane >> GB) & ((1 << LB) - 1);
+    const int tl = (wave << SUB) | (lane >> (GB + LB));
+
+    const TileAddr ta = tile_addr<S>(blockIdx.y ? im : re, a, blockIdx.x, tl, g);
+    const GlobalLayout<LB, EB> gl(ta.lane_bytes, rl, ta.row_bytes);
+    V x[E];
+    if (ta.active && a.ld_nt) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] = load16_nt<V>(ta.p, gl.base + (uint32_t)j * gl.jstride);
+    } else if (ta.active) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] = load16<V>(ta.p, gl.base + (uint32_t)j * gl.jstride);
+    } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] = V{};
+    }
+    if (ROW) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            in_vector(x[j]);
+    }
+    register_stages<EB, E>(x);
+    LaneStages<0, LB, GB, E, V, T>::run(x, lane);
+    if (a.do_scale) {
+        const T c = (T)a.scale;
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] *= c;
+    }
+    if (ta.active && a.st_nt) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            store16_nt<V>(ta.p, gl.base + (uint32_t)j * gl.jstride, x[j]);
+    } else if (ta.active) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            store16<V>(ta.p, gl.base + (uint32_t)j * gl.jstride, x[j]);
+    }
+}
+
 __global__ void __launch_bounds__(256)
     pair_f32_kernel(float* __restrict__ re, float* __restrict__ im, int64_t pairs, int do_scale,
                     float scale)
@@ -458,12 +640,12 @@ struct Entry {
 template <typename T, bool ROW, int KR, int EB, int GB, int PHB>
 void add_variant(std::vector<Entry>& v)
 {
-    v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, PHB, ROW ? 1 : 0, 0},
+    v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, PHB, ROW ? 1 : 0, 0, 0},
                  reinterpret_cast<const void*>(&tile_kernel<T, KR, EB, GB, PHB, ROW>)});
     // The pipelined form, for tiles of at least 32 KiB whose workgroup fits
     // 512 threads (it holds two register sets).
     if constexpr (KR + GB >= 11 && KR - EB + GB <= 9 && EB <= 4)
-        v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, PHB, ROW ? 1 : 0, 1},
+        v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, PHB, ROW ? 1 : 0, 1, 0},
                      reinterpret_cast<const void*>(&tile_kernel_pipe<T, KR, EB, GB, PHB, ROW>)});
 }
 
@@ -505,10 +687,50 @@ struct Register {
     }
 };
 
+// Wave-tile kernels: EB = the fewest register bits that leave at most
+// 6 - GB row bits for the lanes (at least 1 when lane bits 4/5 are used,
+// whose swaps pair registers), and one more where it fits.
+template <typename T, bool ROW, int KR, int GB, int EB>
+void add_wave(std::vector<Entry>& v)
+{
+    constexpr int LB = KR - EB;
+    if constexpr (EB >= 0 && EB <= 5 && EB <= KR && LB >= 0 && LB + GB <= 6 &&
+                  !(EB == 0 && LB + GB >= 5))
+        v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, 0, ROW ? 1 : 0, 0, 1},
+                     reinterpret_cast<const void*>(&wave_kernel<T, KR, EB, GB, ROW>)});
+}
+
+template <typename T, bool ROW, int KR, int GB>
+struct WaveVariants {
+    static constexpr int lane_room = 6 - GB;
+    static constexpr int eb0 = KR - lane_room > 0 ? KR - lane_room : 0;
+    static void add(std::vector<Entry>& v)
+    {
+        add_wave<T, ROW, KR, GB, eb0>(v);
+        add_wave<T, ROW, KR, GB, eb0 + 1>(v);
+        if constexpr (!ROW && GB < 4)
+            WaveVariants<T, ROW, KR, GB + 1>::add(v);
+    }
+};
+
+template <typename T, bool ROW, int KR, int KRMIN>
+struct RegisterWave {
+    static void add(std::vector<Entry>& v)
+    {
+        WaveVariants<T, ROW, KR, 0>::add(v);
+        if constexpr (KR > KRMIN)
+            RegisterWave<T, ROW, KR - 1, KRMIN>::add(v);
+    }
+};
+
 const std::vector<Entry>& table()
 {
     static const std::vector<Entry> t = [] {
         std::vector<Entry> v;
+        RegisterWave<float, true, 11, 0>::add(v);
+        RegisterWave<double, true, 11, 0>::add(v);
+        RegisterWave<float, false, 11, 1>::add(v);
+        RegisterWave<double, false, 11, 1>::add(v);
         Register<float, true, 13, 0>::add(v);
         Register<double, true, 13, 0>::add(v);
         Register<float, false, 12, 1>::add(v);
@@ -522,7 +744,8 @@ const void* find(const KernelKey& k)
 {
     for (const Entry& e : table())
         if (e.key.f64 == k.f64 && e.key.kr == k.kr && e.key.eb == k.eb && e.key.gb == k.gb &&
-            e.key.phb == k.phb && e.key.row == k.row && e.key.pipe == k.pipe)
+            e.key.phb == k.phb && e.key.row == k.row && e.key.pipe == k.pipe &&
+            e.key.wave == k.wave)
             return e.fn;
     return nullptr;
 }

@@ -39,3 +39,19 @@ PIPE_CASES = [
     ("f64", 16, (13, 3), (4, -1), (1, 0), 3), ("f64", 20, (10, 10), (-1, 4), (0, 1), 2),
     ("f32", 19, (9, 10), (-1, 4), (-1, 1), 1), ("f64", 24, (14, 10), (4, -1), (1, 0), 1),
     ("f32", 14, (14,), (4,), (1,), 7), ("f32", 20, (13, 7), (4, 3), (1, 1), 2)]
+
+# (dtype, n, split, eb, gbits, wave, batch): the wave-tile kernel (whole
+# tile in one wave; lane bits crossed with DPP, ds_swizzle and permlane
+# swaps), row and column passes, every lane-bit count and column-group count
+WAVE_CASES = [
+    ("f32", 12, (12,), None, None, (1,), 3), ("f32", 13, (13,), None, None, (1,), 2),
+    ("f32", 10, (10,), None, None, (1,), 5), ("f32", 5, (5,), None, None, (1,), 9),
+    ("f32", 8, (8,), None, None, (1,), 33), ("f32", 3, (3,), None, None, (1,), 7),
+    ("f64", 12, (12,), None, None, (1,), 2), ("f64", 7, (7,), None, None, (1,), 9),
+    ("f64", 2, (2,), None, None, (1,), 5), ("f64", 9, (9,), None, None, (1,), 4),
+    ("f32", 16, (9, 7), None, None, (1, 1), 1), ("f32", 16, (9, 7), None, (-1, 4), (1, 1), 1),
+    ("f64", 15, (8, 7), None, (-1, 2), (0, 1), 1), ("f32", 14, (7, 7), None, (-1, 1), (1, 1), 2),
+    ("f32", 13, (4, 9), None, (-1, 0), (1, 1), 3), ("f64", 12, (3, 9), None, (-1, 0), (1, 1), 3),
+    ("f32", 20, (13, 7), None, None, (1, 1), 2), ("f32", 20, (13, 7), None, (-1, 4), (1, 1), 2),
+    ("f64", 18, (11, 7), None, None, (1, 1), 2), ("f32", 12, (12,), (5,), None, (1,), 2),
+    ("f32", 14, (10, 4), None, (-1, 3), (1, 1), 3)]

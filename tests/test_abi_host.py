@@ -40,15 +40,18 @@ def _create(lib, n, dtype=0, path=0):
     return st, h
 
 
-def _split(lib, n, dtype, bits, eb=None, gbits=None, phases=None, pipe=None):
+def _split(lib, n, dtype, bits, eb=None, gbits=None, phases=None, pipe=None, wave=None):
     h = ctypes.c_void_p()
     arr = (ctypes.c_int * len(bits))(*bits)
-    if eb is None and gbits is None and phases is None and pipe is None:
+    knobs = {"eb": eb, "gbits": gbits, "phases": phases, "pipe": pipe, "wave": wave}
+    if all(v is None for v in knobs.values()):
         st = lib.fwt_plan_create_split(ctypes.byref(h), n, dtype, len(bits), arr)
     else:
-        mk = lambda v: (ctypes.c_int * len(bits))(*v) if v is not None else None
-        st = lib.fwt_plan_create_tuned(ctypes.byref(h), n, dtype, len(bits), arr, mk(eb),
-                                       mk(gbits), mk(phases), mk(pipe))
+        tun = (qse.PassTuning * len(bits))()
+        for i in range(len(bits)):
+            for name, vals in knobs.items():
+                setattr(tun[i], name, -1 if vals is None else vals[i])
+        st = lib.fwt_plan_create_tuned(ctypes.byref(h), n, dtype, len(bits), arr, tun)
     if st == 0:
         lib.fwt_plan_destroy(h)
     return st
@@ -135,6 +138,14 @@ def test_tuned_validation(lib):
     assert _split(lib, 24, 1, [14, 10], pipe=[0, 1]) == 0
     assert _split(lib, 24, 1, [14, 10], pipe=[2, 0]) == qse.FWT_EINVAL
     assert _split(lib, 12, 0, [2, 10], pipe=[1, -1]) == qse.FWT_EUNSUPPORTED  # tiny tile
+    # wave-tile passes: lane bits are limited to 6 - gbits
+    assert _split(lib, 12, 0, [12], wave=[1]) == 0                 # kr 10 = 4 regs + 6 lanes
+    assert _split(lib, 13, 0, [13], wave=[1]) == 0                 # kr 11 = 5 + 6
+    assert _split(lib, 14, 0, [14], wave=[1]) == qse.FWT_EINVAL    # kr 12 > 11
+    assert _split(lib, 12, 0, [12], eb=[3], wave=[1]) == qse.FWT_EINVAL   # 7 lane bits
+    assert _split(lib, 20, 0, [13, 7], wave=[1, 1]) == 0           # column pass: 8 groups, 3 lane bits
+    assert _split(lib, 20, 0, [13, 7], wave=[1, 1], gbits=[-1, 4]) == 0
+    assert _split(lib, 20, 0, [13, 7], wave=[1, 1], phases=[-1, 1]) == qse.FWT_EINVAL
     # a forced group count that breaks the thread limit is rejected, not replaced
     assert _split(lib, 16, 0, [6, 10], eb=[-1, 3], gbits=[-1, 4]) == qse.FWT_EINVAL
 
@@ -142,11 +153,14 @@ def test_tuned_validation(lib):
 def test_every_gpu_test_plan_is_valid(lib):
     """Each plan the GPU parity suite builds is accepted by the planner and
     has the forced properties (caught here, on the CPU)."""
-    from plan_cases import FORCED_SPLITS, PIPE_CASES, VARIANTS
+    from plan_cases import FORCED_SPLITS, PIPE_CASES, VARIANTS, WAVE_CASES
     for dtype, n, split in FORCED_SPLITS:
         assert qse.Plan(n, dtype, split=split).pass_bits == list(split)
     for dtype, n, split, eb, gbits, phases in VARIANTS:
         qse.Plan(n, dtype, split=split, eb=eb, gbits=gbits, phases=phases)
+    for dtype, n, split, eb, gbits, wave, batch in WAVE_CASES:
+        p = qse.Plan(n, dtype, split=split, eb=eb, gbits=gbits, wave=wave)
+        assert [p.pass_config(i)["wave"] for i in range(p.num_passes)] == list(wave)
     for dtype, n, split, eb, pipe, batch in PIPE_CASES:
         p = qse.Plan(n, dtype, split=split, eb=eb, pipe=pipe)
         for i, pv in enumerate(pipe):

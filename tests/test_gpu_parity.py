@@ -20,7 +20,7 @@ import pytest
 import oracle
 import quantum_state_encoding_amd as qse
 import workloads
-from plan_cases import FORCED_SPLITS, PIPE_CASES, VARIANTS
+from plan_cases import FORCED_SPLITS, PIPE_CASES, VARIANTS, WAVE_CASES
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -146,6 +146,28 @@ def test_integer_pipelined_kernels(dtype, n, split, eb, pipe, batch):
     gre, gim = run(plan, re, im, False)
     assert_exact(gre, re, n, False)
     assert_exact(gim, im, n, False)
+
+
+@pytest.mark.parametrize("dtype,n,split,eb,gbits,wave,batch", WAVE_CASES)
+def test_integer_wave_tile_kernels(dtype, n, split, eb, gbits, wave, batch):
+    """The wave-tile kernel: register butterflies plus lane stages (DPP quad
+    permutes, ds_swizzle, permlane16/32 swaps), exactly against the oracle,
+    unnormalised and normalised."""
+    say("wave %s n=%d split=%s eb=%s gbits=%s wave=%s batch=%d" % (dtype, n, split, eb, gbits,
+                                                                     wave, batch))
+    npd = np.float32 if dtype == "f32" else np.float64
+    plan = qse.Plan(n, dtype, split=split, eb=eb, gbits=gbits, wave=wave)
+    for i, wv in enumerate(wave):
+        assert plan.pass_config(i)["wave"] == wv
+    re = ints((batch, 1 << n), 97_000 + n, npd)
+    im = ints((batch, 1 << n), 98_000 + n, npd)
+    gre, gim = run(plan, re, im, False)
+    assert_exact(gre, re, n, False)
+    assert_exact(gim, im, n, False)
+    if n % 2 == 0:
+        gre, gim = run(plan, re, im, True)
+        assert_exact(gre, re, n, True)
+        assert_exact(gim, im, n, True)
 
 
 @pytest.mark.parametrize("dtype,n,batch", [("f32", 12, 1), ("f32", 12, 3), ("f32", 12, 257),
@@ -352,6 +374,23 @@ def test_timed_passes_follow_the_chunk_schedule():
     gre, gim = run(plan, re, im, False)
     assert np.array_equal(tre.cpu().numpy(), gre) and np.array_equal(tim.cpu().numpy(), gim)
     assert_exact(gre[: 3], re[: 3], n, False)
+
+
+def test_bound_call_keeps_its_plan_alive():
+    """A callable from Plan.bind stays valid after the Plan object itself
+    goes out of scope."""
+    say("bind lifetime")
+    import gc
+    n = 10
+    re = ints((4, 1 << n), 5, np.float32)
+    tre = to_dev(re)
+    step = qse.Plan(n, "f32").bind(tre, None, normalize=False)
+    gc.collect()
+    torch.cuda.synchronize()
+    assert np.array_equal(tre.cpu().numpy(), re)     # binding runs nothing
+    step()
+    torch.cuda.synchronize()
+    assert_exact(tre.cpu().numpy(), re, n, False)
 
 
 def test_stream_copy():
