@@ -167,7 +167,7 @@ def _find(dirpath, suffix):
     raise FileNotFoundError("no *%s under %s" % (suffix, dirpath))
 
 
-def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command):
+def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=None):
     """Turn rocprofv3 CSV output of this benchmark into the text summaries
     under profiles/ and profiles/traffic.json (HBM bytes per launch)."""
     import quantum_state_encoding_amd as qse
@@ -230,7 +230,38 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command):
                 i, short(name), len(fv), np.mean(fv), np.mean(wv), b, 2 * chunk_bytes,
                 b / (2 * chunk_bytes), rec["avg_us"]))
         passes[str(i)] = rec
+    lds_lines = []
+    if lds_dir:
+        per = {}
+        for r in _read_csv(_find(lds_dir, "counter_collection.csv")):
+            key = (r["Kernel_Name"], int(r["Grid_Size"]), r["Dispatch_Id"])
+            per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        agg = {}
+        for (name, grid, _), cs in per.items():
+            a = agg.setdefault((short(name), grid), {})
+            for k, v in cs.items():
+                a[k] = a.get(k, 0.0) + v
+            a["dispatches"] = a.get("dispatches", 0) + 1
+        lds_lines = ["# rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS "
+                     "SQ_LDS_MEM_VIOLATIONS SQ_LDS_UNALIGNED_STALL: %s" % workload,
+                     "# command: " + command.replace("--kernel-trace --stats",
+                                                     "--pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+                                                     "SQ_INSTS_LDS SQ_LDS_MEM_VIOLATIONS "
+                                                     "SQ_LDS_UNALIGNED_STALL"),
+                     "# kernel | grid | dispatches | LDS instructions | LDS active cycles | "
+                     "bank-conflict cycles | conflict / active | memory violations | "
+                     "unaligned stalls"]
+        for (name, grid), a in sorted(agg.items(), key=lambda kv: -kv[1].get("SQ_LDS_IDX_ACTIVE", 0)):
+            act = a.get("SQ_LDS_IDX_ACTIVE", 0.0)
+            bc = a.get("SQ_LDS_BANK_CONFLICT", 0.0)
+            lds_lines.append("%s | %d | %d | %.0f | %.0f | %.0f | %.4f | %.0f | %.0f" % (
+                name, grid, a["dispatches"], a.get("SQ_INSTS_LDS", 0.0), act, bc,
+                bc / act if act else 0.0, a.get("SQ_LDS_MEM_VIOLATIONS", 0.0),
+                a.get("SQ_LDS_UNALIGNED_STALL", 0.0)))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    if lds_lines:
+        with open(os.path.join(ROOT, "profiles", "%s_lds.txt" % workload), "w") as f:
+            f.write("\n".join(lds_lines) + "\n")
     with open(os.path.join(ROOT, "profiles", "%s_kernel_trace.txt" % workload), "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(os.path.join(ROOT, "profiles", "%s_traffic.txt" % workload), "w") as f:
@@ -246,7 +277,7 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(allt, f, indent=1, sort_keys=True)
         f.write("\n")
-    print("\n".join(lines + [""] + tl))
+    print("\n".join(lines + [""] + tl + [""] + lds_lines))
 
 
 def main():
@@ -256,13 +287,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="n20_b256_f32", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--summarize-profile", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/ summaries from rocprofv3 CSV output of this benchmark")
+    ap.add_argument("--summarize-profile", nargs="+",
+                    metavar="DIR", help="KT_DIR FETCH_DIR WRITE_DIR [LDS_DIR]: write profiles/ "
+                    "summaries from rocprofv3 CSV output of this benchmark")
     ap.add_argument("--profile-command", default="",
                     help="the rocprofv3 command line recorded in the summaries")
     args = ap.parse_args()
     if args.summarize_profile:
-        summarize_profile(args.workload, *args.summarize_profile, args.profile_command)
+        d = args.summarize_profile
+        if len(d) not in (3, 4):
+            ap.error("--summarize-profile takes 3 or 4 directories")
+        summarize_profile(args.workload, d[0], d[1], d[2], args.profile_command,
+                          d[3] if len(d) == 4 else None)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
