@@ -280,6 +280,37 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
     print("\n".join(lines + [""] + tl + [""] + lds_lines))
 
 
+def bench_ablations(torch, w, steps=3):
+    """Time the pages' designs on the workload's state: one launch per
+    butterfly stage, and the popcount-GEMM Kronecker scaffold with its batch
+    transposes (fwt_ablation_execute).  ms per step, same accounting."""
+    import quantum_state_encoding_amd as qse
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if w.dtype == "f32" else torch.float64
+    re = torch.randn(w.batch, w.N, device=dev, dtype=tdt) / 1024
+    im = torch.randn_like(re)
+    stream = torch.cuda.current_stream()
+    out = {}
+    kinds = [("stagewise", qse.ABLATION_STAGEWISE, w.n)]
+    if w.n <= 20:
+        kinds.append(("popc_gemm_transpose", qse.ABLATION_POPC_GEMM, 2))
+    for name, kind, launches in kinds:
+        wsb = qse.ablation_workspace(kind, w.batch, w.n, w.dtype, True)
+        ws = torch.empty(wsb // 4, device=dev) if wsb else None
+        fn = lambda: qse.ablation_execute(kind, re, im, n=w.n, normalize=w.normalize,
+                                          workspace=ws)
+        fn()
+        torch.cuda.synchronize()
+        ms = time_events(torch, stream, fn, steps)
+        out[name] = {"ms_per_step": ms, "amplitudes_per_s": w.batch * w.N / (ms * 1e-3),
+                     "gbps_algorithmic": 2 * w.state_bytes / (ms * 1e-3) / 1e9}
+        del ws
+    del re, im
+    torch.cuda.empty_cache()
+    log("ablations: " + ", ".join("%s %.3f ms" % (k, v["ms_per_step"]) for k, v in out.items()))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,6 +318,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="n20_b256_f32", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-ablations", action="store_true",
+                    help="skip timing the pages' designs (stage-wise, popcount GEMM)")
     ap.add_argument("--summarize-profile", nargs="+",
                     metavar="DIR", help="KT_DIR FETCH_DIR WRITE_DIR [LDS_DIR]: write profiles/ "
                     "summaries from rocprofv3 CSV output of this benchmark")
@@ -342,6 +375,11 @@ def main():
                            "note": "%.0f KiB state, resident in cache across steps; "
                                    "latency-bound" % (ws.state_bytes / 1024)}
 
+    # The pages' own designs for the same transform, on the same state.
+    ablations = {}
+    if not args.no_ablations:
+        ablations = bench_ablations(torch, w)
+
     cpu = None if args.no_cpu else cpu_baseline(w)
     out = {
         "metric": "FWT amplitudes/sec + achieved HBM GB/s (% of peak)",
@@ -375,6 +413,7 @@ def main():
                      "launches_per_step": r["passes"] * (-(-w.batch // r["chunk"]))},
         "cpu_baseline": cpu,
         "also": also,
+        "ablations": ablations,
     }
     print(json.dumps(out), flush=True)
 

@@ -203,6 +203,41 @@ const char* fwt_strerror(int status);
  * thread (hipSuccess if none). */
 int fwt_last_hip_error(void);
 
+/* ---- Ablations: the pages' own designs for the same transform ----------
+ * Each computes exactly what fwt_execute computes (the same sums in a
+ * different association), so they share its parity bars; they exist to be
+ * measured against the tile passes. */
+typedef enum {
+    /* One launch per butterfly stage, each streaming the whole state: the
+     * global-memory FWT of the Apache Mahout pull request "[QDP] [feature]
+     * Pr4 kronecker fwt" ("Benchmark Results", "Why submit PR4").
+     * n >= 2 (fp32) / 1 (fp64). */
+    FWT_ABLATION_STAGEWISE = 1,
+    /* The pull request's Kronecker scaffold (section "How"): on the
+     * 2^(n/2) x 2^(n - n/2) view, every row times H_{n-n/2} by a direct
+     * sum with each sign generated from popcount(k AND i), a batch
+     * transpose into the workspace, the same GEMM for H_{n/2}, a transpose
+     * back.  2 <= n <= 26; needs a workspace of the state's size. */
+    FWT_ABLATION_POPC_GEMM = 2,
+    /* Reserved for the matrix-core block-Hadamard variant. */
+    FWT_ABLATION_MFMA = 3
+} fwt_ablation;
+
+/* Workspace bytes fwt_ablation_execute needs for `batch` vectors (0 if
+ * none).  Returns FWT_OK or FWT_EINVAL. */
+int fwt_ablation_workspace(int kind, int64_t batch, int n, fwt_dtype dtype, int with_im,
+                           size_t* out);
+
+/* Run ablation `kind` on planar device buffers in place, asynchronously on
+ * `stream`, with the argument rules of fwt_execute; `workspace` (device
+ * memory of at least fwt_ablation_workspace bytes, 16-byte aligned, not
+ * overlapping re/im; NULL when none is needed) is scratch owned by the
+ * caller.  Returns FWT_OK, FWT_EINVAL, FWT_EALIGN, FWT_EUNSUPPORTED (kind
+ * or n outside its range) or FWT_EHIP. */
+int fwt_ablation_execute(int kind, int64_t batch, int n, fwt_dtype dtype, void* re, void* im,
+                         int normalize, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* Measurement aid, not part of the transform: copies `bytes` (a multiple
  * of 16) from src to dst with the same 16-byte streaming access the passes
  * use, so a benchmark can price one read plus one write of the state.

@@ -17,6 +17,8 @@ import ctypes
 import os
 
 __all__ = ["Plan", "FwtError", "execute", "stream_copy", "library_path", "load_library",
+           "ablation_workspace", "ablation_execute", "ABLATION_STAGEWISE", "ABLATION_POPC_GEMM",
+           "ABLATION_MFMA", "PassTuning",
            "PATH_AUTO", "PATH_SINGLE_BLOCK", "PATH_MULTIPASS", "PATH_MFMA_ABLATION",
            "FWT_OK", "FWT_EINVAL", "FWT_EALIGN", "FWT_EUNSUPPORTED", "FWT_EHIP",
            "FWT_ENOMEM", "EXPORTED_SYMBOLS"]
@@ -34,7 +36,8 @@ EXPORTED_SYMBOLS = ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create
                     "fwt_execute_check",
                     "fwt_plan_num_passes", "fwt_plan_pass_config", "fwt_plan_pass_bits",
                     "fwt_plan_destroy", "fwt_strerror", "fwt_last_hip_error",
-                    "fwt_stream_copy", "fwt_plan_chunk_vectors")
+                    "fwt_stream_copy", "fwt_plan_chunk_vectors", "fwt_ablation_workspace",
+                    "fwt_ablation_execute")
 
 _lib = None
 
@@ -89,6 +92,8 @@ def load_library():
     lib.fwt_strerror.restype = ctypes.c_char_p
     lib.fwt_last_hip_error.argtypes = []
     lib.fwt_stream_copy.argtypes = [vp, vp, i64, vp]
+    lib.fwt_ablation_workspace.argtypes = [i32, i64, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fwt_ablation_execute.argtypes = [i32, i64, i32, i32, vp, vp, i32, vp, ctypes.c_size_t, vp]
     for name in ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create_tuned",
                  "fwt_execute", "fwt_execute_pass", "fwt_execute_pass_timed",
                  "fwt_execute_check", "fwt_plan_num_passes", "fwt_plan_pass_bits",
@@ -331,6 +336,40 @@ def execute(re, im=None, n=None, normalize=True, stream=None, path=PATH_AUTO):
     if dtype is None:
         raise ValueError("re must be float32 or float64")
     return Plan(n, dtype, path).execute(re, im, normalize, stream)
+
+
+ABLATION_STAGEWISE, ABLATION_POPC_GEMM, ABLATION_MFMA = 1, 2, 3
+
+
+def ablation_workspace(kind, batch, n, dtype="f32", with_im=True):
+    """Workspace bytes an ablation needs (see fwt_ablation_workspace)."""
+    out = ctypes.c_size_t()
+    st = load_library().fwt_ablation_workspace(int(kind), int(batch), int(n), _DTYPES[dtype],
+                                               1 if with_im else 0, ctypes.byref(out))
+    if st != FWT_OK:
+        raise FwtError(st, "fwt_ablation_workspace")
+    return out.value
+
+
+def ablation_execute(kind, re, im=None, n=None, normalize=True, workspace=None, stream=None):
+    """Run one of the pages' designs (fwt_ablation_execute) on torch tensors
+    in place; `workspace` is a device tensor of at least ablation_workspace
+    bytes when the kind needs one."""
+    if n is None:
+        n = re.shape[-1].bit_length() - 1
+    dtype = {"torch.float32": "f32", "torch.float64": "f64"}.get(str(re.dtype))
+    if dtype is None:
+        raise ValueError("re must be float32 or float64")
+    batch = re.numel() >> n
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().fwt_ablation_execute(
+        int(kind), batch, int(n), _DTYPES[dtype], ctypes.c_void_p(re.data_ptr()),
+        ctypes.c_void_p(im.data_ptr() if im is not None else None), 1 if normalize else 0,
+        ctypes.c_void_p(ws_ptr), ws_bytes, _stream_handle(stream))
+    if st != FWT_OK:
+        raise FwtError(st, "fwt_ablation_execute")
+    return re, im
 
 
 def stream_copy(dst, src, stream=None):

@@ -6,7 +6,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfwt.so")
-SOURCES = [os.path.join(CSRC, "fwt_kernels.hip"), os.path.join(CSRC, "fwt_api.cpp")]
+SOURCES = [os.path.join(CSRC, "fwt_kernels.hip"), os.path.join(CSRC, "fwt_ablation.hip"),
+           os.path.join(CSRC, "fwt_api.cpp")]
 HEADERS = [os.path.join(CSRC, "fwt_internal.h"), os.path.join(ROOT, "include", "fwt.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

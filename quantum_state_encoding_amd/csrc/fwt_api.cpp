@@ -694,6 +694,106 @@ int fwt_plan_pass_bits(fwt_plan_t plan, int i, int* out_bits)
     return FWT_OK;
 }
 
+// ---- ablations ---------------------------------------------------------------
+
+namespace {
+
+size_t ablation_workspace_bytes(int kind, int64_t batch, int n, fwt_dtype dtype, int with_im)
+{
+    if (kind != FWT_ABLATION_POPC_GEMM)
+        return 0;
+    const size_t esize = dtype == FWT_F64 ? 8 : 4;
+    return (size_t)batch * ((size_t)1 << n) * esize * (with_im ? 2 : 1);
+}
+
+int ablation_check(int kind, int64_t batch, int n, fwt_dtype dtype, const void* re,
+                   const void* im, const void* ws, size_t ws_bytes)
+{
+    if (dtype != FWT_F32 && dtype != FWT_F64)
+        return FWT_EINVAL;
+    const int vb = vec_bits(dtype);
+    if (kind == FWT_ABLATION_STAGEWISE) {
+        if (n < vb || n > FWT_MAX_N)
+            return n < 0 || n > FWT_MAX_N ? FWT_EINVAL : FWT_EUNSUPPORTED;
+    } else if (kind == FWT_ABLATION_POPC_GEMM) {
+        if (n < 2 || n > 26)
+            return n < 0 || n > FWT_MAX_N ? FWT_EINVAL : FWT_EUNSUPPORTED;
+    } else if (kind == FWT_ABLATION_MFMA) {
+        return FWT_EUNSUPPORTED;
+    } else {
+        return FWT_EINVAL;
+    }
+    if (!re || batch < 0)
+        return FWT_EINVAL;
+    if (((uintptr_t)re & 15u) || ((uintptr_t)im & 15u) || ((uintptr_t)ws & 15u))
+        return FWT_EALIGN;
+    if (re == im)
+        return FWT_EINVAL;
+    const size_t esize = dtype == FWT_F64 ? 8 : 4;
+    if (batch > INT64_MAX / ((int64_t)1 << n) / (int64_t)esize)
+        return FWT_EINVAL;
+    const size_t bytes = (size_t)batch * ((size_t)1 << n) * esize;
+    auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+        const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+        return x < y + nb && y < x + na;
+    };
+    if (im && overlap(re, bytes, im, bytes))
+        return FWT_EINVAL;
+    const size_t need = ablation_workspace_bytes(kind, batch, n, dtype, im != nullptr);
+    if (need) {
+        if (!ws || ws_bytes < need)
+            return FWT_EINVAL;
+        if (overlap(ws, need, re, bytes) || (im && overlap(ws, need, im, bytes)))
+            return FWT_EINVAL;
+    }
+    if (batch == 0)
+        return FWT_OK;
+    int rc = check_range(re, bytes);
+    if (rc == FWT_OK && im)
+        rc = check_range(im, bytes);
+    if (rc == FWT_OK && need)
+        rc = check_range(ws, need);
+    return rc;
+}
+
+}  // namespace
+
+int fwt_ablation_workspace(int kind, int64_t batch, int n, fwt_dtype dtype, int with_im,
+                           size_t* out)
+{
+    if (!out || batch < 0 || n < 0 || n > FWT_MAX_N)
+        return FWT_EINVAL;
+    if (kind < FWT_ABLATION_STAGEWISE || kind > FWT_ABLATION_MFMA)
+        return FWT_EINVAL;
+    *out = ablation_workspace_bytes(kind, batch, n, dtype, with_im);
+    return FWT_OK;
+}
+
+int fwt_ablation_execute(int kind, int64_t batch, int n, fwt_dtype dtype, void* re, void* im,
+                         int normalize, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream)
+{
+    int rc = ablation_check(kind, batch, n, dtype, re, im, workspace, workspace_bytes);
+    if (rc != FWT_OK || batch == 0)
+        return rc;
+    int cus = 1;
+    rc = ensure_device_init(&cus);
+    if (rc != FWT_OK)
+        return rc;
+    const double c = dtype == FWT_F64 ? norm_constant(n) : (double)(float)norm_constant(n);
+    const int f64 = dtype == FWT_F64 ? 1 : 0;
+    hipError_t e;
+    if (kind == FWT_ABLATION_STAGEWISE) {
+        e = qse::ablation_stagewise(f64, re, im, batch, n, normalize, c, stream);
+    } else {
+        const size_t esize = f64 ? 8 : 4;
+        void* ws_im = im ? (char*)workspace + (size_t)batch * ((size_t)1 << n) * esize : nullptr;
+        e = qse::ablation_popc_gemm(f64, re, im, workspace, ws_im, batch, n, normalize, c,
+                                    stream);
+    }
+    return e == hipSuccess ? FWT_OK : hip_fail(e);
+}
+
 int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out)
 {
     if (!valid_plan(plan) || !out || i < 0 || i >= plan->npasses)

@@ -86,4 +86,10 @@ hipError_t launch_pair_f32(float* re, float* im, int64_t pairs, int do_scale,
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes,
                               hipStream_t stream);
 
+// Ablations (fwt_ablation.hip): the pages' own designs for the transform.
+hipError_t ablation_stagewise(int f64, void* re, void* im, int64_t batch, int n, int normalize,
+                              double c, hipStream_t stream);
+hipError_t ablation_popc_gemm(int f64, void* re, void* im, void* ws_re, void* ws_im,
+                              int64_t batch, int n, int normalize, double c, hipStream_t stream);
+
 }  // namespace qse

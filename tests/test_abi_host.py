@@ -225,3 +225,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     with pytest.raises(ImportError):
         qse.Plan(4, "f32")
     importlib.reload(qse)
+
+
+def test_ablation_workspace_and_validation(lib):
+    assert qse.ablation_workspace(qse.ABLATION_POPC_GEMM, 64, 14, "f32", True) == 2 * 64 * 4 << 14
+    assert qse.ablation_workspace(qse.ABLATION_POPC_GEMM, 3, 10, "f64", False) == 3 * 8 << 10
+    assert qse.ablation_workspace(qse.ABLATION_STAGEWISE, 64, 14, "f32", True) == 0
+    ex = lib.fwt_ablation_execute
+    N = 1 << 10
+    # every case below fails before any HIP call
+    assert ex(9, 1, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EINVAL
+    assert ex(qse.ABLATION_MFMA, 1, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EUNSUPPORTED
+    assert ex(qse.ABLATION_STAGEWISE, 1, 1, 0, FAKE, FAKE + 64, 1, None, 0, None) == qse.FWT_EUNSUPPORTED
+    assert ex(qse.ABLATION_POPC_GEMM, 1, 27, 0, FAKE, FAKE + (4 << 27), 1, None, 0, None) == qse.FWT_EUNSUPPORTED
+    assert ex(qse.ABLATION_STAGEWISE, 1, 10, 0, FAKE + 4, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EALIGN
+    assert ex(qse.ABLATION_STAGEWISE, 2, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EINVAL
+    ws = FAKE + (1 << 30)
+    assert ex(qse.ABLATION_POPC_GEMM, 1, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EINVAL
+    assert ex(qse.ABLATION_POPC_GEMM, 1, 10, 0, FAKE, FAKE + 4 * N, 1, ws, 4 * N, None) == qse.FWT_EINVAL
+    assert ex(qse.ABLATION_POPC_GEMM, 1, 10, 0, FAKE, FAKE + 4 * N, 1, FAKE + 8, 8 * N, None) == qse.FWT_EALIGN
+    assert ex(qse.ABLATION_POPC_GEMM, 1, 10, 0, FAKE, FAKE + 4 * N, 1, FAKE, 8 * N, None) == qse.FWT_EINVAL
+    assert ex(qse.ABLATION_STAGEWISE, 0, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_OK

@@ -376,6 +376,46 @@ def test_timed_passes_follow_the_chunk_schedule():
     assert_exact(gre[: 3], re[: 3], n, False)
 
 
+@pytest.mark.parametrize("kind", ["stagewise", "popc_gemm"])
+@pytest.mark.parametrize("dtype,n,batch", [("f32", 2, 5), ("f32", 5, 3), ("f32", 10, 8), ("f32", 13, 2),
+                                           ("f32", 14, 3), ("f64", 1, 4), ("f64", 2, 3), ("f64", 9, 5),
+                                           ("f64", 14, 2), ("f32", 17, 1)])
+def test_integer_ablations(kind, dtype, n, batch):
+    """The pages' designs (one launch per stage; popcount GEMM + transposes)
+    compute exactly the same transform."""
+    k = {"stagewise": qse.ABLATION_STAGEWISE, "popc_gemm": qse.ABLATION_POPC_GEMM}[kind]
+    if kind == "popc_gemm" and n < 2:
+        pytest.skip("the scaffold needs n >= 2")
+    say("ablation %s %s n=%d batch=%d" % (kind, dtype, n, batch))
+    npd = np.float32 if dtype == "f32" else np.float64
+    re = ints((batch, 1 << n), 99_000 + n, npd)
+    im = ints((batch, 1 << n), 99_500 + n, npd)
+    for normalize in (False, True):
+        if normalize and n % 2:
+            continue
+        tre, tim = to_dev(re), to_dev(im)
+        wsb = qse.ablation_workspace(k, batch, n, dtype, True)
+        ws = torch.empty(max(wsb, 16) // 4, dtype=torch.float32, device="cuda") if wsb else None
+        qse.ablation_execute(k, tre, tim, n=n, normalize=normalize, workspace=ws)
+        torch.cuda.synchronize()
+        assert_exact(tre.cpu().numpy(), re, n, normalize)
+        assert_exact(tim.cpu().numpy(), im, n, normalize)
+
+
+@pytest.mark.parametrize("kind", ["stagewise", "popc_gemm"])
+def test_gaussian_ablations_n20(kind):
+    k = {"stagewise": qse.ABLATION_STAGEWISE, "popc_gemm": qse.ABLATION_POPC_GEMM}[kind]
+    say("ablation gauss %s n=20" % kind)
+    w = workloads.custom(20, 2, "f32", "gauss", True, seed=77)
+    re, im = workloads.gen(w)
+    tre, tim = to_dev(re), to_dev(im)
+    wsb = qse.ablation_workspace(k, 2, 20, "f32", True)
+    ws = torch.empty(wsb // 4, device="cuda") if wsb else None
+    qse.ablation_execute(k, tre, tim, n=20, normalize=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close("f32", 20, re, im, tre.cpu().numpy(), tim.cpu().numpy())
+
+
 def test_bound_call_keeps_its_plan_alive():
     """A callable from Plan.bind stays valid after the Plan object itself
     goes out of scope."""
