@@ -282,8 +282,10 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
 
 def bench_ablations(torch, w, steps=3):
     """Time the pages' designs on the workload's state: one launch per
-    butterfly stage, and the popcount-GEMM Kronecker scaffold with its batch
-    transposes (fwt_ablation_execute).  ms per step, same accounting."""
+    butterfly stage, the popcount-GEMM Kronecker scaffold with its batch
+    transposes, and the matrix-core block-Hadamard row kernel followed by
+    the column passes (fwt_ablation_execute).  ms per step, same
+    accounting."""
     import quantum_state_encoding_amd as qse
     dev = torch.device("cuda:0")
     tdt = torch.float32 if w.dtype == "f32" else torch.float64
@@ -294,6 +296,8 @@ def bench_ablations(torch, w, steps=3):
     kinds = [("stagewise", qse.ABLATION_STAGEWISE, w.n)]
     if w.n <= 20:
         kinds.append(("popc_gemm_transpose", qse.ABLATION_POPC_GEMM, 2))
+    if w.n >= 8:
+        kinds.append(("mfma_block_hadamard", qse.ABLATION_MFMA, 2))
     for name, kind, launches in kinds:
         wsb = qse.ablation_workspace(kind, w.batch, w.n, w.dtype, True)
         ws = torch.empty(wsb // 4, device=dev) if wsb else None
@@ -319,7 +323,8 @@ def main():
     ap.add_argument("--workload", default="n20_b256_f32", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-ablations", action="store_true",
-                    help="skip timing the pages' designs (stage-wise, popcount GEMM)")
+                    help="skip timing the pages' designs (stage-wise, popcount GEMM, "
+                    "matrix-core blocks)")
     ap.add_argument("--summarize-profile", nargs="+",
                     metavar="DIR", help="KT_DIR FETCH_DIR WRITE_DIR [LDS_DIR]: write profiles/ "
                     "summaries from rocprofv3 CSV output of this benchmark")

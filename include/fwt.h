@@ -219,7 +219,12 @@ typedef enum {
      * transpose into the workspace, the same GEMM for H_{n/2}, a transpose
      * back.  2 <= n <= 26; needs a workspace of the state's size. */
     FWT_ABLATION_POPC_GEMM = 2,
-    /* Reserved for the matrix-core block-Hadamard variant. */
+    /* Matrix-core block Hadamard (the iThome "Day 18" native-FWT article,
+     * "Kronecker block GEMM idea", "TF32 path"): the low min(n, 12) bits
+     * as dense H_16 block products on the fp32 / fp64 16x16x4 matrix
+     * instructions (leftover bits butterflied in LDS), the higher bits on
+     * the ordinary column passes.  8 <= n <= 30 (fp32) / 29 (fp64); no
+     * workspace. */
     FWT_ABLATION_MFMA = 3
 } fwt_ablation;
 

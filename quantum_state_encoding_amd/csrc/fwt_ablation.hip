@@ -6,6 +6,11 @@
 //    request "[QDP] [feature] Pr4 kronecker fwt" benchmarks against,
 //    sections "Benchmark Results" and "Why submit PR4": one DRAM
 //    traversal per stage);
+//  * matrix-core block Hadamard: the contiguous row pass rewritten as
+//    dense H_16 block products on v_mfma_*_16x16x4 (the iThome "Day 18"
+//    native-FWT article, sections "Kronecker block GEMM idea" and "TF32
+//    path": reshape, block Hadamard GEMM, with the layout change fused into
+//    the kernel; gfx950 has no TF32, so fp32 and fp64 matrix cores);
 //  * Kronecker GEMM scaffold: Z = X . H_{n2} on every row of the
 //    2^n1 x 2^n2 view with each Walsh entry generated from the population
 //    count of k AND i, a batched transpose, the same GEMM for H_{n1}, and a
@@ -174,6 +179,174 @@ __global__ void __launch_bounds__(256)
     }
 }
 
+// ---- matrix-core block Hadamard row pass -----------------------------------
+//
+// A workgroup stages TPW contiguous tiles of 2^KM elements in LDS (one pad
+// element per 16).  For each group of 4 index bits [4q, 4q + 4), q < KM / 4,
+// the tile's 2^(KM-4) "lines" (16 elements differing only in those bits)
+// are multiplied by H_16 on the matrix cores: 16 lines at a time form the
+// A operand (lane l holds line l mod 16, column 4 kb + l / 16), the B
+// operand is the H_16 slab with entries (-1)^popcount(k AND j), and four
+// K = 4 products accumulate the 16 x 16 result, written back over the same
+// lines.  The KM mod 4 remaining top bits are butterflied in LDS.
+
+template <typename T>
+struct MfmaOps;
+template <>
+struct MfmaOps<float> {
+    typedef float acc_t __attribute__((ext_vector_type(4)));
+    __device__ __forceinline__ static acc_t mma(float a, float b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    // Result row (line within the block) of lane l, register r.
+    __device__ __forceinline__ static int row(int l, int r) { return 4 * (l >> 4) + r; }
+};
+template <>
+struct MfmaOps<double> {
+    typedef double acc_t __attribute__((ext_vector_type(4)));
+    __device__ __forceinline__ static acc_t mma(double a, double b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static int row(int l, int r) { return (l >> 4) + 4 * r; }
+};
+
+__device__ __forceinline__ int pad16(int e) { return e + (e >> 4); }
+
+// Element index of line lam, column k (4 bits) for the bit group at 4q.
+__device__ __forceinline__ int line_elem(int lam, int k, int q)
+{
+    const int lo = lam & ((1 << (4 * q)) - 1);
+    const int hi = lam >> (4 * q);
+    return (hi << (4 * q + 4)) | (k << (4 * q)) | lo;
+}
+
+template <typename T, int KM>
+__global__ void __launch_bounds__(256)
+    mfma_row_kernel(T* __restrict__ re, T* __restrict__ im, int64_t tiles, int do_scale, T scale)
+{
+    using Ops = MfmaOps<T>;
+    using acc_t = typename Ops::acc_t;
+    constexpr int TPW = KM >= 12 ? 1 : 1 << (12 - KM);   // tiles per workgroup
+    constexpr int L = 1 << KM;
+    constexpr int TL = L + (L >> 4);                      // padded tile length
+    constexpr int G = KM / 4;                             // MFMA bit groups
+    constexpr int LINES = L >> 4;                         // lines per tile and group
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    T* const lds = reinterpret_cast<T*>(lds_raw);
+    T* const buf = blockIdx.y ? im : re;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * TPW;
+    const int ntile = (int)(tiles - t0 < TPW ? tiles - t0 : TPW);
+
+    // 16-byte global accesses; the W elements of one vector stay inside one
+    // padded run of 16, so they land on consecutive LDS words.
+    using V = typename Vec16<T>::type;
+    constexpr int W = 16 / sizeof(T);
+    V* const gv = reinterpret_cast<V*>(buf + t0 * L);
+    for (int i = tid; i < ntile * (L / W); i += 256) {
+        const V v = gv[i];
+        const int e = i * W;
+        T* const d = lds + (e / L) * TL + pad16(e % L);
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            d[w] = v[w];
+    }
+    __syncthreads();
+
+    // B operand slabs: B[kb][l] = H_16[4 kb + l / 16][l mod 16].
+    T h[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+        h[kb] = (__builtin_popcount((unsigned)((4 * kb + (lane >> 4)) & (lane & 15))) & 1) ? T(-1)
+                                                                                            : T(1);
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        // blocks of 16 lines, over all tiles of the workgroup, split by wave
+        const int blocks = ntile * (LINES >> 4);
+        for (int blk = wave; blk < blocks; blk += 4) {
+            const int tile = blk / (LINES >> 4);
+            const int lam0 = (blk % (LINES >> 4)) << 4;
+            T* const tl = lds + tile * TL;
+            acc_t acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const T a = tl[pad16(line_elem(lam0 + (lane & 15), 4 * kb + (lane >> 4), q))];
+                acc = Ops::mma(a, h[kb], acc);
+            }
+            // every lane has read its operands (the MFMA consumed them)
+            // before any lane of this wave writes the block back
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                tl[pad16(line_elem(lam0 + Ops::row(lane, r), lane & 15, q))] = acc[r];
+        }
+        __syncthreads();
+    }
+    // remaining top bits [4G, KM): butterflies in LDS
+#pragma unroll
+    for (int b = 4 * G; b < KM; ++b) {
+        for (int i = tid; i < ntile * (L >> 1); i += 256) {
+            const int tile = i / (L >> 1), p = i % (L >> 1);
+            const int e = ((p >> b) << (b + 1)) | (p & ((1 << b) - 1));
+            T* const tl = lds + tile * TL;
+            const T x = tl[pad16(e)], y = tl[pad16(e + (1 << b))];
+            tl[pad16(e)] = x + y;
+            tl[pad16(e + (1 << b))] = x - y;
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < ntile * (L / W); i += 256) {
+        const int e = i * W;
+        const T* const d = lds + (e / L) * TL + pad16(e % L);
+        V v;
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            v[w] = do_scale ? d[w] * scale : d[w];
+        gv[i] = v;
+    }
+}
+
+template <typename T, int KM>
+hipError_t mfma_row_launch(T* re, T* im, int64_t tiles, int do_scale, double c,
+                           hipStream_t stream)
+{
+    constexpr int TPW = KM >= 12 ? 1 : 1 << (12 - KM);
+    constexpr size_t lds = (size_t)TPW * ((1 << KM) + ((1 << KM) >> 4)) * sizeof(T);
+    const void* fn = reinterpret_cast<const void*>(&mfma_row_kernel<T, KM>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess)
+        return e;
+    // at most 2^20 workgroups (2^28 work-items) per launch
+    const int64_t per_launch = (int64_t)TPW << 20;
+    for (int64_t t0 = 0; t0 < tiles; t0 += per_launch) {
+        const int64_t nt = tiles - t0 < per_launch ? tiles - t0 : per_launch;
+        const int64_t off = t0 << KM;
+        hipLaunchKernelGGL((mfma_row_kernel<T, KM>), dim3((unsigned)((nt + TPW - 1) / TPW), im ? 2 : 1),
+                           dim3(256), lds, stream, re + off, im ? im + off : nullptr, nt, do_scale,
+                           (T)c);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+template <typename T>
+hipError_t mfma_row_dispatch(T* re, T* im, int64_t tiles, int km, int do_scale, double c,
+                             hipStream_t stream)
+{
+    switch (km) {
+    case 8: return mfma_row_launch<T, 8>(re, im, tiles, do_scale, c, stream);
+    case 9: return mfma_row_launch<T, 9>(re, im, tiles, do_scale, c, stream);
+    case 10: return mfma_row_launch<T, 10>(re, im, tiles, do_scale, c, stream);
+    case 11: return mfma_row_launch<T, 11>(re, im, tiles, do_scale, c, stream);
+    case 12: return mfma_row_launch<T, 12>(re, im, tiles, do_scale, c, stream);
+    case 13: return mfma_row_launch<T, 13>(re, im, tiles, do_scale, c, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 unsigned grid_for(int64_t work, int64_t per_block)
 {
     int64_t g = (work + per_block - 1) / per_block;
@@ -245,6 +418,15 @@ hipError_t popc_gemm_impl(T* re, T* im, T* ws_re, T* ws_im, int64_t batch, int n
 }
 
 }  // namespace
+
+hipError_t ablation_mfma_row(int f64, void* re, void* im, int64_t batch, int n, int km,
+                             int do_scale, double c, hipStream_t stream)
+{
+    const int64_t tiles = batch << (n - km);
+    if (f64)
+        return mfma_row_dispatch<double>((double*)re, (double*)im, tiles, km, do_scale, c, stream);
+    return mfma_row_dispatch<float>((float*)re, (float*)im, tiles, km, do_scale, c, stream);
+}
 
 hipError_t ablation_stagewise(int f64, void* re, void* im, int64_t batch, int n, int normalize,
                               double c, hipStream_t stream)

@@ -31,6 +31,9 @@ namespace {
 
 constexpr uint64_t kPlanMagic = 0x46575450'4c414e31ull;  // "FWTPLAN1"
 constexpr int kMaxPasses = 4;
+// Row bits of the matrix-core ablation's block-Hadamard kernel.
+constexpr int kMfmaRowMin = 8;
+constexpr int kMfmaRowMax = 12;
 constexpr int kRowKrMax = 13;          // rows bits of a row pass (vectors)
 constexpr int kColKrMax = 12;          // rows bits of a column pass
 constexpr size_t kLdsMax = 160 * 1024; // per workgroup on gfx950
@@ -719,7 +722,8 @@ int ablation_check(int kind, int64_t batch, int n, fwt_dtype dtype, const void* 
         if (n < 2 || n > 26)
             return n < 0 || n > FWT_MAX_N ? FWT_EINVAL : FWT_EUNSUPPORTED;
     } else if (kind == FWT_ABLATION_MFMA) {
-        return FWT_EUNSUPPORTED;
+        if (n < kMfmaRowMin || n > (dtype == FWT_F64 ? 29 : FWT_MAX_N))
+            return n < 0 || n > FWT_MAX_N ? FWT_EINVAL : FWT_EUNSUPPORTED;
     } else {
         return FWT_EINVAL;
     }
@@ -756,6 +760,63 @@ int ablation_check(int kind, int64_t batch, int n, fwt_dtype dtype, const void* 
     return rc;
 }
 
+// Matrix-core ablation: the low min(n, 12) bits on the block-Hadamard row
+// kernel, the remaining bits on the ordinary column tile passes of a plan
+// whose pass 0 covers those same low bits (never launched).  Plans are made
+// once per (dtype, n) and kept for the life of the process.
+fwt_plan_t g_mfma_plans[2][FWT_MAX_N + 1];
+std::mutex g_mfma_mutex;
+
+int mfma_rest_plan(int n, fwt_dtype dtype, int km, fwt_plan_t* out)
+{
+    std::lock_guard<std::mutex> lock(g_mfma_mutex);
+    fwt_plan_t& slot = g_mfma_plans[dtype == FWT_F64 ? 1 : 0][n];
+    if (!slot) {
+        int bits[kMaxPasses] = {km, 0, 0, 0};
+        const int rest = n - km;
+        int np = 1;
+        if (rest > kColKrMax) {
+            bits[np++] = rest - rest / 2;
+            bits[np++] = rest / 2;
+        } else if (rest > 0) {
+            bits[np++] = rest;
+        }
+        const int rc = make_plan(&slot, n, dtype, np, bits, nullptr);
+        if (rc != FWT_OK)
+            return rc;
+    }
+    *out = slot;
+    return FWT_OK;
+}
+
+int ablation_mfma(int64_t batch, int n, fwt_dtype dtype, void* re, void* im, int normalize,
+                  double c, hipStream_t stream)
+{
+    const int km = n < kMfmaRowMax ? n : kMfmaRowMax;
+    fwt_plan_t plan = nullptr;
+    int rc = mfma_rest_plan(n, dtype, km, &plan);
+    if (rc != FWT_OK)
+        return rc;
+    const int f64 = dtype == FWT_F64 ? 1 : 0;
+    int64_t cv = chunk_vectors(plan, batch, im ? 2 : 1);
+    if (cv == 0)
+        cv = batch;
+    const size_t vec_bytes = ((size_t)1 << n) * (f64 ? 8 : 4);
+    for (int64_t b0 = 0; b0 < batch; b0 += cv) {
+        const int64_t nb = batch - b0 < cv ? batch - b0 : cv;
+        void* cre = (char*)re + (size_t)b0 * vec_bytes;
+        void* cim = im ? (char*)im + (size_t)b0 * vec_bytes : nullptr;
+        const hipError_t e = qse::ablation_mfma_row(f64, cre, cim, nb, n, km,
+                                                    normalize && plan->npasses == 1, c, stream);
+        if (e != hipSuccess)
+            return hip_fail(e);
+        rc = launch_passes(plan, 1, plan->npasses, nb, n, cre, cim, normalize, stream);
+        if (rc != FWT_OK)
+            return rc;
+    }
+    return FWT_OK;
+}
+
 }  // namespace
 
 int fwt_ablation_workspace(int kind, int64_t batch, int n, fwt_dtype dtype, int with_im,
@@ -783,6 +844,8 @@ int fwt_ablation_execute(int kind, int64_t batch, int n, fwt_dtype dtype, void* 
     const double c = dtype == FWT_F64 ? norm_constant(n) : (double)(float)norm_constant(n);
     const int f64 = dtype == FWT_F64 ? 1 : 0;
     hipError_t e;
+    if (kind == FWT_ABLATION_MFMA)
+        return ablation_mfma(batch, n, dtype, re, im, normalize, c, stream);
     if (kind == FWT_ABLATION_STAGEWISE) {
         e = qse::ablation_stagewise(f64, re, im, batch, n, normalize, c, stream);
     } else {

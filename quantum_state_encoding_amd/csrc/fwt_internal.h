@@ -91,5 +91,8 @@ hipError_t ablation_stagewise(int f64, void* re, void* im, int64_t batch, int n,
                               double c, hipStream_t stream);
 hipError_t ablation_popc_gemm(int f64, void* re, void* im, void* ws_re, void* ws_im,
                               int64_t batch, int n, int normalize, double c, hipStream_t stream);
+// Matrix-core row pass over the km contiguous low bits (8 <= km <= 13).
+hipError_t ablation_mfma_row(int f64, void* re, void* im, int64_t batch, int n, int km,
+                             int do_scale, double c, hipStream_t stream);
 
 }  // namespace qse

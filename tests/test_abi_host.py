@@ -235,7 +235,12 @@ def test_ablation_workspace_and_validation(lib):
     N = 1 << 10
     # every case below fails before any HIP call
     assert ex(9, 1, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EINVAL
-    assert ex(qse.ABLATION_MFMA, 1, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EUNSUPPORTED
+    assert ex(qse.ABLATION_MFMA, 1, 7, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EUNSUPPORTED
+    assert ex(qse.ABLATION_MFMA, 1, 30, 1, FAKE, FAKE + (8 << 30), 1, None, 0, None) == qse.FWT_EUNSUPPORTED
+    assert ex(qse.ABLATION_MFMA, 1, 31, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EINVAL
+    assert ex(qse.ABLATION_MFMA, 1, 10, 0, FAKE + 4, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EALIGN
+    assert ex(qse.ABLATION_MFMA, 0, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_OK
+    assert qse.ablation_workspace(qse.ABLATION_MFMA, 64, 14, "f32", True) == 0
     assert ex(qse.ABLATION_STAGEWISE, 1, 1, 0, FAKE, FAKE + 64, 1, None, 0, None) == qse.FWT_EUNSUPPORTED
     assert ex(qse.ABLATION_POPC_GEMM, 1, 27, 0, FAKE, FAKE + (4 << 27), 1, None, 0, None) == qse.FWT_EUNSUPPORTED
     assert ex(qse.ABLATION_STAGEWISE, 1, 10, 0, FAKE + 4, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EALIGN

@@ -376,16 +376,22 @@ def test_timed_passes_follow_the_chunk_schedule():
     assert_exact(gre[: 3], re[: 3], n, False)
 
 
-@pytest.mark.parametrize("kind", ["stagewise", "popc_gemm"])
+ABLATION_KINDS = {"stagewise": qse.ABLATION_STAGEWISE, "popc_gemm": qse.ABLATION_POPC_GEMM,
+                  "mfma": qse.ABLATION_MFMA}
+
+
+@pytest.mark.parametrize("kind", ["stagewise", "popc_gemm", "mfma"])
 @pytest.mark.parametrize("dtype,n,batch", [("f32", 2, 5), ("f32", 5, 3), ("f32", 10, 8), ("f32", 13, 2),
                                            ("f32", 14, 3), ("f64", 1, 4), ("f64", 2, 3), ("f64", 9, 5),
                                            ("f64", 14, 2), ("f32", 17, 1)])
 def test_integer_ablations(kind, dtype, n, batch):
-    """The pages' designs (one launch per stage; popcount GEMM + transposes)
-    compute exactly the same transform."""
-    k = {"stagewise": qse.ABLATION_STAGEWISE, "popc_gemm": qse.ABLATION_POPC_GEMM}[kind]
+    """The pages' designs (one launch per stage; popcount GEMM + transposes;
+    H_16 blocks on the matrix cores) compute exactly the same transform."""
+    k = ABLATION_KINDS[kind]
     if kind == "popc_gemm" and n < 2:
         pytest.skip("the scaffold needs n >= 2")
+    if kind == "mfma" and n < 8:
+        pytest.skip("the matrix-core row kernel needs n >= 8")
     say("ablation %s %s n=%d batch=%d" % (kind, dtype, n, batch))
     npd = np.float32 if dtype == "f32" else np.float64
     re = ints((batch, 1 << n), 99_000 + n, npd)
@@ -402,9 +408,31 @@ def test_integer_ablations(kind, dtype, n, batch):
         assert_exact(tim.cpu().numpy(), im, n, normalize)
 
 
-@pytest.mark.parametrize("kind", ["stagewise", "popc_gemm"])
+# Matrix-core ablation at every row width it has (8..12 low bits; 13 for
+# n = 13 is not reached since the row kernel takes min(n, 12)), with ragged
+# last workgroups (11 bits: 2 tiles per workgroup, odd tile counts), a
+# one-column-pass remainder, a two-column-pass remainder (n = 26: 12 | 7 | 7)
+# and a state larger than one cache chunk (fp32 n = 20, 80 vectors).
+@pytest.mark.parametrize("dtype,n,batch", [("f32", 8, 7), ("f64", 8, 3), ("f32", 11, 33),
+                                           ("f64", 11, 5), ("f32", 12, 3), ("f64", 12, 2),
+                                           ("f32", 16, 3), ("f64", 21, 1), ("f32", 26, 1),
+                                           ("f32", 20, 80)])
+def test_integer_mfma_ablation(dtype, n, batch):
+    say("ablation mfma %s n=%d batch=%d" % (dtype, n, batch))
+    npd = np.float32 if dtype == "f32" else np.float64
+    re = ints((batch, 1 << n), 98_000 + n, npd)
+    im = ints((batch, 1 << n), 98_500 + n, npd)
+    normalize = n % 2 == 0
+    tre, tim = to_dev(re), to_dev(im)
+    qse.ablation_execute(qse.ABLATION_MFMA, tre, tim, n=n, normalize=normalize)
+    torch.cuda.synchronize()
+    assert_exact(tre.cpu().numpy(), re, n, normalize)
+    assert_exact(tim.cpu().numpy(), im, n, normalize)
+
+
+@pytest.mark.parametrize("kind", ["stagewise", "popc_gemm", "mfma"])
 def test_gaussian_ablations_n20(kind):
-    k = {"stagewise": qse.ABLATION_STAGEWISE, "popc_gemm": qse.ABLATION_POPC_GEMM}[kind]
+    k = ABLATION_KINDS[kind]
     say("ablation gauss %s n=20" % kind)
     w = workloads.custom(20, 2, "f32", "gauss", True, seed=77)
     re, im = workloads.gen(w)
