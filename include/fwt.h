@@ -111,7 +111,10 @@ typedef struct {
                     workgroup fills a CU's LDS */
     int wave;    /* 1: wave-tile kernel (a whole tile in one wave, lane bits
                     crossed with DPP / ds_swizzle / permlane swaps, no LDS;
-                    row bits - eb <= 6 - gbits); 0 or default: LDS tiles */
+                    row bits - eb <= 6 - gbits); 0: LDS tiles; default: the
+                    wave-tile kernel for a one-pass plan with 3 <= n <= 10
+                    when every other field of the entry is -1, else LDS
+                    tiles */
 } fwt_pass_tuning;
 
 /* As fwt_plan_create_split, with the on-chip tiling of each pass forced

@@ -55,3 +55,7 @@ WAVE_CASES = [
     ("f32", 20, (13, 7), None, None, (1, 1), 2), ("f32", 20, (13, 7), None, (-1, 4), (1, 1), 2),
     ("f64", 18, (11, 7), None, None, (1, 1), 2), ("f32", 12, (12,), (5,), None, (1,), 2),
     ("f32", 14, (10, 4), None, (-1, 3), (1, 1), 3)]
+
+# (dtype, n): one-pass plans with the LDS-tile kernel forced (wave 0) where
+# the default plan picks the wave-tile kernel (3 <= n <= 10), and either side
+LDS_SINGLE_CASES = [(dt, n) for dt in ("f32", "f64") for n in range(2, 12)]

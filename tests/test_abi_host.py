@@ -153,7 +153,9 @@ def test_tuned_validation(lib):
 def test_every_gpu_test_plan_is_valid(lib):
     """Each plan the GPU parity suite builds is accepted by the planner and
     has the forced properties (caught here, on the CPU)."""
-    from plan_cases import FORCED_SPLITS, PIPE_CASES, VARIANTS, WAVE_CASES
+    from plan_cases import FORCED_SPLITS, LDS_SINGLE_CASES, PIPE_CASES, VARIANTS, WAVE_CASES
+    for dtype, n in LDS_SINGLE_CASES:
+        assert qse.Plan(n, dtype, split=(n,), wave=(0,)).pass_config(0)["wave"] == 0
     for dtype, n, split in FORCED_SPLITS:
         assert qse.Plan(n, dtype, split=split).pass_bits == list(split)
     for dtype, n, split, eb, gbits, phases in VARIANTS:
@@ -166,6 +168,29 @@ def test_every_gpu_test_plan_is_valid(lib):
         for i, pv in enumerate(pipe):
             if pv >= 0:
                 assert p.pass_config(i)["pipe"] == pv
+
+
+def test_default_kernel_choice(lib):
+    """Row passes of 3..10 bits default to the wave-tile kernel; wider row
+    passes, column passes and entries with any field forced use the LDS
+    tiles.  Mid sizes split so that the row pass is a wave-tile one."""
+    for dtype in ("f32", "f64"):
+        for n in range(2, 15 if dtype == "f32" else 14):
+            want = 1 if 3 <= n <= 10 else 0
+            assert qse.Plan(n, dtype).pass_config(0)["wave"] == want, (dtype, n)
+            assert qse.Plan(n, dtype, split=(n,)).pass_config(0)["wave"] == want, (dtype, n)
+        assert qse.Plan(8, dtype, split=(8,), eb=(3,)).pass_config(0)["wave"] == 0
+        for split, want in (((5, 5), [1, 0]), ((2, 8), [0, 0]), ((11, 9), [0, 0]),
+                            ((3, 3, 4), [1, 0, 0])):
+            p = qse.Plan(sum(split), dtype, split=split)
+            assert [p.pass_config(i)["wave"] for i in range(p.num_passes)] == want, split
+    mid = {("f32", 16): [9, 7], ("f32", 17): [10, 7], ("f32", 18): [10, 8], ("f32", 19): [10, 9],
+           ("f32", 20): [13, 7], ("f64", 15): [9, 6], ("f64", 18): [9, 9], ("f64", 19): [11, 8],
+           ("f64", 24): [14, 10]}
+    for (dtype, n), bits in mid.items():
+        p = qse.Plan(n, dtype)
+        assert p.pass_bits == bits, (dtype, n)
+        assert [p.pass_config(i)["wave"] for i in range(2)] == [1 if bits[0] <= 10 else 0, 0]
 
 
 def test_destroy(lib):

@@ -20,7 +20,7 @@ import pytest
 import oracle
 import quantum_state_encoding_amd as qse
 import workloads
-from plan_cases import FORCED_SPLITS, PIPE_CASES, VARIANTS, WAVE_CASES
+from plan_cases import FORCED_SPLITS, LDS_SINGLE_CASES, PIPE_CASES, VARIANTS, WAVE_CASES
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -104,6 +104,23 @@ def test_integer_sweep_auto_plan(dtype, n):
         gre, gim = run(plan, re, im, True)
         assert_exact(gre, re, n, True)
         assert_exact(gim, im, n, True)
+
+
+@pytest.mark.parametrize("dtype,n", LDS_SINGLE_CASES)
+def test_integer_lds_tile_single_pass(dtype, n):
+    """The LDS-tile kernel on the small one-pass sizes whose default plan
+    takes the wave-tile kernel, exactly, unnormalised and normalised."""
+    say("lds tile %s n=%d" % (dtype, n))
+    npd = np.float32 if dtype == "f32" else np.float64
+    re = ints((5, 1 << n), 12_000 + n, npd)
+    im = ints((5, 1 << n), 22_000 + n, npd)
+    plan = qse.Plan(n, dtype, split=(n,), wave=(0,))
+    for normalize in (False, True):
+        if normalize and n % 2:
+            continue
+        gre, gim = run(plan, re, im, normalize)
+        assert_exact(gre, re, n, normalize)
+        assert_exact(gim, im, n, normalize)
 
 
 @pytest.mark.parametrize("dtype,n,split", FORCED_SPLITS)
