@@ -283,9 +283,9 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
 def bench_ablations(torch, w, steps=3):
     """Time the pages' designs on the workload's state: one launch per
     butterfly stage, the popcount-GEMM Kronecker scaffold with its batch
-    transposes, and the matrix-core block-Hadamard row kernel followed by
-    the column passes (fwt_ablation_execute).  ms per step, same
-    accounting."""
+    transposes, the matrix-core block-Hadamard row kernel followed by the
+    column passes, and (fp64) the INT8 / CRT emulation
+    (fwt_ablation_execute).  ms per step, same accounting."""
     import quantum_state_encoding_amd as qse
     dev = torch.device("cuda:0")
     tdt = torch.float32 if w.dtype == "f32" else torch.float64
@@ -298,6 +298,8 @@ def bench_ablations(torch, w, steps=3):
         kinds.append(("popc_gemm_transpose", qse.ABLATION_POPC_GEMM, 2))
     if w.n >= 8:
         kinds.append(("mfma_block_hadamard", qse.ABLATION_MFMA, 2))
+    if w.dtype == "f64" and 5 <= w.n <= 28:
+        kinds.append(("ozaki_int8_crt", qse.ABLATION_OZAKI, 3))
     for name, kind, launches in kinds:
         wsb = qse.ablation_workspace(kind, w.batch, w.n, w.dtype, True)
         ws = torch.empty(wsb // 4, device=dev) if wsb else None

@@ -228,7 +228,20 @@ typedef enum {
      * instructions (leftover bits butterflied in LDS), the higher bits on
      * the ordinary column passes.  8 <= n <= 30 (fp32) / 29 (fp64); no
      * workspace. */
-    FWT_ABLATION_MFMA = 3
+    FWT_ABLATION_MFMA = 3,
+    /* INT8 / CRT emulation of the fp64 transform (the iThome article,
+     * "INT8 / Ozaki path", "Data flow of the implementation", radix form
+     * of "case_3 experimental judgements"): each vector component scaled
+     * by its own power of two to integers of at most 48 bits, split into
+     * residues mod m <= 10 primes below 256 (balanced int8), transformed
+     * in residue space by Kronecker passes of 32-position blocks on
+     * v_mfma_i32_16x16x32_i8 with reduction mod p, rebuilt by CRT
+     * (Garner digits summed in 128-bit integers) and scaled back.  Exact
+     * for integer-valued inputs; otherwise within 2^-46 of max |x| times
+     * sqrt(2^n) per output.  fp64 only (fp32: FWT_EUNSUPPORTED); finite
+     * inputs; 5 <= n <= 28; needs a workspace (the residue planes, m bytes
+     * per element, plus per-vector scales). */
+    FWT_ABLATION_OZAKI = 4
 } fwt_ablation;
 
 /* Workspace bytes fwt_ablation_execute needs for `batch` vectors (0 if

@@ -18,7 +18,7 @@ import os
 
 __all__ = ["Plan", "FwtError", "execute", "stream_copy", "library_path", "load_library",
            "ablation_workspace", "ablation_execute", "ABLATION_STAGEWISE", "ABLATION_POPC_GEMM",
-           "ABLATION_MFMA", "PassTuning",
+           "ABLATION_MFMA", "ABLATION_OZAKI", "PassTuning",
            "PATH_AUTO", "PATH_SINGLE_BLOCK", "PATH_MULTIPASS", "PATH_MFMA_ABLATION",
            "FWT_OK", "FWT_EINVAL", "FWT_EALIGN", "FWT_EUNSUPPORTED", "FWT_EHIP",
            "FWT_ENOMEM", "EXPORTED_SYMBOLS"]
@@ -338,7 +338,7 @@ def execute(re, im=None, n=None, normalize=True, stream=None, path=PATH_AUTO):
     return Plan(n, dtype, path).execute(re, im, normalize, stream)
 
 
-ABLATION_STAGEWISE, ABLATION_POPC_GEMM, ABLATION_MFMA = 1, 2, 3
+ABLATION_STAGEWISE, ABLATION_POPC_GEMM, ABLATION_MFMA, ABLATION_OZAKI = 1, 2, 3, 4
 
 
 def ablation_workspace(kind, batch, n, dtype="f32", with_im=True):

@@ -735,6 +735,12 @@ namespace {
 
 size_t ablation_workspace_bytes(int kind, int64_t batch, int n, fwt_dtype dtype, int with_im)
 {
+    if (kind == FWT_ABLATION_OZAKI) {
+        if (n < qse::kOzMinN || n > qse::kOzMaxN)
+            return 0;
+        size_t a, b;
+        return qse::oz_workspace_layout(batch, n, with_im ? 2 : 1, &a, &b);
+    }
     if (kind != FWT_ABLATION_POPC_GEMM)
         return 0;
     const size_t esize = dtype == FWT_F64 ? 8 : 4;
@@ -756,6 +762,11 @@ int ablation_check(int kind, int64_t batch, int n, fwt_dtype dtype, const void* 
     } else if (kind == FWT_ABLATION_MFMA) {
         if (n < kMfmaRowMin || n > (dtype == FWT_F64 ? 29 : FWT_MAX_N))
             return n < 0 || n > FWT_MAX_N ? FWT_EINVAL : FWT_EUNSUPPORTED;
+    } else if (kind == FWT_ABLATION_OZAKI) {
+        if (n < 0 || n > FWT_MAX_N)
+            return FWT_EINVAL;
+        if (dtype != FWT_F64 || n < qse::kOzMinN || n > qse::kOzMaxN)
+            return FWT_EUNSUPPORTED;
     } else {
         return FWT_EINVAL;
     }
@@ -856,7 +867,7 @@ int fwt_ablation_workspace(int kind, int64_t batch, int n, fwt_dtype dtype, int 
 {
     if (!out || batch < 0 || n < 0 || n > FWT_MAX_N)
         return FWT_EINVAL;
-    if (kind < FWT_ABLATION_STAGEWISE || kind > FWT_ABLATION_MFMA)
+    if (kind < FWT_ABLATION_STAGEWISE || kind > FWT_ABLATION_OZAKI)
         return FWT_EINVAL;
     *out = ablation_workspace_bytes(kind, batch, n, dtype, with_im);
     return FWT_OK;
@@ -878,6 +889,11 @@ int fwt_ablation_execute(int kind, int64_t batch, int n, fwt_dtype dtype, void* 
     hipError_t e;
     if (kind == FWT_ABLATION_MFMA)
         return ablation_mfma(batch, n, dtype, re, im, normalize, c, stream);
+    if (kind == FWT_ABLATION_OZAKI) {
+        e = qse::ablation_ozaki((double*)re, (double*)im, batch, n, normalize ? c : 1.0,
+                                workspace, stream);
+        return e == hipSuccess ? FWT_OK : hip_fail(e);
+    }
     if (kind == FWT_ABLATION_STAGEWISE) {
         e = qse::ablation_stagewise(f64, re, im, batch, n, normalize, c, stream);
     } else {

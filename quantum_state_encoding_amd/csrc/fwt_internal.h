@@ -91,6 +91,36 @@ hipError_t ablation_stagewise(int f64, void* re, void* im, int64_t batch, int n,
                               double c, hipStream_t stream);
 hipError_t ablation_popc_gemm(int f64, void* re, void* im, void* ws_re, void* ws_im,
                               int64_t batch, int n, int normalize, double c, hipStream_t stream);
+// ---- INT8 / CRT (Ozaki) ablation, fp64 (fwt_ozaki.hip) ----
+constexpr int kOzMaxModuli = 16;
+constexpr int kOzScaleBits = 48;     // |X| <= 2^48 after scaling
+constexpr int kOzRowTileBits = 14;   // residues per row-pass tile
+constexpr int kOzMinN = 5;
+constexpr int kOzMaxN = 28;
+// The 16 largest primes below 256: balanced residues fit int8.
+constexpr int kOzPrimes[kOzMaxModuli] = {251, 241, 239, 233, 229, 227, 223, 211,
+                                         199, 197, 193, 191, 181, 179, 173, 167};
+struct OzConst {
+    int m;                          // moduli in use
+    int p[kOzMaxModuli];
+    float inv_pf[kOzMaxModuli];
+    double inv_pd[kOzMaxModuli];
+    unsigned char ginv[kOzMaxModuli][kOzMaxModuli];   // p_i^-1 mod p_j, i < j
+};
+// A Kronecker pass over the residue planes: row (bits [0, kt), xb line
+// bits per tile) or column (bits [lo, lo + kt), 2^xb-byte row segments).
+struct OzPass {
+    int row, lo, kt, xb;
+};
+int oz_num_moduli(int n);
+void oz_pass_plan(int n, OzPass* passes, int* npasses);
+// Workspace bytes for `comps` components; offsets of the partial maxima
+// and the exponents inside it (the residue planes start at 0).
+size_t oz_workspace_layout(int64_t batch, int n, int comps, size_t* off_partial,
+                           size_t* off_exps);
+hipError_t ablation_ozaki(double* re, double* im, int64_t batch, int n, double c, void* ws,
+                          hipStream_t stream);
+
 // Matrix-core row pass over the km contiguous low bits (8 <= km <= 13).
 hipError_t ablation_mfma_row(int f64, void* re, void* im, int64_t batch, int n, int km,
                              int do_scale, double c, hipStream_t stream);

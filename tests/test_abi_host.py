@@ -266,6 +266,19 @@ def test_ablation_workspace_and_validation(lib):
     assert ex(qse.ABLATION_MFMA, 1, 10, 0, FAKE + 4, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EALIGN
     assert ex(qse.ABLATION_MFMA, 0, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_OK
     assert qse.ablation_workspace(qse.ABLATION_MFMA, 64, 14, "f32", True) == 0
+    # INT8 / CRT: fp64, 5 <= n <= 28, residue planes (m bytes per element,
+    # m = 8 moduli at n = 10) plus per-vector scales
+    oz = qse.ABLATION_OZAKI
+    assert qse.ablation_workspace(oz, 4, 10, "f64", True) >= 2 * 8 * 4 * N
+    assert qse.ablation_workspace(oz, 4, 10, "f64", False) < qse.ablation_workspace(oz, 4, 10, "f64", True)
+    assert qse.ablation_workspace(oz, 4, 4, "f64", True) == 0
+    wsb = qse.ablation_workspace(oz, 1, 10, "f64", True)
+    assert ex(oz, 1, 10, 0, FAKE, FAKE + 4 * N, 1, FAKE + 16 * N, wsb, None) == qse.FWT_EUNSUPPORTED
+    assert ex(oz, 1, 4, 1, FAKE, FAKE + 8 * N, 1, FAKE + 16 * N, wsb, None) == qse.FWT_EUNSUPPORTED
+    assert ex(oz, 1, 29, 1, FAKE, FAKE + (8 << 29), 1, None, 0, None) == qse.FWT_EUNSUPPORTED
+    assert ex(oz, 1, 10, 1, FAKE, FAKE + 8 * N, 1, None, 0, None) == qse.FWT_EINVAL
+    assert ex(oz, 1, 10, 1, FAKE, FAKE + 8 * N, 1, FAKE + 16 * N, wsb - 1, None) == qse.FWT_EINVAL
+    assert ex(oz, 1, 10, 1, FAKE, FAKE + 8 * N, 1, FAKE + 8, wsb, None) == qse.FWT_EALIGN
     assert ex(qse.ABLATION_STAGEWISE, 1, 1, 0, FAKE, FAKE + 64, 1, None, 0, None) == qse.FWT_EUNSUPPORTED
     assert ex(qse.ABLATION_POPC_GEMM, 1, 27, 0, FAKE, FAKE + (4 << 27), 1, None, 0, None) == qse.FWT_EUNSUPPORTED
     assert ex(qse.ABLATION_STAGEWISE, 1, 10, 0, FAKE + 4, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EALIGN

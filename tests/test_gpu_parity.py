@@ -447,6 +447,56 @@ def test_integer_mfma_ablation(dtype, n, batch):
     assert_exact(tim.cpu().numpy(), im, n, normalize)
 
 
+# INT8 / CRT ablation (fp64): every pass shape it plans (row pass only,
+# one and two column passes of 1..9 bits), ragged batches, real-only.
+@pytest.mark.parametrize("n,batch", [(5, 3), (7, 5), (9, 2), (10, 1), (11, 3), (12, 2), (13, 1),
+                                     (16, 3), (19, 1), (20, 2), (21, 1), (24, 1)])
+def test_integer_ozaki_ablation(n, batch):
+    say("ablation ozaki n=%d batch=%d" % (n, batch))
+    re = ints((batch, 1 << n), 91_000 + n, np.float64)
+    im = ints((batch, 1 << n), 91_500 + n, np.float64)
+    for normalize in ((False, True) if n % 2 == 0 else (False,)):
+        tre, tim = to_dev(re), to_dev(im)
+        wsb = qse.ablation_workspace(qse.ABLATION_OZAKI, batch, n, "f64", True)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        qse.ablation_execute(qse.ABLATION_OZAKI, tre, tim, n=n, normalize=normalize, workspace=ws)
+        torch.cuda.synchronize()
+        assert_exact(tre.cpu().numpy(), re, n, normalize)
+        assert_exact(tim.cpu().numpy(), im, n, normalize)
+    # real-only
+    tre = to_dev(re)
+    wsb = qse.ablation_workspace(qse.ABLATION_OZAKI, batch, n, "f64", False)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    qse.ablation_execute(qse.ABLATION_OZAKI, tre, None, n=n, normalize=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert_exact(tre.cpu().numpy(), re, n, False)
+
+
+@pytest.mark.parametrize("n,batch", [(13, 3), (20, 2), (24, 1)])
+def test_gaussian_ozaki_ablation(n, batch):
+    """Gaussian states, with per-vector scales far apart (1e-100, 1, 1e100
+    and an all-zero vector): each vector's own power-of-two scale keeps the
+    fp64 tolerance.  (Scales stay where the squared norm of the bound does
+    not underflow.)"""
+    say("ablation ozaki gauss n=%d batch=%d" % (n, batch))
+    w = workloads.custom(n, batch, "f64", "gauss", True, seed=300 + n)
+    re, im = workloads.gen(w)
+    re, im = re.reshape(batch, -1).copy(), im.reshape(batch, -1).copy()
+    scales = [1e-100, 1.0, 1e100][:batch]
+    for b, sc in enumerate(scales):
+        re[b] *= sc
+        im[b] *= sc
+    if batch >= 3:
+        re[1] = 0.0
+        im[1] = 0.0
+    tre, tim = to_dev(re), to_dev(im)
+    wsb = qse.ablation_workspace(qse.ABLATION_OZAKI, batch, n, "f64", True)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    qse.ablation_execute(qse.ABLATION_OZAKI, tre, tim, n=n, normalize=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close("f64", n, re, im, tre.cpu().numpy(), tim.cpu().numpy())
+
+
 @pytest.mark.parametrize("kind", ["stagewise", "popc_gemm", "mfma"])
 def test_gaussian_ablations_n20(kind):
     k = ABLATION_KINDS[kind]
