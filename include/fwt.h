@@ -239,8 +239,8 @@ typedef enum {
      * (Garner digits summed in 128-bit integers) and scaled back.  Exact
      * for integer-valued inputs; otherwise within 2^-46 of max |x| times
      * sqrt(2^n) per output.  fp64 only (fp32: FWT_EUNSUPPORTED); finite
-     * inputs; 5 <= n <= 28; needs a workspace (the residue planes, m bytes
-     * per element, plus per-vector scales). */
+     * inputs; 5 <= n <= 28; needs a workspace (the residues, 4 ceil(m / 4)
+     * bytes per element, plus per-vector scales). */
     FWT_ABLATION_OZAKI = 4
 } fwt_ablation;
 

@@ -94,7 +94,8 @@ hipError_t ablation_popc_gemm(int f64, void* re, void* im, void* ws_re, void* ws
 // ---- INT8 / CRT (Ozaki) ablation, fp64 (fwt_ozaki.hip) ----
 constexpr int kOzMaxModuli = 16;
 constexpr int kOzScaleBits = 48;     // |X| <= 2^48 after scaling
-constexpr int kOzRowTileBits = 14;   // residues per row-pass tile
+constexpr int kOzRowTileBits = 12;   // residue words per row-pass tile
+constexpr int kOzPack = 4;           // moduli per 32-bit residue word
 constexpr int kOzMinN = 5;
 constexpr int kOzMaxN = 28;
 // The 16 largest primes below 256: balanced residues fit int8.
@@ -105,17 +106,20 @@ struct OzConst {
     int p[kOzMaxModuli];
     float inv_pf[kOzMaxModuli];
     double inv_pd[kOzMaxModuli];
-    unsigned char ginv[kOzMaxModuli][kOzMaxModuli];   // p_i^-1 mod p_j, i < j
+    int crt_c[kOzMaxModuli];        // (M / p_j)^-1 mod p_j
+    uint64_t crt_lo[kOzMaxModuli];  // M / p_j, low and high 64 bits
+    uint64_t crt_hi[kOzMaxModuli];
+    uint64_t m_lo, m_hi;            // M = prod of the m moduli
 };
-// A Kronecker pass over the residue planes: row (bits [0, kt), xb line
-// bits per tile) or column (bits [lo, lo + kt), 2^xb-byte row segments).
+// A Kronecker pass over the residue words: row (bits [0, kt), xb line
+// bits per tile) or column (bits [lo, lo + kt), 2^xb-word row segments).
 struct OzPass {
     int row, lo, kt, xb;
 };
 int oz_num_moduli(int n);
 void oz_pass_plan(int n, OzPass* passes, int* npasses);
 // Workspace bytes for `comps` components; offsets of the partial maxima
-// and the exponents inside it (the residue planes start at 0).
+// and the exponents inside it (the residue words start at 0).
 size_t oz_workspace_layout(int64_t batch, int n, int comps, size_t* off_partial,
                            size_t* off_exps);
 hipError_t ablation_ozaki(double* re, double* im, int64_t batch, int n, double c, void* ws,

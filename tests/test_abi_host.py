@@ -266,8 +266,8 @@ def test_ablation_workspace_and_validation(lib):
     assert ex(qse.ABLATION_MFMA, 1, 10, 0, FAKE + 4, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EALIGN
     assert ex(qse.ABLATION_MFMA, 0, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_OK
     assert qse.ablation_workspace(qse.ABLATION_MFMA, 64, 14, "f32", True) == 0
-    # INT8 / CRT: fp64, 5 <= n <= 28, residue planes (m bytes per element,
-    # m = 8 moduli at n = 10) plus per-vector scales
+    # INT8 / CRT: fp64, 5 <= n <= 28, residues (m = 8 moduli at n = 10, two
+    # 4-byte words per element) plus per-vector scales
     oz = qse.ABLATION_OZAKI
     assert qse.ablation_workspace(oz, 4, 10, "f64", True) >= 2 * 8 * 4 * N
     assert qse.ablation_workspace(oz, 4, 10, "f64", False) < qse.ablation_workspace(oz, 4, 10, "f64", True)
