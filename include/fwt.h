@@ -54,7 +54,11 @@ typedef enum { FWT_F32 = 0, FWT_F64 = 1 } fwt_dtype;
  *                single-pass limit.
  *  MULTIPASS     Kronecker split into >= 2 passes whenever n allows it
  *                (n >= 2 for fp32, n >= 2 for fp64; below that one pass).
- *  MFMA_ABLATION reserved for a matrix-core variant; FWT_EUNSUPPORTED. */
+ *  MFMA_ABLATION the pages' matrix-core form, for measurement: the low
+ *                min(n, 12) bits as dense H_16 block products on the 16x16x4
+ *                fp32 / fp64 matrix instructions (see FWT_ABLATION_MFMA),
+ *                the rest in column passes of at most 12 bits;
+ *                FWT_EUNSUPPORTED for n < 8 (and fp64 n > 29). */
 typedef enum {
     FWT_PATH_AUTO = 0,
     FWT_PATH_SINGLE_BLOCK = 1,

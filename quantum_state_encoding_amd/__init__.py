@@ -189,7 +189,7 @@ class Plan:
         keys = ("lo", "bits", "kind", "kr", "eb", "gbits", "phase_bits", "block", "lds",
                 "tpw_bits", "pipe", "wave")
         d = dict(zip(keys, list(out)))
-        d["kind"] = ("row", "column", "pair")[d["kind"]]
+        d["kind"] = ("row", "column", "pair", "mfma")[d["kind"]]
         return d
 
     def kernel_name(self, i):
@@ -198,6 +198,8 @@ class Plan:
         if c["kind"] == "pair":
             return "pair_f32_kernel"
         t = "float" if self.dtype == "f32" else "double"
+        if c["kind"] == "mfma":
+            return "mfma_row_kernel<%s, %d>" % (t, c["bits"])
         if c["wave"]:
             return "wave_kernel<%s, %d, %d, %d, %s>" % (
                 t, c["kr"], c["eb"], c["gbits"], "true" if c["kind"] == "row" else "false")

@@ -58,6 +58,7 @@ struct Pass {
     unsigned block = 0;
     size_t lds = 0;
     int tiles_bits = 0;  // log2 tiles per vector (per component)
+    int mfma = 0;        // matrix-core block-Hadamard row pass (lo = 0)
 };
 
 }  // namespace
@@ -406,7 +407,7 @@ int default_split(int n, fwt_dtype dtype, fwt_path path, int* bits)
 }
 
 int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* bits,
-              const fwt_pass_tuning* tuning)
+              const fwt_pass_tuning* tuning, bool mfma_row = false)
 {
     if (!out)
         return FWT_EINVAL;
@@ -432,6 +433,17 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
     p->npasses = n == 0 ? 0 : npasses;
     int lo = 0;
     for (int i = 0; i < p->npasses; ++i) {
+        if (i == 0 && mfma_row) {
+            if (bits[0] < kMfmaRowMin || bits[0] > kMfmaRowMax) {
+                delete p;
+                return FWT_EUNSUPPORTED;
+            }
+            p->passes[0] = Pass{};
+            p->passes[0].k = bits[0];
+            p->passes[0].mfma = 1;
+            lo += bits[0];
+            continue;
+        }
         const fwt_pass_tuning dflt{-1, -1, -1, -1, -1};
         const int rc = build_pass(p->passes[i], n, dtype, lo, bits[i], tuning ? tuning[i] : dflt,
                                   p->npasses > 1);
@@ -449,7 +461,8 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
             std::fprintf(stderr,
                          "[fwt]   pass %d: bits [%d,%d) %s kr=%d eb=%d G=%d phases=%d pipe=%d "
                          "wave=%d threads/tile=%d block=%u lds=%zu store_back=%d tiles/vec=2^%d\n",
-                         i, q.lo, q.lo + q.k, q.pair ? "pair" : (q.key.row ? "row" : "col"),
+                         i, q.lo, q.lo + q.k,
+                         q.mfma ? "mfma" : (q.pair ? "pair" : (q.key.row ? "row" : "col")),
                          q.key.kr, q.key.eb, 1 << q.gbits, 1 << q.phb, q.key.pipe, q.key.wave,
                          1 << q.tt_bits, q.block, q.lds, q.store_back, q.tiles_bits);
         }
@@ -590,7 +603,16 @@ int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, vo
         const bool final_pass = (i == plan->npasses - 1);
         const int do_scale = (normalize && final_pass) ? 1 : 0;
         hipError_t e;
-        if (p.pair) {
+        if (p.mfma) {
+            e = hipSuccess;
+            if (i == first && start)
+                e = hipEventRecord(start, stream);
+            if (e == hipSuccess)
+                e = qse::ablation_mfma_row(plan->dtype == FWT_F64 ? 1 : 0, re, im, batch, n, p.k,
+                                           do_scale, c, stream);
+            if (e == hipSuccess && i == last - 1 && stop)
+                e = hipEventRecord(stop, stream);
+        } else if (p.pair) {
             e = qse::launch_pair_f32((float*)re, (float*)im, batch, do_scale, (float)c, stream,
                                      i == first ? start : nullptr,
                                      i == last - 1 ? stop : nullptr);
@@ -631,8 +653,22 @@ int fwt_plan_create(fwt_plan_t* out, int n, fwt_dtype dtype, fwt_path path)
     *out = nullptr;
     if (n < 0 || n > FWT_MAX_N || (dtype != FWT_F32 && dtype != FWT_F64))
         return FWT_EINVAL;
-    if (path == FWT_PATH_MFMA_ABLATION)
-        return FWT_EUNSUPPORTED;
+    if (path == FWT_PATH_MFMA_ABLATION) {
+        // the low min(n, 12) bits on the matrix-core row kernel, the rest
+        // in column passes of at most 12 bits
+        if (n < kMfmaRowMin || (dtype == FWT_F64 && n > 29))
+            return FWT_EUNSUPPORTED;
+        int bits[kMaxPasses] = {n < kMfmaRowMax ? n : kMfmaRowMax, 0, 0, 0};
+        const int rest = n - bits[0];
+        int np = 1;
+        if (rest > kColKrMax) {
+            bits[np++] = rest - rest / 2;
+            bits[np++] = rest / 2;
+        } else if (rest > 0) {
+            bits[np++] = rest;
+        }
+        return make_plan(out, n, dtype, np, bits, nullptr, true);
+    }
     if (path != FWT_PATH_AUTO && path != FWT_PATH_SINGLE_BLOCK && path != FWT_PATH_MULTIPASS)
         return FWT_EINVAL;
     int bits[kMaxPasses] = {0, 0, 0, 0};
@@ -803,61 +839,26 @@ int ablation_check(int kind, int64_t batch, int n, fwt_dtype dtype, const void* 
     return rc;
 }
 
-// Matrix-core ablation: the low min(n, 12) bits on the block-Hadamard row
-// kernel, the remaining bits on the ordinary column tile passes of a plan
-// whose pass 0 covers those same low bits (never launched).  Plans are made
-// once per (dtype, n) and kept for the life of the process.
+// Matrix-core ablation: an FWT_PATH_MFMA_ABLATION plan, made once per
+// (dtype, n) and kept for the life of the process.
 fwt_plan_t g_mfma_plans[2][FWT_MAX_N + 1];
 std::mutex g_mfma_mutex;
 
-int mfma_rest_plan(int n, fwt_dtype dtype, int km, fwt_plan_t* out)
-{
-    std::lock_guard<std::mutex> lock(g_mfma_mutex);
-    fwt_plan_t& slot = g_mfma_plans[dtype == FWT_F64 ? 1 : 0][n];
-    if (!slot) {
-        int bits[kMaxPasses] = {km, 0, 0, 0};
-        const int rest = n - km;
-        int np = 1;
-        if (rest > kColKrMax) {
-            bits[np++] = rest - rest / 2;
-            bits[np++] = rest / 2;
-        } else if (rest > 0) {
-            bits[np++] = rest;
-        }
-        const int rc = make_plan(&slot, n, dtype, np, bits, nullptr);
-        if (rc != FWT_OK)
-            return rc;
-    }
-    *out = slot;
-    return FWT_OK;
-}
-
 int ablation_mfma(int64_t batch, int n, fwt_dtype dtype, void* re, void* im, int normalize,
-                  double c, hipStream_t stream)
+                  hipStream_t stream)
 {
-    const int km = n < kMfmaRowMax ? n : kMfmaRowMax;
     fwt_plan_t plan = nullptr;
-    int rc = mfma_rest_plan(n, dtype, km, &plan);
-    if (rc != FWT_OK)
-        return rc;
-    const int f64 = dtype == FWT_F64 ? 1 : 0;
-    int64_t cv = chunk_vectors(plan, batch, im ? 2 : 1);
-    if (cv == 0)
-        cv = batch;
-    const size_t vec_bytes = ((size_t)1 << n) * (f64 ? 8 : 4);
-    for (int64_t b0 = 0; b0 < batch; b0 += cv) {
-        const int64_t nb = batch - b0 < cv ? batch - b0 : cv;
-        void* cre = (char*)re + (size_t)b0 * vec_bytes;
-        void* cim = im ? (char*)im + (size_t)b0 * vec_bytes : nullptr;
-        const hipError_t e = qse::ablation_mfma_row(f64, cre, cim, nb, n, km,
-                                                    normalize && plan->npasses == 1, c, stream);
-        if (e != hipSuccess)
-            return hip_fail(e);
-        rc = launch_passes(plan, 1, plan->npasses, nb, n, cre, cim, normalize, stream);
-        if (rc != FWT_OK)
-            return rc;
+    {
+        std::lock_guard<std::mutex> lock(g_mfma_mutex);
+        fwt_plan_t& slot = g_mfma_plans[dtype == FWT_F64 ? 1 : 0][n];
+        if (!slot) {
+            const int rc = fwt_plan_create(&slot, n, dtype, FWT_PATH_MFMA_ABLATION);
+            if (rc != FWT_OK)
+                return rc;
+        }
+        plan = slot;
     }
-    return FWT_OK;
+    return fwt_execute(plan, batch, n, re, im, normalize, stream);
 }
 
 }  // namespace
@@ -888,7 +889,7 @@ int fwt_ablation_execute(int kind, int64_t batch, int n, fwt_dtype dtype, void* 
     const int f64 = dtype == FWT_F64 ? 1 : 0;
     hipError_t e;
     if (kind == FWT_ABLATION_MFMA)
-        return ablation_mfma(batch, n, dtype, re, im, normalize, c, stream);
+        return ablation_mfma(batch, n, dtype, re, im, normalize, stream);
     if (kind == FWT_ABLATION_OZAKI) {
         e = qse::ablation_ozaki((double*)re, (double*)im, batch, n, normalize ? c : 1.0,
                                 workspace, stream);
@@ -912,7 +913,7 @@ int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out)
     const Pass& p = plan->passes[i];
     out[0] = p.lo;
     out[1] = p.k;
-    out[2] = p.pair ? 2 : (p.key.row ? 0 : 1);
+    out[2] = p.mfma ? 3 : (p.pair ? 2 : (p.key.row ? 0 : 1));
     out[3] = p.key.kr;
     out[4] = p.key.eb;
     out[5] = p.gbits;

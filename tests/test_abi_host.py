@@ -97,7 +97,8 @@ def test_plan_create_errors(lib):
     assert _create(lib, 31)[0] == qse.FWT_EINVAL
     assert _create(lib, 10, dtype=2)[0] == qse.FWT_EINVAL
     assert _create(lib, 10, path=9)[0] == qse.FWT_EINVAL
-    assert _create(lib, 10, path=qse.PATH_MFMA_ABLATION)[0] == qse.FWT_EUNSUPPORTED
+    assert _create(lib, 7, path=qse.PATH_MFMA_ABLATION)[0] == qse.FWT_EUNSUPPORTED
+    assert _create(lib, 30, 1, qse.PATH_MFMA_ABLATION)[0] == qse.FWT_EUNSUPPORTED
     assert _create(lib, 16, 0, qse.PATH_SINGLE_BLOCK)[0] == qse.FWT_EUNSUPPORTED
     assert _create(lib, 15, 1, qse.PATH_SINGLE_BLOCK)[0] == qse.FWT_EUNSUPPORTED
     assert _create(lib, 30, 1)[0] == qse.FWT_EUNSUPPORTED
@@ -191,6 +192,19 @@ def test_default_kernel_choice(lib):
         p = qse.Plan(n, dtype)
         assert p.pass_bits == bits, (dtype, n)
         assert [p.pass_config(i)["wave"] for i in range(2)] == [1 if bits[0] <= 10 else 0, 0]
+
+
+def test_mfma_path_plans(lib):
+    """FWT_PATH_MFMA_ABLATION: the low min(n, 12) bits on the matrix-core row
+    kernel, the rest in column passes of at most 12 bits."""
+    for dtype, n, bits in (("f32", 8, [8]), ("f32", 12, [12]), ("f32", 20, [12, 8]),
+                           ("f64", 24, [12, 12]), ("f32", 26, [12, 7, 7]), ("f64", 29, [12, 9, 8])):
+        p = qse.Plan(n, dtype, path=qse.PATH_MFMA_ABLATION)
+        assert p.pass_bits == bits, (dtype, n)
+        assert p.pass_config(0)["kind"] == "mfma"
+        assert p.kernel_name(0) == "mfma_row_kernel<%s, %d>" % (
+            "float" if dtype == "f32" else "double", bits[0])
+        assert all(p.pass_config(i)["kind"] == "column" for i in range(1, p.num_passes))
 
 
 def test_destroy(lib):

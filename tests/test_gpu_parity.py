@@ -497,6 +497,33 @@ def test_gaussian_ozaki_ablation(n, batch):
     assert_close("f64", n, re, im, tre.cpu().numpy(), tim.cpu().numpy())
 
 
+@pytest.mark.parametrize("dtype,n,batch", [("f32", 9, 5), ("f32", 20, 3), ("f64", 13, 3),
+                                           ("f64", 24, 1)])
+def test_mfma_path_plan(dtype, n, batch):
+    """A FWT_PATH_MFMA_ABLATION plan through fwt_execute, and pass by pass
+    through the dispatch-timed entry, exactly."""
+    say("mfma path %s n=%d batch=%d" % (dtype, n, batch))
+    npd = np.float32 if dtype == "f32" else np.float64
+    re = ints((batch, 1 << n), 93_000 + n, npd)
+    im = ints((batch, 1 << n), 93_500 + n, npd)
+    plan = qse.Plan(n, dtype, path=qse.PATH_MFMA_ABLATION)
+    assert plan.pass_config(0)["kind"] == "mfma"
+    normalize = n % 2 == 0
+    gre, gim = run(plan, re, im, normalize)
+    assert_exact(gre, re, n, normalize)
+    assert_exact(gim, im, n, normalize)
+    tre, tim = to_dev(re), to_dev(im)
+    evs = []
+    for i in range(plan.num_passes):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        plan.execute_pass_timed(i, tre, tim, a, b, normalize=normalize)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    assert all(a.elapsed_time(b) > 0 for a, b in evs)
+    assert np.array_equal(tre.cpu().numpy(), gre) and np.array_equal(tim.cpu().numpy(), gim)
+
+
 @pytest.mark.parametrize("kind", ["stagewise", "popc_gemm", "mfma"])
 def test_gaussian_ablations_n20(kind):
     k = ABLATION_KINDS[kind]
