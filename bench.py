@@ -280,6 +280,39 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
     print("\n".join(lines + [""] + tl + [""] + lds_lines))
 
 
+def summarize_ablations(workload, kt_dir, command):
+    """Per-kernel durations of everything in the trace that is neither a pass
+    of the workload's plan nor the streaming copy (the ablations, and the
+    small workloads timed alongside the default one) into
+    profiles/<workload>_ablations_kernel_trace.txt."""
+    import quantum_state_encoding_amd as qse
+    w = workloads.WORKLOADS[workload]
+    plan = qse.Plan(w.n, w.dtype, split=w.split or None)
+    main = [plan.kernel_name(i) for i in range(plan.num_passes)] + ["stream_copy_kernel"]
+    groups = {}
+    for r in _read_csv(_find(kt_dir, "kernel_trace.csv")):
+        name = r["Kernel_Name"]
+        if any(m in name for m in main) or "at::native" in name:
+            continue
+        key = (name.replace("qse::(anonymous namespace)::", "").split("(")[0],
+               int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = ["# rocprofv3 kernel trace: %s, every kernel other than the workload's own passes "
+             "and the streaming copy: the ablations (3 timed calls after one warm-up call "
+             "each) and, for the default workload, the small workloads bench.py also times"
+             % workload,
+             "# command: " + command,
+             "# kernel | grid (threads x, y) | dispatches | avg us | min us | max us | total ms"]
+    for (name, gx, gy), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append("%s | %d x %d | %d | %.2f | %.2f | %.2f | %.3f" % (
+            name, gx, gy, len(d), np.mean(d) / 1e3, np.min(d) / 1e3, np.max(d) / 1e3,
+            np.sum(d) / 1e6))
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "%s_ablations_kernel_trace.txt" % workload), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def bench_ablations(torch, w, steps=3):
     """Time the pages' designs on the workload's state: one launch per
     butterfly stage, the popcount-GEMM Kronecker scaffold with its batch
@@ -330,6 +363,9 @@ def main():
     ap.add_argument("--summarize-profile", nargs="+",
                     metavar="DIR", help="KT_DIR FETCH_DIR WRITE_DIR [LDS_DIR]: write profiles/ "
                     "summaries from rocprofv3 CSV output of this benchmark")
+    ap.add_argument("--summarize-ablations", metavar="KT_DIR",
+                    help="write profiles/<workload>_ablations_kernel_trace.txt from a rocprofv3 "
+                    "kernel trace of this benchmark")
     ap.add_argument("--profile-command", default="",
                     help="the rocprofv3 command line recorded in the summaries")
     args = ap.parse_args()
@@ -339,6 +375,9 @@ def main():
             ap.error("--summarize-profile takes 3 or 4 directories")
         summarize_profile(args.workload, d[0], d[1], d[2], args.profile_command,
                           d[3] if len(d) == 4 else None)
+        return
+    if args.summarize_ablations:
+        summarize_ablations(args.workload, args.summarize_ablations, args.profile_command)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

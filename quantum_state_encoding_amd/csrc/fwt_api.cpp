@@ -31,7 +31,7 @@ namespace {
 
 constexpr uint64_t kPlanMagic = 0x46575450'4c414e31ull;  // "FWTPLAN1"
 constexpr int kMaxPasses = 4;
-// Row passes of this many bits use the wave-tile kernel by default.
+// One-pass plans of this range of n use the wave-tile kernel by default.
 constexpr int kWaveDefaultMin = 3;
 constexpr int kWaveDefaultMax = 10;
 // Row bits of the matrix-core ablation's block-Hadamard kernel.
@@ -174,14 +174,16 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
         return FWT_EINVAL;
     if (t.wave == 1)
         return build_wave_pass(p, n, dtype, lo, k, kr, row, t);
-    // Row passes of 3..10 bits default to the wave-tile kernel.  Measured on
-    // 512 MiB states: one-pass plans of 3 <= n <= 10 ran at 6.0 TB/s
-    // against 5.0-5.4 for the LDS tiles (both dtypes), and the row pass of
-    // a two-pass plan took about 5 % less; from 11 bits its register tiles
-    // cost more than the LDS exchanges save.
+    // One-pass plans of 3 <= n <= 10 default to the wave-tile kernel: on
+    // 512 MiB states it ran at 6.0 TB/s against 5.0-5.4 for the LDS tiles
+    // (both dtypes), and on cache-resident batches 2-12 % faster.  From 11
+    // bits its register tiles cost more than the LDS exchanges save.  (As
+    // the row pass of a two-pass plan it gained 3-5 % on HBM-bound states
+    // but lost up to 20 % on cache-resident ones, so it is not the default
+    // there.)
     const bool all_default =
         t.eb < 0 && t.gbits < 0 && t.phases < 0 && t.pipe < 0 && t.wave < 0;
-    if (all_default && row && k >= kWaveDefaultMin && k <= kWaveDefaultMax) {
+    if (all_default && row && !multipass && k >= kWaveDefaultMin && k <= kWaveDefaultMax) {
         const int rc = build_wave_pass(p, n, dtype, lo, k, kr, row, t);
         if (rc == FWT_OK)
             return rc;
@@ -354,8 +356,6 @@ int build_wave_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool
 // Default Kronecker split (bit counts, lowest bits first), from sweeps on
 // MI355X:
 //  - one pass while a vector fits one tile: n <= 15 (fp32), 14 (fp64);
-//  - two passes for n <= 19 (fp32) / 18 (fp64): a wave-tile row pass of
-//    min(n - 7, 10) (fp32) / 9 (fp64) bits, the rest in the column pass;
 //  - two passes up to n = 24: a column factor of 7 (fp32) / 8 (fp64) bits
 //    (col tiles of 128 rows x 256 B / 256 rows x 128 B), the rest in the
 //    contiguous row pass, which takes at most 13 (fp32) / 14 (fp64) bits;
@@ -378,18 +378,6 @@ int default_split(int n, fwt_dtype dtype, fwt_path path, int* bits)
     if (path == FWT_PATH_MULTIPASS && n <= single_max) {
         bits[1] = n / 2 < n - vb ? n / 2 : n - vb;   // column factor
         bits[0] = n - bits[1];
-        return 2;
-    }
-    // Mid sizes: a row pass of at most 10 (fp32) / exactly 9 (fp64) bits,
-    // which runs on the wave-tile kernel.
-    if (dtype == FWT_F32 && n <= 19) {
-        bits[0] = n - 7 < 10 ? n - 7 : 10;
-        bits[1] = n - bits[0];
-        return 2;
-    }
-    if (dtype == FWT_F64 && n <= 18) {
-        bits[0] = 9;
-        bits[1] = n - 9;
         return 2;
     }
     if (n <= 24) {

@@ -172,26 +172,23 @@ def test_every_gpu_test_plan_is_valid(lib):
 
 
 def test_default_kernel_choice(lib):
-    """Row passes of 3..10 bits default to the wave-tile kernel; wider row
-    passes, column passes and entries with any field forced use the LDS
-    tiles.  Mid sizes split so that the row pass is a wave-tile one."""
+    """One-pass plans of 3 <= n <= 10 default to the wave-tile kernel; wider
+    one-pass plans, every pass of a multi-pass plan and entries with any
+    field forced use the LDS tiles."""
     for dtype in ("f32", "f64"):
         for n in range(2, 15 if dtype == "f32" else 14):
             want = 1 if 3 <= n <= 10 else 0
             assert qse.Plan(n, dtype).pass_config(0)["wave"] == want, (dtype, n)
             assert qse.Plan(n, dtype, split=(n,)).pass_config(0)["wave"] == want, (dtype, n)
         assert qse.Plan(8, dtype, split=(8,), eb=(3,)).pass_config(0)["wave"] == 0
-        for split, want in (((5, 5), [1, 0]), ((2, 8), [0, 0]), ((11, 9), [0, 0]),
-                            ((3, 3, 4), [1, 0, 0])):
+        for split in ((5, 5), (7, 7), (2, 8), (11, 9), (3, 3, 4)):
             p = qse.Plan(sum(split), dtype, split=split)
-            assert [p.pass_config(i)["wave"] for i in range(p.num_passes)] == want, split
-    mid = {("f32", 16): [9, 7], ("f32", 17): [10, 7], ("f32", 18): [10, 8], ("f32", 19): [10, 9],
-           ("f32", 20): [13, 7], ("f64", 15): [9, 6], ("f64", 18): [9, 9], ("f64", 19): [11, 8],
-           ("f64", 24): [14, 10]}
-    for (dtype, n), bits in mid.items():
+            assert all(p.pass_config(i)["wave"] == 0 for i in range(p.num_passes)), split
+    for (dtype, n), bits in {("f32", 16): [9, 7], ("f32", 18): [11, 7], ("f32", 20): [13, 7],
+                             ("f64", 15): [7, 8], ("f64", 18): [10, 8], ("f64", 24): [14, 10]}.items():
         p = qse.Plan(n, dtype)
         assert p.pass_bits == bits, (dtype, n)
-        assert [p.pass_config(i)["wave"] for i in range(2)] == [1 if bits[0] <= 10 else 0, 0]
+        assert [p.pass_config(i)["wave"] for i in range(2)] == [0, 0]
 
 
 def test_mfma_path_plans(lib):
