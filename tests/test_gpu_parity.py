@@ -272,6 +272,37 @@ def test_full_size_n24_b16_f64():
     _full_size("n24_b16_f64", samples=(0, 9, 15))
 
 
+@pytest.mark.parametrize("dtype,n,batch", [("f32", 4, 1 << 24), ("f64", 3, 1 << 23),
+                                           ("f32", 10, (1 << 16) + 3)])
+def test_large_batch_one_pass(dtype, n, batch):
+    """One-pass plans (the wave-tile kernel by default) at the largest
+    batches a 1-2 GiB state holds, ragged in the last case: sampled vectors
+    exactly against the oracle, and every vector through the exact
+    normalised involution (integer inputs, even n: H H / 2^n = I)."""
+    say("large batch %s n=%d batch=%d" % (dtype, n, batch))
+    tdt = torch.float32 if dtype == "f32" else torch.float64
+    g = torch.Generator(device="cuda").manual_seed(4242 + n)
+    re = torch.randint(-8, 9, (batch, 1 << n), generator=g, device="cuda").to(tdt)
+    im = torch.randint(-8, 9, (batch, 1 << n), generator=g, device="cuda").to(tdt)
+    plan = qse.Plan(n, dtype)
+    rows = [0, 1, batch // 3, batch - 1]
+    re0, im0 = re[rows].cpu().numpy(), im[rows].cpu().numpy()
+    ore, oim = re.clone(), im.clone()
+    plan.execute(re, im, normalize=False)
+    torch.cuda.synchronize()
+    assert_exact(re[rows].cpu().numpy(), re0, n, False)
+    assert_exact(im[rows].cpu().numpy(), im0, n, False)
+    if n % 2 == 0:
+        re.copy_(ore)
+        im.copy_(oim)
+        plan.execute(re, im, normalize=True)
+        plan.execute(re, im, normalize=True)
+        torch.cuda.synchronize()
+        assert torch.equal(re, ore) and torch.equal(im, oim)
+    del re, im, ore, oim
+    torch.cuda.empty_cache()
+
+
 # ---- API behaviour on the device ----------------------------------------------
 
 def test_real_only_transform():
