@@ -54,11 +54,11 @@ typedef enum { FWT_F32 = 0, FWT_F64 = 1 } fwt_dtype;
  *                single-pass limit.
  *  MULTIPASS     Kronecker split into >= 2 passes whenever n allows it
  *                (n >= 2 for fp32, n >= 2 for fp64; below that one pass).
- *  MFMA_ABLATION the pages' matrix-core form, for measurement: the low
- *                min(n, 12) bits as dense H_16 block products on the 16x16x4
- *                fp32 / fp64 matrix instructions (see FWT_ABLATION_MFMA),
- *                the rest in column passes of at most 12 bits;
- *                FWT_EUNSUPPORTED for n < 8 (and fp64 n > 29). */
+ *  MFMA_ABLATION the pages' matrix-core form, for measurement: AUTO's
+ *                split, with the row pass (the low 8..15 bits) done as dense
+ *                H_16 block products on the 16x16x4 fp32 / fp64 matrix
+ *                instructions (see FWT_ABLATION_MFMA); FWT_EUNSUPPORTED for
+ *                n < 8 and where AUTO is. */
 typedef enum {
     FWT_PATH_AUTO = 0,
     FWT_PATH_SINGLE_BLOCK = 1,
@@ -227,11 +227,11 @@ typedef enum {
      * back.  2 <= n <= 26; needs a workspace of the state's size. */
     FWT_ABLATION_POPC_GEMM = 2,
     /* Matrix-core block Hadamard (the iThome "Day 18" native-FWT article,
-     * "Kronecker block GEMM idea", "TF32 path"): the low min(n, 12) bits
-     * as dense H_16 block products on the fp32 / fp64 16x16x4 matrix
-     * instructions (leftover bits butterflied in LDS), the higher bits on
-     * the ordinary column passes.  8 <= n <= 30 (fp32) / 29 (fp64); no
-     * workspace. */
+     * "Kronecker block GEMM idea", "TF32 path"): a FWT_PATH_MFMA_ABLATION
+     * plan, i.e. fwt_execute's split and column passes with the row pass
+     * (the low 8..15 bits) done as dense H_16 block products on the fp32
+     * / fp64 16x16x4 matrix instructions (leftover bits butterflied in
+     * LDS).  8 <= n <= 30 (fp32) / 29 (fp64); no workspace. */
     FWT_ABLATION_MFMA = 3,
     /* INT8 / CRT emulation of the fp64 transform (the iThome article,
      * "INT8 / Ozaki path", "Data flow of the implementation", radix form

@@ -222,10 +222,15 @@ __device__ __forceinline__ int line_elem(int lam, int k, int q)
     return (hi << (4 * q + 4)) | (k << (4 * q)) | lo;
 }
 
+// Workgroups of 256 threads, 1024 for tiles of 2^13 elements and more.
+template <int KM>
+constexpr int mfma_threads() { return KM >= 13 ? 1024 : 256; }
+
 template <typename T, int KM>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(mfma_threads<KM>())
     mfma_row_kernel(T* __restrict__ re, T* __restrict__ im, int64_t tiles, int do_scale, T scale)
 {
+    constexpr int NT = mfma_threads<KM>(), NW = NT / 64;
     using Ops = MfmaOps<T>;
     using acc_t = typename Ops::acc_t;
     constexpr int TPW = KM >= 12 ? 1 : 1 << (12 - KM);   // tiles per workgroup
@@ -245,7 +250,7 @@ __global__ void __launch_bounds__(256)
     using V = typename Vec16<T>::type;
     constexpr int W = 16 / sizeof(T);
     V* const gv = reinterpret_cast<V*>(buf + t0 * L);
-    for (int i = tid; i < ntile * (L / W); i += 256) {
+    for (int i = tid; i < ntile * (L / W); i += NT) {
         const V v = gv[i];
         const int e = i * W;
         T* const d = lds + (e / L) * TL + pad16(e % L);
@@ -265,7 +270,7 @@ __global__ void __launch_bounds__(256)
     for (int q = 0; q < G; ++q) {
         // blocks of 16 lines, over all tiles of the workgroup, split by wave
         const int blocks = ntile * (LINES >> 4);
-        for (int blk = wave; blk < blocks; blk += 4) {
+        for (int blk = wave; blk < blocks; blk += NW) {
             const int tile = blk / (LINES >> 4);
             const int lam0 = (blk % (LINES >> 4)) << 4;
             T* const tl = lds + tile * TL;
@@ -286,7 +291,7 @@ __global__ void __launch_bounds__(256)
     // remaining top bits [4G, KM): butterflies in LDS
 #pragma unroll
     for (int b = 4 * G; b < KM; ++b) {
-        for (int i = tid; i < ntile * (L >> 1); i += 256) {
+        for (int i = tid; i < ntile * (L >> 1); i += NT) {
             const int tile = i / (L >> 1), p = i % (L >> 1);
             const int e = ((p >> b) << (b + 1)) | (p & ((1 << b) - 1));
             T* const tl = lds + tile * TL;
@@ -296,7 +301,7 @@ __global__ void __launch_bounds__(256)
         }
         __syncthreads();
     }
-    for (int i = tid; i < ntile * (L / W); i += 256) {
+    for (int i = tid; i < ntile * (L / W); i += NT) {
         const int e = i * W;
         const T* const d = lds + (e / L) * TL + pad16(e % L);
         V v;
@@ -323,8 +328,8 @@ hipError_t mfma_row_launch(T* re, T* im, int64_t tiles, int do_scale, double c,
         const int64_t nt = tiles - t0 < per_launch ? tiles - t0 : per_launch;
         const int64_t off = t0 << KM;
         hipLaunchKernelGGL((mfma_row_kernel<T, KM>), dim3((unsigned)((nt + TPW - 1) / TPW), im ? 2 : 1),
-                           dim3(256), lds, stream, re + off, im ? im + off : nullptr, nt, do_scale,
-                           (T)c);
+                           dim3(mfma_threads<KM>()), lds, stream, re + off, im ? im + off : nullptr,
+                           nt, do_scale, (T)c);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -343,6 +348,12 @@ hipError_t mfma_row_dispatch(T* re, T* im, int64_t tiles, int km, int do_scale, 
     case 11: return mfma_row_launch<T, 11>(re, im, tiles, do_scale, c, stream);
     case 12: return mfma_row_launch<T, 12>(re, im, tiles, do_scale, c, stream);
     case 13: return mfma_row_launch<T, 13>(re, im, tiles, do_scale, c, stream);
+    case 14: return mfma_row_launch<T, 14>(re, im, tiles, do_scale, c, stream);
+    case 15:
+        // 2^15 padded fp64 elements exceed the LDS
+        if (sizeof(T) == 4)
+            return mfma_row_launch<T, 15>(re, im, tiles, do_scale, c, stream);
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }

@@ -34,9 +34,10 @@ constexpr int kMaxPasses = 4;
 // One-pass plans of this range of n use the wave-tile kernel by default.
 constexpr int kWaveDefaultMin = 3;
 constexpr int kWaveDefaultMax = 10;
-// Row bits of the matrix-core ablation's block-Hadamard kernel.
+// Row bits of the matrix-core ablation's block-Hadamard kernel: at least
+// 8, at most what one padded tile in LDS holds.
 constexpr int kMfmaRowMin = 8;
-constexpr int kMfmaRowMax = 12;
+int mfma_row_max(fwt_dtype dtype) { return dtype == FWT_F64 ? 14 : 15; }
 constexpr int kRowKrMax = 13;          // rows bits of a row pass (vectors)
 constexpr int kColKrMax = 12;          // rows bits of a column pass
 constexpr size_t kLdsMax = 160 * 1024; // per workgroup on gfx950
@@ -422,7 +423,7 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
     int lo = 0;
     for (int i = 0; i < p->npasses; ++i) {
         if (i == 0 && mfma_row) {
-            if (bits[0] < kMfmaRowMin || bits[0] > kMfmaRowMax) {
+            if (bits[0] < kMfmaRowMin || bits[0] > mfma_row_max(dtype)) {
                 delete p;
                 return FWT_EUNSUPPORTED;
             }
@@ -642,19 +643,13 @@ int fwt_plan_create(fwt_plan_t* out, int n, fwt_dtype dtype, fwt_path path)
     if (n < 0 || n > FWT_MAX_N || (dtype != FWT_F32 && dtype != FWT_F64))
         return FWT_EINVAL;
     if (path == FWT_PATH_MFMA_ABLATION) {
-        // the low min(n, 12) bits on the matrix-core row kernel, the rest
-        // in column passes of at most 12 bits
-        if (n < kMfmaRowMin || (dtype == FWT_F64 && n > 29))
+        // the default split, with the row pass on the matrix-core kernel
+        if (n < kMfmaRowMin)
             return FWT_EUNSUPPORTED;
-        int bits[kMaxPasses] = {n < kMfmaRowMax ? n : kMfmaRowMax, 0, 0, 0};
-        const int rest = n - bits[0];
-        int np = 1;
-        if (rest > kColKrMax) {
-            bits[np++] = rest - rest / 2;
-            bits[np++] = rest / 2;
-        } else if (rest > 0) {
-            bits[np++] = rest;
-        }
+        int bits[kMaxPasses] = {0, 0, 0, 0};
+        const int np = default_split(n, dtype, FWT_PATH_AUTO, bits);
+        if (np < 0)
+            return FWT_EUNSUPPORTED;
         return make_plan(out, n, dtype, np, bits, nullptr, true);
     }
     if (path != FWT_PATH_AUTO && path != FWT_PATH_SINGLE_BLOCK && path != FWT_PATH_MULTIPASS)

@@ -125,7 +125,8 @@ size_t oz_workspace_layout(int64_t batch, int n, int comps, size_t* off_partial,
 hipError_t ablation_ozaki(double* re, double* im, int64_t batch, int n, double c, void* ws,
                           hipStream_t stream);
 
-// Matrix-core row pass over the km contiguous low bits (8 <= km <= 13).
+// Matrix-core row pass over the km contiguous low bits (8 <= km <= 15
+// for fp32, 14 for fp64).
 hipError_t ablation_mfma_row(int f64, void* re, void* im, int64_t batch, int n, int km,
                              int do_scale, double c, hipStream_t stream);
 

@@ -192,10 +192,11 @@ def test_default_kernel_choice(lib):
 
 
 def test_mfma_path_plans(lib):
-    """FWT_PATH_MFMA_ABLATION: the low min(n, 12) bits on the matrix-core row
-    kernel, the rest in column passes of at most 12 bits."""
-    for dtype, n, bits in (("f32", 8, [8]), ("f32", 12, [12]), ("f32", 20, [12, 8]),
-                           ("f64", 24, [12, 12]), ("f32", 26, [12, 7, 7]), ("f64", 29, [12, 9, 8])):
+    """FWT_PATH_MFMA_ABLATION: AUTO's split, with the row pass on the
+    matrix-core kernel."""
+    for dtype, n, bits in (("f32", 8, [8]), ("f32", 12, [12]), ("f32", 15, [15]), ("f64", 14, [14]),
+                           ("f32", 20, [13, 7]), ("f64", 24, [14, 10]), ("f32", 26, [10, 8, 8]),
+                           ("f64", 29, [10, 10, 9])):
         p = qse.Plan(n, dtype, path=qse.PATH_MFMA_ABLATION)
         assert p.pass_bits == bits, (dtype, n)
         assert p.pass_config(0)["kind"] == "mfma"

@@ -456,15 +456,16 @@ def test_integer_ablations(kind, dtype, n, batch):
         assert_exact(tim.cpu().numpy(), im, n, normalize)
 
 
-# Matrix-core ablation at every row width it has (8..12 low bits; 13 for
-# n = 13 is not reached since the row kernel takes min(n, 12)), with ragged
-# last workgroups (11 bits: 2 tiles per workgroup, odd tile counts), a
-# one-column-pass remainder, a two-column-pass remainder (n = 26: 12 | 7 | 7)
-# and a state larger than one cache chunk (fp32 n = 20, 80 vectors).
+# Matrix-core ablation at every row width it has (8..15 low bits fp32,
+# 8..14 fp64; 1024-thread workgroups from 13), with ragged last workgroups
+# (11 bits: 2 tiles per workgroup, odd tile counts), one and two column
+# passes (n = 26: 10 | 8 | 8) and a state larger than one cache chunk (fp32
+# n = 20, 80 vectors).
 @pytest.mark.parametrize("dtype,n,batch", [("f32", 8, 7), ("f64", 8, 3), ("f32", 11, 33),
                                            ("f64", 11, 5), ("f32", 12, 3), ("f64", 12, 2),
-                                           ("f32", 16, 3), ("f64", 21, 1), ("f32", 26, 1),
-                                           ("f32", 20, 80)])
+                                           ("f32", 13, 3), ("f64", 13, 2), ("f32", 14, 2),
+                                           ("f64", 14, 3), ("f32", 15, 2), ("f32", 16, 3),
+                                           ("f64", 21, 1), ("f32", 26, 1), ("f32", 20, 80)])
 def test_integer_mfma_ablation(dtype, n, batch):
     say("ablation mfma %s n=%d batch=%d" % (dtype, n, batch))
     npd = np.float32 if dtype == "f32" else np.float64
