@@ -272,6 +272,58 @@ def test_full_size_n24_b16_f64():
     _full_size("n24_b16_f64", samples=(0, 9, 15))
 
 
+@pytest.mark.parametrize("dtype,n", [("f32", 25), ("f32", 27), ("f64", 25), ("f64", 26)])
+def test_three_pass_default_plans(dtype, n):
+    """The default three-pass plans (n > 24) at their real size, one vector,
+    inputs in {-1, 0, 1}: every partial sum stays an exact integer far below
+    2^24, so the result is exact; compared whole with the oracle."""
+    say("three-pass %s n=%d" % (dtype, n))
+    npd = np.float32 if dtype == "f32" else np.float64
+    rng = np.random.default_rng(77_000 + n)
+    re = rng.integers(-1, 2, size=(1, 1 << n)).astype(npd)
+    im = rng.integers(-1, 2, size=(1, 1 << n)).astype(npd)
+    plan = qse.Plan(n, dtype)
+    assert plan.num_passes == 3
+    gre, gim = run(plan, re, im, False)
+    assert_exact(gre, re, n, False)
+    assert_exact(gim, im, n, False)
+
+
+def _parity(t):
+    """popcount(t) mod 2 for a non-negative int64 tensor (below 2^32)."""
+    for sh in (16, 8, 4, 2, 1):
+        t = t ^ (t >> sh)
+    return t & 1
+
+
+@pytest.mark.parametrize("dtype,n", [("f32", 30), ("f64", 29)])
+def test_largest_n_closed_form(dtype, n):
+    """The largest n each dtype supports: x = e_j + 2 e_k (re) and e_k - e_j
+    (im) transform to (-1)^popcount(i AND j) + 2 (-1)^popcount(i AND k) and
+    so on, checked for all 2^n outputs on the device (exact)."""
+    say("largest n %s n=%d" % (dtype, n))
+    tdt = torch.float32 if dtype == "f32" else torch.float64
+    N = 1 << n
+    j, k = 0x2AAAAAAA & (N - 1), 0x15555555 & (N - 1) | (1 << (n - 1))
+    re = torch.zeros(1, N, dtype=tdt, device="cuda")
+    im = torch.zeros(1, N, dtype=tdt, device="cuda")
+    re[0, j] = 1.0
+    re[0, k] = 2.0
+    im[0, k] = 1.0
+    im[0, j] = -1.0
+    plan = qse.Plan(n, dtype)
+    plan.execute(re, im, normalize=False)
+    torch.cuda.synchronize()
+    i = torch.arange(N, device="cuda", dtype=torch.int64)
+    sj = (1 - 2 * _parity(i & j)).to(tdt)
+    sk = (1 - 2 * _parity(i & k)).to(tdt)
+    del i
+    assert torch.equal(re[0], sj + 2 * sk)
+    assert torch.equal(im[0], sk - sj)
+    del re, im, sj, sk
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype,n,batch", [("f32", 4, 1 << 24), ("f64", 3, 1 << 23),
                                            ("f32", 10, (1 << 16) + 3)])
 def test_large_batch_one_pass(dtype, n, batch):
