@@ -104,8 +104,8 @@ constexpr int kOzPrimes[kOzMaxModuli] = {251, 241, 239, 233, 229, 227, 223, 211,
 struct OzConst {
     int m;                          // moduli in use
     int p[kOzMaxModuli];
-    float inv_pf[kOzMaxModuli];
     double inv_pd[kOzMaxModuli];
+    int magic[kOzMaxModuli];        // round(2^20 / p_j), for reduce_mod
     int crt_c[kOzMaxModuli];        // (M / p_j)^-1 mod p_j
     uint64_t crt_lo[kOzMaxModuli];  // M / p_j, low and high 64 bits
     uint64_t crt_hi[kOzMaxModuli];

@@ -12,7 +12,7 @@
 //   m primes p_j <= 251 with prod p_j > 2^(49 + n) carry Y through CRT:
 //   residues r_j = X mod p_j (|r| <= 127, int8, four moduli packed in a
 //   32-bit word per element), transformed in residue space, then Y rebuilt from the residues by the CRT with a
-//   rounded quotient: t_j = r_j (M / p_j)^-1 mod p_j (balanced),
+//   rounded quotient: t_j = r_j (M / p_j)^-1 mod p_j (within p_j / 2 + 1),
 //   q = nearest integer to sum_j t_j / p_j (fp64), Y = sum_j t_j M / p_j -
 //   q M in 128-bit integers (exact: |Y| / M stays below 1/2 by a margin of
 //   at least 0.003, the fp64 quotient errs by under 1e-12), and
@@ -160,9 +160,13 @@ __device__ __forceinline__ int window_addr(int lam, int k, int w)
     return ((lam >> w) << (w + 5)) | (k << w) | (lam & ((1 << w) - 1));
 }
 
-__device__ __forceinline__ int reduce_mod(int d, int p, float inv_p)
+// d - p * q with q the integer nearest to d / p up to 0.015: for |d| <=
+// 31500 the result is congruent to d and within p / 2 + 1 of zero (so an
+// int8 for p <= 251), in three full-rate 24-bit integer operations.
+__device__ __forceinline__ int reduce_mod(int d, int p, int magic)
 {
-    return d - p * (int)rintf((float)d * inv_p);
+    const int q = (__mul24(d, magic) + (1 << 19)) >> 20;
+    return d - __mul24(q, p);
 }
 
 // o[q] = byte q of d[0], d[1], d[2], d[3] (in that byte order)
@@ -185,12 +189,11 @@ __global__ void __launch_bounds__(256, 8)
     uint32_t* const lds = reinterpret_cast<uint32_t*>(lds_raw);
     const int TB = kt + xb;
     const int grp = blockIdx.y % G;
-    int p[kOzPack];
-    float inv_p[kOzPack];
+    int p[kOzPack], magic[kOzPack];
 #pragma unroll
     for (int q = 0; q < kOzPack; ++q) {
         p[q] = k.p[kOzPack * grp + q];
-        inv_p[q] = k.inv_pf[kOzPack * grp + q];
+        magic[q] = k.magic[kOzPack * grp + q];
     }
     uint32_t* const pl = words + (int64_t)blockIdx.y * plane_len;
     const int64_t tile = tile0 + blockIdx.x;
@@ -265,9 +268,9 @@ __global__ void __launch_bounds__(256, 8)
                 uint32_t v0 = 0, v1 = 0;
 #pragma unroll
                 for (int q = 0; q < kOzPack; ++q) {
-                    v0 |= (uint32_t)(uint8_t)(int8_t)reduce_mod(acc[q][0][r], p[q], inv_p[q])
+                    v0 |= (uint32_t)(uint8_t)(int8_t)reduce_mod(acc[q][0][r], p[q], magic[q])
                           << (8 * q);
-                    v1 |= (uint32_t)(uint8_t)(int8_t)reduce_mod(acc[q][1][r], p[q], inv_p[q])
+                    v1 |= (uint32_t)(uint8_t)(int8_t)reduce_mod(acc[q][1][r], p[q], magic[q])
                           << (8 * q);
                 }
                 const int o = 4 * (lane >> 4) + r;
@@ -328,7 +331,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
             for (int j = 0; j < M; ++j) {
                 const int r = (int)(int8_t)(uint8_t)(res[j / kOzPack][i] >> (8 * (j % kOzPack)));
-                const int t = reduce_mod(r * k.crt_c[j], k.p[j], k.inv_pf[j]);
+                const int t = reduce_mod(r * k.crt_c[j], k.p[j], k.magic[j]);
                 f = fma((double)t, k.inv_pd[j], f);
                 a0 += (int64_t)t * (uint32_t)k.crt_lo[j];
                 a1 += (int64_t)t * (uint32_t)(k.crt_lo[j] >> 32);
@@ -398,7 +401,7 @@ OzConst oz_constants(int n)
     k.m_hi = (uint64_t)(M >> 64);
     for (int j = 0; j < kOzMaxModuli; ++j) {
         k.p[j] = kOzPrimes[j];
-        k.inv_pf[j] = 1.0f / (float)kOzPrimes[j];
+        k.magic[j] = (int)((1 << 20) / (double)kOzPrimes[j] + 0.5);
         k.inv_pd[j] = 1.0 / (double)kOzPrimes[j];
         if (j < k.m) {
             const unsigned __int128 cj = M / (unsigned)kOzPrimes[j];
