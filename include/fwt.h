@@ -103,7 +103,8 @@ int fwt_plan_create_split(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
  * selects the default. */
 typedef struct {
     int eb;      /* log2 of the 16-byte vectors a thread holds per register
-                    round (0..5) */
+                    round (0..5, at most the pass's row bits; LDS tiles with
+                    row bits need at least 1) */
     int gbits;   /* log2 of the 16-byte column groups per tile of a column
                     pass (0..4; 0 or -1 for the first pass) */
     int phases;  /* log2 of the phases a column pass splits each LDS exchange

@@ -193,7 +193,9 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
         p.k = k;
     }
     const int eb = eb_req < 0 ? default_eb(kr, dtype, multipass, row) : eb_req;
-    if (eb > kr || eb < 0 || eb > 5)
+    // A round of LDS tiles butterflies eb register bits, so a tile with row
+    // bits needs eb >= 1 (rounds_of divides by eb).
+    if (eb > kr || eb < 0 || eb > 5 || (eb == 0 && kr > 0))
         return FWT_EINVAL;
     const int tt_max = ilog2(max_threads(eb));
     const int nr = qse::rounds_of(kr, eb);

@@ -151,6 +151,61 @@ def test_tuned_validation(lib):
     assert _split(lib, 16, 0, [6, 10], eb=[-1, 3], gbits=[-1, 4]) == qse.FWT_EINVAL
 
 
+def test_tuned_eb_zero(lib):
+    # LDS tiles with row bits need at least one register bit per round.
+    assert _split(lib, 12, 0, [12], eb=[0]) == qse.FWT_EINVAL
+    assert _split(lib, 16, 0, [8, 8], eb=[0, 3]) == qse.FWT_EINVAL
+    assert _split(lib, 16, 0, [8, 8], eb=[3, 0]) == qse.FWT_EINVAL
+    assert _split(lib, 6, 1, [6], eb=[0]) == qse.FWT_EINVAL
+    # the wave-tile kernel may keep every row bit in lanes
+    assert _split(lib, 6, 0, [6], eb=[0], wave=[1]) == 0
+
+
+FUZZ_SCRIPT = r'''
+import ctypes, random, sys
+sys.path.insert(0, sys.argv[1])
+import quantum_state_encoding_amd as qse
+lib = qse.load_library()
+rng = random.Random(20240611)
+counts = {}
+for it in range(20000):
+    n = rng.randint(1, 30)
+    dtype = rng.randint(0, 1)
+    npasses = rng.randint(1, 4)
+    cuts = sorted(rng.sample(range(1, n), min(npasses - 1, n - 1))) if n > 1 else []
+    bits = [b - a for a, b in zip([0] + cuts, cuts + [n])]
+    arr = (ctypes.c_int * len(bits))(*bits)
+    tun = (qse.PassTuning * len(bits))()
+    for i in range(len(bits)):
+        tun[i].eb = rng.randint(-1, 6)
+        tun[i].gbits = rng.randint(-1, 5)
+        tun[i].phases = rng.randint(-1, 3)
+        tun[i].pipe = rng.randint(-1, 2)
+        tun[i].wave = rng.randint(-1, 2)
+    h = ctypes.c_void_p()
+    st = lib.fwt_plan_create_tuned(ctypes.byref(h), n, dtype, len(bits), arr, tun)
+    counts[st] = counts.get(st, 0) + 1
+    if st == 0:
+        npass = ctypes.c_int()
+        assert lib.fwt_plan_num_passes(h, ctypes.byref(npass)) == 0 and npass.value == len(bits)
+        lib.fwt_plan_destroy(h)
+print(sorted(counts.items()))
+'''
+
+
+def test_tuned_fuzz_never_crashes():
+    # Random tunings, splits, n and dtype, in a child process so that a
+    # crash in plan creation fails this test instead of ending the run.
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "-c", FUZZ_SCRIPT, ROOT], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, (r.returncode, r.stderr[-2000:])
+    counts = dict(eval(r.stdout.strip().splitlines()[-1]))
+    assert counts.get(0, 0) > 100                     # many valid plans were built
+    assert set(counts) <= {0, qse.FWT_EINVAL, qse.FWT_EUNSUPPORTED}
+
+
 def test_every_gpu_test_plan_is_valid(lib):
     """Each plan the GPU parity suite builds is accepted by the planner and
     has the forced properties (caught here, on the CPU)."""
