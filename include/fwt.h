@@ -116,10 +116,20 @@ typedef struct {
                     workgroup fills a CU's LDS */
     int wave;    /* 1: wave-tile kernel (a whole tile in one wave, lane bits
                     crossed with DPP / ds_swizzle / permlane swaps, no LDS;
-                    row bits - eb <= 6 - gbits); 0: LDS tiles; default: the
-                    wave-tile kernel for a one-pass plan with 3 <= n <= 10
-                    when every other field of the entry is -1, else LDS
-                    tiles */
+                    row bits - eb <= 6 - gbits); 2: lane-exchange kernel
+                    (row passes only: lanes hold the 6 lowest row bits, a
+                    workgroup of 2^(6 + w) threads holds the tile with
+                    w = row bits - 6 - eb wave bits, 1 <= w <= 4 and
+                    2 <= eb <= 5 or eb = w = 1, and ceil(w / eb) LDS
+                    exchanges move the wave bits into registers; default
+                    eb gives w = min(4, row bits - 8), or 1 below 10 row
+                    bits); 0: LDS tiles.  Default, when every field of the
+                    entry is -1: the wave-tile kernel for a one-pass plan
+                    with 3 <= n <= 10; else the lane-exchange kernel for a
+                    row pass of 8..13 row bits, except the row pass of a
+                    multi-pass plan with 11; else LDS tiles.  "Row bits"
+                    counts 16-byte vectors: the pass's bits less 2 (fp32)
+                    or 1 (fp64). */
 } fwt_pass_tuning;
 
 /* As fwt_plan_create_split, with the on-chip tiling of each pass forced

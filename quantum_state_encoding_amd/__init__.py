@@ -200,6 +200,8 @@ class Plan:
         t = "float" if self.dtype == "f32" else "double"
         if c["kind"] == "mfma":
             return "mfma_row_kernel<%s, %d>" % (t, c["bits"])
+        if c["wave"] == 2:
+            return "lx_kernel<%s, %d, %d, %d>" % (t, c["kr"], c["eb"], c["kr"] - 6 - c["eb"])
         if c["wave"]:
             return "wave_kernel<%s, %d, %d, %d, %s>" % (
                 t, c["kr"], c["eb"], c["gbits"], "true" if c["kind"] == "row" else "false")

@@ -39,6 +39,7 @@ constexpr int kWaveDefaultMax = 10;
 constexpr int kMfmaRowMin = 8;
 int mfma_row_max(fwt_dtype dtype) { return dtype == FWT_F64 ? 14 : 15; }
 constexpr int kRowKrMax = 13;          // rows bits of a row pass (vectors)
+constexpr int kLxDefaultMin = 8;       // lane-exchange kernel by default from here
 constexpr int kColKrMax = 12;          // rows bits of a column pass
 constexpr size_t kLdsMax = 160 * 1024; // per workgroup on gfx950
 constexpr size_t kPhaseLdsTarget = 68 * 1024;  // two tiles per CU
@@ -143,6 +144,8 @@ bool phases_allowed(int kr, int eb, int gbits, int phb)
 // error.
 int build_wave_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool row,
                     const fwt_pass_tuning& t);
+int build_lx_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool row,
+                  const fwt_pass_tuning& t);
 
 int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tuning& t,
                bool multipass)
@@ -171,10 +174,12 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
         if (kr < 1 || kr > kColKrMax)
             return FWT_EINVAL;
     }
-    if (t.wave > 1 || t.pipe > 1)
+    if (t.wave > 2 || t.pipe > 1)
         return FWT_EINVAL;
     if (t.wave == 1)
         return build_wave_pass(p, n, dtype, lo, k, kr, row, t);
+    if (t.wave == 2)
+        return build_lx_pass(p, n, dtype, lo, k, kr, row, t);
     // One-pass plans of 3 <= n <= 10 default to the wave-tile kernel: on
     // 512 MiB states it ran at 6.0 TB/s against 5.0-5.4 for the LDS tiles
     // (both dtypes), and on cache-resident batches 2-12 % faster.  From 11
@@ -186,6 +191,21 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
         t.eb < 0 && t.gbits < 0 && t.phases < 0 && t.pipe < 0 && t.wave < 0;
     if (all_default && row && !multipass && k >= kWaveDefaultMin && k <= kWaveDefaultMax) {
         const int rc = build_wave_pass(p, n, dtype, lo, k, kr, row, t);
+        if (rc == FWT_OK)
+            return rc;
+        p = Pass{};
+        p.lo = lo;
+        p.k = k;
+    }
+    // Other row passes of 8..13 vector bits default to the lane-exchange
+    // kernel: against the LDS tiles it took one-pass plans 4-22 % faster
+    // (n = 11..15, cache-resident and 512 MiB states) and fp64 two-pass row
+    // passes 1-5 % faster (n = 17..24).  Two-pass row passes of 11 vector
+    // bits (fp32 n = 20..24, fp64 n = 20) measured 0.3-0.8 % slower in it
+    // and stay on the LDS tiles.
+    if (all_default && row && kr >= kLxDefaultMin && kr <= kRowKrMax &&
+        !(multipass && kr == 11)) {
+        const int rc = build_lx_pass(p, n, dtype, lo, k, kr, row, t);
         if (rc == FWT_OK)
             return rc;
         p = Pass{};
@@ -353,6 +373,36 @@ int build_wave_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool
     p.lds = 0;
     p.store_back = 0;
     p.tiles_bits = row ? (n - k) : (n - lo - k) + p.nblk_bits;
+    return check_offsets(p, dtype, row, kr, vb);
+}
+
+// A row pass in the lane-exchange kernel: a tile of 2^kr 16-byte vectors in
+// a workgroup of 2^(6 + W) threads holding 2^eb vectors each, kr = eb + 6 + W
+// with 1 <= W <= 4 and 2 <= eb <= 5 (or eb = W = 1): lane stages for the 6
+// lowest row bits and ceil(W / eb) LDS exchanges.  Default: the most threads
+// with eb >= 2, W = min(4, kr - 8), and W = 1 below 10 row bits (measured:
+// best, or within 4 % of the best variant, at every n and batch tried).
+int build_lx_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool row,
+                  const fwt_pass_tuning& t)
+{
+    const int vb = vec_bits(dtype);
+    if (!row || t.gbits > 0 || t.phases > 0 || t.pipe > 0)
+        return FWT_EINVAL;
+    const int eb = t.eb >= 0 ? t.eb : kr - 6 - (kr >= 10 ? (kr - 8 < 4 ? kr - 8 : 4) : 1);
+    const int w = kr - 6 - eb;
+    if (w < 1 || w > 4 || eb > 5 || eb < 1 || (eb == 1 && w != 1))
+        return FWT_EINVAL;
+    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, 0, 0, 1, 0, 2};
+    if (!qse::kernel_available(p.key))
+        return FWT_EUNSUPPORTED;
+    p.gbits = 0;
+    p.phb = 0;
+    p.tt_bits = 6 + w;
+    p.tpw_bits = 0;
+    p.block = 64u << w;
+    p.lds = (size_t)16 << kr;
+    p.store_back = 0;
+    p.tiles_bits = n - k;
     return check_offsets(p, dtype, row, kr, vb);
 }
 

@@ -40,7 +40,8 @@ struct KernelKey {
     int phb;   // log2 of the phases an LDS exchange is split into
     int row;   // 1: contiguous row pass
     int pipe;  // 1: persistent software-pipelined kernel
-    int wave;  // 1: wave-tile kernel (whole tile in one wave, lane stages)
+    int wave;  // 1: wave-tile kernel (whole tile in one wave, lane stages);
+               // 2: lane-exchange row kernel (lane stages, one LDS exchange)
 };
 
 // Number of register rounds of a (kr, eb) kernel: ceil(kr / eb), at least 1.

@@ -586,6 +586,139 @@ __global__ void __launch_bounds__(256)
     }
 }
 
+// ---- lane-exchange tiles: lane stages plus LDS exchanges of wave bits ---
+//
+// A row tile of 2^KR 16-byte vectors in one workgroup of 2^(6 + W) threads,
+// each holding E = 2^EB vectors, KR = EB + 6 + W.  Lanes always hold the 6
+// lowest row bits, whose stages cross lanes as in wave_kernel.  In the load
+// layout the W wave bits are row bits [6, 6 + W) and the register bits the
+// top EB row bits.  After the register, lane and in-vector stages, each
+// exchange through LDS swaps the next min(EB, bits left) wave bits with the
+// low register bits, whose stages then run in registers: ceil(W / EB)
+// exchanges in all.  The lanes of a wave always touch 64 consecutive
+// 16-byte slots (in LDS and in memory), so the exchanges need no padding
+// and every global access of a wave covers 1 KiB.
+
+// Row bit held by wave bit i (register bit i when REG) after X exchanges.
+template <int W, int EB>
+__host__ __device__ constexpr int lx_pos(int x, int i, bool reg)
+{
+    int wp[4] = {6, 7, 8, 9};
+    int rp[5] = {6 + W, 7 + W, 8 + W, 9 + W, 10 + W};
+    for (int e = 0; e < x; ++e) {
+        const int c = W - e * EB < EB ? W - e * EB : EB;
+        for (int q = 0; q < c; ++q) {
+            const int t = wp[e * EB + q];
+            wp[e * EB + q] = rp[q];
+            rp[q] = t;
+        }
+    }
+    return reg ? rp[i] : wp[i];
+}
+
+// Offset (in 16-byte slots) of register j in layout X: a compile-time
+// constant once j is unrolled.
+template <int W, int EB, int X>
+__device__ __forceinline__ constexpr uint32_t lx_reg_part(int j)
+{
+    uint32_t r = 0;
+    for (int i = 0; i < EB; ++i)
+        r |= (uint32_t)((j >> i) & 1) << lx_pos<W, EB>(X, i, true);
+    return r;
+}
+
+template <int W, int EB, int X>
+__device__ __forceinline__ uint32_t lx_thread_part(int lane, int wave)
+{
+    uint32_t r = (uint32_t)lane;
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+        r |= (uint32_t)((wave >> i) & 1) << lx_pos<W, EB>(X, i, false);
+    return r;
+}
+
+// Exchanges X + 1 .. NX: move the next wave bits into the low register
+// bits through LDS, then their stages.
+template <typename V, int W, int EB, int X, int NX>
+struct LxRounds {
+    __device__ __forceinline__ static void run(V* x, V* L, int lane, int wave)
+    {
+        constexpr int E = 1 << EB;
+        constexpr int C = W - X * EB < EB ? W - X * EB : EB;   // wave bits moved
+        const uint32_t from = lx_thread_part<W, EB, X>(lane, wave);
+        const uint32_t to = lx_thread_part<W, EB, X + 1>(lane, wave);
+        if (X > 0)
+            __syncthreads();   // the previous exchange's reads are done
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            L[from + lx_reg_part<W, EB, X>(j)] = x[j];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] = L[to + lx_reg_part<W, EB, X + 1>(j)];
+        register_stages<C, E>(x);
+        LxRounds<V, W, EB, X + 1, NX>::run(x, L, lane, wave);
+    }
+};
+template <typename V, int W, int EB, int NX>
+struct LxRounds<V, W, EB, NX, NX> {
+    __device__ __forceinline__ static void run(V*, V*, int, int) {}
+};
+
+template <typename T, int KR, int EB, int W>
+__global__ void __launch_bounds__(64 << W)
+    lx_kernel(T* __restrict__ re, T* __restrict__ im, TileArgs a)
+{
+    using V = typename Vec<T>::type;
+    constexpr int WB = Vec<T>::WB;
+    constexpr int E = 1 << EB;
+    constexpr int NX = (W + EB - 1) / EB;   // exchanges
+    static_assert(KR == EB + 6 + W && EB >= 1 && W >= 1 && W <= 4, "lane-exchange tile");
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    V* const L = reinterpret_cast<V*>(lds_raw);
+    const int64_t t = a.tile0 + blockIdx.x;
+    if (t >= a.tiles)
+        return;   // uniform across the workgroup
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    T* const buf = blockIdx.y ? im : re;
+    unsigned char* const p = reinterpret_cast<unsigned char*>(buf + (t << (KR + WB)));
+
+    const uint32_t r0 = lx_thread_part<W, EB, 0>(lane, wave);
+    V x[E];
+    if (a.ld_nt) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] = load16_nt<V>(p, (r0 + lx_reg_part<W, EB, 0>(j)) << 4);
+    } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] = load16<V>(p, (r0 + lx_reg_part<W, EB, 0>(j)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        in_vector(x[j]);
+    register_stages<EB, E>(x);
+    LaneStages<0, 6, 0, E, V, T>::run(x, lane);
+    LxRounds<V, W, EB, 0, NX>::run(x, L, lane, wave);
+    if (a.do_scale) {
+        const T c = (T)a.scale;
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            x[j] *= c;
+    }
+    const uint32_t rf = lx_thread_part<W, EB, NX>(lane, wave);
+    if (a.st_nt) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            store16_nt<V>(p, (rf + lx_reg_part<W, EB, NX>(j)) << 4, x[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            store16<V>(p, (rf + lx_reg_part<W, EB, NX>(j)) << 4, x[j]);
+    }
+}
+
 __global__ void __launch_bounds__(256)
     pair_f32_kernel(float* __restrict__ re, float* __restrict__ im, int64_t pairs, int do_scale,
                     float scale)
@@ -723,6 +856,30 @@ struct RegisterWave {
     }
 };
 
+// Lane-exchange row tiles: W in [1, 4] with EB = KR - 6 - W in [2, 5], or
+// EB = W = 1.
+template <typename T, int KR, int W>
+void add_lx(std::vector<Entry>& v)
+{
+    constexpr int EB = KR - 6 - W;
+    if constexpr (W >= 1 && W <= 4 && ((EB >= 2 && EB <= 5) || (EB == 1 && W == 1)))
+        v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, 0, 0, 1, 0, 2},
+                     reinterpret_cast<const void*>(&lx_kernel<T, KR, EB, W>)});
+}
+
+template <typename T, int KR, int KRMIN>
+struct LaneExchange {
+    static void add(std::vector<Entry>& v)
+    {
+        add_lx<T, KR, 1>(v);
+        add_lx<T, KR, 2>(v);
+        add_lx<T, KR, 3>(v);
+        add_lx<T, KR, 4>(v);
+        if constexpr (KR > KRMIN)
+            LaneExchange<T, KR - 1, KRMIN>::add(v);
+    }
+};
+
 const std::vector<Entry>& table()
 {
     static const std::vector<Entry> t = [] {
@@ -731,6 +888,8 @@ const std::vector<Entry>& table()
         RegisterWave<double, true, 11, 0>::add(v);
         RegisterWave<float, false, 11, 1>::add(v);
         RegisterWave<double, false, 11, 1>::add(v);
+        LaneExchange<float, 13, 8>::add(v);
+        LaneExchange<double, 13, 8>::add(v);
         Register<float, true, 13, 0>::add(v);
         Register<double, true, 13, 0>::add(v);
         Register<float, false, 12, 1>::add(v);

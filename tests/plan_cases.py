@@ -59,3 +59,24 @@ WAVE_CASES = [
 # (dtype, n): one-pass plans with the LDS-tile kernel forced (wave 0) where
 # the default plan picks the wave-tile kernel (3 <= n <= 10), and either side
 LDS_SINGLE_CASES = [(dt, n) for dt in ("f32", "f64") for n in range(2, 12)]
+
+
+# (dtype, n, split, eb, wave, batch): the lane-exchange row kernel (lanes hold
+# the 6 lowest row bits, LDS exchanges move the wave bits into registers),
+# every compiled (row bits, eb, wave bits) variant as a one-pass plan, and
+# as the row pass of two-pass plans
+def _lx_cases():
+    out = []
+    for dtype, vb in (("f32", 2), ("f64", 1)):
+        for kr in range(8, 14):
+            for w in (1, 2, 3, 4):
+                eb = kr - 6 - w
+                if 2 <= eb <= 5 or eb == w == 1:
+                    out.append((dtype, kr + vb, (kr + vb,), (eb,), (2,), 3))
+    out += [("f32", 20, (13, 7), (3, -1), (2, 0), 2), ("f32", 20, (13, 7), (4, -1), (2, 0), 2),
+            ("f64", 24, (14, 10), (4, -1), (2, 0), 1), ("f64", 20, (12, 8), None, (2, 0), 3),
+            ("f32", 18, (11, 7), None, (2, 0), 5), ("f32", 14, (14,), None, (2,), 65),
+            ("f32", 12, (12,), None, (2,), 1), ("f64", 13, (13,), None, (2,), 129),
+            ("f32", 20, (13, 7), (2, -1), (2, 0), 2), ("f32", 15, (15,), (3,), (2,), 33)]
+    return out
+LX_CASES = _lx_cases()

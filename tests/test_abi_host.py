@@ -209,7 +209,8 @@ def test_tuned_fuzz_never_crashes():
 def test_every_gpu_test_plan_is_valid(lib):
     """Each plan the GPU parity suite builds is accepted by the planner and
     has the forced properties (caught here, on the CPU)."""
-    from plan_cases import FORCED_SPLITS, LDS_SINGLE_CASES, PIPE_CASES, VARIANTS, WAVE_CASES
+    from plan_cases import (FORCED_SPLITS, LDS_SINGLE_CASES, LX_CASES, PIPE_CASES, VARIANTS,
+                            WAVE_CASES)
     for dtype, n in LDS_SINGLE_CASES:
         assert qse.Plan(n, dtype, split=(n,), wave=(0,)).pass_config(0)["wave"] == 0
     for dtype, n, split in FORCED_SPLITS:
@@ -224,26 +225,60 @@ def test_every_gpu_test_plan_is_valid(lib):
         for i, pv in enumerate(pipe):
             if pv >= 0:
                 assert p.pass_config(i)["pipe"] == pv
+    for dtype, n, split, eb, wave, batch in LX_CASES:
+        p = qse.Plan(n, dtype, split=split, eb=eb, wave=wave)
+        assert [p.pass_config(i)["wave"] for i in range(p.num_passes)] == list(wave)
+    assert len(LX_CASES) == 38   # all 28 compiled variants appear
+
+
+def test_lane_exchange_plans(lib):
+    # lanes hold 6 row bits, w wave bits (default: the most threads with
+    # eb >= 2), one tile per workgroup
+    for dtype, vb in (("f32", 2), ("f64", 1)):
+        for kr in range(8, 14):
+            p = qse.Plan(kr + vb, dtype, split=(kr + vb,), wave=(2,))
+            c = p.pass_config(0)
+            w = kr - 6 - c["eb"]
+            assert w == (min(4, kr - 8) if kr >= 10 else 1)
+            assert c["block"] == 64 << w and c["lds"] == 16 << kr and c["tpw_bits"] == 0
+            assert p.kernel_name(0) == "lx_kernel<%s, %d, %d, %d>" % (
+                "float" if dtype == "f32" else "double", kr, c["eb"], w)
+        kr = 10
+        n = kr + vb
+        assert _split(lib, n, vb == 1, [n], eb=[4], wave=[2]) == qse.FWT_EINVAL    # w = 0
+        assert _split(lib, n, vb == 1, [n], eb=[1], wave=[2]) == qse.FWT_EINVAL    # 3 exchanges
+        assert _split(lib, n + 1, vb == 1, [n + 1], eb=[2], wave=[2]) == 0       # w = 3, 2 exchanges
+        assert _split(lib, n + 2, vb == 1, [n + 2], eb=[2], wave=[2]) == 0       # w = 4
+        assert _split(lib, n + 3, vb == 1, [n + 3], eb=[2], wave=[2]) == qse.FWT_EINVAL  # w = 5
+        assert _split(lib, n, vb == 1, [n], gbits=[1], wave=[2]) == qse.FWT_EINVAL
+        assert _split(lib, n + 7, vb == 1, [n, 7], wave=[0, 2]) == qse.FWT_EINVAL  # column pass
+    assert _split(lib, 9, 0, [9], wave=[2]) == qse.FWT_EINVAL     # 7 row bits: no wave bit
 
 
 def test_default_kernel_choice(lib):
-    """One-pass plans of 3 <= n <= 10 default to the wave-tile kernel; wider
-    one-pass plans, every pass of a multi-pass plan and entries with any
-    field forced use the LDS tiles."""
-    for dtype in ("f32", "f64"):
+    """One-pass plans of 3 <= n <= 10 default to the wave-tile kernel; other
+    row passes of 8..13 vector bits to the lane-exchange kernel (except a
+    multi-pass row pass of 11); column passes, the rest and entries with
+    any field forced use the LDS tiles."""
+    for dtype, vb in (("f32", 2), ("f64", 1)):
         for n in range(2, 15 if dtype == "f32" else 14):
-            want = 1 if 3 <= n <= 10 else 0
+            want = 1 if 3 <= n <= 10 else (2 if n - vb >= 8 else 0)
             assert qse.Plan(n, dtype).pass_config(0)["wave"] == want, (dtype, n)
             assert qse.Plan(n, dtype, split=(n,)).pass_config(0)["wave"] == want, (dtype, n)
         assert qse.Plan(8, dtype, split=(8,), eb=(3,)).pass_config(0)["wave"] == 0
-        for split in ((5, 5), (7, 7), (2, 8), (11, 9), (3, 3, 4)):
+        assert qse.Plan(12, dtype, split=(12,), eb=(3,)).pass_config(0)["wave"] == 0
+        for split in ((5, 5), (7, 7), (2, 8), (3, 3, 4), (11, 9)):
             p = qse.Plan(sum(split), dtype, split=split)
-            assert all(p.pass_config(i)["wave"] == 0 for i in range(p.num_passes)), split
-    for (dtype, n), bits in {("f32", 16): [9, 7], ("f32", 18): [11, 7], ("f32", 20): [13, 7],
-                             ("f64", 15): [7, 8], ("f64", 18): [10, 8], ("f64", 24): [14, 10]}.items():
+            want = [2 if i == 0 and b - vb >= 8 and b - vb != 11 else 0 for i, b in enumerate(split)]
+            assert [p.pass_config(i)["wave"] for i in range(p.num_passes)] == want, split
+    for (dtype, n), (bits, wave) in {
+            ("f32", 16): ([9, 7], [0, 0]), ("f32", 18): ([11, 7], [2, 0]),
+            ("f32", 19): ([12, 7], [2, 0]), ("f32", 20): ([13, 7], [0, 0]),
+            ("f64", 15): ([7, 8], [0, 0]), ("f64", 18): ([10, 8], [2, 0]),
+            ("f64", 20): ([12, 8], [0, 0]), ("f64", 24): ([14, 10], [2, 0])}.items():
         p = qse.Plan(n, dtype)
         assert p.pass_bits == bits, (dtype, n)
-        assert [p.pass_config(i)["wave"] for i in range(2)] == [0, 0]
+        assert [p.pass_config(i)["wave"] for i in range(2)] == wave, (dtype, n)
 
 
 def test_mfma_path_plans(lib):

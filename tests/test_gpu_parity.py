@@ -20,7 +20,8 @@ import pytest
 import oracle
 import quantum_state_encoding_amd as qse
 import workloads
-from plan_cases import FORCED_SPLITS, LDS_SINGLE_CASES, PIPE_CASES, VARIANTS, WAVE_CASES
+from plan_cases import (FORCED_SPLITS, LDS_SINGLE_CASES, LX_CASES, PIPE_CASES, VARIANTS,
+                        WAVE_CASES)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -178,6 +179,27 @@ def test_integer_wave_tile_kernels(dtype, n, split, eb, gbits, wave, batch):
         assert plan.pass_config(i)["wave"] == wv
     re = ints((batch, 1 << n), 97_000 + n, npd)
     im = ints((batch, 1 << n), 98_000 + n, npd)
+    gre, gim = run(plan, re, im, False)
+    assert_exact(gre, re, n, False)
+    assert_exact(gim, im, n, False)
+    if n % 2 == 0:
+        gre, gim = run(plan, re, im, True)
+        assert_exact(gre, re, n, True)
+        assert_exact(gim, im, n, True)
+
+
+@pytest.mark.parametrize("dtype,n,split,eb,wave,batch", LX_CASES)
+def test_integer_lane_exchange_kernels(dtype, n, split, eb, wave, batch):
+    """The lane-exchange row kernel: register and lane stages, one LDS
+    exchange of the wave bits, exactly against the oracle, unnormalised and
+    normalised."""
+    say("lx %s n=%d split=%s eb=%s wave=%s batch=%d" % (dtype, n, split, eb, wave, batch))
+    npd = np.float32 if dtype == "f32" else np.float64
+    plan = qse.Plan(n, dtype, split=split, eb=eb, wave=wave)
+    for i, wv in enumerate(wave):
+        assert plan.pass_config(i)["wave"] == wv
+    re = ints((batch, 1 << n), 99_000 + n, npd)
+    im = ints((batch, 1 << n), 99_500 + n, npd)
     gre, gim = run(plan, re, im, False)
     assert_exact(gre, re, n, False)
     assert_exact(gim, im, n, False)
