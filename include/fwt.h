@@ -109,7 +109,9 @@ typedef struct {
                     pass (0..4; 0 or -1 for the first pass) */
     int phases;  /* log2 of the phases a column pass splits each LDS exchange
                     into (0..2, at most gbits; column passes of >= 9 bits and
-                    >= 8 groups only) */
+                    >= 8 groups only); for the lane-exchange kernel
+                    (wave = 2), 0 or 1, where 1 needs w < eb and halves the
+                    tile's LDS */
     int pipe;    /* 1: persistent software-pipelined kernel (tiles of >= 2^11
                     16-byte vectors in workgroups of <= 512 threads); 0: one
                     workgroup per tile group; default: pipelined when one
@@ -123,7 +125,9 @@ typedef struct {
                     2 <= eb <= 5 or eb = w = 1, and ceil(w / eb) LDS
                     exchanges move the wave bits into registers; default
                     eb gives w = min(4, row bits - 8), or 1 below 10 row
-                    bits); 0: LDS tiles.  Default, when every field of the
+                    bits, except eb = 4 with 2 exchange phases for the
+                    13-row-bit row pass of a multi-pass plan); 0: LDS
+                    tiles.  Default, when every field of the
                     entry is -1: the wave-tile kernel for a one-pass plan
                     with 3 <= n <= 10; else the lane-exchange kernel for a
                     row pass of 8..13 row bits, except the row pass of a

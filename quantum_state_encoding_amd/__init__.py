@@ -201,7 +201,8 @@ class Plan:
         if c["kind"] == "mfma":
             return "mfma_row_kernel<%s, %d>" % (t, c["bits"])
         if c["wave"] == 2:
-            return "lx_kernel<%s, %d, %d, %d>" % (t, c["kr"], c["eb"], c["kr"] - 6 - c["eb"])
+            return "lx_kernel<%s, %d, %d, %d, %d>" % (t, c["kr"], c["eb"], c["kr"] - 6 - c["eb"],
+                                                       c["phase_bits"])
         if c["wave"]:
             return "wave_kernel<%s, %d, %d, %d, %s>" % (
                 t, c["kr"], c["eb"], c["gbits"], "true" if c["kind"] == "row" else "false")

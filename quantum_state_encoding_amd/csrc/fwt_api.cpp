@@ -145,7 +145,7 @@ bool phases_allowed(int kr, int eb, int gbits, int phb)
 int build_wave_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool row,
                     const fwt_pass_tuning& t);
 int build_lx_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool row,
-                  const fwt_pass_tuning& t);
+                  const fwt_pass_tuning& t, bool multipass);
 
 int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tuning& t,
                bool multipass)
@@ -165,7 +165,8 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
         if (k < vb)
             return FWT_EINVAL;
         kr = k - vb;
-        if (kr > kRowKrMax || gbits_req > 0 || phb_req > 0)
+        // exchange phases of a row pass: the lane-exchange kernel only
+        if (kr > kRowKrMax || gbits_req > 0 || (phb_req > 0 && t.wave != 2))
             return FWT_EINVAL;
     } else {
         if (lo < vb)
@@ -179,7 +180,7 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
     if (t.wave == 1)
         return build_wave_pass(p, n, dtype, lo, k, kr, row, t);
     if (t.wave == 2)
-        return build_lx_pass(p, n, dtype, lo, k, kr, row, t);
+        return build_lx_pass(p, n, dtype, lo, k, kr, row, t, multipass);
     // One-pass plans of 3 <= n <= 10 default to the wave-tile kernel: on
     // 512 MiB states it ran at 6.0 TB/s against 5.0-5.4 for the LDS tiles
     // (both dtypes), and on cache-resident batches 2-12 % faster.  From 11
@@ -205,7 +206,7 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
     // and stay on the LDS tiles.
     if (all_default && row && kr >= kLxDefaultMin && kr <= kRowKrMax &&
         !(multipass && kr == 11)) {
-        const int rc = build_lx_pass(p, n, dtype, lo, k, kr, row, t);
+        const int rc = build_lx_pass(p, n, dtype, lo, k, kr, row, t, multipass);
         if (rc == FWT_OK)
             return rc;
         p = Pass{};
@@ -381,26 +382,36 @@ int build_wave_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool
 // with 1 <= W <= 4 and 2 <= eb <= 5 (or eb = W = 1): lane stages for the 6
 // lowest row bits and ceil(W / eb) LDS exchanges.  Default: the most threads
 // with eb >= 2, W = min(4, kr - 8), and W = 1 below 10 row bits (measured:
-// best, or within 4 % of the best variant, at every n and batch tried).
+// best, or within 4 % of the best variant, at every n and batch tried);
+// except the row pass of a multi-pass plan with a 128 KiB tile (kr = 13,
+// fp64 n = 22..24): W = 3, eb = 4, one exchange in two phases through 64 KiB
+// of LDS, so that two tiles share a CU (3.3 % faster there).
 int build_lx_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool row,
-                  const fwt_pass_tuning& t)
+                  const fwt_pass_tuning& t, bool multipass)
 {
     const int vb = vec_bits(dtype);
-    if (!row || t.gbits > 0 || t.phases > 0 || t.pipe > 0)
+    if (!row || t.gbits > 0 || t.phases > 1 || t.pipe > 0)
         return FWT_EINVAL;
-    const int eb = t.eb >= 0 ? t.eb : kr - 6 - (kr >= 10 ? (kr - 8 < 4 ? kr - 8 : 4) : 1);
+    const bool two_tiles = multipass && kr == 13;
+    const int eb = t.eb >= 0 ? t.eb
+                             : (two_tiles ? 4 : kr - 6 - (kr >= 10 ? (kr - 8 < 4 ? kr - 8 : 4) : 1));
     const int w = kr - 6 - eb;
     if (w < 1 || w > 4 || eb > 5 || eb < 1 || (eb == 1 && w != 1))
         return FWT_EINVAL;
-    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, 0, 0, 1, 0, 2};
+    // Two exchange phases need one exchange (w < eb) whose top register bit
+    // stays put.
+    const int phb = t.phases >= 0 ? t.phases : (two_tiles && w < eb ? 1 : 0);
+    if (phb && w >= eb)
+        return FWT_EINVAL;
+    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, 0, phb, 1, 0, 2};
     if (!qse::kernel_available(p.key))
         return FWT_EUNSUPPORTED;
     p.gbits = 0;
-    p.phb = 0;
+    p.phb = phb;
     p.tt_bits = 6 + w;
     p.tpw_bits = 0;
     p.block = 64u << w;
-    p.lds = (size_t)16 << kr;
+    p.lds = (size_t)16 << (kr - phb);
     p.store_back = 0;
     p.tiles_bits = n - k;
     return check_offsets(p, dtype, row, kr, vb);

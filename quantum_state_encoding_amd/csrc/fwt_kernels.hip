@@ -598,6 +598,12 @@ __global__ void __launch_bounds__(256)
 // exchanges in all.  The lanes of a wave always touch 64 consecutive
 // 16-byte slots (in LDS and in memory), so the exchanges need no padding
 // and every global access of a wave covers 1 KiB.
+//
+// With PHB > 0 (one exchange, W < EB) the exchange runs in 2^PHB phases:
+// the top PHB register bits do not move, they are the top row bits in both
+// layouts, so phase ph moves the registers whose top bits are ph through
+// an LDS region 2^PHB times smaller than the tile, and two tiles of 128 KiB
+// fit one CU.
 
 // Row bit held by wave bit i (register bit i when REG) after X exchanges.
 template <int W, int EB>
@@ -639,33 +645,39 @@ __device__ __forceinline__ uint32_t lx_thread_part(int lane, int wave)
 
 // Exchanges X + 1 .. NX: move the next wave bits into the low register
 // bits through LDS, then their stages.
-template <typename V, int W, int EB, int X, int NX>
+template <typename V, int KR, int W, int EB, int PHB, int X, int NX>
 struct LxRounds {
     __device__ __forceinline__ static void run(V* x, V* L, int lane, int wave)
     {
         constexpr int E = 1 << EB;
         constexpr int C = W - X * EB < EB ? W - X * EB : EB;   // wave bits moved
+        constexpr int EP = E >> PHB;                           // registers per phase
+        constexpr uint32_t MASK = (1u << (KR - PHB)) - 1;      // slot within a phase
+        static_assert(PHB == 0 || (NX == 1 && EB - C >= PHB), "phases keep their bits");
         const uint32_t from = lx_thread_part<W, EB, X>(lane, wave);
         const uint32_t to = lx_thread_part<W, EB, X + 1>(lane, wave);
-        if (X > 0)
-            __syncthreads();   // the previous exchange's reads are done
 #pragma unroll
-        for (int j = 0; j < E; ++j)
-            L[from + lx_reg_part<W, EB, X>(j)] = x[j];
-        __syncthreads();
+        for (int ph = 0; ph < (1 << PHB); ++ph) {
+            if (X > 0 || ph > 0)
+                __syncthreads();   // the previous reads of this region are done
 #pragma unroll
-        for (int j = 0; j < E; ++j)
-            x[j] = L[to + lx_reg_part<W, EB, X + 1>(j)];
+            for (int j = ph * EP; j < (ph + 1) * EP; ++j)
+                L[(from + lx_reg_part<W, EB, X>(j)) & MASK] = x[j];
+            __syncthreads();
+#pragma unroll
+            for (int j = ph * EP; j < (ph + 1) * EP; ++j)
+                x[j] = L[(to + lx_reg_part<W, EB, X + 1>(j)) & MASK];
+        }
         register_stages<C, E>(x);
-        LxRounds<V, W, EB, X + 1, NX>::run(x, L, lane, wave);
+        LxRounds<V, KR, W, EB, PHB, X + 1, NX>::run(x, L, lane, wave);
     }
 };
-template <typename V, int W, int EB, int NX>
-struct LxRounds<V, W, EB, NX, NX> {
+template <typename V, int KR, int W, int EB, int PHB, int NX>
+struct LxRounds<V, KR, W, EB, PHB, NX, NX> {
     __device__ __forceinline__ static void run(V*, V*, int, int) {}
 };
 
-template <typename T, int KR, int EB, int W>
+template <typename T, int KR, int EB, int W, int PHB>
 __global__ void __launch_bounds__(64 << W)
     lx_kernel(T* __restrict__ re, T* __restrict__ im, TileArgs a)
 {
@@ -700,7 +712,7 @@ __global__ void __launch_bounds__(64 << W)
         in_vector(x[j]);
     register_stages<EB, E>(x);
     LaneStages<0, 6, 0, E, V, T>::run(x, lane);
-    LxRounds<V, W, EB, 0, NX>::run(x, L, lane, wave);
+    LxRounds<V, KR, W, EB, PHB, 0, NX>::run(x, L, lane, wave);
     if (a.do_scale) {
         const T c = (T)a.scale;
 #pragma unroll
@@ -857,14 +869,18 @@ struct RegisterWave {
 };
 
 // Lane-exchange row tiles: W in [1, 4] with EB = KR - 6 - W in [2, 5], or
-// EB = W = 1.
+// EB = W = 1; tiles of 2^11+ slots with W < EB also in two phases.
 template <typename T, int KR, int W>
 void add_lx(std::vector<Entry>& v)
 {
     constexpr int EB = KR - 6 - W;
-    if constexpr (W >= 1 && W <= 4 && ((EB >= 2 && EB <= 5) || (EB == 1 && W == 1)))
+    if constexpr (W >= 1 && W <= 4 && ((EB >= 2 && EB <= 5) || (EB == 1 && W == 1))) {
         v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, 0, 0, 1, 0, 2},
-                     reinterpret_cast<const void*>(&lx_kernel<T, KR, EB, W>)});
+                     reinterpret_cast<const void*>(&lx_kernel<T, KR, EB, W, 0>)});
+        if constexpr (KR >= 11 && W < EB)
+            v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, 0, 1, 1, 0, 2},
+                         reinterpret_cast<const void*>(&lx_kernel<T, KR, EB, W, 1>)});
+    }
 }
 
 template <typename T, int KR, int KRMIN>

@@ -80,3 +80,17 @@ def _lx_cases():
             ("f32", 20, (13, 7), (2, -1), (2, 0), 2), ("f32", 15, (15,), (3,), (2,), 33)]
     return out
 LX_CASES = _lx_cases()
+
+# (dtype, n, split, eb, batch): the lane-exchange kernel with its single
+# exchange in two phases (half the LDS), every compiled variant
+def _lx_phase_cases():
+    out = []
+    for dtype, vb in (("f32", 2), ("f64", 1)):
+        for kr in range(11, 14):
+            for w in (1, 2, 3, 4):
+                eb = kr - 6 - w
+                if 2 <= eb <= 5 and w < eb:
+                    out.append((dtype, kr + vb, (kr + vb,), (eb,), 3))
+    out += [("f64", 24, (14, 10), (4, -1), 1), ("f32", 20, (13, 7), (4, -1), 2)]
+    return out
+LX_PHASE_CASES = _lx_phase_cases()

@@ -209,8 +209,8 @@ def test_tuned_fuzz_never_crashes():
 def test_every_gpu_test_plan_is_valid(lib):
     """Each plan the GPU parity suite builds is accepted by the planner and
     has the forced properties (caught here, on the CPU)."""
-    from plan_cases import (FORCED_SPLITS, LDS_SINGLE_CASES, LX_CASES, PIPE_CASES, VARIANTS,
-                            WAVE_CASES)
+    from plan_cases import (FORCED_SPLITS, LDS_SINGLE_CASES, LX_CASES, LX_PHASE_CASES,
+                            PIPE_CASES, VARIANTS, WAVE_CASES)
     for dtype, n in LDS_SINGLE_CASES:
         assert qse.Plan(n, dtype, split=(n,), wave=(0,)).pass_config(0)["wave"] == 0
     for dtype, n, split in FORCED_SPLITS:
@@ -229,6 +229,11 @@ def test_every_gpu_test_plan_is_valid(lib):
         p = qse.Plan(n, dtype, split=split, eb=eb, wave=wave)
         assert [p.pass_config(i)["wave"] for i in range(p.num_passes)] == list(wave)
     assert len(LX_CASES) == 38   # all 28 compiled variants appear
+    for dtype, n, split, eb, batch in LX_PHASE_CASES:
+        p = qse.Plan(n, dtype, split=split, eb=eb, phases=(1,) + (-1,) * (len(split) - 1),
+                     wave=(2,) + (-1,) * (len(split) - 1))
+        assert (p.pass_config(0)["wave"], p.pass_config(0)["phase_bits"]) == (2, 1)
+    assert len(LX_PHASE_CASES) == 14   # all 12 compiled phased variants appear
 
 
 def test_lane_exchange_plans(lib):
@@ -241,7 +246,7 @@ def test_lane_exchange_plans(lib):
             w = kr - 6 - c["eb"]
             assert w == (min(4, kr - 8) if kr >= 10 else 1)
             assert c["block"] == 64 << w and c["lds"] == 16 << kr and c["tpw_bits"] == 0
-            assert p.kernel_name(0) == "lx_kernel<%s, %d, %d, %d>" % (
+            assert p.kernel_name(0) == "lx_kernel<%s, %d, %d, %d, 0>" % (
                 "float" if dtype == "f32" else "double", kr, c["eb"], w)
         kr = 10
         n = kr + vb
@@ -253,6 +258,14 @@ def test_lane_exchange_plans(lib):
         assert _split(lib, n, vb == 1, [n], gbits=[1], wave=[2]) == qse.FWT_EINVAL
         assert _split(lib, n + 7, vb == 1, [n, 7], wave=[0, 2]) == qse.FWT_EINVAL  # column pass
     assert _split(lib, 9, 0, [9], wave=[2]) == qse.FWT_EINVAL     # 7 row bits: no wave bit
+    # two exchange phases: one exchange with w < eb, half the LDS
+    p = qse.Plan(24, "f64", split=(14, 10), eb=(4, -1), phases=(1, -1), wave=(2, -1))
+    c = p.pass_config(0)
+    assert (c["wave"], c["phase_bits"], c["lds"], c["block"]) == (2, 1, 64 << 10, 512)
+    assert p.kernel_name(0) == "lx_kernel<double, 13, 4, 3, 1>"
+    assert _split(lib, 15, 0, [15], eb=[3], phases=[1], wave=[2]) == qse.FWT_EINVAL  # w = eb
+    assert _split(lib, 15, 0, [15], eb=[4], phases=[2], wave=[2]) == qse.FWT_EINVAL
+    assert _split(lib, 12, 0, [12], eb=[3], phases=[1], wave=[2]) == qse.FWT_EUNSUPPORTED  # kr 10
 
 
 def test_default_kernel_choice(lib):
@@ -279,6 +292,11 @@ def test_default_kernel_choice(lib):
         p = qse.Plan(n, dtype)
         assert p.pass_bits == bits, (dtype, n)
         assert [p.pass_config(i)["wave"] for i in range(2)] == wave, (dtype, n)
+    # the 14-bit fp64 row pass of a two-pass plan: one exchange in two phases
+    for n in (22, 23, 24):
+        assert qse.Plan(n, "f64").kernel_name(0) == "lx_kernel<double, 13, 4, 3, 1>"
+    assert qse.Plan(14, "f64").kernel_name(0) == "lx_kernel<double, 13, 3, 4, 0>"
+    assert qse.Plan(15, "f32").kernel_name(0) == "lx_kernel<float, 13, 3, 4, 0>"
 
 
 def test_mfma_path_plans(lib):

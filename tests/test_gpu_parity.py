@@ -20,8 +20,8 @@ import pytest
 import oracle
 import quantum_state_encoding_amd as qse
 import workloads
-from plan_cases import (FORCED_SPLITS, LDS_SINGLE_CASES, LX_CASES, PIPE_CASES, VARIANTS,
-                        WAVE_CASES)
+from plan_cases import (FORCED_SPLITS, LDS_SINGLE_CASES, LX_CASES, LX_PHASE_CASES, PIPE_CASES,
+                        VARIANTS, WAVE_CASES)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -200,6 +200,26 @@ def test_integer_lane_exchange_kernels(dtype, n, split, eb, wave, batch):
         assert plan.pass_config(i)["wave"] == wv
     re = ints((batch, 1 << n), 99_000 + n, npd)
     im = ints((batch, 1 << n), 99_500 + n, npd)
+    gre, gim = run(plan, re, im, False)
+    assert_exact(gre, re, n, False)
+    assert_exact(gim, im, n, False)
+    if n % 2 == 0:
+        gre, gim = run(plan, re, im, True)
+        assert_exact(gre, re, n, True)
+        assert_exact(gim, im, n, True)
+
+
+@pytest.mark.parametrize("dtype,n,split,eb,batch", LX_PHASE_CASES)
+def test_integer_lane_exchange_phases(dtype, n, split, eb, batch):
+    """The lane-exchange kernel with its exchange in two phases through
+    half the LDS, exactly against the oracle."""
+    say("lx phases %s n=%d split=%s eb=%s batch=%d" % (dtype, n, split, eb, batch))
+    npd = np.float32 if dtype == "f32" else np.float64
+    rest = (-1,) * (len(split) - 1)
+    plan = qse.Plan(n, dtype, split=split, eb=eb, phases=(1,) + rest, wave=(2,) + rest)
+    assert plan.pass_config(0)["phase_bits"] == 1
+    re = ints((batch, 1 << n), 99_700 + n, npd)
+    im = ints((batch, 1 << n), 99_800 + n, npd)
     gre, gim = run(plan, re, im, False)
     assert_exact(gre, re, n, False)
     assert_exact(gim, im, n, False)
