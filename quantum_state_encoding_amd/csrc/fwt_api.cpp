@@ -41,6 +41,8 @@ int mfma_row_max(fwt_dtype dtype) { return dtype == FWT_F64 ? 14 : 15; }
 constexpr int kRowKrMax = 13;          // rows bits of a row pass (vectors)
 constexpr int kLxDefaultMin = 8;       // lane-exchange kernel by default from here
 constexpr int kColKrMax = 12;          // rows bits of a column pass
+constexpr int kColPref = 9;            // column factor of the default two-pass split
+constexpr int kColTwoPassMax = 11;     // widest column factor of a default two-pass plan
 constexpr size_t kLdsMax = 160 * 1024; // per workgroup on gfx950
 constexpr size_t kPhaseLdsTarget = 68 * 1024;  // two tiles per CU
 constexpr size_t kChunkBytes = (size_t)256 << 20;  // Infinity Cache capacity
@@ -417,12 +419,16 @@ int build_lx_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool r
     return check_offsets(p, dtype, row, kr, vb);
 }
 
-// Default Kronecker split (bit counts, lowest bits first), from sweeps on
-// MI355X:
+// Default Kronecker split (bit counts, lowest bits first), from sweeps of
+// every two-pass split on MI355X (2 GiB states, n = 15..26):
 //  - one pass while a vector fits one tile: n <= 15 (fp32), 14 (fp64);
-//  - two passes up to n = 24: a column factor of 7 (fp32) / 8 (fp64) bits
-//    (col tiles of 128 rows x 256 B / 256 rows x 128 B), the rest in the
-//    contiguous row pass, which takes at most 13 (fp32) / 14 (fp64) bits;
+//  - two passes while the column factor stays within 11 bits: the row pass
+//    takes n - 9 bits (a 9-bit column factor: tiles of 512 rows x 128 B),
+//    but at least 8 vector bits (its lane-exchange tile of 8 vector bits
+//    was the fastest row pass for n = 15..19), never exactly 9 vector bits
+//    (10 measured faster there: n = 20 fp32 as 12|8, n = 19 fp64 as 11|8),
+//    and at most what one tile holds (15 fp32, 14 fp64 bits), the column
+//    factor taking the rest (10-11 bits at n = 25-26 fp32, 24-25 fp64);
 //  - three passes above: 10 row bits, the rest split evenly.
 int default_split(int n, fwt_dtype dtype, fwt_path path, int* bits)
 {
@@ -444,11 +450,16 @@ int default_split(int n, fwt_dtype dtype, fwt_path path, int* bits)
         bits[0] = n - bits[1];
         return 2;
     }
-    if (n <= 24) {
-        const int row_max = dtype == FWT_F64 ? 14 : 13;
-        const int col_pref = dtype == FWT_F64 ? 8 : 7;
-        bits[1] = n - row_max > col_pref ? n - row_max : col_pref;
-        bits[0] = n - bits[1];
+    if (n - single_max <= kColTwoPassMax) {
+        int row = n - kColPref;
+        if (row - vb < 8)
+            row = 8 + vb;
+        if (row - vb == 9)
+            row = 10 + vb;
+        if (row > single_max)
+            row = single_max;
+        bits[0] = row;
+        bits[1] = n - row;
         return 2;
     }
     const int rest = n - 10;

@@ -75,10 +75,22 @@ def test_plan_shapes_of_the_workloads(lib):
     assert qse.Plan(12, "f32").pass_bits == [12]
     assert qse.Plan(14, "f32").pass_bits == [14]
     assert qse.Plan(14, "f32", split=(7, 7)).pass_bits == [7, 7]
-    assert qse.Plan(20, "f32").pass_bits == [13, 7]
+    assert qse.Plan(20, "f32").pass_bits == [12, 8]
     assert qse.Plan(24, "f64").pass_bits == [14, 10]
-    assert qse.Plan(24, "f32").pass_bits == [13, 11]
-    assert qse.Plan(25, "f32").pass_bits == [10, 8, 7]
+
+
+def test_default_splits(lib):
+    # two passes: a 9-bit column factor, a row pass of >= 8 vector bits (not
+    # 9) and at most one tile; column factors up to 11 bits; then 3 passes
+    want = {"f32": {16: [10, 6], 17: [10, 7], 18: [10, 8], 19: [10, 9], 20: [12, 8],
+                    21: [12, 9], 22: [13, 9], 23: [14, 9], 24: [15, 9], 25: [15, 10],
+                    26: [15, 11], 27: [10, 9, 8], 30: [10, 10, 10]},
+            "f64": {15: [9, 6], 18: [9, 9], 19: [11, 8], 20: [11, 9], 21: [12, 9],
+                    22: [13, 9], 23: [14, 9], 24: [14, 10], 25: [14, 11], 26: [10, 8, 8],
+                    29: [10, 10, 9]}}
+    for dtype, table in want.items():
+        for n, bits in table.items():
+            assert qse.Plan(n, dtype).pass_bits == bits, (dtype, n)
 
 
 def test_chunk_schedule(lib):
@@ -285,16 +297,18 @@ def test_default_kernel_choice(lib):
             want = [2 if i == 0 and b - vb >= 8 and b - vb != 11 else 0 for i, b in enumerate(split)]
             assert [p.pass_config(i)["wave"] for i in range(p.num_passes)] == want, split
     for (dtype, n), (bits, wave) in {
-            ("f32", 16): ([9, 7], [0, 0]), ("f32", 18): ([11, 7], [2, 0]),
-            ("f32", 19): ([12, 7], [2, 0]), ("f32", 20): ([13, 7], [0, 0]),
-            ("f64", 15): ([7, 8], [0, 0]), ("f64", 18): ([10, 8], [2, 0]),
-            ("f64", 20): ([12, 8], [0, 0]), ("f64", 24): ([14, 10], [2, 0])}.items():
+            ("f32", 16): ([10, 6], [2, 0]), ("f32", 19): ([10, 9], [2, 0]),
+            ("f32", 20): ([12, 8], [2, 0]), ("f32", 22): ([13, 9], [0, 0]),
+            ("f64", 15): ([9, 6], [2, 0]), ("f64", 19): ([11, 8], [2, 0]),
+            ("f64", 21): ([12, 9], [0, 0]), ("f64", 24): ([14, 10], [2, 0])}.items():
         p = qse.Plan(n, dtype)
         assert p.pass_bits == bits, (dtype, n)
         assert [p.pass_config(i)["wave"] for i in range(2)] == wave, (dtype, n)
-    # the 14-bit fp64 row pass of a two-pass plan: one exchange in two phases
-    for n in (22, 23, 24):
+    # a 13-vector-bit row pass of a two-pass plan: one exchange in two phases
+    for n in (23, 24, 25):
         assert qse.Plan(n, "f64").kernel_name(0) == "lx_kernel<double, 13, 4, 3, 1>"
+    for n in (24, 25, 26):
+        assert qse.Plan(n, "f32").kernel_name(0) == "lx_kernel<float, 13, 4, 3, 1>"
     assert qse.Plan(14, "f64").kernel_name(0) == "lx_kernel<double, 13, 3, 4, 0>"
     assert qse.Plan(15, "f32").kernel_name(0) == "lx_kernel<float, 13, 3, 4, 0>"
 
@@ -303,8 +317,8 @@ def test_mfma_path_plans(lib):
     """FWT_PATH_MFMA_ABLATION: AUTO's split, with the row pass on the
     matrix-core kernel."""
     for dtype, n, bits in (("f32", 8, [8]), ("f32", 12, [12]), ("f32", 15, [15]), ("f64", 14, [14]),
-                           ("f32", 20, [13, 7]), ("f64", 24, [14, 10]), ("f32", 26, [10, 8, 8]),
-                           ("f64", 29, [10, 10, 9])):
+                           ("f32", 20, [12, 8]), ("f64", 24, [14, 10]), ("f32", 26, [15, 11]),
+                           ("f32", 27, [10, 9, 8]), ("f64", 29, [10, 10, 9])):
         p = qse.Plan(n, dtype, path=qse.PATH_MFMA_ABLATION)
         assert p.pass_bits == bits, (dtype, n)
         assert p.pass_config(0)["kind"] == "mfma"

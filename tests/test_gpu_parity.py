@@ -314,18 +314,20 @@ def test_full_size_n24_b16_f64():
     _full_size("n24_b16_f64", samples=(0, 9, 15))
 
 
-@pytest.mark.parametrize("dtype,n", [("f32", 25), ("f32", 27), ("f64", 25), ("f64", 26)])
-def test_three_pass_default_plans(dtype, n):
-    """The default three-pass plans (n > 24) at their real size, one vector,
-    inputs in {-1, 0, 1}: every partial sum stays an exact integer far below
-    2^24, so the result is exact; compared whole with the oracle."""
-    say("three-pass %s n=%d" % (dtype, n))
+@pytest.mark.parametrize("dtype,n,passes", [("f32", 24, 2), ("f32", 25, 2), ("f32", 26, 2),
+                                            ("f32", 27, 3), ("f64", 25, 2), ("f64", 26, 3)])
+def test_wide_default_plans(dtype, n, passes):
+    """The default plans above n = 23 at their real size (two passes with
+    10- and 11-bit column factors, then three), one vector, inputs in
+    {-1, 0, 1}: every partial sum stays an exact integer far below 2^24, so
+    the result is exact; compared whole with the oracle."""
+    say("wide default plan %s n=%d" % (dtype, n))
     npd = np.float32 if dtype == "f32" else np.float64
     rng = np.random.default_rng(77_000 + n)
     re = rng.integers(-1, 2, size=(1, 1 << n)).astype(npd)
     im = rng.integers(-1, 2, size=(1, 1 << n)).astype(npd)
     plan = qse.Plan(n, dtype)
-    assert plan.num_passes == 3
+    assert plan.num_passes == passes
     gre, gim = run(plan, re, im, False)
     assert_exact(gre, re, n, False)
     assert_exact(gim, im, n, False)
