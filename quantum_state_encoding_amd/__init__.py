@@ -201,8 +201,10 @@ class Plan:
         if c["kind"] == "mfma":
             return "mfma_row_kernel<%s, %d>" % (t, c["bits"])
         if c["wave"] == 2:
-            return "lx_kernel<%s, %d, %d, %d, %d>" % (t, c["kr"], c["eb"], c["kr"] - 6 - c["eb"],
-                                                       c["phase_bits"])
+            w = c["kr"] - (6 - c["gbits"]) - c["eb"]
+            return "lx_kernel<%s, %d, %d, %d, %d, %d, %s>" % (
+                t, c["kr"], c["eb"], w, c["phase_bits"], c["gbits"],
+                "true" if c["kind"] == "row" else "false")
         if c["wave"]:
             return "wave_kernel<%s, %d, %d, %d, %s>" % (
                 t, c["kr"], c["eb"], c["gbits"], "true" if c["kind"] == "row" else "false")

@@ -215,6 +215,18 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
         p.lo = lo;
         p.k = k;
     }
+    // Column passes of 8..10 bits with rows of at least 8 groups default to
+    // it as well: measured 0.2-5.5 % faster per call (fp32 n = 19..25, fp64
+    // n = 23..24; the n = 24 fp64 workload 2.9 %), and within 0.4 % at fp64
+    // n = 20.
+    if (all_default && !row && kr >= 8 && kr <= 10 && lo - vec_bits(dtype) >= 3) {
+        const int rc = build_lx_pass(p, n, dtype, lo, k, kr, row, t, multipass);
+        if (rc == FWT_OK)
+            return rc;
+        p = Pass{};
+        p.lo = lo;
+        p.k = k;
+    }
     const int eb = eb_req < 0 ? default_eb(kr, dtype, multipass, row) : eb_req;
     // A round of LDS tiles butterflies eb register bits, so a tile with row
     // bits needs eb >= 1 (rounds_of divides by eb).
@@ -379,43 +391,73 @@ int build_wave_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool
     return check_offsets(p, dtype, row, kr, vb);
 }
 
-// A row pass in the lane-exchange kernel: a tile of 2^kr 16-byte vectors in
-// a workgroup of 2^(6 + W) threads holding 2^eb vectors each, kr = eb + 6 + W
-// with 1 <= W <= 4 and 2 <= eb <= 5 (or eb = W = 1): lane stages for the 6
-// lowest row bits and ceil(W / eb) LDS exchanges.  Default: the most threads
-// with eb >= 2, W = min(4, kr - 8), and W = 1 below 10 row bits (measured:
-// best, or within 4 % of the best variant, at every n and batch tried);
-// except the row pass of a multi-pass plan with a 128 KiB tile (kr = 13,
-// fp64 n = 22..24): W = 3, eb = 4, one exchange in two phases through 64 KiB
-// of LDS, so that two tiles share a CU (3.3 % faster there).
+// A pass in the lane-exchange kernel.  Row pass: a tile of 2^kr 16-byte
+// vectors in a workgroup of 2^(6 + W) threads holding 2^eb vectors each,
+// kr = eb + 6 + W, with 1 <= W <= 4 and 2 <= eb <= 5 (or eb = W = 1): lane
+// stages for the 6 lowest row bits and ceil(W / eb) LDS exchanges.
+// Default: the most threads with eb >= 2, W = min(4, kr - 8), and W = 1
+// below 10 row bits (measured: best, or within 4 % of the best variant, at
+// every n and batch tried); except the row pass of a multi-pass plan with a
+// 128 KiB tile (kr = 13, fp64 n = 22..24): W = 3, eb = 4, one exchange in
+// two phases through 64 KiB of LDS, so that two tiles share a CU (3.3 %
+// faster there).  Column pass: 2^kr rows x 2^gbits 16-byte groups (gbits 3
+// or 4: 128- or 256-byte row segments); lanes hold the groups and 6 - gbits
+// row bits, kr = eb + (6 - gbits) + W.  Default (measured best for 7..10
+// column bits): 16 groups while the tile fits 128 KiB of LDS, else 8;
+// eb = 4 (W = 2 or 3); one exchange in two phases, so that a tile takes
+// 64 KiB of LDS (32 KiB at 8 row bits) and two or more share a CU.
 int build_lx_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool row,
                   const fwt_pass_tuning& t, bool multipass)
 {
     const int vb = vec_bits(dtype);
-    if (!row || t.gbits > 0 || t.phases > 1 || t.pipe > 0)
+    if (t.phases > 1 || t.pipe > 0)
         return FWT_EINVAL;
-    const bool two_tiles = multipass && kr == 13;
-    const int eb = t.eb >= 0 ? t.eb
-                             : (two_tiles ? 4 : kr - 6 - (kr >= 10 ? (kr - 8 < 4 ? kr - 8 : 4) : 1));
-    const int w = kr - 6 - eb;
+    int gbits = 0;
+    if (row) {
+        if (t.gbits > 0)
+            return FWT_EINVAL;
+    } else {
+        const int gmax_cols = lo - vb;   // log2 16-byte groups in a row
+        gbits = t.gbits >= 0 ? t.gbits : (kr + 4 <= 13 && gmax_cols >= 4 ? 4 : 3);
+        if (gbits < 3 || gbits > 4 || gbits > gmax_cols)
+            return FWT_EINVAL;
+        p.nblk_bits = gmax_cols - gbits;
+    }
+    const int lr = 6 - gbits;   // row bits held by lanes
+    const bool two_tiles = row && multipass && kr == 13;
+    int eb;
+    if (t.eb >= 0)
+        eb = t.eb;
+    else if (two_tiles)
+        eb = 4;
+    else if (row)
+        eb = kr - 6 - (kr >= 10 ? (kr - 8 < 4 ? kr - 8 : 4) : 1);
+    else
+        eb = kr - lr - 1 < 4 ? kr - lr - 1 : 4;
+    const int w = kr - lr - eb;
     if (w < 1 || w > 4 || eb > 5 || eb < 1 || (eb == 1 && w != 1))
         return FWT_EINVAL;
     // Two exchange phases need one exchange (w < eb) whose top register bit
     // stays put.
-    const int phb = t.phases >= 0 ? t.phases : (two_tiles && w < eb ? 1 : 0);
+    // Two phases by default for fp64-sized row tiles of two-pass plans and
+    // for column tiles of 2^11+ slots (compiled from there on), and where
+    // the tile would exceed 128 KiB of LDS.
+    const bool col_phased = !row && kr + gbits >= 11;
+    const int phb = t.phases >= 0 ? t.phases
+                                  : ((two_tiles || col_phased || kr + gbits > 13) && w < eb ? 1 : 0);
     if (phb && w >= eb)
         return FWT_EINVAL;
-    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, 0, phb, 1, 0, 2};
+    p.key = KernelKey{dtype == FWT_F64 ? 1 : 0, kr, eb, gbits, phb, row ? 1 : 0, 0, 2};
     if (!qse::kernel_available(p.key))
         return FWT_EUNSUPPORTED;
-    p.gbits = 0;
+    p.gbits = gbits;
     p.phb = phb;
     p.tt_bits = 6 + w;
     p.tpw_bits = 0;
     p.block = 64u << w;
-    p.lds = (size_t)16 << (kr - phb);
+    p.lds = (size_t)16 << (kr + gbits - phb);
     p.store_back = 0;
-    p.tiles_bits = n - k;
+    p.tiles_bits = row ? n - k : (n - lo - k) + p.nblk_bits;
     return check_offsets(p, dtype, row, kr, vb);
 }
 

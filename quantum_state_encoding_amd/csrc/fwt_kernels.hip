@@ -588,16 +588,19 @@ __global__ void __launch_bounds__(256)
 
 // ---- lane-exchange tiles: lane stages plus LDS exchanges of wave bits ---
 //
-// A row tile of 2^KR 16-byte vectors in one workgroup of 2^(6 + W) threads,
-// each holding E = 2^EB vectors, KR = EB + 6 + W.  Lanes always hold the 6
-// lowest row bits, whose stages cross lanes as in wave_kernel.  In the load
-// layout the W wave bits are row bits [6, 6 + W) and the register bits the
-// top EB row bits.  After the register, lane and in-vector stages, each
-// exchange through LDS swaps the next min(EB, bits left) wave bits with the
-// low register bits, whose stages then run in registers: ceil(W / EB)
-// exchanges in all.  The lanes of a wave always touch 64 consecutive
-// 16-byte slots (in LDS and in memory), so the exchanges need no padding
-// and every global access of a wave covers 1 KiB.
+// A tile of 2^KR rows x 2^GB 16-byte column groups (row passes: GB = 0, a
+// row is one 16-byte vector) in one workgroup of 2^(6 + W) threads, each
+// holding E = 2^EB vectors, KR = LR + W + EB with LR = 6 - GB.  A lane
+// holds column group lane mod 2^GB and the LR lowest row bits, whose stages
+// cross lanes as in wave_kernel.  In the load layout the W wave bits are
+// row bits [LR, LR + W) and the register bits the top EB row bits.  After
+// the register, lane and (row passes) in-vector stages, each exchange
+// through LDS swaps the next min(EB, bits left) wave bits with the low
+// register bits, whose stages then run in registers: ceil(W / EB)
+// exchanges in all.  Lane bits never move, so the lanes of a wave always
+// touch 64 consecutive 16-byte LDS slots (slot = row * 2^GB + group): the
+// exchanges need no padding.  In memory a wave covers 2^LR rows of 2^GB
+// consecutive 16-byte groups (1 KiB for row passes).
 //
 // With PHB > 0 (one exchange, W < EB) the exchange runs in 2^PHB phases:
 // the top PHB register bits do not move, they are the top row bits in both
@@ -606,11 +609,11 @@ __global__ void __launch_bounds__(256)
 // fit one CU.
 
 // Row bit held by wave bit i (register bit i when REG) after X exchanges.
-template <int W, int EB>
+template <int W, int EB, int LR>
 __host__ __device__ constexpr int lx_pos(int x, int i, bool reg)
 {
-    int wp[4] = {6, 7, 8, 9};
-    int rp[5] = {6 + W, 7 + W, 8 + W, 9 + W, 10 + W};
+    int wp[4] = {LR, LR + 1, LR + 2, LR + 3};
+    int rp[5] = {LR + W, LR + W + 1, LR + W + 2, LR + W + 3, LR + W + 4};
     for (int e = 0; e < x; ++e) {
         const int c = W - e * EB < EB ? W - e * EB : EB;
         for (int q = 0; q < c; ++q) {
@@ -622,70 +625,74 @@ __host__ __device__ constexpr int lx_pos(int x, int i, bool reg)
     return reg ? rp[i] : wp[i];
 }
 
-// Offset (in 16-byte slots) of register j in layout X: a compile-time
-// constant once j is unrolled.
-template <int W, int EB, int X>
-__device__ __forceinline__ constexpr uint32_t lx_reg_part(int j)
+// Row bits of register j in layout X: a compile-time constant once j is
+// unrolled.
+template <int W, int EB, int LR, int X>
+__device__ __forceinline__ constexpr uint32_t lx_reg_row(int j)
 {
     uint32_t r = 0;
     for (int i = 0; i < EB; ++i)
-        r |= (uint32_t)((j >> i) & 1) << lx_pos<W, EB>(X, i, true);
+        r |= (uint32_t)((j >> i) & 1) << lx_pos<W, EB, LR>(X, i, true);
     return r;
 }
 
-template <int W, int EB, int X>
-__device__ __forceinline__ uint32_t lx_thread_part(int lane, int wave)
+// Row bits held by the thread (lane row bits and wave bits) in layout X.
+template <int W, int EB, int LR, int X>
+__device__ __forceinline__ uint32_t lx_thread_row(int lane_row, int wave)
 {
-    uint32_t r = (uint32_t)lane;
+    uint32_t r = (uint32_t)lane_row;
 #pragma unroll
     for (int i = 0; i < W; ++i)
-        r |= (uint32_t)((wave >> i) & 1) << lx_pos<W, EB>(X, i, false);
+        r |= (uint32_t)((wave >> i) & 1) << lx_pos<W, EB, LR>(X, i, false);
     return r;
 }
 
 // Exchanges X + 1 .. NX: move the next wave bits into the low register
 // bits through LDS, then their stages.
-template <typename V, int KR, int W, int EB, int PHB, int X, int NX>
+template <typename V, int KR, int GB, int W, int EB, int PHB, int X, int NX>
 struct LxRounds {
-    __device__ __forceinline__ static void run(V* x, V* L, int lane, int wave)
+    __device__ __forceinline__ static void run(V* x, V* L, int lane_row, int g, int wave)
     {
+        constexpr int LR = 6 - GB;
         constexpr int E = 1 << EB;
         constexpr int C = W - X * EB < EB ? W - X * EB : EB;   // wave bits moved
         constexpr int EP = E >> PHB;                           // registers per phase
-        constexpr uint32_t MASK = (1u << (KR - PHB)) - 1;      // slot within a phase
+        constexpr uint32_t MASK = (1u << (KR + GB - PHB)) - 1; // slot within a phase
         static_assert(PHB == 0 || (NX == 1 && EB - C >= PHB), "phases keep their bits");
-        const uint32_t from = lx_thread_part<W, EB, X>(lane, wave);
-        const uint32_t to = lx_thread_part<W, EB, X + 1>(lane, wave);
+        const uint32_t from = (lx_thread_row<W, EB, LR, X>(lane_row, wave) << GB) | (uint32_t)g;
+        const uint32_t to = (lx_thread_row<W, EB, LR, X + 1>(lane_row, wave) << GB) | (uint32_t)g;
 #pragma unroll
         for (int ph = 0; ph < (1 << PHB); ++ph) {
             if (X > 0 || ph > 0)
                 __syncthreads();   // the previous reads of this region are done
 #pragma unroll
             for (int j = ph * EP; j < (ph + 1) * EP; ++j)
-                L[(from + lx_reg_part<W, EB, X>(j)) & MASK] = x[j];
+                L[(from + (lx_reg_row<W, EB, LR, X>(j) << GB)) & MASK] = x[j];
             __syncthreads();
 #pragma unroll
             for (int j = ph * EP; j < (ph + 1) * EP; ++j)
-                x[j] = L[(to + lx_reg_part<W, EB, X + 1>(j)) & MASK];
+                x[j] = L[(to + (lx_reg_row<W, EB, LR, X + 1>(j) << GB)) & MASK];
         }
         register_stages<C, E>(x);
-        LxRounds<V, KR, W, EB, PHB, X + 1, NX>::run(x, L, lane, wave);
+        LxRounds<V, KR, GB, W, EB, PHB, X + 1, NX>::run(x, L, lane_row, g, wave);
     }
 };
-template <typename V, int KR, int W, int EB, int PHB, int NX>
-struct LxRounds<V, KR, W, EB, PHB, NX, NX> {
-    __device__ __forceinline__ static void run(V*, V*, int, int) {}
+template <typename V, int KR, int GB, int W, int EB, int PHB, int NX>
+struct LxRounds<V, KR, GB, W, EB, PHB, NX, NX> {
+    __device__ __forceinline__ static void run(V*, V*, int, int, int) {}
 };
 
-template <typename T, int KR, int EB, int W, int PHB>
+template <typename T, int KR, int EB, int W, int PHB, int GB, bool ROW>
 __global__ void __launch_bounds__(64 << W)
     lx_kernel(T* __restrict__ re, T* __restrict__ im, TileArgs a)
 {
     using V = typename Vec<T>::type;
     constexpr int WB = Vec<T>::WB;
     constexpr int E = 1 << EB;
+    constexpr int LR = 6 - GB;              // row bits held by lanes
     constexpr int NX = (W + EB - 1) / EB;   // exchanges
-    static_assert(KR == EB + 6 + W && EB >= 1 && W >= 1 && W <= 4, "lane-exchange tile");
+    static_assert(KR == EB + LR + W && EB >= 1 && W >= 1 && W <= 4, "lane-exchange tile");
+    static_assert(!ROW || GB == 0, "row passes have one column group");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     V* const L = reinterpret_cast<V*>(lds_raw);
     const int64_t t = a.tile0 + blockIdx.x;
@@ -693,41 +700,58 @@ __global__ void __launch_bounds__(64 << W)
         return;   // uniform across the workgroup
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int g = lane & ((1 << GB) - 1);
+    const int lane_row = lane >> GB;
     T* const buf = blockIdx.y ? im : re;
-    unsigned char* const p = reinterpret_cast<unsigned char*>(buf + (t << (KR + WB)));
+    // Workgroup-uniform tile base, then 32-bit lane offsets: group g of row
+    // r sits at gbase + (r << rsh) bytes.
+    int64_t base;
+    uint32_t rsh;
+    if (ROW) {
+        base = t << (KR + WB);
+        rsh = 4;
+    } else {
+        const int64_t blk_mask = ((int64_t)1 << a.nblk_bits) - 1;
+        base = ((t >> a.nblk_bits) << (a.lo + KR)) + ((t & blk_mask) << (GB + WB));
+        rsh = (uint32_t)a.lo + (sizeof(T) == 8 ? 3u : 2u);
+    }
+    unsigned char* const p = reinterpret_cast<unsigned char*>(buf + base);
+    const uint32_t gbase = (uint32_t)g << 4;
 
-    const uint32_t r0 = lx_thread_part<W, EB, 0>(lane, wave);
+    const uint32_t r0 = lx_thread_row<W, EB, LR, 0>(lane_row, wave);
     V x[E];
     if (a.ld_nt) {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            x[j] = load16_nt<V>(p, (r0 + lx_reg_part<W, EB, 0>(j)) << 4);
+            x[j] = load16_nt<V>(p, gbase + ((r0 + lx_reg_row<W, EB, LR, 0>(j)) << rsh));
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            x[j] = load16<V>(p, (r0 + lx_reg_part<W, EB, 0>(j)) << 4);
+            x[j] = load16<V>(p, gbase + ((r0 + lx_reg_row<W, EB, LR, 0>(j)) << rsh));
     }
+    if (ROW) {
 #pragma unroll
-    for (int j = 0; j < E; ++j)
-        in_vector(x[j]);
+        for (int j = 0; j < E; ++j)
+            in_vector(x[j]);
+    }
     register_stages<EB, E>(x);
-    LaneStages<0, 6, 0, E, V, T>::run(x, lane);
-    LxRounds<V, KR, W, EB, PHB, 0, NX>::run(x, L, lane, wave);
+    LaneStages<0, LR, GB, E, V, T>::run(x, lane);
+    LxRounds<V, KR, GB, W, EB, PHB, 0, NX>::run(x, L, lane_row, g, wave);
     if (a.do_scale) {
         const T c = (T)a.scale;
 #pragma unroll
         for (int j = 0; j < E; ++j)
             x[j] *= c;
     }
-    const uint32_t rf = lx_thread_part<W, EB, NX>(lane, wave);
+    const uint32_t rf = lx_thread_row<W, EB, LR, NX>(lane_row, wave);
     if (a.st_nt) {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            store16_nt<V>(p, (rf + lx_reg_part<W, EB, NX>(j)) << 4, x[j]);
+            store16_nt<V>(p, gbase + ((rf + lx_reg_row<W, EB, LR, NX>(j)) << rsh), x[j]);
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            store16<V>(p, (rf + lx_reg_part<W, EB, NX>(j)) << 4, x[j]);
+            store16<V>(p, gbase + ((rf + lx_reg_row<W, EB, LR, NX>(j)) << rsh), x[j]);
     }
 }
 
@@ -868,31 +892,35 @@ struct RegisterWave {
     }
 };
 
-// Lane-exchange row tiles: W in [1, 4] with EB = KR - 6 - W in [2, 5], or
-// EB = W = 1; tiles of 2^11+ slots with W < EB also in two phases.
-template <typename T, int KR, int W>
+// Lane-exchange tiles: W in [1, 4] with EB = KR - (6 - GB) - W in [2, 5],
+// or EB = W = 1; tiles of 2^11+ slots with W < EB also in two phases.  Row
+// passes (GB = 0) for KR in [8, 13]; column passes with 8 or 16 groups
+// (128- or 256-byte row segments) for KR in [6, 11].
+template <typename T, int KR, int W, int GB, bool ROW>
 void add_lx(std::vector<Entry>& v)
 {
-    constexpr int EB = KR - 6 - W;
+    constexpr int EB = KR - (6 - GB) - W;
     if constexpr (W >= 1 && W <= 4 && ((EB >= 2 && EB <= 5) || (EB == 1 && W == 1))) {
-        v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, 0, 0, 1, 0, 2},
-                     reinterpret_cast<const void*>(&lx_kernel<T, KR, EB, W, 0>)});
-        if constexpr (KR >= 11 && W < EB)
-            v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, 0, 1, 1, 0, 2},
-                         reinterpret_cast<const void*>(&lx_kernel<T, KR, EB, W, 1>)});
+        // LDS: 2^(KR + GB) 16-byte slots, halved by the phases; at most 128 KiB
+        if constexpr (KR + GB <= 13)
+            v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, 0, ROW ? 1 : 0, 0, 2},
+                         reinterpret_cast<const void*>(&lx_kernel<T, KR, EB, W, 0, GB, ROW>)});
+        if constexpr (KR + GB >= 11 && KR + GB <= 14 && W < EB)
+            v.push_back({{sizeof(T) == 8 ? 1 : 0, KR, EB, GB, 1, ROW ? 1 : 0, 0, 2},
+                         reinterpret_cast<const void*>(&lx_kernel<T, KR, EB, W, 1, GB, ROW>)});
     }
 }
 
-template <typename T, int KR, int KRMIN>
+template <typename T, int KR, int KRMIN, int GB, bool ROW>
 struct LaneExchange {
     static void add(std::vector<Entry>& v)
     {
-        add_lx<T, KR, 1>(v);
-        add_lx<T, KR, 2>(v);
-        add_lx<T, KR, 3>(v);
-        add_lx<T, KR, 4>(v);
+        add_lx<T, KR, 1, GB, ROW>(v);
+        add_lx<T, KR, 2, GB, ROW>(v);
+        add_lx<T, KR, 3, GB, ROW>(v);
+        add_lx<T, KR, 4, GB, ROW>(v);
         if constexpr (KR > KRMIN)
-            LaneExchange<T, KR - 1, KRMIN>::add(v);
+            LaneExchange<T, KR - 1, KRMIN, GB, ROW>::add(v);
     }
 };
 
@@ -904,8 +932,12 @@ const std::vector<Entry>& table()
         RegisterWave<double, true, 11, 0>::add(v);
         RegisterWave<float, false, 11, 1>::add(v);
         RegisterWave<double, false, 11, 1>::add(v);
-        LaneExchange<float, 13, 8>::add(v);
-        LaneExchange<double, 13, 8>::add(v);
+        LaneExchange<float, 13, 8, 0, true>::add(v);
+        LaneExchange<double, 13, 8, 0, true>::add(v);
+        LaneExchange<float, 11, 6, 3, false>::add(v);
+        LaneExchange<float, 11, 6, 4, false>::add(v);
+        LaneExchange<double, 11, 6, 3, false>::add(v);
+        LaneExchange<double, 11, 6, 4, false>::add(v);
         Register<float, true, 13, 0>::add(v);
         Register<double, true, 13, 0>::add(v);
         Register<float, false, 12, 1>::add(v);

@@ -94,3 +94,29 @@ def _lx_phase_cases():
     out += [("f64", 24, (14, 10), (4, -1), 1), ("f32", 20, (13, 7), (4, -1), 2)]
     return out
 LX_PHASE_CASES = _lx_phase_cases()
+
+
+# (dtype, n, split, eb, gbits, phases, batch): the lane-exchange kernel on a
+# column pass (lanes hold 8 or 16 column groups and 3 or 2 row bits), every
+# compiled variant, with 4-8 column blocks per row and two outer indices
+def _lx_column_cases():
+    out = []
+    for dtype, vb in (("f32", 2), ("f64", 1)):
+        for gb in (3, 4):
+            lr = 6 - gb
+            for kr in range(6, 12):
+                for w in (1, 2, 3, 4):
+                    eb = kr - lr - w
+                    if not (2 <= eb <= 5 or eb == w == 1):
+                        continue
+                    for ph in (0, 1):
+                        if ph == 0 and kr + gb > 13:
+                            continue
+                        if ph == 1 and not (11 <= kr + gb <= 14 and w < eb):
+                            continue
+                        lo = gb + vb + 2          # 4 column blocks per row
+                        out.append((dtype, lo + kr + 1, (lo, kr, 1), eb, gb, ph, 1))
+    out += [("f32", 20, (12, 8), -1, -1, -1, 3), ("f64", 24, (14, 10), -1, -1, -1, 1),
+            ("f64", 20, (11, 9), -1, -1, -1, 2), ("f32", 19, (10, 9), -1, 3, -1, 5)]
+    return out
+LX_COLUMN_CASES = _lx_column_cases()

@@ -221,8 +221,8 @@ def test_tuned_fuzz_never_crashes():
 def test_every_gpu_test_plan_is_valid(lib):
     """Each plan the GPU parity suite builds is accepted by the planner and
     has the forced properties (caught here, on the CPU)."""
-    from plan_cases import (FORCED_SPLITS, LDS_SINGLE_CASES, LX_CASES, LX_PHASE_CASES,
-                            PIPE_CASES, VARIANTS, WAVE_CASES)
+    from plan_cases import (FORCED_SPLITS, LDS_SINGLE_CASES, LX_CASES, LX_COLUMN_CASES,
+                            LX_PHASE_CASES, PIPE_CASES, VARIANTS, WAVE_CASES)
     for dtype, n in LDS_SINGLE_CASES:
         assert qse.Plan(n, dtype, split=(n,), wave=(0,)).pass_config(0)["wave"] == 0
     for dtype, n, split in FORCED_SPLITS:
@@ -246,6 +246,13 @@ def test_every_gpu_test_plan_is_valid(lib):
                      wave=(2,) + (-1,) * (len(split) - 1))
         assert (p.pass_config(0)["wave"], p.pass_config(0)["phase_bits"]) == (2, 1)
     assert len(LX_PHASE_CASES) == 14   # all 12 compiled phased variants appear
+    for dtype, n, split, eb, gbits, phases, batch in LX_COLUMN_CASES:
+        k = len(split)
+        knobs = {name: tuple(v if i == 1 else -1 for i in range(k))
+                 for name, v in (("eb", eb), ("gbits", gbits), ("phases", phases), ("wave", 2))}
+        c = qse.Plan(n, dtype, split=split, **knobs).pass_config(1)
+        assert c["wave"] == 2 and c["kind"] == "column"
+    assert len(LX_COLUMN_CASES) == 82  # all 78 compiled column variants appear
 
 
 def test_lane_exchange_plans(lib):
@@ -258,7 +265,7 @@ def test_lane_exchange_plans(lib):
             w = kr - 6 - c["eb"]
             assert w == (min(4, kr - 8) if kr >= 10 else 1)
             assert c["block"] == 64 << w and c["lds"] == 16 << kr and c["tpw_bits"] == 0
-            assert p.kernel_name(0) == "lx_kernel<%s, %d, %d, %d, 0>" % (
+            assert p.kernel_name(0) == "lx_kernel<%s, %d, %d, %d, 0, 0, true>" % (
                 "float" if dtype == "f32" else "double", kr, c["eb"], w)
         kr = 10
         n = kr + vb
@@ -268,13 +275,14 @@ def test_lane_exchange_plans(lib):
         assert _split(lib, n + 2, vb == 1, [n + 2], eb=[2], wave=[2]) == 0       # w = 4
         assert _split(lib, n + 3, vb == 1, [n + 3], eb=[2], wave=[2]) == qse.FWT_EINVAL  # w = 5
         assert _split(lib, n, vb == 1, [n], gbits=[1], wave=[2]) == qse.FWT_EINVAL
-        assert _split(lib, n + 7, vb == 1, [n, 7], wave=[0, 2]) == qse.FWT_EINVAL  # column pass
+        assert _split(lib, n + 7, vb == 1, [n, 7], wave=[0, 2]) == 0   # column pass, 16 groups
+        assert _split(lib, n + 7, vb == 1, [n, 7], gbits=[-1, 2], wave=[0, 2]) == qse.FWT_EINVAL
     assert _split(lib, 9, 0, [9], wave=[2]) == qse.FWT_EINVAL     # 7 row bits: no wave bit
     # two exchange phases: one exchange with w < eb, half the LDS
     p = qse.Plan(24, "f64", split=(14, 10), eb=(4, -1), phases=(1, -1), wave=(2, -1))
     c = p.pass_config(0)
     assert (c["wave"], c["phase_bits"], c["lds"], c["block"]) == (2, 1, 64 << 10, 512)
-    assert p.kernel_name(0) == "lx_kernel<double, 13, 4, 3, 1>"
+    assert p.kernel_name(0) == "lx_kernel<double, 13, 4, 3, 1, 0, true>"
     assert _split(lib, 15, 0, [15], eb=[3], phases=[1], wave=[2]) == qse.FWT_EINVAL  # w = eb
     assert _split(lib, 15, 0, [15], eb=[4], phases=[2], wave=[2]) == qse.FWT_EINVAL
     assert _split(lib, 12, 0, [12], eb=[3], phases=[1], wave=[2]) == qse.FWT_EUNSUPPORTED  # kr 10
@@ -283,8 +291,9 @@ def test_lane_exchange_plans(lib):
 def test_default_kernel_choice(lib):
     """One-pass plans of 3 <= n <= 10 default to the wave-tile kernel; other
     row passes of 8..13 vector bits to the lane-exchange kernel (except a
-    multi-pass row pass of 11); column passes, the rest and entries with
-    any field forced use the LDS tiles."""
+    multi-pass row pass of 11), and so do column passes of 8..10 bits with
+    rows of at least 8 groups; the rest, and entries with any field forced,
+    use the LDS tiles."""
     for dtype, vb in (("f32", 2), ("f64", 1)):
         for n in range(2, 15 if dtype == "f32" else 14):
             want = 1 if 3 <= n <= 10 else (2 if n - vb >= 8 else 0)
@@ -292,25 +301,36 @@ def test_default_kernel_choice(lib):
             assert qse.Plan(n, dtype, split=(n,)).pass_config(0)["wave"] == want, (dtype, n)
         assert qse.Plan(8, dtype, split=(8,), eb=(3,)).pass_config(0)["wave"] == 0
         assert qse.Plan(12, dtype, split=(12,), eb=(3,)).pass_config(0)["wave"] == 0
-        for split in ((5, 5), (7, 7), (2, 8), (3, 3, 4), (11, 9)):
+        for split in ((5, 5), (7, 7), (2, 8), (3, 3, 4), (11, 9), (6, 10), (10, 7)):
             p = qse.Plan(sum(split), dtype, split=split)
-            want = [2 if i == 0 and b - vb >= 8 and b - vb != 11 else 0 for i, b in enumerate(split)]
+            lo, want = 0, []
+            for i, b in enumerate(split):
+                if i == 0:
+                    want.append(2 if b - vb >= 8 and b - vb != 11 else 0)
+                else:
+                    want.append(2 if 8 <= b <= 10 and lo - vb >= 3 else 0)
+                lo += b
             assert [p.pass_config(i)["wave"] for i in range(p.num_passes)] == want, split
     for (dtype, n), (bits, wave) in {
-            ("f32", 16): ([10, 6], [2, 0]), ("f32", 19): ([10, 9], [2, 0]),
-            ("f32", 20): ([12, 8], [2, 0]), ("f32", 22): ([13, 9], [0, 0]),
-            ("f64", 15): ([9, 6], [2, 0]), ("f64", 19): ([11, 8], [2, 0]),
-            ("f64", 21): ([12, 9], [0, 0]), ("f64", 24): ([14, 10], [2, 0])}.items():
+            ("f32", 16): ([10, 6], [2, 0]), ("f32", 19): ([10, 9], [2, 2]),
+            ("f32", 20): ([12, 8], [2, 2]), ("f32", 22): ([13, 9], [0, 2]),
+            ("f32", 26): ([15, 11], [2, 0]), ("f64", 15): ([9, 6], [2, 0]),
+            ("f64", 19): ([11, 8], [2, 2]), ("f64", 21): ([12, 9], [0, 2]),
+            ("f64", 24): ([14, 10], [2, 2])}.items():
         p = qse.Plan(n, dtype)
         assert p.pass_bits == bits, (dtype, n)
         assert [p.pass_config(i)["wave"] for i in range(2)] == wave, (dtype, n)
+    # column passes: eb = 4, two exchange phases, 16 groups up to 9 bits
+    assert qse.Plan(20, "f32").kernel_name(1) == "lx_kernel<float, 8, 4, 2, 1, 4, false>"
+    assert qse.Plan(24, "f64").kernel_name(1) == "lx_kernel<double, 10, 4, 3, 1, 3, false>"
+    assert qse.Plan(25, "f32").kernel_name(1) == "lx_kernel<float, 10, 4, 3, 1, 3, false>"
     # a 13-vector-bit row pass of a two-pass plan: one exchange in two phases
     for n in (23, 24, 25):
-        assert qse.Plan(n, "f64").kernel_name(0) == "lx_kernel<double, 13, 4, 3, 1>"
+        assert qse.Plan(n, "f64").kernel_name(0) == "lx_kernel<double, 13, 4, 3, 1, 0, true>"
     for n in (24, 25, 26):
-        assert qse.Plan(n, "f32").kernel_name(0) == "lx_kernel<float, 13, 4, 3, 1>"
-    assert qse.Plan(14, "f64").kernel_name(0) == "lx_kernel<double, 13, 3, 4, 0>"
-    assert qse.Plan(15, "f32").kernel_name(0) == "lx_kernel<float, 13, 3, 4, 0>"
+        assert qse.Plan(n, "f32").kernel_name(0) == "lx_kernel<float, 13, 4, 3, 1, 0, true>"
+    assert qse.Plan(14, "f64").kernel_name(0) == "lx_kernel<double, 13, 3, 4, 0, 0, true>"
+    assert qse.Plan(15, "f32").kernel_name(0) == "lx_kernel<float, 13, 3, 4, 0, 0, true>"
 
 
 def test_mfma_path_plans(lib):

@@ -20,8 +20,8 @@ import pytest
 import oracle
 import quantum_state_encoding_amd as qse
 import workloads
-from plan_cases import (FORCED_SPLITS, LDS_SINGLE_CASES, LX_CASES, LX_PHASE_CASES, PIPE_CASES,
-                        VARIANTS, WAVE_CASES)
+from plan_cases import (FORCED_SPLITS, LDS_SINGLE_CASES, LX_CASES, LX_COLUMN_CASES, LX_PHASE_CASES,
+                        PIPE_CASES, VARIANTS, WAVE_CASES)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -220,6 +220,33 @@ def test_integer_lane_exchange_phases(dtype, n, split, eb, batch):
     assert plan.pass_config(0)["phase_bits"] == 1
     re = ints((batch, 1 << n), 99_700 + n, npd)
     im = ints((batch, 1 << n), 99_800 + n, npd)
+    gre, gim = run(plan, re, im, False)
+    assert_exact(gre, re, n, False)
+    assert_exact(gim, im, n, False)
+    if n % 2 == 0:
+        gre, gim = run(plan, re, im, True)
+        assert_exact(gre, re, n, True)
+        assert_exact(gim, im, n, True)
+
+
+def lx_column_plan(dtype, n, split, eb, gbits, phases):
+    k = len(split)
+    knobs = {name: tuple(v if i == 1 else -1 for i in range(k))
+             for name, v in (("eb", eb), ("gbits", gbits), ("phases", phases), ("wave", 2))}
+    return qse.Plan(n, dtype, split=split, **knobs)
+
+
+@pytest.mark.parametrize("dtype,n,split,eb,gbits,phases,batch", LX_COLUMN_CASES)
+def test_integer_lane_exchange_columns(dtype, n, split, eb, gbits, phases, batch):
+    """The lane-exchange kernel on a column pass (lanes hold the column
+    groups and the lowest row bits), exactly against the oracle."""
+    say("lx column %s n=%d split=%s eb=%d gbits=%d phases=%d batch=%d" % (
+        dtype, n, split, eb, gbits, phases, batch))
+    npd = np.float32 if dtype == "f32" else np.float64
+    plan = lx_column_plan(dtype, n, split, eb, gbits, phases)
+    assert plan.pass_config(1)["wave"] == 2
+    re = ints((batch, 1 << n), 99_900 + n, npd)
+    im = ints((batch, 1 << n), 99_950 + n, npd)
     gre, gim = run(plan, re, im, False)
     assert_exact(gre, re, n, False)
     assert_exact(gim, im, n, False)
