@@ -136,6 +136,32 @@ def bench_workload(torch, w, steps, warmup, with_passes=True, split="configured"
             tot[i] += a.elapsed_time(b)
             cnt[i] += 1
         per_pass = [tot[i] / cnt[i] for i in range(passes)]
+    # Self-check without the oracle: H is its own inverse up to 2^n
+    # (H H = 2^n I), so two calls from the original input must give the
+    # input back (normalised) or 2^n times it (unnormalised, exact for the
+    # integer workload).  Sampled vectors are compared on the host.
+    check = None
+    if with_passes:
+        re.copy_(hre, non_blocking=False)
+        im.copy_(him, non_blocking=False)
+        step()
+        step()
+        torch.cuda.synchronize()
+        scale = 1.0 if w.normalize else float(2 ** w.n)
+        rows = sorted(set(int(r) for r in np.linspace(0, w.batch - 1, min(8, w.batch))))
+        worst = 0.0
+        exact = True
+        for r in rows:
+            x_re = hre[r].numpy().astype(np.float64)
+            x_im = him[r].numpy().astype(np.float64)
+            g_re = re[r].cpu().numpy().astype(np.float64)
+            g_im = im[r].cpu().numpy().astype(np.float64)
+            err = max(np.abs(g_re - scale * x_re).max(), np.abs(g_im - scale * x_im).max())
+            norm = np.sqrt(np.sum(x_re ** 2) + np.sum(x_im ** 2)) * scale
+            worst = max(worst, err / norm if norm > 0 else err)
+            exact = exact and err == 0.0
+        check = {"calls": 2, "vectors": len(rows), "max_err_over_norm": worst,
+                 "exact": bool(exact)}
     # Stream-copy ceiling: one read and one write of the whole state.
     copy_ms = None
     if with_passes:
@@ -150,7 +176,8 @@ def bench_workload(torch, w, steps, warmup, with_passes=True, split="configured"
     torch.cuda.empty_cache()
     S = w.state_bytes
     return {"ms": ms, "wall_ms": wall_ms, "passes": passes, "pass_bits": plan.pass_bits,
-            "per_pass_ms": per_pass, "copy_ms": copy_ms, "S": S, "chunk": chunk}
+            "per_pass_ms": per_pass, "copy_ms": copy_ms, "S": S, "chunk": chunk,
+            "check": check}
 
 
 def _read_csv(path):
@@ -459,6 +486,10 @@ def main():
                      "bytes_per_launch": launch_bytes,
                      "launches_per_step": r["passes"] * (-(-w.batch // r["chunk"]))},
         "cpu_baseline": cpu,
+        "involution_check": r["check"],
+        "gpu_name": torch.cuda.get_device_name(0),
+        "gpu_arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
+        "hip_version": getattr(torch.version, "hip", None),
         "also": also,
         "ablations": ablations,
     }
