@@ -1,0 +1,59 @@
+"""AddressSanitizer, LeakSanitizer and UndefinedBehaviorSanitizer runs of
+the host code (CPU only): the C oracle through every entry point, and the
+library's planner and argument validation (fwt_api.cpp, with its kernel
+entry points stubbed) through 20 000 random plans, every query and every
+early-return error path.  A sanitizer report makes the driver exit
+non-zero."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HERE = os.path.join(ROOT, "tests", "sanitize")
+SAN = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+       "-fno-omit-frame-pointer"]
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def _run(cmd, cwd, timeout=600):
+    r = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True, timeout=timeout)
+    return r.returncode, r.stdout + r.stderr
+
+
+@pytest.fixture
+def workdir(tmp_path):
+    return str(tmp_path)
+
+
+def test_oracle_under_sanitizers(workdir):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not found")
+    exe = os.path.join(workdir, "oracle_driver")
+    rc, out = _run(["gcc"] + SAN + ["-ffp-contract=off", "-std=c99", "-D_POSIX_C_SOURCE=200809L",
+                                    os.path.join(HERE, "oracle_driver.c"),
+                                    os.path.join(ROOT, "oracle", "oracle.c"),
+                                    "-o", exe, "-lm", "-lpthread"], workdir)
+    assert rc == 0, out
+    rc, out = _run([exe], workdir)
+    assert rc == 0 and "oracle driver: ok" in out, out
+
+
+def test_planner_under_sanitizers(workdir):
+    if shutil.which("g++") is None or not os.path.exists(os.path.join(ROCM, "lib",
+                                                                       "libamdhip64.so")):
+        pytest.skip("g++ or the HIP runtime library not found")
+    exe = os.path.join(workdir, "planner_driver")
+    rc, out = _run(["g++"] + SAN + ["-std=c++17", "-D__HIP_PLATFORM_AMD__",
+                                    "-I", os.path.join(ROOT, "include"),
+                                    "-I", os.path.join(ROCM, "include"),
+                                    os.path.join(HERE, "planner_driver.cpp"),
+                                    os.path.join(HERE, "kernel_stubs.cpp"),
+                                    os.path.join(ROOT, "quantum_state_encoding_amd", "csrc",
+                                                 "fwt_api.cpp"),
+                                    "-o", exe, "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+                                    "-Wl,-rpath," + os.path.join(ROCM, "lib")], workdir)
+    assert rc == 0, out
+    rc, out = _run([exe], workdir)
+    assert rc == 0 and "planner driver:" in out and " ok" in out, out
