@@ -254,8 +254,9 @@ typedef enum {
      * by its own power of two to integers of at most 48 bits, split into
      * residues mod m <= 10 primes below 256 (balanced int8), transformed
      * in residue space by Kronecker passes of 32-position blocks on
-     * v_mfma_i32_16x16x32_i8 with reduction mod p, rebuilt by CRT
-     * (Garner digits summed in 128-bit integers) and scaled back.  Exact
+     * v_mfma_i32_16x16x32_i8 with reduction mod p, rebuilt by CRT with a
+     * rounded fp64 quotient (the sum exact in 128-bit integers) and scaled
+     * back.  Exact
      * for integer-valued inputs; otherwise within 2^-46 of max |x| times
      * sqrt(2^n) per output.  fp64 only (fp32: FWT_EUNSUPPORTED); finite
      * inputs; 5 <= n <= 28; needs a workspace (the residues, 4 ceil(m / 4)
