@@ -145,7 +145,9 @@ typedef struct {
 int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
                           const int* bits, const fwt_pass_tuning* tuning);
 
-/* Transform in place, asynchronously on `stream` (0 = the null stream).
+/* Transform in place, asynchronously on `stream` (0 = the null stream;
+ * otherwise a stream of the calling thread's current device, else
+ * FWT_EINVAL).
  *  re, im   device buffers of batch * 2^n elements of the plan's dtype,
  *           vector b at offset b * 2^n; 16-byte aligned; must not overlap.
  *           im may be NULL (real-only transform).  The caller owns them.

@@ -700,6 +700,19 @@ int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, vo
     int rc = ensure_device_init(&cus);
     if (rc != FWT_OK)
         return rc;
+    if (stream) {
+        // Kernel attributes and the grid sizes are set up for the current
+        // device: the stream must belong to it.
+        int cur = 0;
+        hipDevice_t sdev = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess)
+            e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess)
+            return hip_fail(e);
+        if ((int)sdev != cur)
+            return FWT_EINVAL;
+    }
     const int ncomp = im ? 2 : 1;
     const double c = norm_constant(n);
     const bool multi = plan->npasses >= 2;
