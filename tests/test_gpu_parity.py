@@ -456,6 +456,47 @@ def test_non_default_stream_and_determinism():
     assert_close("f32", n, re, im, a_re.cpu().numpy(), a_im.cpu().numpy())
 
 
+def test_one_plan_from_several_threads_and_streams():
+    """One plan used at once from four host threads, each on its own
+    stream and buffers (ctypes releases the GIL during the call): every
+    result equals the single-threaded one bit for bit."""
+    import threading
+    say("threads + streams")
+    n = 18
+    w = workloads.custom(n, 6, "f32", "gauss", True, seed=12)
+    re, im = workloads.gen(w)
+    plan = qse.Plan(n, "f32")
+    ref_re, ref_im = to_dev(re), to_dev(im)
+    plan.execute(ref_re, ref_im, normalize=True)
+    torch.cuda.synchronize()
+    bufs = [(to_dev(re), to_dev(im), torch.cuda.Stream()) for _ in range(4)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(b_re, b_im, stream):
+        try:
+            for _ in range(8):   # an even count: back to the input ...
+                plan.execute(b_re, b_im, normalize=True, stream=stream)
+            plan.execute(b_re, b_im, normalize=True, stream=stream)   # ... then once more
+        except Exception as e:   # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=b) for b in bufs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for b_re, b_im, _ in bufs:
+        assert_close("f32", n, re, im, b_re.cpu().numpy(), b_im.cpu().numpy())
+        # nine calls differ from one only by rounding
+        assert torch.allclose(b_re, ref_re, atol=1e-5) and torch.allclose(b_im, ref_im, atol=1e-5)
+    # identical inputs and call sequences give identical results
+    for b_re, b_im, _ in bufs[1:]:
+        assert torch.equal(b_re, bufs[0][0]) and torch.equal(b_im, bufs[0][1])
+
+
 def test_involution_normalised():
     say("involution")
     for n, dtype in ((13, "f32"), (20, "f32"), (17, "f64")):
