@@ -161,7 +161,9 @@ int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
  * batch * 2^n elements; FWT_EALIGN for misalignment.  A launch failure
  * returns FWT_EHIP (earlier passes may already be enqueued; the buffers
  * are then undefined).  Faults during execution surface at the caller's
- * next synchronisation of the stream. */
+ * next synchronisation of the stream.  The call only enqueues kernel
+ * launches (no memsets, no allocation, no synchronisation), so it may be
+ * captured into a HIP graph. */
 int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im,
                 int normalize, hipStream_t stream);
 

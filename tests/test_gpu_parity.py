@@ -497,6 +497,43 @@ def test_one_plan_from_several_threads_and_streams():
         assert torch.equal(b_re, bufs[0][0]) and torch.equal(b_im, bufs[0][1])
 
 
+@pytest.mark.parametrize("n,batch,dtype", [(12, 5, "f32"), (20, 4, "f32"), (22, 2, "f64")])
+def test_hip_graph_capture_and_replay(n, batch, dtype):
+    """fwt_execute captured into a HIP graph (torch's default capture mode)
+    and replayed three times, with other eager work and synchronisations
+    between the replays: every replay equals the eager call bit for bit.
+    The library records kernel launches only (no memset nodes)."""
+    say("graph %s n=%d batch=%d" % (dtype, n, batch))
+    w = workloads.custom(n, batch, dtype, "gauss", True, seed=31)
+    re0, im0 = workloads.gen(w)
+    plan = qse.Plan(n, dtype)
+    e_re, e_im = to_dev(re0), to_dev(im0)
+    plan.execute(e_re, e_im, normalize=True)
+    torch.cuda.synchronize()
+    x_re, x_im = to_dev(re0), to_dev(im0)
+    g_re, g_im = torch.empty_like(x_re), torch.empty_like(x_im)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        fn = plan.bind(g_re, g_im, normalize=True, stream=s)
+        g_re.copy_(x_re)
+        g_im.copy_(x_im)
+        fn()                         # warm-up outside the capture
+        s.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            fn()
+    for rep in range(3):
+        g_re.copy_(x_re)
+        g_im.copy_(x_im)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g_re, e_re) and torch.equal(g_im, e_im), "replay %d" % rep
+        junk = torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")
+        torch.cuda.synchronize()
+        del junk
+
+
 def test_involution_normalised():
     say("involution")
     for n, dtype in ((13, "f32"), (20, "f32"), (17, "f64")):
