@@ -447,6 +447,16 @@ def main():
                            (rs["ms"] * 1e-3) / 1e9,
                            "note": "%.0f KiB state, resident in cache across steps; "
                                    "latency-bound" % (ws.state_bytes / 1024)}
+        # The fp64 workload (4 GiB, HBM-bound), with the same accounting.
+        ws = workloads.WORKLOADS["n24_b16_f64"]
+        rs = bench_workload(torch, ws, max(20, args.steps // 5), args.warmup, with_passes=False)
+        gb = 2 * ws.state_bytes * rs["passes"] / (rs["ms"] * 1e-3) / 1e9
+        also["n24_b16_f64"] = {"ms_per_step": rs["ms"], "passes": rs["passes"],
+                               "pass_bits": rs["pass_bits"],
+                               "amplitudes_per_s": ws.batch * ws.N / (rs["ms"] * 1e-3),
+                               "gbps_accounted": gb,
+                               "pct_peak_accounted": 100 * gb / HBM_PEAK_GBS,
+                               "note": "4 GiB state, HBM-bound; %d steps" % max(20, args.steps // 5)}
 
     # The pages' own designs for the same transform, on the same state.
     ablations = {}
