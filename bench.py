@@ -38,10 +38,10 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload, dominant_pass):
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 counter summary, or None if absent or taken on an older
-    kernel source."""
+def traffic_record(workload, dominant_pass):
+    """The committed rocprofv3 counter record of the dominant kernel
+    (profiles/traffic.json), or None if absent or taken on an older kernel
+    source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -51,7 +51,35 @@ def measured_traffic(workload, dominant_pass):
     if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     p = rec.get("passes", {}).get(str(dominant_pass))
+    if p is None:
+        return None
+    out = dict(p)
+    out["fetch_scale"], out["write_scale"] = rec.get("fetch_scale"), rec.get("write_scale")
+    return out
+
+
+def measured_traffic(workload, dominant_pass):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, or None if absent or taken on an older
+    kernel source."""
+    p = traffic_record(workload, dominant_pass)
     return None if p is None else p.get("bytes_per_launch")
+
+
+def lds_conflicts(workload, kernel):
+    """Bank-conflict cycles per LDS-active cycle of `kernel` from the
+    committed profiles/<workload>_lds.txt, or None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "%s_lds.txt" % workload)) as f:
+            for line in f:
+                cols = [c.strip() for c in line.split("|")]
+                if len(cols) >= 7 and cols[0] == kernel:
+                    return {"kernel": kernel, "conflict_cycles": float(cols[5]),
+                            "lds_active_cycles": float(cols[4]),
+                            "conflict_per_active": float(cols[6])}
+    except (OSError, ValueError):
+        return None
+    return None
 
 
 def time_events(torch, stream, fn, reps):
@@ -83,6 +111,7 @@ def cpu_baseline(w, repeats=2):
     t = float(np.median(times))
     amps = w.batch * w.N
     return {"value": amps / t, "unit": "amplitudes/s", "cores": int(used), "kind": "oracle",
+            "ms": t * 1e3,
             "sample": "whole workload: %d complex vectors of 2^%d (%d real transforms, %s), "
                       "median of %d runs of %.3f s" % (w.batch, w.n, 2 * w.batch, w.dtype,
                                                      repeats, t)}
@@ -113,6 +142,9 @@ def bench_workload(torch, w, steps, warmup, with_passes=True, split="configured"
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ms = ms_events
+    # Spread: five more short repeats, after the timed region.
+    reps = [time_events(torch, stream, step, max(5, steps // 10)) for _ in range(5)] \
+        if with_passes else []
     # Per-kernel durations: the schedule fwt_execute runs (all passes of one
     # chunk of vectors, chunk after chunk), each kernel timed by HIP events
     # that its own dispatch records at its start and end; averaged per pass
@@ -177,7 +209,8 @@ def bench_workload(torch, w, steps, warmup, with_passes=True, split="configured"
     S = w.state_bytes
     return {"ms": ms, "wall_ms": wall_ms, "passes": passes, "pass_bits": plan.pass_bits,
             "per_pass_ms": per_pass, "copy_ms": copy_ms, "S": S, "chunk": chunk,
-            "check": check}
+            "check": check, "reps_ms": reps,
+            "kernel_names": [plan.kernel_name(i) for i in range(passes)]}
 
 
 def _read_csv(path):
@@ -428,6 +461,10 @@ def main():
     launch_bytes = 2 * S * r["chunk"] // w.batch     # read + write of one chunk's state
     achieved = launch_bytes / (dom_ms * 1e-3) / 1e9
     traffic = measured_traffic(w.name, dom)
+    trec = traffic_record(w.name, dom)
+    lds = None
+    if trec is not None:   # the LDS counters come from the same profiling session
+        lds = lds_conflicts(w.name, trec.get("kernel", ""))
 
     # The other workloads, briefly: the metric also names n=14 (batch 64),
     # reported with its configured 7|7 split and with the default plan.
@@ -473,6 +510,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": r["ms"],
+        "t_ms_median": float(np.median(r["reps_ms"])) if r["reps_ms"] else None,
+        "t_ms_min": float(np.min(r["reps_ms"])) if r["reps_ms"] else None,
+        "seed": w.seed,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -491,6 +531,12 @@ def main():
         "wall_ms_per_step": r["wall_ms"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "fetch_bytes": None if trec is None else
+                     trec["fetch_kib"] * trec["fetch_scale"] * 1024,
+                     "write_bytes": None if trec is None else
+                     trec["write_kib"] * trec["write_scale"] * 1024,
+                     "lds_bank_conflicts": lds,
+                     "kernel_name": r["kernel_names"][dom] if r["kernel_names"] else None,
                      "kernel": "pass %d (%d bits, %s)" % (dom, r["pass_bits"][dom] if r["pass_bits"] else 0,
                                                            "row" if dom == 0 else "column"),
                      "bytes_per_launch": launch_bytes,
