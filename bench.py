@@ -440,7 +440,7 @@ def main():
         summarize_ablations(args.workload, args.summarize_ablations, args.profile_command)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(batches shard across GPUs with no communication); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
