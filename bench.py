@@ -377,8 +377,9 @@ def bench_ablations(torch, w, steps=3):
     """Time the pages' designs on the workload's state: one launch per
     butterfly stage, the popcount-GEMM Kronecker scaffold with its batch
     transposes, the matrix-core block-Hadamard row kernel followed by the
-    column passes, and (fp64) the INT8 / CRT emulation
-    (fwt_ablation_execute).  ms per step, same accounting."""
+    column passes, matrix-core blocks on both factors with transposes in
+    between, and (fp64) the INT8 / CRT emulation (fwt_ablation_execute).
+    ms per step, same accounting."""
     import quantum_state_encoding_amd as qse
     dev = torch.device("cuda:0")
     tdt = torch.float32 if w.dtype == "f32" else torch.float64
@@ -391,6 +392,8 @@ def bench_ablations(torch, w, steps=3):
         kinds.append(("popc_gemm_transpose", qse.ABLATION_POPC_GEMM, 2))
     if w.n >= 8:
         kinds.append(("mfma_block_hadamard", qse.ABLATION_MFMA, 2))
+    if 16 <= w.n <= (30 if w.dtype == "f32" else 28):
+        kinds.append(("mfma_blocks_with_transposes", qse.ABLATION_MFMA_TRANSPOSE, 4))
     if w.dtype == "f64" and 5 <= w.n <= 28:
         kinds.append(("ozaki_int8_crt", qse.ABLATION_OZAKI, 3))
     for name, kind, launches in kinds:

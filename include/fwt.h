@@ -265,7 +265,15 @@ typedef enum {
      * sqrt(2^n) per output.  fp64 only (fp32: FWT_EUNSUPPORTED); finite
      * inputs; 5 <= n <= 28; needs a workspace (the residues, 4 ceil(m / 4)
      * bytes per element, plus per-vector scales). */
-    FWT_ABLATION_OZAKI = 4
+    FWT_ABLATION_OZAKI = 4,
+    /* Matrix-core block Hadamard on both Kronecker factors with a
+     * transposed staging buffer (the iThome article's TF32 data flow on
+     * the fp32 / fp64 16x16x4 matrix instructions): block products on the
+     * contiguous n - n/2 bits, a transpose of every vector into the
+     * workspace, block products on the n/2 bits, a transpose back.
+     * 16 <= n <= 30 (fp32) / 28 (fp64); needs a workspace of the state's
+     * size. */
+    FWT_ABLATION_MFMA_TRANSPOSE = 5
 } fwt_ablation;
 
 /* Workspace bytes fwt_ablation_execute needs for `batch` vectors (0 if

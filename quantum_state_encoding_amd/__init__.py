@@ -18,7 +18,7 @@ import os
 
 __all__ = ["Plan", "FwtError", "execute", "stream_copy", "library_path", "load_library",
            "ablation_workspace", "ablation_execute", "ABLATION_STAGEWISE", "ABLATION_POPC_GEMM",
-           "ABLATION_MFMA", "ABLATION_OZAKI", "PassTuning",
+           "ABLATION_MFMA", "ABLATION_OZAKI", "ABLATION_MFMA_TRANSPOSE", "PassTuning",
            "PATH_AUTO", "PATH_SINGLE_BLOCK", "PATH_MULTIPASS", "PATH_MFMA_ABLATION",
            "FWT_OK", "FWT_EINVAL", "FWT_EALIGN", "FWT_EUNSUPPORTED", "FWT_EHIP",
            "FWT_ENOMEM", "EXPORTED_SYMBOLS"]
@@ -346,6 +346,7 @@ def execute(re, im=None, n=None, normalize=True, stream=None, path=PATH_AUTO):
 
 
 ABLATION_STAGEWISE, ABLATION_POPC_GEMM, ABLATION_MFMA, ABLATION_OZAKI = 1, 2, 3, 4
+ABLATION_MFMA_TRANSPOSE = 5
 
 
 def ablation_workspace(kind, batch, n, dtype="f32", with_im=True):

@@ -428,7 +428,47 @@ hipError_t popc_gemm_impl(T* re, T* im, T* ws_re, T* ws_im, int64_t batch, int n
     return transpose(ws_re, ws_im, re, im, n2, n1);
 }
 
+// The matrix-core design with a transposed staging buffer, in the order of
+// the iThome "Day 18" native-FWT article's TF32 data flow: block-Hadamard
+// products on the contiguous n2 = n - n/2 bits, a transpose of every
+// 2^n1 x 2^n2 matrix into the workspace, block products on the n1 bits
+// (now contiguous), and a transpose back.
+template <typename T>
+hipError_t mfma_transpose_impl(T* re, T* im, T* ws_re, T* ws_im, int64_t batch, int n,
+                               int normalize, double c, hipStream_t stream)
+{
+    const int ncomp = im ? 2 : 1;
+    const int n1 = n / 2, n2 = n - n1;
+    auto transpose = [&](const T* sa, const T* sb, T* da, T* db, int rbits, int cbits) {
+        const int tr = rbits < 5 ? 1 << rbits : 32, tc = cbits < 5 ? 1 << cbits : 32;
+        const int64_t tiles = batch * ((int64_t)1 << (rbits + cbits)) / ((int64_t)tr * tc);
+        hipLaunchKernelGGL(transpose_kernel<T>, dim3(grid_for(tiles, 1), 1, ncomp), dim3(256), 0,
+                           stream, sa, sb, da, db, rbits, cbits, batch);
+        return hipGetLastError();
+    };
+    hipError_t e;
+    if ((e = mfma_row_dispatch<T>(re, im, batch << n1, n2, 0, c, stream)) != hipSuccess)
+        return e;
+    if ((e = transpose(re, im, ws_re, ws_im, n1, n2)) != hipSuccess)
+        return e;
+    if ((e = mfma_row_dispatch<T>(ws_re, ws_im, batch << n2, n1, normalize, c, stream)) !=
+        hipSuccess)
+        return e;
+    return transpose(ws_re, ws_im, re, im, n2, n1);
+}
+
 }  // namespace
+
+hipError_t ablation_mfma_transpose(int f64, void* re, void* im, void* ws_re, void* ws_im,
+                                   int64_t batch, int n, int normalize, double c,
+                                   hipStream_t stream)
+{
+    if (f64)
+        return mfma_transpose_impl<double>((double*)re, (double*)im, (double*)ws_re,
+                                           (double*)ws_im, batch, n, normalize, c, stream);
+    return mfma_transpose_impl<float>((float*)re, (float*)im, (float*)ws_re, (float*)ws_im,
+                                      batch, n, normalize, c, stream);
+}
 
 hipError_t ablation_mfma_row(int f64, void* re, void* im, int64_t batch, int n, int km,
                              int do_scale, double c, hipStream_t stream)

@@ -889,7 +889,7 @@ size_t ablation_workspace_bytes(int kind, int64_t batch, int n, fwt_dtype dtype,
         size_t a, b;
         return qse::oz_workspace_layout(batch, n, with_im ? 2 : 1, &a, &b);
     }
-    if (kind != FWT_ABLATION_POPC_GEMM)
+    if (kind != FWT_ABLATION_POPC_GEMM && kind != FWT_ABLATION_MFMA_TRANSPOSE)
         return 0;
     const size_t esize = dtype == FWT_F64 ? 8 : 4;
     return (size_t)batch * ((size_t)1 << n) * esize * (with_im ? 2 : 1);
@@ -915,6 +915,10 @@ int ablation_check(int kind, int64_t batch, int n, fwt_dtype dtype, const void* 
             return FWT_EINVAL;
         if (dtype != FWT_F64 || n < qse::kOzMinN || n > qse::kOzMaxN)
             return FWT_EUNSUPPORTED;
+    } else if (kind == FWT_ABLATION_MFMA_TRANSPOSE) {
+        // both factors n / 2 and n - n / 2 within the matrix-core row kernel
+        if (n < 2 * kMfmaRowMin || n > 2 * mfma_row_max(dtype))
+            return n < 0 || n > FWT_MAX_N ? FWT_EINVAL : FWT_EUNSUPPORTED;
     } else {
         return FWT_EINVAL;
     }
@@ -980,7 +984,7 @@ int fwt_ablation_workspace(int kind, int64_t batch, int n, fwt_dtype dtype, int 
 {
     if (!out || batch < 0 || n < 0 || n > FWT_MAX_N)
         return FWT_EINVAL;
-    if (kind < FWT_ABLATION_STAGEWISE || kind > FWT_ABLATION_OZAKI)
+    if (kind < FWT_ABLATION_STAGEWISE || kind > FWT_ABLATION_MFMA_TRANSPOSE)
         return FWT_EINVAL;
     *out = ablation_workspace_bytes(kind, batch, n, dtype, with_im);
     return FWT_OK;
@@ -1012,8 +1016,12 @@ int fwt_ablation_execute(int kind, int64_t batch, int n, fwt_dtype dtype, void* 
     } else {
         const size_t esize = f64 ? 8 : 4;
         void* ws_im = im ? (char*)workspace + (size_t)batch * ((size_t)1 << n) * esize : nullptr;
-        e = qse::ablation_popc_gemm(f64, re, im, workspace, ws_im, batch, n, normalize, c,
-                                    stream);
+        if (kind == FWT_ABLATION_MFMA_TRANSPOSE)
+            e = qse::ablation_mfma_transpose(f64, re, im, workspace, ws_im, batch, n, normalize,
+                                             c, stream);
+        else
+            e = qse::ablation_popc_gemm(f64, re, im, workspace, ws_im, batch, n, normalize, c,
+                                        stream);
     }
     return e == hipSuccess ? FWT_OK : hip_fail(e);
 }

@@ -126,6 +126,13 @@ size_t oz_workspace_layout(int64_t batch, int n, int comps, size_t* off_partial,
 hipError_t ablation_ozaki(double* re, double* im, int64_t batch, int n, double c, void* ws,
                           hipStream_t stream);
 
+// Matrix-core block products on both Kronecker factors with a transposed
+// staging buffer in between (n1 = n / 2, n2 = n - n1, each 8..15 for fp32,
+// 8..14 for fp64); ws_re / ws_im hold batch * 2^n elements each.
+hipError_t ablation_mfma_transpose(int f64, void* re, void* im, void* ws_re, void* ws_im,
+                                   int64_t batch, int n, int normalize, double c,
+                                   hipStream_t stream);
+
 // Matrix-core row pass over the km contiguous low bits (8 <= km <= 15
 // for fp32, 14 for fp64).
 hipError_t ablation_mfma_row(int f64, void* re, void* im, int64_t batch, int n, int km,

@@ -45,6 +45,11 @@ hipError_t ablation_ozaki(double*, double*, int64_t, int, double, void*, hipStre
 {
     return hipErrorNotSupported;
 }
+hipError_t ablation_mfma_transpose(int, void*, void*, void*, void*, int64_t, int, int, double,
+                                   hipStream_t)
+{
+    return hipErrorNotSupported;
+}
 hipError_t ablation_mfma_row(int, void*, void*, int64_t, int, int, int, double, hipStream_t)
 {
     return hipErrorNotSupported;

@@ -420,6 +420,15 @@ def test_ablation_workspace_and_validation(lib):
     assert ex(qse.ABLATION_MFMA, 1, 10, 0, FAKE + 4, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EALIGN
     assert ex(qse.ABLATION_MFMA, 0, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_OK
     assert qse.ablation_workspace(qse.ABLATION_MFMA, 64, 14, "f32", True) == 0
+    mt = qse.ABLATION_MFMA_TRANSPOSE
+    assert qse.ablation_workspace(mt, 4, 20, "f32", True) == 2 * 4 * 4 << 20
+    assert qse.ablation_workspace(mt, 4, 20, "f64", False) == 4 * 8 << 20
+    for n, dtype, want in ((15, "f32", qse.FWT_EUNSUPPORTED), (31, "f32", qse.FWT_EINVAL),
+                           (29, "f64", qse.FWT_EUNSUPPORTED), (16, "f32", qse.FWT_EINVAL)):
+        # n = 16 passes the range check and then fails on the missing workspace
+        st = lib.fwt_ablation_execute(mt, 1, n, 0 if dtype == "f32" else 1, FAKE, FAKE + (8 << 30),
+                                      1, None, 0, None)
+        assert st == want, (n, dtype, st)
     # INT8 / CRT: fp64, 5 <= n <= 28, residues (m = 8 moduli at n = 10, two
     # 4-byte words per element) plus per-vector scales
     oz = qse.ABLATION_OZAKI

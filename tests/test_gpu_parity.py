@@ -626,7 +626,7 @@ def test_timed_passes_follow_the_chunk_schedule():
 
 
 ABLATION_KINDS = {"stagewise": qse.ABLATION_STAGEWISE, "popc_gemm": qse.ABLATION_POPC_GEMM,
-                  "mfma": qse.ABLATION_MFMA}
+                  "mfma": qse.ABLATION_MFMA, "mfma_transpose": qse.ABLATION_MFMA_TRANSPOSE}
 
 
 @pytest.mark.parametrize("kind", ["stagewise", "popc_gemm", "mfma"])
@@ -757,7 +757,7 @@ def test_mfma_path_plan(dtype, n, batch):
     assert np.array_equal(tre.cpu().numpy(), gre) and np.array_equal(tim.cpu().numpy(), gim)
 
 
-@pytest.mark.parametrize("kind", ["stagewise", "popc_gemm", "mfma"])
+@pytest.mark.parametrize("kind", ["stagewise", "popc_gemm", "mfma", "mfma_transpose"])
 def test_gaussian_ablations_n20(kind):
     k = ABLATION_KINDS[kind]
     say("ablation gauss %s n=20" % kind)
@@ -769,6 +769,63 @@ def test_gaussian_ablations_n20(kind):
     qse.ablation_execute(k, tre, tim, n=20, normalize=True, workspace=ws)
     torch.cuda.synchronize()
     assert_close("f32", 20, re, im, tre.cpu().numpy(), tim.cpu().numpy())
+
+
+# Matrix-core block products on both factors with the transposed staging
+# buffer: every split n/2 | n - n/2 from 8 | 8 to the widest (15 | 15 fp32,
+# 14 | 14 fp64), odd n, several vectors.
+@pytest.mark.parametrize("dtype,n,batch", [("f32", 16, 3), ("f32", 17, 2), ("f32", 20, 2),
+                                           ("f32", 23, 1), ("f64", 16, 3), ("f64", 19, 2),
+                                           ("f64", 23, 1)])
+def test_integer_mfma_transpose_ablation(dtype, n, batch):
+    say("ablation mfma+transpose %s n=%d batch=%d" % (dtype, n, batch))
+    k = qse.ABLATION_MFMA_TRANSPOSE
+    npd = np.float32 if dtype == "f32" else np.float64
+    # n >= 23: inputs in {-1, 0, 1} keep every partial sum an exact integer
+    lo, hi = (-8, 9) if n < 23 else (-1, 2)
+    rng = np.random.default_rng(98_000 + n)
+    re = rng.integers(lo, hi, size=(batch, 1 << n)).astype(npd)
+    im = rng.integers(lo, hi, size=(batch, 1 << n)).astype(npd)
+    for normalize in (False, True):
+        if normalize and (n % 2 or n >= 23):
+            continue
+        tre, tim = to_dev(re), to_dev(im)
+        wsb = qse.ablation_workspace(k, batch, n, dtype, True)
+        ws = torch.empty(wsb // 4, dtype=torch.float32, device="cuda")
+        qse.ablation_execute(k, tre, tim, n=n, normalize=normalize, workspace=ws)
+        torch.cuda.synchronize()
+        assert_exact(tre.cpu().numpy(), re, n, normalize)
+        assert_exact(tim.cpu().numpy(), im, n, normalize)
+        del ws
+
+
+@pytest.mark.parametrize("dtype,n", [("f32", 30), ("f64", 28)])
+def test_mfma_transpose_ablation_widest(dtype, n):
+    """The widest split (15 | 15 fp32, 14 | 14 fp64): a two-hot input
+    against its closed form at all 2^n outputs, on the device (exact)."""
+    say("ablation mfma+transpose widest %s n=%d" % (dtype, n))
+    tdt = torch.float32 if dtype == "f32" else torch.float64
+    N = 1 << n
+    j, k = 0x2AAAAAAA & (N - 1), 0x15555555 & (N - 1) | (1 << (n - 1))
+    re = torch.zeros(1, N, dtype=tdt, device="cuda")
+    im = torch.zeros(1, N, dtype=tdt, device="cuda")
+    re[0, j] = 1.0
+    re[0, k] = 2.0
+    im[0, k] = 1.0
+    im[0, j] = -1.0
+    kind = qse.ABLATION_MFMA_TRANSPOSE
+    ws = torch.empty(qse.ablation_workspace(kind, 1, n, dtype, True) // 4, device="cuda")
+    qse.ablation_execute(kind, re, im, n=n, normalize=False, workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+    i = torch.arange(N, device="cuda", dtype=torch.int64)
+    sj = (1 - 2 * _parity(i & j)).to(tdt)
+    sk = (1 - 2 * _parity(i & k)).to(tdt)
+    del i
+    assert torch.equal(re[0], sj + 2 * sk)
+    assert torch.equal(im[0], sk - sj)
+    del re, im, sj, sk
+    torch.cuda.empty_cache()
 
 
 def test_bound_call_keeps_its_plan_alive():
