@@ -215,11 +215,12 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
         p.lo = lo;
         p.k = k;
     }
-    // Column passes of 8..10 bits with rows of at least 8 groups default to
+    // Column passes of 8..11 bits with rows of at least 8 groups default to
     // it as well: measured 0.2-5.5 % faster per call (fp32 n = 19..25, fp64
     // n = 23..24; the n = 24 fp64 workload 2.9 %), and within 0.4 % at fp64
-    // n = 20.
-    if (all_default && !row && kr >= 8 && kr <= 10 && lo - vec_bits(dtype) >= 3) {
+    // n = 20.  The 11-bit column factor (fp32 n = 26, fp64 n = 25, 2 GiB
+    // states) took a call 13 % less time than on the LDS tiles.
+    if (all_default && !row && kr >= 8 && kr <= 11 && lo - vec_bits(dtype) >= 3) {
         const int rc = build_lx_pass(p, n, dtype, lo, k, kr, row, t, multipass);
         if (rc == FWT_OK)
             return rc;
@@ -405,7 +406,9 @@ int build_wave_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool
 // row bits, kr = eb + (6 - gbits) + W.  Default (measured best for 7..10
 // column bits): 16 groups while the tile fits 128 KiB of LDS, else 8;
 // eb = 4 (W = 2 or 3); one exchange in two phases, so that a tile takes
-// 64 KiB of LDS (32 KiB at 8 row bits) and two or more share a CU.
+// 64 KiB of LDS (32 KiB at 8 row bits) and two or more share a CU.  At 11
+// column bits (8 groups, 128 KiB of slots) the two phases need W < eb:
+// eb = 5, W = 3.
 int build_lx_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool row,
                   const fwt_pass_tuning& t, bool multipass)
 {
@@ -432,6 +435,8 @@ int build_lx_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool r
         eb = 4;
     else if (row)
         eb = kr - 6 - (kr >= 10 ? (kr - 8 < 4 ? kr - 8 : 4) : 1);
+    else if (kr + gbits > 13)
+        eb = (kr - lr + 2) / 2;   // two phases: w < eb
     else
         eb = kr - lr - 1 < 4 ? kr - lr - 1 : 4;
     const int w = kr - lr - eb;

@@ -291,7 +291,7 @@ def test_lane_exchange_plans(lib):
 def test_default_kernel_choice(lib):
     """One-pass plans of 3 <= n <= 10 default to the wave-tile kernel; other
     row passes of 8..13 vector bits to the lane-exchange kernel (except a
-    multi-pass row pass of 11), and so do column passes of 8..10 bits with
+    multi-pass row pass of 11), and so do column passes of 8..11 bits with
     rows of at least 8 groups; the rest, and entries with any field forced,
     use the LDS tiles."""
     for dtype, vb in (("f32", 2), ("f64", 1)):
@@ -301,20 +301,22 @@ def test_default_kernel_choice(lib):
             assert qse.Plan(n, dtype, split=(n,)).pass_config(0)["wave"] == want, (dtype, n)
         assert qse.Plan(8, dtype, split=(8,), eb=(3,)).pass_config(0)["wave"] == 0
         assert qse.Plan(12, dtype, split=(12,), eb=(3,)).pass_config(0)["wave"] == 0
-        for split in ((5, 5), (7, 7), (2, 8), (3, 3, 4), (11, 9), (6, 10), (10, 7)):
+        for split in ((5, 5), (7, 7), (2, 8), (3, 3, 4), (11, 9), (6, 10), (10, 7),
+                      (10, 11), (4, 11), (5, 11)):
             p = qse.Plan(sum(split), dtype, split=split)
             lo, want = 0, []
             for i, b in enumerate(split):
                 if i == 0:
                     want.append(2 if b - vb >= 8 and b - vb != 11 else 0)
                 else:
-                    want.append(2 if 8 <= b <= 10 and lo - vb >= 3 else 0)
+                    want.append(2 if 8 <= b <= 11 and lo - vb >= 3 else 0)
                 lo += b
             assert [p.pass_config(i)["wave"] for i in range(p.num_passes)] == want, split
     for (dtype, n), (bits, wave) in {
             ("f32", 16): ([10, 6], [2, 0]), ("f32", 19): ([10, 9], [2, 2]),
             ("f32", 20): ([12, 8], [2, 2]), ("f32", 22): ([13, 9], [0, 2]),
-            ("f32", 26): ([15, 11], [2, 0]), ("f64", 15): ([9, 6], [2, 0]),
+            ("f32", 26): ([15, 11], [2, 2]), ("f64", 15): ([9, 6], [2, 0]),
+            ("f64", 25): ([14, 11], [2, 2]),
             ("f64", 19): ([11, 8], [2, 2]), ("f64", 21): ([12, 9], [0, 2]),
             ("f64", 24): ([14, 10], [2, 2])}.items():
         p = qse.Plan(n, dtype)
@@ -324,6 +326,9 @@ def test_default_kernel_choice(lib):
     assert qse.Plan(20, "f32").kernel_name(1) == "lx_kernel<float, 8, 4, 2, 1, 4, false>"
     assert qse.Plan(24, "f64").kernel_name(1) == "lx_kernel<double, 10, 4, 3, 1, 3, false>"
     assert qse.Plan(25, "f32").kernel_name(1) == "lx_kernel<float, 10, 4, 3, 1, 3, false>"
+    # 11 column bits: 8 groups, eb = 5, W = 3, two phases
+    assert qse.Plan(26, "f32").kernel_name(1) == "lx_kernel<float, 11, 5, 3, 1, 3, false>"
+    assert qse.Plan(25, "f64").kernel_name(1) == "lx_kernel<double, 11, 5, 3, 1, 3, false>"
     # a 13-vector-bit row pass of a two-pass plan: one exchange in two phases
     for n in (23, 24, 25):
         assert qse.Plan(n, "f64").kernel_name(0) == "lx_kernel<double, 13, 4, 3, 1, 0, true>"
