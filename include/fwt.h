@@ -91,8 +91,8 @@ int fwt_plan_create(fwt_plan_t* out, int n, fwt_dtype dtype, fwt_path path);
  * bit counts bits[0..npasses-1] sum to n.  bits[0] is the factor on the
  * lowest (contiguous) index bits, bits[1] the next, and so on; so the
  * two-factor split n = n1 + n2 of the pull request's section "How" is
- * {n2, n1}.  Each factor must be within the per-pass limit (14 bits fp32 /
- * 13 bits fp64 for bits[0], 12 bits for the others) and every factor after
+ * {n2, n1}.  Each factor must be within the per-pass limit (15 bits fp32 /
+ * 14 bits fp64 for bits[0], 12 bits for the others) and every factor after
  * the first needs at least 2 (fp32) / 1 (fp64) bits below it.
  * Returns FWT_OK, FWT_EINVAL (null pointers, npasses < 1, sum != n, a
  * factor < 1 or out of its limit), FWT_ENOMEM or FWT_EHIP. */
@@ -119,21 +119,31 @@ typedef struct {
     int wave;    /* 1: wave-tile kernel (a whole tile in one wave, lane bits
                     crossed with DPP / ds_swizzle / permlane swaps, no LDS;
                     row bits - eb <= 6 - gbits); 2: lane-exchange kernel
-                    (row passes only: lanes hold the 6 lowest row bits, a
-                    workgroup of 2^(6 + w) threads holds the tile with
-                    w = row bits - 6 - eb wave bits, 1 <= w <= 4 and
-                    2 <= eb <= 5 or eb = w = 1, and ceil(w / eb) LDS
-                    exchanges move the wave bits into registers; default
-                    eb gives w = min(4, row bits - 8), or 1 below 10 row
-                    bits, except eb = 4 with 2 exchange phases for the
-                    13-row-bit row pass of a multi-pass plan); 0: LDS
-                    tiles.  Default, when every field of the
-                    entry is -1: the wave-tile kernel for a one-pass plan
-                    with 3 <= n <= 10; else the lane-exchange kernel for a
-                    row pass of 8..13 row bits, except the row pass of a
-                    multi-pass plan with 11; else LDS tiles.  "Row bits"
-                    counts 16-byte vectors: the pass's bits less 2 (fp32)
-                    or 1 (fp64). */
+                    (lanes hold the 6 - gbits lowest row bits and, in a
+                    column pass, the gbits column-group bits; a workgroup
+                    of 2^(6 + w) threads holds the tile with
+                    w = row bits - (6 - gbits) - eb wave bits, 1 <= w <= 4
+                    and 2 <= eb <= 5 or eb = w = 1, and ceil(w / eb) LDS
+                    exchanges move the wave bits into registers.  Row
+                    passes: 8..13 row bits; default eb gives
+                    w = min(4, row bits - 8), or 1 below 10 row bits,
+                    except eb = 4 with 2 exchange phases for the
+                    13-row-bit row pass of a multi-pass plan.  Column
+                    passes: 6..11 bits, gbits 3 or 4 (2^(bits + gbits)
+                    16-byte slots at most 2^14, and at most 2^13 without
+                    phases); default gbits 4 up to 9 bits when a row
+                    holds 16 groups, else 3; eb = min(4, row bits -
+                    (6 - gbits) - 1), or 5 at 11 bits; 2 phases from
+                    2^11 slots when w < eb); 0: LDS tiles.  Default, when
+                    every field of the entry is -1: the wave-tile kernel
+                    for a one-pass plan with 3 <= n <= 10; else the
+                    lane-exchange kernel for a row pass of 8..13 row bits,
+                    except the row pass of a multi-pass plan with 11, and
+                    for a column pass of 8..11 bits whose rows hold at
+                    least 8 groups; else LDS tiles.  "Row bits" of a row
+                    pass counts 16-byte vectors: the pass's bits less 2
+                    (fp32) or 1 (fp64); of a column pass, the pass's
+                    bits. */
 } fwt_pass_tuning;
 
 /* As fwt_plan_create_split, with the on-chip tiling of each pass forced
