@@ -94,6 +94,26 @@ def time_events(torch, stream, fn, reps):
     return start.elapsed_time(end) / reps
 
 
+def cache_copy_ceiling(torch, mib=64, reps=200):
+    """GB/s of the streaming copy between two mib-MiB buffers that stay in
+    the Infinity Cache across calls (read + write bytes per call): the
+    ceiling of a chunked pass, whose chunk also stays there between its
+    passes."""
+    import quantum_state_encoding_amd as qse
+    dev = torch.device("cuda:0")
+    src = torch.randn((mib << 20) // 4, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    fn = lambda: qse.stream_copy(dst, src)
+    for _ in range(10):
+        fn()
+    torch.cuda.synchronize()
+    ms = min(time_events(torch, stream, fn, reps) for _ in range(3))
+    del src, dst
+    return {"gbps": 2 * (mib << 20) / (ms * 1e-3) / 1e9, "bytes_per_call": 2 * (mib << 20),
+            "us_per_call": ms * 1e3}
+
+
 def cpu_baseline(w, repeats=2):
     """The oracle's timed mode (textbook transform in the workload's dtype,
     a pool of POSIX threads over the real vectors) on the whole batch."""
@@ -498,6 +518,10 @@ def main():
                                "pct_peak_accounted": 100 * gb / HBM_PEAK_GBS,
                                "note": "4 GiB state, HBM-bound; %d steps" % max(20, args.steps // 5)}
 
+    # Copy ceilings: the whole state through HBM (copy_gbps) and a working
+    # set that stays in the Infinity Cache, as a chunk does between passes.
+    cache_copy = cache_copy_ceiling(torch)
+
     # The pages' own designs for the same transform, on the same state.
     ablations = {}
     if not args.no_ablations:
@@ -531,6 +555,7 @@ def main():
         "per_pass_ms": r["per_pass_ms"],
         "copy_ms": r["copy_ms"],
         "copy_gbps": 2 * S / (r["copy_ms"] * 1e-3) / 1e9 if r["copy_ms"] else None,
+        "cache_copy": cache_copy,
         "wall_ms_per_step": r["wall_ms"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -543,6 +568,7 @@ def main():
                      "kernel": "pass %d (%d bits, %s)" % (dom, r["pass_bits"][dom] if r["pass_bits"] else 0,
                                                            "row" if dom == 0 else "column"),
                      "bytes_per_launch": launch_bytes,
+                     "frac_of_cache_copy": achieved / cache_copy["gbps"],
                      "launches_per_step": r["passes"] * (-(-w.batch // r["chunk"]))},
         "cpu_baseline": cpu,
         "involution_check": r["check"],
