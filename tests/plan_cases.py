@@ -117,6 +117,9 @@ def _lx_column_cases():
                         lo = gb + vb + 2          # 4 column blocks per row
                         out.append((dtype, lo + kr + 1, (lo, kr, 1), eb, gb, ph, 1))
     out += [("f32", 20, (12, 8), -1, -1, -1, 3), ("f64", 24, (14, 10), -1, -1, -1, 1),
-            ("f64", 20, (11, 9), -1, -1, -1, 2), ("f32", 19, (10, 9), -1, 3, -1, 5)]
+            ("f64", 20, (11, 9), -1, -1, -1, 2), ("f32", 19, (10, 9), -1, 3, -1, 5),
+            # default 11-bit columns whose rows are exactly one tile wide
+            ("f32", 16, (5, 11), -1, -1, -1, 3), ("f64", 15, (4, 11), -1, -1, -1, 2),
+            ("f32", 19, (8, 11), -1, -1, -1, 1)]
     return out
 LX_COLUMN_CASES = _lx_column_cases()

@@ -252,7 +252,7 @@ def test_every_gpu_test_plan_is_valid(lib):
                  for name, v in (("eb", eb), ("gbits", gbits), ("phases", phases), ("wave", 2))}
         c = qse.Plan(n, dtype, split=split, **knobs).pass_config(1)
         assert c["wave"] == 2 and c["kind"] == "column"
-    assert len(LX_COLUMN_CASES) == 82  # all 78 compiled column variants appear
+    assert len(LX_COLUMN_CASES) == 85  # all 78 compiled column variants appear
 
 
 def test_lane_exchange_plans(lib):
