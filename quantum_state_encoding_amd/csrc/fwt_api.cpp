@@ -149,6 +149,25 @@ int build_wave_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool
 int build_lx_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool row,
                   const fwt_pass_tuning& t, bool multipass);
 
+// Largest 32-bit lane offset of a pass's tile group must fit (lanes address
+// from the workgroup's first tile).  Returns FWT_OK or FWT_EUNSUPPORTED.
+int check_offsets(const Pass& p, fwt_dtype dtype, bool row, int kr, int vb)
+{
+    const int esize_bits = dtype == FWT_F64 ? 3 : 2;
+    const uint64_t tmax = ((uint64_t)1 << p.tpw_bits) - 1;
+    uint64_t max_el;
+    if (row) {
+        max_el = ((tmax + 1) << p.k) - 1;
+    } else {
+        const uint64_t mask = ((uint64_t)1 << p.nblk_bits) - 1;
+        max_el = ((tmax >> p.nblk_bits) << (p.lo + kr)) + ((tmax & mask) << (p.gbits + vb)) +
+                 ((((uint64_t)1 << kr) - 1) << p.lo) + ((uint64_t)1 << (p.gbits + vb)) - 1;
+    }
+    if ((max_el << esize_bits) + ((uint64_t)1 << esize_bits) - 1 > 0xFFFFFFFFull)
+        return FWT_EUNSUPPORTED;
+    return FWT_OK;
+}
+
 int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tuning& t,
                bool multipass)
 {
@@ -294,20 +313,9 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
     }
     // Lanes address from the workgroup's first tile with 32-bit byte
     // offsets; the largest one must fit.
-    {
-        const int esize_bits = dtype == FWT_F64 ? 3 : 2;
-        const uint64_t tmax = ((uint64_t)1 << tpw_bits) - 1;
-        uint64_t max_el;
-        if (row) {
-            max_el = ((tmax + 1) << k) - 1;
-        } else {
-            const uint64_t mask = ((uint64_t)1 << p.nblk_bits) - 1;
-            max_el = ((tmax >> p.nblk_bits) << (lo + kr)) + ((tmax & mask) << (gbits + vb)) +
-                     ((((uint64_t)1 << kr) - 1) << lo) + ((uint64_t)1 << (gbits + vb)) - 1;
-        }
-        if ((max_el << esize_bits) + ((uint64_t)1 << esize_bits) - 1 > 0xFFFFFFFFull)
-            return FWT_EUNSUPPORTED;
-    }
+    p.tpw_bits = tpw_bits;
+    if (check_offsets(p, dtype, row, kr, vb) != FWT_OK)
+        return FWT_EUNSUPPORTED;
     if (!qse::kernel_available(p.key))
         return FWT_EUNSUPPORTED;
     // Tiles so large that a CU holds one workgroup run in the persistent
@@ -328,25 +336,6 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
     p.block = 1u << (p.tt_bits + tpw_bits);
     p.lds = needs_lds ? (tile_lds << tpw_bits) : 0;
     p.tiles_bits = row ? (n - k) : (n - lo - k) + p.nblk_bits;
-    return FWT_OK;
-}
-
-// Largest 32-bit lane offset of a pass's tile group must fit (lanes address
-// from the workgroup's first tile).  Returns FWT_OK or FWT_EUNSUPPORTED.
-int check_offsets(const Pass& p, fwt_dtype dtype, bool row, int kr, int vb)
-{
-    const int esize_bits = dtype == FWT_F64 ? 3 : 2;
-    const uint64_t tmax = ((uint64_t)1 << p.tpw_bits) - 1;
-    uint64_t max_el;
-    if (row) {
-        max_el = ((tmax + 1) << p.k) - 1;
-    } else {
-        const uint64_t mask = ((uint64_t)1 << p.nblk_bits) - 1;
-        max_el = ((tmax >> p.nblk_bits) << (p.lo + kr)) + ((tmax & mask) << (p.gbits + vb)) +
-                 ((((uint64_t)1 << kr) - 1) << p.lo) + ((uint64_t)1 << (p.gbits + vb)) - 1;
-    }
-    if ((max_el << esize_bits) + ((uint64_t)1 << esize_bits) - 1 > 0xFFFFFFFFull)
-        return FWT_EUNSUPPORTED;
     return FWT_OK;
 }
 
