@@ -635,16 +635,23 @@ ABLATION_KINDS = {"stagewise": qse.ABLATION_STAGEWISE, "popc_gemm": qse.ABLATION
                                            ("f64", 14, 2), ("f32", 17, 1)])
 def test_integer_ablations(kind, dtype, n, batch):
     """The pages' designs (one launch per stage; popcount GEMM + transposes;
-    H_16 blocks on the matrix cores) compute exactly the same transform."""
+    H_16 blocks on the matrix cores) compute exactly the same transform.
+    Below their smallest size (the scaffold: n < 2; the matrix-core row
+    kernel: n < 8) they refuse with FWT_EUNSUPPORTED and leave the data as
+    it was."""
     k = ABLATION_KINDS[kind]
-    if kind == "popc_gemm" and n < 2:
-        pytest.skip("the scaffold needs n >= 2")
-    if kind == "mfma" and n < 8:
-        pytest.skip("the matrix-core row kernel needs n >= 8")
     say("ablation %s %s n=%d batch=%d" % (kind, dtype, n, batch))
     npd = np.float32 if dtype == "f32" else np.float64
     re = ints((batch, 1 << n), 99_000 + n, npd)
     im = ints((batch, 1 << n), 99_500 + n, npd)
+    if (kind == "popc_gemm" and n < 2) or (kind == "mfma" and n < 8):
+        tre, tim = to_dev(re), to_dev(im)
+        with pytest.raises(qse.FwtError) as ei:
+            qse.ablation_execute(k, tre, tim, n=n, normalize=False, workspace=None)
+        assert ei.value.status == qse.FWT_EUNSUPPORTED
+        torch.cuda.synchronize()
+        assert np.array_equal(tre.cpu().numpy(), re) and np.array_equal(tim.cpu().numpy(), im)
+        return
     for normalize in (False, True):
         if normalize and n % 2:
             continue
