@@ -123,3 +123,61 @@ def _lx_column_cases():
             ("f32", 19, (8, 11), -1, -1, -1, 1)]
     return out
 LX_COLUMN_CASES = _lx_column_cases()
+
+
+# Seeded random plans: a Kronecker split of n into 1-4 factors and, per
+# pass, the default kernel or one family forced (LDS tiles, wave tiles,
+# lane exchange) with random tiling fields.  `valid(dtype, n, split, kw)`
+# tells whether the planner accepts the plan; only accepted plans are kept.
+# Each case: (dtype, n, split, kw, batch), kw the Plan keyword arguments.
+RANDOM_MODES = ("default", "lds", "wave", "lx")
+
+
+def random_plan_cases(valid, count=80, seed=20_261_202):
+    import numpy as np
+    rng = np.random.default_rng(seed)
+
+    def pick(choices):
+        # the default (-1) half of the time, else one of choices
+        return -1 if rng.random() < 0.5 else int(rng.choice(choices))
+
+    out = []
+    tries = 0
+    while len(out) < count and tries < 200_000:
+        tries += 1
+        dtype = ("f32", "f64")[int(rng.integers(0, 2))]
+        n = int(rng.integers(4, 21))
+        npasses = int(rng.choice([1, 2, 3, 4], p=[0.15, 0.35, 0.3, 0.2]))
+        if npasses > n:
+            continue
+        cuts = sorted(int(c) for c in rng.choice(np.arange(1, n), npasses - 1, replace=False))
+        split = tuple(b - a for a, b in zip([0] + cuts, cuts + [n]))
+        fields = {f: [] for f in ("eb", "gbits", "phases", "pipe", "wave")}
+        modes = []
+        for i in range(npasses):
+            mode = RANDOM_MODES[int(rng.integers(0, len(RANDOM_MODES)))]
+            modes.append(mode)
+            v = {f: -1 for f in fields}
+            if mode == "lds":
+                v["wave"] = 0
+                v["eb"] = pick([1, 2, 3, 4, 5])
+                v["gbits"] = pick([0, 1, 2, 3, 4]) if i else -1
+                v["phases"] = pick([0, 1, 2]) if i else -1
+                v["pipe"] = pick([0, 1])
+            elif mode == "wave":
+                v["wave"] = 1
+                v["eb"] = pick([0, 1, 2, 3, 4, 5])
+                v["gbits"] = pick([0, 1, 2, 3, 4]) if i else -1
+            elif mode == "lx":
+                v["wave"] = 2
+                v["eb"] = pick([1, 2, 3, 4, 5])
+                v["gbits"] = pick([3, 4]) if i else -1
+                v["phases"] = pick([0, 1])
+            for f in fields:
+                fields[f].append(v[f])
+        kw = {f: tuple(vals) for f, vals in fields.items()}
+        if not valid(dtype, n, split, kw):
+            continue
+        batch = max(1, min(int(rng.integers(1, 6)), (1 << 22) >> n))
+        out.append((dtype, n, split, kw, batch, tuple(modes)))
+    return out

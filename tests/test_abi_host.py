@@ -255,6 +255,31 @@ def test_every_gpu_test_plan_is_valid(lib):
     assert len(LX_COLUMN_CASES) == 85  # all 78 compiled column variants appear
 
 
+def test_random_plan_cases_keep_their_mix(lib):
+    """The seeded random plans of the GPU suite: 80 accepted plans, each
+    kernel family forced in at least 10 passes, at least 30 multi-pass
+    plans, and every forced family actually selected by the planner."""
+    from collections import Counter
+    from plan_cases import random_plan_cases
+
+    def accepts(dtype, n, split, kw):
+        try:
+            qse.Plan(n, dtype, split=split, **kw)
+            return True
+        except qse.FwtError:
+            return False
+    cases = random_plan_cases(accepts)
+    assert len(cases) == 80
+    modes = Counter(m for c in cases for m in c[5])
+    assert all(modes[m] >= 10 for m in ("default", "lds", "wave", "lx")), modes
+    assert sum(len(c[2]) > 1 for c in cases) >= 30
+    for dtype, n, split, kw, batch, mode in cases:
+        p = qse.Plan(n, dtype, split=split, **kw)
+        for i, m in enumerate(mode):
+            if m != "default" and not (dtype == "f32" and n == 1):
+                assert p.pass_config(i)["wave"] == {"lds": 0, "wave": 1, "lx": 2}[m]
+
+
 def test_lane_exchange_plans(lib):
     # lanes hold 6 row bits, w wave bits (default: the most threads with
     # eb >= 2), one tile per workgroup

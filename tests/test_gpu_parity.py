@@ -21,7 +21,7 @@ import oracle
 import quantum_state_encoding_amd as qse
 import workloads
 from plan_cases import (FORCED_SPLITS, LDS_SINGLE_CASES, LX_CASES, LX_COLUMN_CASES, LX_PHASE_CASES,
-                        PIPE_CASES, VARIANTS, WAVE_CASES)
+                        PIPE_CASES, VARIANTS, WAVE_CASES, random_plan_cases)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -254,6 +254,37 @@ def test_integer_lane_exchange_columns(dtype, n, split, eb, gbits, phases, batch
         gre, gim = run(plan, re, im, True)
         assert_exact(gre, re, n, True)
         assert_exact(gim, im, n, True)
+
+
+def _planner_accepts(dtype, n, split, kw):
+    try:
+        qse.Plan(n, dtype, split=split, **kw)
+        return True
+    except qse.FwtError:
+        return False
+
+
+RANDOM_CASES = random_plan_cases(_planner_accepts)
+
+
+@pytest.mark.parametrize("dtype,n,split,kw,batch,modes", RANDOM_CASES,
+                         ids=["r%02d-%s-n%d-%s" % (i, c[0], c[1], "-".join(c[5]))
+                              for i, c in enumerate(RANDOM_CASES)])
+def test_integer_random_plans(dtype, n, split, kw, batch, modes):
+    """Seeded random plans (1-3 factors, each pass on its default kernel
+    or with a kernel family and random tiling fields forced), exactly
+    against the oracle."""
+    say("random plan %s n=%d split=%s %s batch=%d" % (dtype, n, split, kw, batch))
+    npd = np.float32 if dtype == "f32" else np.float64
+    plan = qse.Plan(n, dtype, split=split, **kw)
+    assert plan.pass_bits == list(split)
+    seed = 123_000 + 31 * n + len(split)
+    re = ints((batch, 1 << n), seed, npd)
+    im = ints((batch, 1 << n), seed + 1, npd)
+    for normalize in ((False, True) if n % 2 == 0 else (False,)):
+        gre, gim = run(plan, re, im, normalize)
+        assert_exact(gre, re, n, normalize)
+        assert_exact(gim, im, n, normalize)
 
 
 @pytest.mark.parametrize("dtype,n,batch", [("f32", 12, 1), ("f32", 12, 3), ("f32", 12, 257),
