@@ -230,7 +230,7 @@ def bench_workload(torch, w, steps, warmup, with_passes=True, split="configured"
     return {"ms": ms, "wall_ms": wall_ms, "passes": passes, "pass_bits": plan.pass_bits,
             "per_pass_ms": per_pass, "copy_ms": copy_ms, "S": S, "chunk": chunk,
             "check": check, "reps_ms": reps,
-            "kernel_names": [plan.kernel_name(i) for i in range(passes)]}
+            "kernel_names": [plan.kernel_name(i, w.batch) for i in range(passes)]}
 
 
 def _read_csv(path):
@@ -293,7 +293,7 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
           "# pass | kernel | launches | FETCH KiB | WRITE KiB | scaled HBM bytes/launch | "
           "algorithmic bytes/launch | ratio | avg us (trace)"]
     for i in range(plan.num_passes):
-        kname = plan.kernel_name(i)
+        kname = plan.kernel_name(i, w.batch)
         cand = [(k, v) for k, v in groups.items() if kname in k[0]]
         if not cand:
             continue
@@ -368,7 +368,7 @@ def summarize_ablations(workload, kt_dir, command):
     import quantum_state_encoding_amd as qse
     w = workloads.WORKLOADS[workload]
     plan = qse.Plan(w.n, w.dtype, split=w.split or None)
-    main = [plan.kernel_name(i) for i in range(plan.num_passes)] + ["stream_copy_kernel"]
+    main = [plan.kernel_name(i, w.batch) for i in range(plan.num_passes)] + ["stream_copy_kernel"]
     groups = {}
     for r in _read_csv(_find(kt_dir, "kernel_trace.csv")):
         name = r["Kernel_Name"]
@@ -501,7 +501,7 @@ def main():
             rs = bench_workload(torch, ws, max(args.steps, 200), args.warmup, with_passes=False,
                                 split=sp)
             also[label] = {"ms_per_step": rs["ms"], "passes": rs["passes"],
-                           "pass_bits": rs["pass_bits"],
+                           "pass_bits": rs["pass_bits"], "kernel_names": rs["kernel_names"],
                            "amplitudes_per_s": ws.batch * ws.N / (rs["ms"] * 1e-3),
                            "gbps_accounted": 2 * ws.state_bytes * rs["passes"] /
                            (rs["ms"] * 1e-3) / 1e9,

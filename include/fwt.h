@@ -128,7 +128,9 @@ typedef struct {
                     passes: 8..13 row bits; default eb gives
                     w = min(4, row bits - 8), or 1 below 10 row bits,
                     except eb = 4 with 2 exchange phases for the
-                    13-row-bit row pass of a multi-pass plan.  Column
+                    13-row-bit row pass of a multi-pass plan, and eb = 3
+                    for a one-pass plan of 12 row bits on a state of at
+                    most 256 MiB (fwt_plan_call_pass_config).  Column
                     passes: 6..11 bits, gbits 3 or 4 (2^(bits + gbits)
                     16-byte slots at most 2^14, and at most 2^13 without
                     phases); default gbits 4 up to 9 bits when a row
@@ -228,6 +230,16 @@ int fwt_plan_pass_bits(fwt_plan_t plan, int i, int* out_bits);
  * workgroup, pipelined (1) or not (0), wave-tile kernel (1) or not (0).
  * `out` must hold 12 ints.  Returns FWT_OK or FWT_EINVAL. */
 int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out);
+
+/* The tiling (as fwt_plan_pass_config) that pass i of an fwt_execute call
+ * on `batch` vectors (with_im != 0: both components) launches.  A one-pass
+ * plan may carry a second tiling for states that fit the 256 MiB Infinity
+ * Cache (fp32 n = 14 and fp64 n = 13 by default: one LDS exchange in
+ * 512-thread workgroups instead of two in 1024-thread ones); other plans
+ * launch fwt_plan_pass_config's tiling at every size.  The transform is
+ * the same either way.  Returns FWT_OK or FWT_EINVAL (null argument, i out
+ * of range, batch < 0). */
+int fwt_plan_call_pass_config(fwt_plan_t plan, int i, int64_t batch, int with_im, int* out);
 
 /* Release a plan; NULL is a no-op.  Returns FWT_OK. */
 int fwt_plan_destroy(fwt_plan_t plan);

@@ -34,7 +34,8 @@ _DTYPES = {"f32": 0, "f64": 1}
 EXPORTED_SYMBOLS = ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create_tuned",
                     "fwt_execute", "fwt_execute_pass", "fwt_execute_pass_timed",
                     "fwt_execute_check",
-                    "fwt_plan_num_passes", "fwt_plan_pass_config", "fwt_plan_pass_bits",
+                    "fwt_plan_num_passes", "fwt_plan_pass_config", "fwt_plan_call_pass_config",
+                    "fwt_plan_pass_bits",
                     "fwt_plan_destroy", "fwt_strerror", "fwt_last_hip_error",
                     "fwt_stream_copy", "fwt_plan_chunk_vectors", "fwt_ablation_workspace",
                     "fwt_ablation_execute")
@@ -87,6 +88,7 @@ def load_library():
     lib.fwt_plan_num_passes.argtypes = [vp, pi]
     lib.fwt_plan_pass_bits.argtypes = [vp, i32, pi]
     lib.fwt_plan_pass_config.argtypes = [vp, i32, pi]
+    lib.fwt_plan_call_pass_config.argtypes = [vp, i32, i64, i32, pi]
     lib.fwt_plan_destroy.argtypes = [vp]
     lib.fwt_strerror.argtypes = [i32]
     lib.fwt_strerror.restype = ctypes.c_char_p
@@ -97,7 +99,8 @@ def load_library():
     for name in ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create_tuned",
                  "fwt_execute", "fwt_execute_pass", "fwt_execute_pass_timed",
                  "fwt_execute_check", "fwt_plan_num_passes", "fwt_plan_pass_bits",
-                 "fwt_plan_pass_config", "fwt_plan_destroy", "fwt_last_hip_error",
+                 "fwt_plan_pass_config", "fwt_plan_call_pass_config", "fwt_plan_destroy",
+                 "fwt_last_hip_error",
                  "fwt_stream_copy"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -180,10 +183,16 @@ class Plan:
             bits.append(out.value)
         return bits
 
-    def pass_config(self, i):
-        """Tiling of pass i as a dict (see fwt_plan_pass_config)."""
+    def pass_config(self, i, batch=None, with_im=True):
+        """Tiling of pass i as a dict (fwt_plan_pass_config); with `batch`,
+        the tiling a call on that many vectors launches
+        (fwt_plan_call_pass_config)."""
         out = (ctypes.c_int * 12)()
-        st = load_library().fwt_plan_pass_config(self._h, int(i), out)
+        if batch is None:
+            st = load_library().fwt_plan_pass_config(self._h, int(i), out)
+        else:
+            st = load_library().fwt_plan_call_pass_config(self._h, int(i), int(batch),
+                                                           1 if with_im else 0, out)
         if st != FWT_OK:
             raise FwtError(st, "fwt_plan_pass_config")
         keys = ("lo", "bits", "kind", "kr", "eb", "gbits", "phase_bits", "block", "lds",
@@ -192,9 +201,10 @@ class Plan:
         d["kind"] = ("row", "column", "pair", "mfma")[d["kind"]]
         return d
 
-    def kernel_name(self, i):
-        """Demangled name of pass i's kernel as profilers print it."""
-        c = self.pass_config(i)
+    def kernel_name(self, i, batch=None, with_im=True):
+        """Demangled name of pass i's kernel as profilers print it (for a
+        call on `batch` vectors when given)."""
+        c = self.pass_config(i, batch, with_im)
         if c["kind"] == "pair":
             return "pair_f32_kernel"
         t = "float" if self.dtype == "f32" else "double"

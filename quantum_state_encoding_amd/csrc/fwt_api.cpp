@@ -73,6 +73,10 @@ struct fwt_plan_s {
     fwt_dtype dtype;
     int npasses;
     Pass passes[kMaxPasses];
+    // One-pass plans only: the pass launched instead of passes[0] when the
+    // call's state fits the Infinity Cache (has_small != 0).
+    int has_small;
+    Pass small;
 };
 
 namespace {
@@ -552,6 +556,23 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
         }
         lo += bits[i];
     }
+    // A one-pass plan of 12 vector bits on the lane-exchange kernel keeps a
+    // second tiling for states that fit the Infinity Cache: 512 threads of
+    // 8 vectors and one LDS exchange (eb = 3) instead of 1024 threads of 4
+    // and two (eb = 2).  Measured on MI355X (fp32 n = 14, fp64 n = 13): 3-10 %
+    // faster per call on states of 4-192 MiB (n = 14, batch 64: 6.05 against
+    // 6.28 us), equal at 256 MiB, and 4-5 % slower at 384-512 MiB, where the
+    // extra threads keep more HBM reads in flight.
+    p->has_small = 0;
+    const bool pass0_default =
+        !tuning || (tuning[0].eb < 0 && tuning[0].gbits < 0 && tuning[0].phases < 0 &&
+                    tuning[0].pipe < 0 && tuning[0].wave < 0);
+    if (p->npasses == 1 && !mfma_row && pass0_default && p->passes[0].key.wave == 2 &&
+        p->passes[0].key.row && p->passes[0].key.kr == 12 && p->passes[0].key.eb == 2) {
+        const fwt_pass_tuning t3{3, -1, -1, -1, 2};
+        if (build_lx_pass(p->small, n, dtype, 0, n, 12, true, t3, false) == FWT_OK)
+            p->has_small = 1;
+    }
     if (log_enabled()) {
         std::fprintf(stderr, "[fwt] plan n=%d dtype=%s passes=%d\n", n,
                      dtype == FWT_F64 ? "f64" : "f32", p->npasses);
@@ -682,6 +703,18 @@ int64_t chunk_vectors(const fwt_plan_s* plan, int64_t batch, int ncomp)
     return v > 0 ? v : 1;
 }
 
+// Whether a call on `batch` vectors of ncomp components launches the plan's
+// cache-resident tiling: a one-pass plan that has one, on a state of at
+// most the Infinity Cache's 256 MiB.
+bool use_small(const fwt_plan_s* plan, int64_t batch, int ncomp)
+{
+    if (!plan->has_small)
+        return false;
+    const size_t esize = plan->dtype == FWT_F64 ? 8 : 4;
+    const size_t vec_bytes = ((size_t)1 << plan->n) * esize * (size_t)ncomp;
+    return (size_t)batch <= kChunkBytes / vec_bytes;
+}
+
 // Enqueue passes [first, last) over `batch` vectors starting at re/im.  In
 // a multi-pass plan the first pass reads and the last pass writes with
 // nontemporal hints: their data is not reused by this call, while the
@@ -710,8 +743,9 @@ int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, vo
     const int ncomp = im ? 2 : 1;
     const double c = norm_constant(n);
     const bool multi = plan->npasses >= 2;
+    const bool small = use_small(plan, batch, ncomp);
     for (int i = first; i < last; ++i) {
-        const Pass& p = plan->passes[i];
+        const Pass& p = small ? plan->small : plan->passes[i];
         const bool final_pass = (i == plan->npasses - 1);
         const int do_scale = (normalize && final_pass) ? 1 : 0;
         hipError_t e;
@@ -1020,11 +1054,10 @@ int fwt_ablation_execute(int kind, int64_t batch, int n, fwt_dtype dtype, void* 
     return e == hipSuccess ? FWT_OK : hip_fail(e);
 }
 
-int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out)
+namespace {
+
+void pass_config(const Pass& p, int* out)
 {
-    if (!valid_plan(plan) || !out || i < 0 || i >= plan->npasses)
-        return FWT_EINVAL;
-    const Pass& p = plan->passes[i];
     out[0] = p.lo;
     out[1] = p.k;
     out[2] = p.mfma ? 3 : (p.pair ? 2 : (p.key.row ? 0 : 1));
@@ -1037,6 +1070,23 @@ int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out)
     out[9] = p.tpw_bits;
     out[10] = p.key.pipe;
     out[11] = p.key.wave;
+}
+
+}  // namespace
+
+int fwt_plan_pass_config(fwt_plan_t plan, int i, int* out)
+{
+    if (!valid_plan(plan) || !out || i < 0 || i >= plan->npasses)
+        return FWT_EINVAL;
+    pass_config(plan->passes[i], out);
+    return FWT_OK;
+}
+
+int fwt_plan_call_pass_config(fwt_plan_t plan, int i, int64_t batch, int with_im, int* out)
+{
+    if (!valid_plan(plan) || !out || i < 0 || i >= plan->npasses || batch < 0)
+        return FWT_EINVAL;
+    pass_config(use_small(plan, batch, with_im ? 2 : 1) ? plan->small : plan->passes[i], out);
     return FWT_OK;
 }
 

@@ -37,6 +37,10 @@ int main()
                         int b = 0, cfg[12];
                         bad += fwt_plan_pass_bits(p, i, &b) != FWT_OK;
                         bad += fwt_plan_pass_config(p, i, cfg) != FWT_OK;
+                        for (int64_t batch : {(int64_t)0, (int64_t)64, (int64_t)1 << 40})
+                            for (int w = 0; w <= 1; ++w)
+                                bad += fwt_plan_call_pass_config(p, i, batch, w, cfg) != FWT_OK;
+                        bad += fwt_plan_call_pass_config(p, i, -1, 1, cfg) != FWT_EINVAL;
                         sum += b;
                     }
                     bad += np > 0 && n > 0 && sum != n;
@@ -66,8 +70,10 @@ int main()
         if (st == FWT_OK) {
             int cfg[12], np2 = 0;
             fwt_plan_num_passes(p, &np2);
-            for (int i = 0; i < np2; ++i)
+            for (int i = 0; i < np2; ++i) {
                 bad += fwt_plan_pass_config(p, i, cfg) != FWT_OK;
+                bad += fwt_plan_call_pass_config(p, i, rnd(0, 1 << 20), rnd(0, 1), cfg) != FWT_OK;
+            }
             fwt_plan_destroy(p);
             ++ok;
         } else if (st != FWT_EINVAL && st != FWT_EUNSUPPORTED) {

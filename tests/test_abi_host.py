@@ -255,6 +255,38 @@ def test_every_gpu_test_plan_is_valid(lib):
     assert len(LX_COLUMN_CASES) == 85  # all 78 compiled column variants appear
 
 
+def test_cache_resident_tiling_of_12_bit_one_pass_plans(lib):
+    """Default one-pass plans of 12 vector bits (fp32 n = 14, fp64 n = 13)
+    launch eb = 3 (512 threads, one exchange) on states up to 256 MiB and
+    eb = 2 (1024 threads, two exchanges) above; forced tilings, other n and
+    multi-pass plans launch one tiling at every size."""
+    for dtype, n, esize in (("f32", 14, 4), ("f64", 13, 8)):
+        for plan in (qse.Plan(n, dtype), qse.Plan(n, dtype, split=(n,)),
+                     qse.Plan(n, dtype, split=(n,), eb=(-1,))):
+            assert plan.pass_config(0)["eb"] == 2
+            limit = (256 << 20) // ((1 << n) * esize)      # vectors of one component
+            for batch, with_im, eb in ((0, True, 3), (1, True, 3), (64, True, 3),
+                                       (limit // 2, True, 3), (limit // 2 + 1, True, 2),
+                                       (limit, False, 3), (limit + 1, False, 2)):
+                c = plan.pass_config(0, batch, with_im)
+                assert (c["eb"], c["wave"], c["block"]) == (eb, 2, 512 if eb == 3 else 1024), \
+                    (dtype, batch, with_im)
+            assert plan.kernel_name(0, 64) == "lx_kernel<%s, 12, 3, 3, 0, 0, true>" % (
+                "float" if dtype == "f32" else "double")
+        forced = qse.Plan(n, dtype, split=(n,), eb=(2,), wave=(2,))
+        assert forced.pass_config(0, 64)["eb"] == 2
+    for dtype, n in (("f32", 13), ("f32", 15), ("f64", 14), ("f32", 20), ("f64", 24)):
+        plan = qse.Plan(n, dtype)
+        for i in range(plan.num_passes):
+            assert plan.pass_config(i, 1) == plan.pass_config(i)
+    plan = qse.Plan(14, "f32")
+    out = (ctypes.c_int * 12)()
+    assert lib.fwt_plan_call_pass_config(plan._h, 0, -1, 1, out) == qse.FWT_EINVAL
+    assert lib.fwt_plan_call_pass_config(plan._h, 1, 1, 1, out) == qse.FWT_EINVAL
+    assert lib.fwt_plan_call_pass_config(None, 0, 1, 1, out) == qse.FWT_EINVAL
+    assert lib.fwt_plan_call_pass_config(plan._h, 0, 1, 1, None) == qse.FWT_EINVAL
+
+
 def test_random_plan_cases_keep_their_mix(lib):
     """The seeded random plans of the GPU suite: 80 accepted plans, each
     kernel family forced in at least 10 passes, at least 30 multi-pass

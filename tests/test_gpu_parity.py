@@ -427,18 +427,25 @@ def test_largest_n_closed_form(dtype, n):
 
 
 @pytest.mark.parametrize("dtype,n,batch", [("f32", 4, 1 << 24), ("f64", 3, 1 << 23),
-                                           ("f32", 10, (1 << 16) + 3)])
+                                           ("f32", 10, (1 << 16) + 3), ("f32", 14, 2048),
+                                           ("f32", 14, 2049), ("f64", 13, 2048),
+                                           ("f64", 13, 2051)])
 def test_large_batch_one_pass(dtype, n, batch):
     """One-pass plans (the wave-tile kernel by default) at the largest
-    batches a 1-2 GiB state holds, ragged in the last case: sampled vectors
-    exactly against the oracle, and every vector through the exact
-    normalised involution (integer inputs, even n: H H / 2^n = I)."""
+    batches a 1-2 GiB state holds, ragged in the last case, and the
+    12-vector-bit plans on either side of their 256 MiB switch between two
+    tilings: sampled vectors exactly against the oracle, and every vector
+    through the exact normalised involution (integer inputs, even n:
+    H H / 2^n = I)."""
     say("large batch %s n=%d batch=%d" % (dtype, n, batch))
     tdt = torch.float32 if dtype == "f32" else torch.float64
     g = torch.Generator(device="cuda").manual_seed(4242 + n)
     re = torch.randint(-8, 9, (batch, 1 << n), generator=g, device="cuda").to(tdt)
     im = torch.randint(-8, 9, (batch, 1 << n), generator=g, device="cuda").to(tdt)
     plan = qse.Plan(n, dtype)
+    if n - (2 if dtype == "f32" else 1) == 12:
+        resident = batch * (2 << n) * (4 if dtype == "f32" else 8) <= 256 << 20
+        assert plan.pass_config(0, batch)["eb"] == (3 if resident else 2)
     rows = [0, 1, batch // 3, batch - 1]
     re0, im0 = re[rows].cpu().numpy(), im[rows].cpu().numpy()
     ore, oim = re.clone(), im.clone()
