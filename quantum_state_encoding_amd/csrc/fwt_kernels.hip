@@ -1,6 +1,11 @@
 // gfx950 kernels for the batched in-place Walsh-Hadamard transform.
 //
-// Every pass is one launch of tile_kernel.  A pass owns the index bits
+// Every pass is one launch of one of three kernel families, all built on
+// the tiles described here: tile_kernel (and its persistent pipelined form
+// tile_kernel_pipe) exchanges through padded LDS tiles; wave_kernel holds a
+// whole tile in one wave and crosses lanes without LDS; lx_kernel keeps the
+// lowest row bits in lanes and moves only the wave bits through unpadded
+// LDS.  The planner picks one per pass.  A pass owns the index bits
 // [lo, lo + k) of each real vector (the Kronecker factor H_{2^k} acting on
 // those bits, Apache Mahout pull request "[QDP] [feature] Pr4 kronecker
 // fwt", sections "Why" and "How"; iThome "Day 18" native-FWT article,
