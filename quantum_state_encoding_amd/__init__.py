@@ -225,23 +225,7 @@ class Plan:
 
     def _check_tensors(self, re, im):
         """Validate torch tensors for this plan; returns the batch size."""
-        import torch
-        want = torch.float32 if self.dtype == "f32" else torch.float64
-        N = 1 << self.n
-        for name, t in (("re", re), ("im", im)):
-            if t is None:
-                continue
-            if not t.is_cuda:
-                raise ValueError("%s must be a device tensor" % name)
-            if t.dtype != want:
-                raise ValueError("%s must be %s" % (name, want))
-            if not t.is_contiguous():
-                raise ValueError("%s must be contiguous" % name)
-            if t.numel() % N:
-                raise ValueError("%s.numel() is not a multiple of 2^%d" % (name, self.n))
-        if im is not None and im.numel() != re.numel():
-            raise ValueError("re and im must have the same number of elements")
-        return re.numel() // N
+        return _check_state(re, im, self.n, self.dtype)
 
     def execute(self, re, im=None, normalize=True, stream=None):
         """Transform torch device tensors re (and im) in place.
@@ -292,8 +276,7 @@ class Plan:
 
     def execute_pass(self, i, re, im=None, normalize=True, stream=None):
         """Enqueue only pass i (see fwt_execute_pass) on torch tensors."""
-        N = 1 << self.n
-        batch = re.numel() // N
+        batch = self._check_tensors(re, im)
         st = load_library().fwt_execute_pass(
             self._h, int(i), batch, self.n, ctypes.c_void_p(re.data_ptr()),
             ctypes.c_void_p(im.data_ptr() if im is not None else None),
@@ -306,13 +289,13 @@ class Plan:
         """Enqueue pass i with torch timing events `start`/`stop` recorded
         by the kernel dispatch itself (see fwt_execute_pass_timed)."""
         import torch
+        batch = self._check_tensors(re, im)
         s = torch.cuda.current_stream() if stream is None else stream
         for ev in (start, stop):
             if not ev.cuda_event:          # torch creates events lazily
                 ev.record(s)
-        N = 1 << self.n
         st = load_library().fwt_execute_pass_timed(
-            self._h, int(i), re.numel() // N, self.n, ctypes.c_void_p(re.data_ptr()),
+            self._h, int(i), batch, self.n, ctypes.c_void_p(re.data_ptr()),
             ctypes.c_void_p(im.data_ptr() if im is not None else None), 1 if normalize else 0,
             ctypes.c_void_p(s.cuda_stream), ctypes.c_void_p(start.cuda_event),
             ctypes.c_void_p(stop.cuda_event))
@@ -369,6 +352,31 @@ def ablation_workspace(kind, batch, n, dtype="f32", with_im=True):
     return out.value
 
 
+def _check_state(re, im, n, dtype):
+    """Validate planar state tensors (dtype "f32"/"f64", vectors of 2^n
+    elements); returns the batch size.  Raises ValueError."""
+    import torch
+    want = torch.float32 if dtype == "f32" else torch.float64
+    N = 1 << n
+    if re is None:
+        raise ValueError("re is required")
+    for name, t in (("re", re), ("im", im)):
+        if t is None:
+            continue
+        if t.dtype != want:
+            raise ValueError("%s must be %s" % (name, want))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.numel() % N:
+            raise ValueError("%s.numel() is not a multiple of 2^%d" % (name, n))
+    if im is not None and im.numel() != re.numel():
+        raise ValueError("re and im must have the same number of elements")
+    for name, t in (("re", re), ("im", im)):
+        if t is not None and not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+    return re.numel() // N
+
+
 def ablation_execute(kind, re, im=None, n=None, normalize=True, workspace=None, stream=None):
     """Run one of the pages' designs (fwt_ablation_execute) on torch tensors
     in place; `workspace` is a device tensor of at least ablation_workspace
@@ -378,7 +386,9 @@ def ablation_execute(kind, re, im=None, n=None, normalize=True, workspace=None, 
     dtype = {"torch.float32": "f32", "torch.float64": "f64"}.get(str(re.dtype))
     if dtype is None:
         raise ValueError("re must be float32 or float64")
-    batch = re.numel() >> n
+    batch = _check_state(re, im, n, dtype)
+    if workspace is not None and not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load_library().fwt_ablation_execute(

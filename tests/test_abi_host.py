@@ -459,6 +459,35 @@ def test_stream_copy_rejects_before_any_hip_call(lib):
     assert lib.fwt_stream_copy(FAKE, FAKE + 4096, 0, None) == qse.FWT_OK
 
 
+def test_binding_validates_tensors_before_the_library(lib):
+    """Every tensor entry point of the binding rejects a wrong dtype, a
+    non-contiguous view, a size that is not whole vectors, mismatched re/im
+    sizes and host tensors with ValueError, before any library call."""
+    torch = pytest.importorskip("torch")
+    p32, p64 = qse.Plan(4, "f32"), qse.Plan(4, "f64")
+    z = torch.zeros
+    bad = [(p32, z(16, dtype=torch.float64), None, "float32"),
+           (p64, z(16), None, "float64"),
+           (p32, z(16), z(16, dtype=torch.float64), "float32"),
+           (p32, z(32)[::2], None, "contiguous"),
+           (p32, z(15), None, "multiple"),
+           (p32, z(16), z(32), "same number"),
+           (p32, z(16), None, "device"),
+           (p32, None, None, "required")]
+    ev = None
+    for plan, re, im, msg in bad:
+        calls = [lambda: plan.execute(re, im), lambda: plan.bind(re, im),
+                 lambda: plan.execute_pass(0, re, im)]
+        if ev is not None:
+            calls.append(lambda: plan.execute_pass_timed(0, re, im, ev, ev))
+        # the ablation entry takes its dtype from re
+        if re is not None and re.dtype == (torch.float32 if plan.dtype == "f32" else torch.float64):
+            calls.append(lambda: qse.ablation_execute(qse.ABLATION_STAGEWISE, re, im, n=4))
+        for call in calls:
+            with pytest.raises(ValueError, match=msg):
+                call()
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import importlib
     monkeypatch.setattr(qse, "_lib", None)
