@@ -16,10 +16,17 @@
 //    count of k AND i, a batched transpose, the same GEMM for H_{n1}, and a
 //    transpose back (the pull request's section "How": the naive implicit
 //    Hadamard GEMM placeholder, the batch transpose between the two GEMM
-//    stages, the temporary buffers; its "4-step blocked algorithm").
+//    stages, the temporary buffers; its "4-step blocked algorithm");
+//  * matrix-core blocks on both Kronecker factors: the block-Hadamard row
+//    kernel on the low n2 bits, a batched transpose into a staging buffer,
+//    the same kernel on the other n1 bits, and a transpose back (the
+//    iThome article, sections "TF32 path" and "Data flow of the
+//    implementation": block GEMM, transpose into a staging buffer, block
+//    GEMM, transpose back).
 //
-// Both compute exactly the transform of the tile passes (a different
-// association of the same sums), so they share its parity tests.
+// All of them compute exactly the transform of the tile passes (a
+// different association of the same sums), so they share its parity
+// tests.
 #include <hip/hip_runtime.h>
 
 #include "fwt_internal.h"
@@ -327,7 +334,8 @@ hipError_t mfma_row_launch(T* re, T* im, int64_t tiles, int do_scale, double c,
     for (int64_t t0 = 0; t0 < tiles; t0 += per_launch) {
         const int64_t nt = tiles - t0 < per_launch ? tiles - t0 : per_launch;
         const int64_t off = t0 << KM;
-        hipLaunchKernelGGL((mfma_row_kernel<T, KM>), dim3((unsigned)((nt + TPW - 1) / TPW), im ? 2 : 1),
+        hipLaunchKernelGGL((mfma_row_kernel<T, KM>),
+                           dim3((unsigned)((nt + TPW - 1) / TPW), im ? 2 : 1),
                            dim3(mfma_threads<KM>()), lds, stream, re + off, im ? im + off : nullptr,
                            nt, do_scale, (T)c);
         e = hipGetLastError();

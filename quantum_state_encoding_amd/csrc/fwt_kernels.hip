@@ -450,8 +450,14 @@ __device__ __forceinline__ double lane_partner(double v)
     return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
-__device__ __forceinline__ float fma_sign(float x, float s, float p) { return __builtin_fmaf(x, s, p); }
-__device__ __forceinline__ double fma_sign(double x, double s, double p) { return __builtin_fma(x, s, p); }
+__device__ __forceinline__ float fma_sign(float x, float s, float p)
+{
+    return __builtin_fmaf(x, s, p);
+}
+__device__ __forceinline__ double fma_sign(double x, double s, double p)
+{
+    return __builtin_fma(x, s, p);
+}
 
 // Swap lane bit 4 (LBIT = 4) or 5 with the register pair (a, b).
 template <int LBIT>

@@ -11,8 +11,9 @@
 //   Y = H_n X is an integer with |Y_k| <= 2^(48 + n);
 //   m primes p_j <= 251 with prod p_j > 2^(49 + n) carry Y through CRT:
 //   residues r_j = X mod p_j (|r| <= 127, int8, four moduli packed in a
-//   32-bit word per element), transformed in residue space, then Y rebuilt from the residues by the CRT with a
-//   rounded quotient: t_j = r_j (M / p_j)^-1 mod p_j (within p_j / 2 + 1),
+//   32-bit word per element), transformed in residue space, then Y
+//   rebuilt from the residues by the CRT with a rounded quotient:
+//   t_j = r_j (M / p_j)^-1 mod p_j (within p_j / 2 + 1),
 //   q = nearest integer to sum_j t_j / p_j (fp64), Y = sum_j t_j M / p_j -
 //   q M in 128-bit integers (exact: |Y| / M stays below 1/2 by a margin of
 //   at least 0.003, the fp64 quotient errs by under 1e-12), and
@@ -523,14 +524,17 @@ hipError_t ablation_ozaki(double* re, double* im, int64_t batch, int n, double c
         }
     }
 
-    const dim3 grid(stride_grid(groups), comps);
+    // The merge kernel is compiled per modulus count (7..10).
+    decltype(&oz_merge_kernel<7>) merge;
     switch (k.m) {
-    case 7: hipLaunchKernelGGL(oz_merge_kernel<7>, grid, dim3(256), 0, stream, re, im, n, groups, exps, batch, words, plane_len, c, k); break;
-    case 8: hipLaunchKernelGGL(oz_merge_kernel<8>, grid, dim3(256), 0, stream, re, im, n, groups, exps, batch, words, plane_len, c, k); break;
-    case 9: hipLaunchKernelGGL(oz_merge_kernel<9>, grid, dim3(256), 0, stream, re, im, n, groups, exps, batch, words, plane_len, c, k); break;
-    case 10: hipLaunchKernelGGL(oz_merge_kernel<10>, grid, dim3(256), 0, stream, re, im, n, groups, exps, batch, words, plane_len, c, k); break;
+    case 7: merge = &oz_merge_kernel<7>; break;
+    case 8: merge = &oz_merge_kernel<8>; break;
+    case 9: merge = &oz_merge_kernel<9>; break;
+    case 10: merge = &oz_merge_kernel<10>; break;
     default: return hipErrorInvalidValue;
     }
+    hipLaunchKernelGGL(merge, dim3(stride_grid(groups), comps), dim3(256), 0, stream, re, im, n,
+                       groups, exps, batch, words, plane_len, c, k);
     return hipGetLastError();
 }
 
