@@ -34,8 +34,15 @@ def log(msg):
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace are
+    dropped first, so that an edit of either keeps the counter record."""
+    import re as _re
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = _re.sub(r"/\*.*?\*/", "", src, flags=_re.S)
+    src = _re.sub(r"//[^\n]*", "", src)
+    src = _re.sub(r"\s+", "", src)
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def traffic_record(workload, dominant_pass):
