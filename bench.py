@@ -563,6 +563,10 @@ def main():
         "copy_ms": r["copy_ms"],
         "copy_gbps": 2 * S / (r["copy_ms"] * 1e-3) / 1e9 if r["copy_ms"] else None,
         "cache_copy": cache_copy,
+        # the step against one same-run copy of the state (read S, write S)
+        "copy_fraction": {"accounted": gbps_accounted / (2 * S / (r["copy_ms"] * 1e-3) / 1e9),
+                          "algorithmic": gbps_alg / (2 * S / (r["copy_ms"] * 1e-3) / 1e9)}
+        if r["copy_ms"] else None,
         "wall_ms_per_step": r["wall_ms"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
