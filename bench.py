@@ -293,8 +293,16 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
         lines.append("%s | %d x %d | %d | %.2f | %.2f | %.2f" % (
             short(name), gx, gy, len(d), np.mean(d) / 1e3, np.min(d) / 1e3, np.max(d) / 1e3))
     passes = {}
+
+    def run_command(counters, out_dir, out_name):
+        # the recorded trace command, with the counter run's options and
+        # output directory
+        c = command.replace("--kernel-trace --stats", counters).replace(" -o kt ", " -o %s " % out_name)
+        return c.replace(os.path.basename(os.path.normpath(kt_dir)),
+                         os.path.basename(os.path.normpath(out_dir)))
     tl = ["# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (separate runs): %s" % workload,
-          "# command: " + command.replace("--kernel-trace --stats", "--pmc FETCH_SIZE|WRITE_SIZE"),
+          "# commands: " + run_command("--pmc FETCH_SIZE", fetch_dir, "f"),
+          "#           " + run_command("--pmc WRITE_SIZE", write_dir, "w"),
           "# calibration on fwt_stream_copy of %.0f KiB each way: FETCH_SIZE x %.4f, "
           "WRITE_SIZE x %.4f" % (half_kib, f_scale or float("nan"), w_scale or float("nan")),
           "# pass | kernel | launches | FETCH KiB | WRITE KiB | scaled HBM bytes/launch | "
@@ -331,10 +339,9 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
             a["dispatches"] = a.get("dispatches", 0) + 1
         lds_lines = ["# rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS "
                      "SQ_LDS_MEM_VIOLATIONS SQ_LDS_UNALIGNED_STALL: %s" % workload,
-                     "# command: " + command.replace("--kernel-trace --stats",
-                                                     "--pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
-                                                     "SQ_INSTS_LDS SQ_LDS_MEM_VIOLATIONS "
-                                                     "SQ_LDS_UNALIGNED_STALL"),
+                     "# command: " + run_command("--pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+                                                 "SQ_INSTS_LDS SQ_LDS_MEM_VIOLATIONS "
+                                                 "SQ_LDS_UNALIGNED_STALL", lds_dir, "l"),
                      "# kernel | grid | dispatches | LDS instructions | LDS active cycles | "
                      "bank-conflict cycles | conflict / active | memory violations | "
                      "unaligned stalls"]
