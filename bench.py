@@ -121,9 +121,11 @@ def cache_copy_ceiling(torch, mib=64, reps=200):
             "us_per_call": ms * 1e3}
 
 
-def cpu_baseline(w, repeats=2):
+def cpu_baseline(w, repeats=5):
     """The oracle's timed mode (textbook transform in the workload's dtype,
-    a pool of POSIX threads over the real vectors) on the whole batch."""
+    a pool of POSIX threads over the real vectors) on the whole batch, run
+    `repeats` times (about 10 thread-seconds of CPU work at n=20, batch
+    256); the median is reported."""
     import oracle
     threads = min(16, len(os.sched_getaffinity(0)))
     re, im = workloads.gen(w)
@@ -140,8 +142,8 @@ def cpu_baseline(w, repeats=2):
     return {"value": amps / t, "unit": "amplitudes/s", "cores": int(used), "kind": "oracle",
             "ms": t * 1e3,
             "sample": "whole workload: %d complex vectors of 2^%d (%d real transforms, %s), "
-                      "median of %d runs of %.3f s" % (w.batch, w.n, 2 * w.batch, w.dtype,
-                                                     repeats, t)}
+                      "median of %d runs of %.3f s on %d threads" % (
+                          w.batch, w.n, 2 * w.batch, w.dtype, repeats, t, int(used))}
 
 
 def bench_workload(torch, w, steps, warmup, with_passes=True, split="configured"):
