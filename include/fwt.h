@@ -183,10 +183,29 @@ int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im,
  * (with_im != 0: both components): a multi-pass call whose state exceeds
  * the 256 MiB Infinity Cache runs every pass on one chunk of vectors before
  * the next chunk, so later passes re-read what earlier passes left in the
- * cache.  *out = 0 means no chunking.  fwt_execute is then exactly, for
- * each chunk in order, fwt_execute_pass for passes 0..P-1 on that chunk.
- * Returns FWT_OK or FWT_EINVAL (null argument, batch < 0). */
+ * cache.  fwt_execute is then exactly, for each chunk in order,
+ * fwt_execute_pass for passes 0..P-1 on that chunk.  *out = 0 means no
+ * chunking by whole vectors: none at all, or the chunks of blocks smaller
+ * than a vector that fwt_plan_call_schedule describes.  Returns FWT_OK or
+ * FWT_EINVAL (null argument, batch < 0). */
 int fwt_plan_chunk_vectors(fwt_plan_t plan, int64_t batch, int with_im, int64_t* out);
+
+/* The whole chunk schedule of an fwt_execute call on `batch` vectors
+ * (with_im != 0: both components).  Passes 0 .. *chunked_passes - 1 run
+ * chunk by chunk, in order, each chunk being *blocks_per_chunk consecutive
+ * blocks of 2^*block_bits elements of each component (the last chunk may
+ * hold fewer); the remaining passes then run over the whole state.
+ * *chunked_passes = 0: no chunking.  Blocks are whole vectors
+ * (*block_bits = n) unless one vector exceeds the 256 MiB Infinity Cache:
+ * then the leading passes whose bits all lie below *block_bits are the
+ * chunked ones (a transform of each block on its own), e.g. fp32 n = 27,
+ * batch 2, passes [10, 9, 8]: passes 0 and 1 on chunks of 64 blocks of
+ * 2^19 elements, then pass 2.  Chunking never changes the arithmetic of a
+ * pass: the result is bit for bit that of running the passes in order
+ * over the whole state.  Returns FWT_OK or FWT_EINVAL (null argument,
+ * batch < 0). */
+int fwt_plan_call_schedule(fwt_plan_t plan, int64_t batch, int with_im, int* chunked_passes,
+                           int* block_bits, int64_t* blocks_per_chunk);
 
 /* Enqueue only pass `pass` (0 <= pass < fwt_plan_num_passes; 0 for an
  * n = 0 plan, which has none and does nothing) of the plan, with the

@@ -37,7 +37,8 @@ EXPORTED_SYMBOLS = ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create
                     "fwt_plan_num_passes", "fwt_plan_pass_config", "fwt_plan_call_pass_config",
                     "fwt_plan_pass_bits",
                     "fwt_plan_destroy", "fwt_strerror", "fwt_last_hip_error",
-                    "fwt_stream_copy", "fwt_plan_chunk_vectors", "fwt_ablation_workspace",
+                    "fwt_stream_copy", "fwt_plan_chunk_vectors", "fwt_plan_call_schedule",
+                    "fwt_ablation_workspace",
                     "fwt_ablation_execute")
 
 _lib = None
@@ -81,6 +82,8 @@ def load_library():
     lib.fwt_plan_create_tuned.argtypes = [ctypes.POINTER(vp), i32, i32, i32, pi,
                                           ctypes.POINTER(PassTuning)]
     lib.fwt_plan_chunk_vectors.argtypes = [vp, i64, i32, ctypes.POINTER(i64)]
+    lib.fwt_plan_call_schedule.argtypes = [vp, i64, i32, pi, pi, ctypes.POINTER(i64)]
+    lib.fwt_plan_call_schedule.restype = i32
     lib.fwt_execute.argtypes = [vp, i64, i32, vp, vp, i32, vp]
     lib.fwt_execute_pass.argtypes = [vp, i32, i64, i32, vp, vp, i32, vp]
     lib.fwt_execute_pass_timed.argtypes = [vp, i32, i64, i32, vp, vp, i32, vp, vp, vp]
@@ -250,6 +253,17 @@ class Plan:
         if st != FWT_OK:
             raise FwtError(st, "fwt_plan_chunk_vectors")
         return out.value
+
+    def call_schedule(self, batch, with_im=True):
+        """(chunked passes, log2 elements per block, blocks per chunk) of a
+        call on `batch` vectors (see fwt_plan_call_schedule)."""
+        cp, bb, bl = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+        st = load_library().fwt_plan_call_schedule(self._h, int(batch), 1 if with_im else 0,
+                                                   ctypes.byref(cp), ctypes.byref(bb),
+                                                   ctypes.byref(bl))
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_plan_call_schedule")
+        return cp.value, bb.value, bl.value
 
     def bind(self, re, im=None, normalize=True, stream=None):
         """A zero-argument callable that enqueues fwt_execute on these

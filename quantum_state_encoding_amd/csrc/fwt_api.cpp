@@ -687,20 +687,65 @@ int validate(fwt_plan_t plan, int64_t batch, int n, const void* re, const void* 
     return rc;
 }
 
-// Vectors per chunk of a call: multi-pass calls whose state exceeds the
-// Infinity Cache run all passes on one chunk of about kChunkBytes before
-// the next chunk starts, so the later passes re-read data the earlier
-// passes left in the cache.  0 = one chunk (the whole batch).
-int64_t chunk_vectors(const fwt_plan_s* plan, int64_t batch, int ncomp)
+// The chunk schedule of a call.  A multi-pass call whose state exceeds the
+// Infinity Cache runs its leading passes on one chunk of about kChunkBytes
+// before the next chunk starts, so that the later passes re-read what the
+// earlier ones left in the cache.  A chunk is `blocks` consecutive blocks
+// of 2^block_bits elements of each component.  Normally a block is a whole
+// vector (block_bits = n) and every pass runs per chunk.  When one vector
+// alone exceeds the cache, the leading passes whose bits all lie below
+// block_bits < n touch each block of 2^block_bits elements on its own, so
+// they run per chunk of such blocks, and the remaining passes then run
+// over the whole state (fp32 n = 27, [10, 9, 8]: passes 0 and 1 per chunk
+// of 64 blocks of 2^19 elements, then pass 2; 14 % faster than whole
+// vectors per chunk).  chunked = 0: no chunking.
+struct Schedule {
+    int chunked;        // leading passes run chunk by chunk
+    int block_bits;     // log2 elements per block
+    int64_t blocks;     // blocks per chunk
+};
+
+Schedule call_schedule(const fwt_plan_s* plan, int64_t batch, int ncomp)
 {
-    if (plan->npasses < 2)
-        return 0;
+    Schedule s{0, plan->n, 0};
+    const int np = plan->npasses;
+    if (np < 2)
+        return s;
     const size_t esize = plan->dtype == FWT_F64 ? 8 : 4;
     const size_t vec_bytes = ((size_t)1 << plan->n) * esize * (size_t)ncomp;
     if ((size_t)batch * vec_bytes <= kChunkBytes)
-        return 0;
-    const int64_t v = (int64_t)(kChunkBytes / vec_bytes);
-    return v > 0 ? v : 1;
+        return s;
+    if (vec_bytes <= kChunkBytes) {
+        s.chunked = np;
+        s.blocks = (int64_t)(kChunkBytes / vec_bytes);
+        return s;
+    }
+    // The longest run of leading passes (not the last, none on the matrix
+    // cores) whose bits fit one cached block.
+    int lead = 0, lead_bits = 0, bits = 0;
+    for (int j = 0; j < np - 1 && !plan->passes[j].mfma; ++j) {
+        bits += plan->passes[j].k;
+        if (((size_t)1 << bits) * esize * (size_t)ncomp > kChunkBytes)
+            break;
+        lead = j + 1;
+        lead_bits = bits;
+    }
+    if (lead >= 2) {
+        s.chunked = lead;
+        s.block_bits = lead_bits;
+        s.blocks = (int64_t)(kChunkBytes / (((size_t)1 << lead_bits) * esize * (size_t)ncomp));
+        return s;
+    }
+    s.chunked = np;   // one vector per chunk
+    s.blocks = 1;
+    return s;
+}
+
+// Vectors per chunk when the chunks hold whole vectors, else 0.
+int64_t chunk_vectors(const fwt_plan_s* plan, int64_t batch, int ncomp)
+{
+    const Schedule s = call_schedule(plan, batch, ncomp);
+    return s.chunked && s.block_bits == plan->n ? s.blocks : 0;
 }
 
 // Whether a call on `batch` vectors of ncomp components launches the plan's
@@ -715,13 +760,15 @@ bool use_small(const fwt_plan_s* plan, int64_t batch, int ncomp)
     return (size_t)batch <= kChunkBytes / vec_bytes;
 }
 
-// Enqueue passes [first, last) over `batch` vectors starting at re/im.  In
-// a multi-pass plan the first pass reads and the last pass writes with
-// nontemporal hints: their data is not reused by this call, while the
-// intermediate data between passes should stay in the caches.
+// Enqueue passes [first, last) over `batch` vectors starting at re/im, or,
+// with sub_bits > 0, over `batch` blocks of 2^(n - sub_bits) elements (for
+// passes whose bits all lie below n - sub_bits).  In a multi-pass plan the
+// first pass reads and the last pass writes with nontemporal hints: their
+// data is not reused by this call, while the intermediate data between
+// passes should stay in the caches.
 int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, void* re, void* im,
                   int normalize, hipStream_t stream, hipEvent_t start = nullptr,
-                  hipEvent_t stop = nullptr)
+                  hipEvent_t stop = nullptr, int sub_bits = 0)
 {
     int cus = 1;
     int rc = ensure_device_init(&cus);
@@ -743,11 +790,13 @@ int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, vo
     const int ncomp = im ? 2 : 1;
     const double c = norm_constant(n);
     const bool multi = plan->npasses >= 2;
-    const bool small = use_small(plan, batch, ncomp);
+    const bool small = sub_bits == 0 && use_small(plan, batch, ncomp);
     for (int i = first; i < last; ++i) {
         const Pass& p = small ? plan->small : plan->passes[i];
         const bool final_pass = (i == plan->npasses - 1);
         const int do_scale = (normalize && final_pass) ? 1 : 0;
+        if (sub_bits && (p.mfma || p.pair || p.lo + p.k > n - sub_bits))
+            return FWT_EINVAL;   // a block schedule covers low-bit tile passes only
         hipError_t e;
         if (p.mfma) {
             e = hipSuccess;
@@ -764,7 +813,7 @@ int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, vo
                                      i == last - 1 ? stop : nullptr);
         } else {
             TileArgs a{};
-            a.tiles = batch << p.tiles_bits;
+            a.tiles = batch << (p.tiles_bits - sub_bits);
             a.wg_count = (a.tiles + ((int64_t)1 << p.tpw_bits) - 1) >> p.tpw_bits;
             a.lo = p.lo;
             a.nblk_bits = p.nblk_bits;
@@ -842,18 +891,23 @@ int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im, int n
     const int rc = validate(plan, batch, n, re, im, &nothing);
     if (rc != FWT_OK || nothing)
         return rc;
-    const int64_t cv = chunk_vectors(plan, batch, im ? 2 : 1);
-    if (cv == 0)
+    const Schedule s = call_schedule(plan, batch, im ? 2 : 1);
+    if (s.chunked == 0)
         return launch_passes(plan, 0, plan->npasses, batch, n, re, im, normalize, stream);
-    const size_t vec_bytes = ((size_t)1 << n) * (plan->dtype == FWT_F64 ? 8 : 4);
-    for (int64_t b0 = 0; b0 < batch; b0 += cv) {
-        const int64_t nb = batch - b0 < cv ? batch - b0 : cv;
-        void* cre = (char*)re + (size_t)b0 * vec_bytes;
-        void* cim = im ? (char*)im + (size_t)b0 * vec_bytes : nullptr;
-        const int r = launch_passes(plan, 0, plan->npasses, nb, n, cre, cim, normalize, stream);
+    const int sub = n - s.block_bits;
+    const int64_t blocks = batch << sub;
+    const size_t block_bytes = ((size_t)1 << s.block_bits) * (plan->dtype == FWT_F64 ? 8 : 4);
+    for (int64_t b0 = 0; b0 < blocks; b0 += s.blocks) {
+        const int64_t nb = blocks - b0 < s.blocks ? blocks - b0 : s.blocks;
+        void* cre = (char*)re + (size_t)b0 * block_bytes;
+        void* cim = im ? (char*)im + (size_t)b0 * block_bytes : nullptr;
+        const int r = launch_passes(plan, 0, s.chunked, nb, n, cre, cim, normalize, stream,
+                                    nullptr, nullptr, sub);
         if (r != FWT_OK)
             return r;
     }
+    if (s.chunked < plan->npasses)
+        return launch_passes(plan, s.chunked, plan->npasses, batch, n, re, im, normalize, stream);
     return FWT_OK;
 }
 
@@ -886,6 +940,18 @@ int fwt_plan_chunk_vectors(fwt_plan_t plan, int64_t batch, int with_im, int64_t*
     if (!valid_plan(plan) || !out || batch < 0)
         return FWT_EINVAL;
     *out = chunk_vectors(plan, batch, with_im ? 2 : 1);
+    return FWT_OK;
+}
+
+int fwt_plan_call_schedule(fwt_plan_t plan, int64_t batch, int with_im, int* chunked_passes,
+                           int* block_bits, int64_t* blocks_per_chunk)
+{
+    if (!valid_plan(plan) || !chunked_passes || !block_bits || !blocks_per_chunk || batch < 0)
+        return FWT_EINVAL;
+    const Schedule s = call_schedule(plan, batch, with_im ? 2 : 1);
+    *chunked_passes = s.chunked;
+    *block_bits = s.block_bits;
+    *blocks_per_chunk = s.blocks;
     return FWT_OK;
 }
 

@@ -46,6 +46,19 @@ int main()
                     bad += np > 0 && n > 0 && sum != n;
                     int64_t cv = -1;
                     bad += fwt_plan_chunk_vectors(p, 1 << 10, 1, &cv) != FWT_OK || cv < 0;
+                    for (int64_t batch : {(int64_t)0, (int64_t)3, (int64_t)1 << 12})
+                        for (int w = 0; w <= 1; ++w) {
+                            int cp = -1, bb = -1;
+                            int64_t bl = -1;
+                            bad += fwt_plan_call_schedule(p, batch, w, &cp, &bb, &bl) != FWT_OK ||
+                                   cp < 0 || cp > np || bb < 0 || bb > n || bl < 0;
+                        }
+                    {
+                        int cp, bb;
+                        int64_t bl;
+                        bad += fwt_plan_call_schedule(p, -1, 1, &cp, &bb, &bl) != FWT_EINVAL;
+                        bad += fwt_plan_call_schedule(p, 1, 1, nullptr, &bb, &bl) != FWT_EINVAL;
+                    }
                     bad += fwt_plan_pass_bits(p, np, nullptr) == FWT_OK;
                     bad += fwt_plan_destroy(p) != FWT_OK;
                     ++ok;

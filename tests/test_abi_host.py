@@ -100,6 +100,26 @@ def test_chunk_schedule(lib):
     assert p20.chunk_vectors(32, True) == 0         # fits: one chunk
     assert qse.Plan(24, "f64").chunk_vectors(16, True) == 1
     assert qse.Plan(12, "f32").chunk_vectors(10**6, True) == 0   # single pass: never chunked
+    # the whole schedule: (chunked passes, log2 elements per block, blocks per chunk)
+    assert p20.call_schedule(256) == (2, 20, 32)
+    assert p20.call_schedule(32) == (0, 20, 0)
+    assert qse.Plan(24, "f64").call_schedule(16) == (2, 24, 1)
+    # one vector above 256 MiB: the leading passes run on chunks of blocks
+    p27 = qse.Plan(27, "f32")
+    assert p27.pass_bits == [10, 9, 8]
+    assert p27.call_schedule(2) == (2, 19, 64) and p27.chunk_vectors(2) == 0
+    assert p27.call_schedule(2, False) == (2, 19, 128)
+    assert qse.Plan(26, "f64").call_schedule(2) == (2, 18, 64)
+    assert qse.Plan(30, "f32").call_schedule(1) == (2, 20, 32)
+    assert qse.Plan(28, "f32", split=(7, 7, 7, 7)).call_schedule(1) == (3, 21, 16)
+    # two-pass plans with such vectors keep one vector per chunk
+    assert qse.Plan(26, "f32").call_schedule(4) == (2, 26, 1)
+    assert qse.Plan(26, "f32").chunk_vectors(4) == 1
+    for pl in (p20, p27):
+        for batch in (1, 3, 64, 1000):
+            cp, bb, bl = pl.call_schedule(batch)
+            cv = pl.chunk_vectors(batch)
+            assert cv == (bl if cp and bb == pl.n else 0)
     assert qse.Plan(14, "f32", path=qse.PATH_MULTIPASS).pass_bits == [7, 7]
     assert qse.Plan(15, "f32", path=qse.PATH_SINGLE_BLOCK).pass_bits == [15]
 

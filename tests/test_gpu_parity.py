@@ -391,6 +391,41 @@ def test_wide_default_plans(dtype, n, passes):
     assert_exact(gim, im, n, False)
 
 
+@pytest.mark.parametrize("dtype,n,batch,split", [("f32", 27, 2, None), ("f64", 26, 1, None),
+                                                 ("f32", 28, 1, (7, 7, 7, 7)),
+                                                 ("f32", 27, 3, (10, 10, 7))])
+def test_block_chunked_schedule_equals_passes_in_order(dtype, n, batch, split):
+    """Vectors larger than the Infinity Cache: fwt_execute runs the leading
+    passes on chunks of sub-vector blocks (fwt_plan_call_schedule), which
+    must give bit for bit what the passes give run one by one over the
+    whole state (Gaussian inputs, normalised)."""
+    say("block chunks %s n=%d batch=%d split=%s" % (dtype, n, batch, split))
+    tdt = torch.float32 if dtype == "f32" else torch.float64
+    plan = qse.Plan(n, dtype, split=split)
+    cp, bb, bl = plan.call_schedule(batch)
+    assert 2 <= cp < plan.num_passes and bb < n and (batch << (n - bb)) > bl
+    g = torch.Generator(device="cuda").manual_seed(n)
+    re = torch.randn(batch, 1 << n, generator=g, device="cuda", dtype=tdt)
+    im = torch.randn(batch, 1 << n, generator=g, device="cuda", dtype=tdt)
+    r1, i1 = re.clone(), im.clone()
+    plan.execute(re, im, normalize=True)
+    for i in range(plan.num_passes):
+        plan.execute_pass(i, r1, i1, normalize=True)
+    torch.cuda.synchronize()
+    assert torch.equal(re, r1) and torch.equal(im, i1)
+    if n > 27:
+        return
+    # and against the oracle on one sampled vector
+    v = batch - 1
+    x_re, x_im = r1[v].cpu().numpy(), i1[v].cpu().numpy()
+    del r1, i1
+    torch.cuda.empty_cache()
+    g = torch.Generator(device="cuda").manual_seed(n)
+    o_re = torch.randn(batch, 1 << n, generator=g, device="cuda", dtype=tdt)[v].cpu().numpy()
+    o_im = torch.randn(batch, 1 << n, generator=g, device="cuda", dtype=tdt)[v].cpu().numpy()
+    assert_close(dtype, n, o_re, o_im, x_re, x_im)
+
+
 def _parity(t):
     """popcount(t) mod 2 for a non-negative int64 tensor (below 2^32)."""
     for sh in (16, 8, 4, 2, 1):
