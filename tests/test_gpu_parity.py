@@ -376,9 +376,10 @@ def test_full_size_n24_b16_f64():
                                             ("f32", 27, 3), ("f64", 25, 2), ("f64", 26, 3)])
 def test_wide_default_plans(dtype, n, passes):
     """The default plans above n = 23 at their real size (two passes with
-    10- and 11-bit column factors, then three), one vector, inputs in
-    {-1, 0, 1}: every partial sum stays an exact integer far below 2^24, so
-    the result is exact; compared whole with the oracle."""
+    10- and 11-bit column factors, then three, whose first two passes run
+    on chunks of sub-vector blocks), one vector, inputs in {-1, 0, 1}: the
+    partial sums stay exact integers far below 2^24, so the result is
+    exact; compared whole with the oracle."""
     say("wide default plan %s n=%d" % (dtype, n))
     npd = np.float32 if dtype == "f32" else np.float64
     rng = np.random.default_rng(77_000 + n)
@@ -386,6 +387,8 @@ def test_wide_default_plans(dtype, n, passes):
     im = rng.integers(-1, 2, size=(1, 1 << n)).astype(npd)
     plan = qse.Plan(n, dtype)
     assert plan.num_passes == passes
+    if passes == 3:
+        assert plan.call_schedule(1)[:2] == (2, sum(plan.pass_bits[:2]))
     gre, gim = run(plan, re, im, False)
     assert_exact(gre, re, n, False)
     assert_exact(gim, im, n, False)
