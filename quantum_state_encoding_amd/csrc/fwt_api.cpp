@@ -570,6 +570,9 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
     if (p->npasses == 1 && !mfma_row && pass0_default && p->passes[0].key.wave == 2 &&
         p->passes[0].key.row && p->passes[0].key.kr == 12 && p->passes[0].key.eb == 2) {
         const fwt_pass_tuning t3{3, -1, -1, -1, 2};
+        p->small = Pass{};
+        p->small.lo = 0;
+        p->small.k = n;
         if (build_lx_pass(p->small, n, dtype, 0, n, 12, true, t3, false) == FWT_OK)
             p->has_small = 1;
     }

@@ -3,17 +3,22 @@
 // and validation code in fwt_api.cpp can be built with g++ under
 // AddressSanitizer and UndefinedBehaviorSanitizer.  Every kernel variant is
 // reported as compiled, which makes the planner take every branch; nothing
-// here launches anything.
-#include "../../quantum_state_encoding_amd/csrc/fwt_internal.h"
+// here launches anything.  A driver may set g_tile_launch_hook to see the
+// tile-pass launches instead.
+#include "stub_hooks.h"
 
 namespace qse {
 
+TileLaunchHook g_tile_launch_hook = nullptr;
+
 bool kernel_available(const KernelKey&) { return true; }
 hipError_t kernels_init_device() { return hipSuccess; }
-hipError_t launch_tile_pass(const KernelKey&, void*, void*, int, const TileArgs&, unsigned, size_t,
-                            hipStream_t, hipEvent_t, hipEvent_t)
+hipError_t launch_tile_pass(const KernelKey& key, void* re, void* im, int ncomp,
+                            const TileArgs& args, unsigned block, size_t lds, hipStream_t,
+                            hipEvent_t, hipEvent_t)
 {
-    return hipErrorNotSupported;
+    return g_tile_launch_hook ? g_tile_launch_hook(key, re, im, ncomp, args, block, lds)
+                              : hipErrorNotSupported;
 }
 hipError_t launch_pair_f32(float*, float*, int64_t, int, float, hipStream_t, hipEvent_t, hipEvent_t)
 {
