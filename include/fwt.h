@@ -21,9 +21,10 @@
  * "Why" and "Why submit PR4"; the iThome article's "Kronecker block GEMM
  * idea").  Each pass streams the state through memory once, in place, with
  * no transpose and no temporary buffer.  n <= 15 (fp32) / 14 (fp64) runs
- * as a single pass whose tiles hold a whole vector on chip; up to n = 24,
- * two passes; above, three.  Large multi-pass calls run in chunks of
- * vectors sized to the Infinity Cache (fwt_plan_chunk_vectors).
+ * as a single pass whose tiles hold a whole vector on chip; up to n = 26
+ * (fp32) / 25 (fp64), two passes; above, three.  Large multi-pass calls run
+ * in chunks sized to the Infinity Cache: chunks of vectors, or of
+ * sub-vector blocks when one vector exceeds it (fwt_plan_call_schedule).
  *
  * Conventions common to every entry point:
  *  - Status codes are the FWT_* values below; no C++ exception crosses
@@ -53,7 +54,8 @@ typedef enum { FWT_F32 = 0, FWT_F64 = 1 } fwt_dtype;
  *  SINGLE_BLOCK  one pass, one vector per tile; FWT_EUNSUPPORTED above the
  *                single-pass limit.
  *  MULTIPASS     Kronecker split into >= 2 passes whenever n allows it
- *                (n >= 2 for fp32, n >= 2 for fp64; below that one pass).
+ *                (n >= 4 for fp32, n >= 3 for fp64, where the first factor
+ *                still holds a 16-byte vector; below that one pass).
  *  MFMA_ABLATION the pages' matrix-core form, for measurement: AUTO's
  *                split, with the row pass (the low 8..15 bits) done as dense
  *                H_16 block products on the 16x16x4 fp32 / fp64 matrix
@@ -70,7 +72,7 @@ enum {
     FWT_OK = 0,
     FWT_EINVAL = -1,       /* bad argument: null, range, n mismatch, overlap */
     FWT_EALIGN = -2,       /* a buffer is not 16-byte aligned */
-    FWT_EUNSUPPORTED = -3, /* valid request this build does not implement */
+    FWT_EUNSUPPORTED = -3, /* valid request the library does not implement */
     FWT_EHIP = -4,         /* the HIP runtime reported an error */
     FWT_ENOMEM = -5        /* host allocation of the plan failed */
 };
