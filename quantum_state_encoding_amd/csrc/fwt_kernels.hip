@@ -693,17 +693,103 @@ struct LxRounds<V, KR, GB, W, EB, PHB, NX, NX> {
     __device__ __forceinline__ static void run(V*, V*, int, int, int) {}
 };
 
+// Compile-time shape of a lane-exchange tile and the steps of one tile:
+// address, load, transform, store.
+template <typename T, int KR_, int EB_, int W_, int PHB_, int GB_, bool ROW_>
+struct LxShape {
+    using V = typename Vec<T>::type;
+    static constexpr int KR = KR_, EB = EB_, W = W_, PHB = PHB_, GB = GB_;
+    static constexpr bool ROW = ROW_;
+    static constexpr int WB = Vec<T>::WB;
+    static constexpr int E = 1 << EB;
+    static constexpr int LR = 6 - GB;              // row bits held by lanes
+    static constexpr int NX = (W + EB - 1) / EB;   // exchanges
+    static_assert(KR == EB + LR + W && EB >= 1 && W >= 1 && W <= 4, "lane-exchange tile");
+    static_assert(!ROW || GB == 0, "row passes have one column group");
+};
+
+// Workgroup-uniform base of tile t; lanes then address group g of row r at
+// (g << 4) + (r << rsh) bytes from it.
+template <typename S, typename T>
+__device__ __forceinline__ unsigned char* lx_tile_base(T* buf, const TileArgs& a, int64_t t,
+                                                       uint32_t* rsh)
+{
+    int64_t base;
+    if (S::ROW) {
+        base = t << (S::KR + S::WB);
+        *rsh = 4;
+    } else {
+        const int64_t blk_mask = ((int64_t)1 << a.nblk_bits) - 1;
+        base = ((t >> a.nblk_bits) << (a.lo + S::KR)) + ((t & blk_mask) << (S::GB + S::WB));
+        *rsh = (uint32_t)a.lo + (sizeof(T) == 8 ? 3u : 2u);
+    }
+    return reinterpret_cast<unsigned char*>(buf + base);
+}
+
+template <typename S>
+__device__ __forceinline__ void lx_load(typename S::V* x, const unsigned char* p, uint32_t gbase,
+                                        uint32_t rsh, uint32_t r0, int nt)
+{
+    using V = typename S::V;
+    if (nt) {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            x[j] = load16_nt<V>(p, gbase + ((r0 + lx_reg_row<S::W, S::EB, S::LR, 0>(j)) << rsh));
+    } else {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            x[j] = load16<V>(p, gbase + ((r0 + lx_reg_row<S::W, S::EB, S::LR, 0>(j)) << rsh));
+    }
+}
+
+// Every stage of the tile, then the scale; leaves x in the layout of the
+// last exchange.  The first exchange writes LDS without a barrier before
+// it, so a caller that reuses L for another tile must place one first.
+template <typename S, typename T>
+__device__ __forceinline__ void lx_process(typename S::V* x, typename S::V* L, int lane,
+                                           int lane_row, int g, int wave, int do_scale,
+                                           double scale)
+{
+    using V = typename S::V;
+    if (S::ROW) {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            in_vector(x[j]);
+    }
+    register_stages<S::EB, S::E>(x);
+    LaneStages<0, S::LR, S::GB, S::E, V, T>::run(x, lane);
+    LxRounds<V, S::KR, S::GB, S::W, S::EB, S::PHB, 0, S::NX>::run(x, L, lane_row, g, wave);
+    if (do_scale) {
+        const T c = (T)scale;
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            x[j] *= c;
+    }
+}
+
+template <typename S>
+__device__ __forceinline__ void lx_store(const typename S::V* x, unsigned char* p, uint32_t gbase,
+                                         uint32_t rsh, uint32_t rf, int nt)
+{
+    using V = typename S::V;
+    if (nt) {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            store16_nt<V>(p, gbase + ((rf + lx_reg_row<S::W, S::EB, S::LR, S::NX>(j)) << rsh),
+                          x[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            store16<V>(p, gbase + ((rf + lx_reg_row<S::W, S::EB, S::LR, S::NX>(j)) << rsh), x[j]);
+    }
+}
+
 template <typename T, int KR, int EB, int W, int PHB, int GB, bool ROW>
 __global__ void __launch_bounds__(64 << W)
     lx_kernel(T* __restrict__ re, T* __restrict__ im, TileArgs a)
 {
-    using V = typename Vec<T>::type;
-    constexpr int WB = Vec<T>::WB;
-    constexpr int E = 1 << EB;
-    constexpr int LR = 6 - GB;              // row bits held by lanes
-    constexpr int NX = (W + EB - 1) / EB;   // exchanges
-    static_assert(KR == EB + LR + W && EB >= 1 && W >= 1 && W <= 4, "lane-exchange tile");
-    static_assert(!ROW || GB == 0, "row passes have one column group");
+    using S = LxShape<T, KR, EB, W, PHB, GB, ROW>;
+    using V = typename S::V;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     V* const L = reinterpret_cast<V*>(lds_raw);
     const int64_t t = a.tile0 + blockIdx.x;
@@ -713,57 +799,13 @@ __global__ void __launch_bounds__(64 << W)
     const int wave = threadIdx.x >> 6;
     const int g = lane & ((1 << GB) - 1);
     const int lane_row = lane >> GB;
-    T* const buf = blockIdx.y ? im : re;
-    // Workgroup-uniform tile base, then 32-bit lane offsets: group g of row
-    // r sits at gbase + (r << rsh) bytes.
-    int64_t base;
     uint32_t rsh;
-    if (ROW) {
-        base = t << (KR + WB);
-        rsh = 4;
-    } else {
-        const int64_t blk_mask = ((int64_t)1 << a.nblk_bits) - 1;
-        base = ((t >> a.nblk_bits) << (a.lo + KR)) + ((t & blk_mask) << (GB + WB));
-        rsh = (uint32_t)a.lo + (sizeof(T) == 8 ? 3u : 2u);
-    }
-    unsigned char* const p = reinterpret_cast<unsigned char*>(buf + base);
+    unsigned char* const p = lx_tile_base<S>(blockIdx.y ? im : re, a, t, &rsh);
     const uint32_t gbase = (uint32_t)g << 4;
-
-    const uint32_t r0 = lx_thread_row<W, EB, LR, 0>(lane_row, wave);
-    V x[E];
-    if (a.ld_nt) {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            x[j] = load16_nt<V>(p, gbase + ((r0 + lx_reg_row<W, EB, LR, 0>(j)) << rsh));
-    } else {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            x[j] = load16<V>(p, gbase + ((r0 + lx_reg_row<W, EB, LR, 0>(j)) << rsh));
-    }
-    if (ROW) {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            in_vector(x[j]);
-    }
-    register_stages<EB, E>(x);
-    LaneStages<0, LR, GB, E, V, T>::run(x, lane);
-    LxRounds<V, KR, GB, W, EB, PHB, 0, NX>::run(x, L, lane_row, g, wave);
-    if (a.do_scale) {
-        const T c = (T)a.scale;
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            x[j] *= c;
-    }
-    const uint32_t rf = lx_thread_row<W, EB, LR, NX>(lane_row, wave);
-    if (a.st_nt) {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            store16_nt<V>(p, gbase + ((rf + lx_reg_row<W, EB, LR, NX>(j)) << rsh), x[j]);
-    } else {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            store16<V>(p, gbase + ((rf + lx_reg_row<W, EB, LR, NX>(j)) << rsh), x[j]);
-    }
+    V x[S::E];
+    lx_load<S>(x, p, gbase, rsh, lx_thread_row<W, EB, S::LR, 0>(lane_row, wave), a.ld_nt);
+    lx_process<S, T>(x, L, lane, lane_row, g, wave, a.do_scale, a.scale);
+    lx_store<S>(x, p, gbase, rsh, lx_thread_row<W, EB, S::LR, S::NX>(lane_row, wave), a.st_nt);
 }
 
 __global__ void __launch_bounds__(256)
