@@ -573,12 +573,15 @@ def test_one_plan_from_several_threads_and_streams():
         assert torch.equal(b_re, bufs[0][0]) and torch.equal(b_im, bufs[0][1])
 
 
-@pytest.mark.parametrize("n,batch,dtype", [(12, 5, "f32"), (20, 4, "f32"), (22, 2, "f64")])
+@pytest.mark.parametrize("n,batch,dtype", [(12, 5, "f32"), (20, 4, "f32"), (22, 2, "f64"),
+                                           (24, 3, "f64"), (27, 1, "f32")])
 def test_hip_graph_capture_and_replay(n, batch, dtype):
     """fwt_execute captured into a HIP graph (torch's default capture mode)
     and replayed three times, with other eager work and synchronisations
     between the replays: every replay equals the eager call bit for bit.
-    The library records kernel launches only (no memset nodes)."""
+    The library records kernel launches only (no memset nodes).  The last
+    two cases capture chunked schedules: chunks of vectors (fp64 n=24) and
+    of sub-vector blocks (fp32 n=27)."""
     say("graph %s n=%d batch=%d" % (dtype, n, batch))
     w = workloads.custom(n, batch, dtype, "gauss", True, seed=31)
     re0, im0 = workloads.gen(w)
