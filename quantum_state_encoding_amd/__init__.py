@@ -269,7 +269,9 @@ class Plan:
         """A zero-argument callable that enqueues fwt_execute on these
         tensors with the arguments marshalled once (for tight loops).
         Binding validates the arguments (fwt_execute_check) but runs
-        nothing; the callable keeps the plan alive."""
+        nothing; the callable keeps the plan and the bound tensors alive,
+        so their memory cannot be handed to another tensor while the
+        callable exists."""
         batch = self._check_tensors(re, im)
         lib = load_library()
         rp = ctypes.c_void_p(re.data_ptr())
@@ -286,6 +288,7 @@ class Plan:
             if st != FWT_OK:
                 raise FwtError(st, "fwt_execute")
         call.plan = plan
+        call.tensors = (re, im)
         return call
 
     def execute_pass(self, i, re, im=None, normalize=True, stream=None):
