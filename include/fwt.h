@@ -30,6 +30,10 @@
  *  - Status codes are the FWT_* values below; no C++ exception crosses
  *    this interface.
  *  - Nothing here allocates device memory; fwt_execute never synchronises.
+ *    (The library's code object holds one static array of
+ *    FWT_STATIC_SCRATCH_BYTES per device, placed by the runtime when the
+ *    library is loaded on that device; only fwt_ablation_execute_static
+ *    uses it.)
  *  - Plans hold host metadata only, are immutable after creation, and may
  *    be used concurrently from several host threads and streams.
  */
@@ -74,7 +78,9 @@ enum {
     FWT_EALIGN = -2,       /* a buffer is not 16-byte aligned */
     FWT_EUNSUPPORTED = -3, /* valid request the library does not implement */
     FWT_EHIP = -4,         /* the HIP runtime reported an error */
-    FWT_ENOMEM = -5        /* host allocation of the plan failed */
+    FWT_ENOMEM = -5,       /* host allocation of the plan failed */
+    FWT_ESCRATCH = -6      /* fwt_ablation_execute_static: the call needs more
+                              workspace than FWT_STATIC_SCRATCH_BYTES */
 };
 
 /* Largest supported n (2^30 amplitudes per vector). */
@@ -333,6 +339,30 @@ int fwt_ablation_workspace(int kind, int64_t batch, int n, fwt_dtype dtype, int 
 int fwt_ablation_execute(int kind, int64_t batch, int n, fwt_dtype dtype, void* re, void* im,
                          int normalize, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* Size of the static device scratch array of fwt_ablation_execute_static
+ * (32 MiB per device, held until the process ends). */
+#define FWT_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* fwt_ablation_execute for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same kinds, arguments, layout and results as
+ * fwt_ablation_execute, but the workspace is the library's static scratch
+ * array on the current device (FWT_STATIC_SCRATCH_BYTES), so no workspace
+ * is passed.  The call allocates no device memory and calls no allocating
+ * routine.  The caller still provides re and im.
+ *  - Returns FWT_ESCRATCH when fwt_ablation_workspace for the call exceeds
+ *    FWT_STATIC_SCRATCH_BYTES (e.g. the popcount GEMM or the transposed
+ *    matrix-core form beyond 32 MiB of state, the INT8 / CRT form beyond
+ *    about 2^21 fp64 elements per component), otherwise the statuses of
+ *    fwt_ablation_execute.
+ *  - Every call on one device shares that device's array, and the array
+ *    keeps the last call's contents (no kernel reads it before writing it).
+ *    Calls that overlap in time on one device (concurrent streams, or host
+ *    threads whose streams are not ordered) race on it and give undefined
+ *    results: order them on one stream. */
+int fwt_ablation_execute_static(int kind, int64_t batch, int n, fwt_dtype dtype, void* re,
+                                void* im, int normalize, hipStream_t stream);
 
 /* Measurement aid, not part of the transform: copies `bytes` (a multiple
  * of 16) from src to dst with the same 16-byte streaming access the passes

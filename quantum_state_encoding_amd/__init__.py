@@ -21,12 +21,15 @@ __all__ = ["Plan", "FwtError", "execute", "stream_copy", "library_path", "load_l
            "ABLATION_MFMA", "ABLATION_OZAKI", "ABLATION_MFMA_TRANSPOSE", "PassTuning",
            "PATH_AUTO", "PATH_SINGLE_BLOCK", "PATH_MULTIPASS", "PATH_MFMA_ABLATION",
            "FWT_OK", "FWT_EINVAL", "FWT_EALIGN", "FWT_EUNSUPPORTED", "FWT_EHIP",
-           "FWT_ENOMEM", "EXPORTED_SYMBOLS"]
+           "FWT_ENOMEM", "FWT_ESCRATCH", "STATIC_SCRATCH_BYTES", "ablation_execute_static",
+           "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfwt.so")
 
 FWT_OK, FWT_EINVAL, FWT_EALIGN, FWT_EUNSUPPORTED, FWT_EHIP, FWT_ENOMEM = 0, -1, -2, -3, -4, -5
+FWT_ESCRATCH = -6
+STATIC_SCRATCH_BYTES = 32 << 20   # FWT_STATIC_SCRATCH_BYTES
 PATH_AUTO, PATH_SINGLE_BLOCK, PATH_MULTIPASS, PATH_MFMA_ABLATION = 0, 1, 2, 3
 _DTYPES = {"f32": 0, "f64": 1}
 
@@ -39,7 +42,7 @@ EXPORTED_SYMBOLS = ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create
                     "fwt_plan_destroy", "fwt_strerror", "fwt_last_hip_error",
                     "fwt_stream_copy", "fwt_plan_chunk_vectors", "fwt_plan_call_schedule",
                     "fwt_ablation_workspace",
-                    "fwt_ablation_execute")
+                    "fwt_ablation_execute", "fwt_ablation_execute_static")
 
 _lib = None
 
@@ -99,12 +102,13 @@ def load_library():
     lib.fwt_stream_copy.argtypes = [vp, vp, i64, vp]
     lib.fwt_ablation_workspace.argtypes = [i32, i64, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.fwt_ablation_execute.argtypes = [i32, i64, i32, i32, vp, vp, i32, vp, ctypes.c_size_t, vp]
+    lib.fwt_ablation_execute_static.argtypes = [i32, i64, i32, i32, vp, vp, i32, vp]
     for name in ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create_tuned",
                  "fwt_execute", "fwt_execute_pass", "fwt_execute_pass_timed",
                  "fwt_execute_check", "fwt_plan_num_passes", "fwt_plan_pass_bits",
                  "fwt_plan_pass_config", "fwt_plan_call_pass_config", "fwt_plan_destroy",
-                 "fwt_last_hip_error",
-                 "fwt_stream_copy"):
+                 "fwt_last_hip_error", "fwt_ablation_workspace", "fwt_ablation_execute",
+                 "fwt_ablation_execute_static", "fwt_stream_copy"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -414,6 +418,26 @@ def ablation_execute(kind, re, im=None, n=None, normalize=True, workspace=None, 
         ctypes.c_void_p(ws_ptr), ws_bytes, _stream_handle(stream))
     if st != FWT_OK:
         raise FwtError(st, "fwt_ablation_execute")
+    return re, im
+
+
+def ablation_execute_static(kind, re, im=None, n=None, normalize=True, stream=None):
+    """fwt_ablation_execute_static on torch tensors in place: the ablation
+    with its workspace in the library's static scratch array (no device
+    allocation; raises FwtError with FWT_ESCRATCH when the call needs more
+    than STATIC_SCRATCH_BYTES)."""
+    if n is None:
+        n = re.shape[-1].bit_length() - 1
+    dtype = {"torch.float32": "f32", "torch.float64": "f64"}.get(str(re.dtype))
+    if dtype is None:
+        raise ValueError("re must be float32 or float64")
+    batch = _check_state(re, im, n, dtype)
+    st = load_library().fwt_ablation_execute_static(
+        int(kind), batch, int(n), _DTYPES[dtype], ctypes.c_void_p(re.data_ptr()),
+        ctypes.c_void_p(im.data_ptr() if im is not None else None), 1 if normalize else 0,
+        _stream_handle(stream))
+    if st != FWT_OK:
+        raise FwtError(st, "fwt_ablation_execute_static")
     return re, im
 
 

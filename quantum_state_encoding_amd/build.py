@@ -7,7 +7,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfwt.so")
 SOURCES = [os.path.join(CSRC, "fwt_kernels.hip"), os.path.join(CSRC, "fwt_ablation.hip"),
-           os.path.join(CSRC, "fwt_ozaki.hip"),
+           os.path.join(CSRC, "fwt_ozaki.hip"), os.path.join(CSRC, "fwt_static.hip"),
            os.path.join(CSRC, "fwt_api.cpp")]
 HEADERS = [os.path.join(CSRC, "fwt_internal.h"), os.path.join(ROOT, "include", "fwt.h")]
 

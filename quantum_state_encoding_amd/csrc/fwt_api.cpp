@@ -992,8 +992,11 @@ size_t ablation_workspace_bytes(int kind, int64_t batch, int n, fwt_dtype dtype,
     return (size_t)batch * ((size_t)1 << n) * esize * (with_im ? 2 : 1);
 }
 
+// Argument checks of an ablation call.  `ws_owned`: the workspace is the
+// library's own static scratch (256-byte aligned, never inside a caller's
+// buffer), so it is not checked at all; its size is checked by the caller.
 int ablation_check(int kind, int64_t batch, int n, fwt_dtype dtype, const void* re,
-                   const void* im, const void* ws, size_t ws_bytes)
+                   const void* im, const void* ws, size_t ws_bytes, bool ws_owned)
 {
     if (dtype != FWT_F32 && dtype != FWT_F64)
         return FWT_EINVAL;
@@ -1021,7 +1024,7 @@ int ablation_check(int kind, int64_t batch, int n, fwt_dtype dtype, const void* 
     }
     if (!re || batch < 0)
         return FWT_EINVAL;
-    if (((uintptr_t)re & 15u) || ((uintptr_t)im & 15u) || ((uintptr_t)ws & 15u))
+    if (((uintptr_t)re & 15u) || ((uintptr_t)im & 15u) || (!ws_owned && ((uintptr_t)ws & 15u)))
         return FWT_EALIGN;
     if (re == im)
         return FWT_EINVAL;
@@ -1036,7 +1039,7 @@ int ablation_check(int kind, int64_t batch, int n, fwt_dtype dtype, const void* 
     if (im && overlap(re, bytes, im, bytes))
         return FWT_EINVAL;
     const size_t need = ablation_workspace_bytes(kind, batch, n, dtype, im != nullptr);
-    if (need) {
+    if (need && !ws_owned) {
         if (!ws || ws_bytes < need)
             return FWT_EINVAL;
         if (overlap(ws, need, re, bytes) || (im && overlap(ws, need, im, bytes)))
@@ -1047,7 +1050,7 @@ int ablation_check(int kind, int64_t batch, int n, fwt_dtype dtype, const void* 
     int rc = check_range(re, bytes);
     if (rc == FWT_OK && im)
         rc = check_range(im, bytes);
-    if (rc == FWT_OK && need)
+    if (rc == FWT_OK && need && !ws_owned)
         rc = check_range(ws, need);
     return rc;
 }
@@ -1091,7 +1094,34 @@ int fwt_ablation_execute(int kind, int64_t batch, int n, fwt_dtype dtype, void* 
                          int normalize, void* workspace, size_t workspace_bytes,
                          hipStream_t stream)
 {
-    int rc = ablation_check(kind, batch, n, dtype, re, im, workspace, workspace_bytes);
+    return qse::ablation_run(kind, batch, n, (int)dtype, re, im, normalize, workspace,
+                             workspace_bytes, false, stream);
+}
+
+}  // extern "C"
+
+int qse::ablation_validate(int kind, int64_t batch, int n, int dtype, const void* re,
+                           const void* im)
+{
+    return ablation_check(kind, batch, n, (fwt_dtype)dtype, re, im, nullptr, 0, true);
+}
+
+int qse::hip_status(hipError_t e)
+{
+    return hip_fail(e);
+}
+
+size_t qse::ablation_workspace_size(int kind, int64_t batch, int n, int dtype, int with_im)
+{
+    return ablation_workspace_bytes(kind, batch, n, (fwt_dtype)dtype, with_im);
+}
+
+int qse::ablation_run(int kind, int64_t batch, int n, int dtype_, void* re, void* im,
+                      int normalize, void* workspace, size_t workspace_bytes, bool ws_owned,
+                      hipStream_t stream)
+{
+    const fwt_dtype dtype = (fwt_dtype)dtype_;
+    int rc = ablation_check(kind, batch, n, dtype, re, im, workspace, workspace_bytes, ws_owned);
     if (rc != FWT_OK || batch == 0)
         return rc;
     int cus = 1;
@@ -1122,6 +1152,8 @@ int fwt_ablation_execute(int kind, int64_t batch, int n, fwt_dtype dtype, void* 
     }
     return e == hipSuccess ? FWT_OK : hip_fail(e);
 }
+
+extern "C" {
 
 namespace {
 
@@ -1179,6 +1211,7 @@ const char* fwt_strerror(int status)
     case FWT_EUNSUPPORTED: return "unsupported configuration";
     case FWT_EHIP: return "HIP runtime error";
     case FWT_ENOMEM: return "out of host memory";
+    case FWT_ESCRATCH: return "workspace larger than the static scratch array";
     default: return "unknown status";
     }
 }

@@ -138,4 +138,19 @@ hipError_t ablation_mfma_transpose(int f64, void* re, void* im, void* ws_re, voi
 hipError_t ablation_mfma_row(int f64, void* re, void* im, int64_t batch, int n, int km,
                              int do_scale, double c, hipStream_t stream);
 
+// Ablation dispatch shared by fwt_ablation_execute (caller workspace) and
+// fwt_ablation_execute_static (the library's static scratch; ws_owned =
+// true skips the allocation-range check of the workspace).  dtype is an
+// fwt_dtype value; returns an FWT_* status.
+int ablation_run(int kind, int64_t batch, int n, int dtype, void* re, void* im, int normalize,
+                 void* ws, size_t ws_bytes, bool ws_owned, hipStream_t stream);
+// The argument checks of ablation_run for a call on the library's own
+// scratch (everything but the workspace); returns an FWT_* status.
+int ablation_validate(int kind, int64_t batch, int n, int dtype, const void* re, const void* im);
+// Records `e` as the calling thread's last HIP error (fwt_last_hip_error)
+// and returns FWT_EHIP.
+int hip_status(hipError_t e);
+// Workspace bytes ablation `kind` needs (0 if none).
+size_t ablation_workspace_size(int kind, int64_t batch, int n, int dtype, int with_im);
+
 }  // namespace qse

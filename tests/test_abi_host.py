@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_strerror_covers_every_status(lib):
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.fwt_strerror(st).decode() != "unknown status"
     assert lib.fwt_strerror(7).decode() == "unknown status"
 
@@ -563,3 +563,28 @@ def test_ablation_workspace_and_validation(lib):
     assert ex(qse.ABLATION_POPC_GEMM, 1, 10, 0, FAKE, FAKE + 4 * N, 1, FAKE + 8, 8 * N, None) == qse.FWT_EALIGN
     assert ex(qse.ABLATION_POPC_GEMM, 1, 10, 0, FAKE, FAKE + 4 * N, 1, FAKE, 8 * N, None) == qse.FWT_EINVAL
     assert ex(qse.ABLATION_STAGEWISE, 0, 10, 0, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_OK
+
+
+def test_static_ablation_validation_before_any_hip_call(lib):
+    """fwt_ablation_execute_static checks its size limit and every argument
+    before any HIP call (there is no device here)."""
+    ex = lib.fwt_ablation_execute_static
+    N = 1 << 16
+    big = 1 + qse.STATIC_SCRATCH_BYTES // (2 * 4 * N)
+    pg, oz, mt = qse.ABLATION_POPC_GEMM, qse.ABLATION_OZAKI, qse.ABLATION_MFMA_TRANSPOSE
+    assert qse.ablation_workspace(pg, big, 16, "f32", True) > qse.STATIC_SCRATCH_BYTES
+    assert qse.ablation_workspace(pg, big - 1, 16, "f32", True) <= qse.STATIC_SCRATCH_BYTES
+    assert ex(pg, big, 16, 0, FAKE, FAKE + (1 << 30), 1, None) == qse.FWT_ESCRATCH
+    assert ex(mt, big, 16, 0, FAKE, FAKE + (1 << 30), 1, None) == qse.FWT_ESCRATCH
+    assert ex(oz, 16, 20, 1, FAKE, FAKE + (1 << 30), 1, None) == qse.FWT_ESCRATCH
+    assert ex(9, 1, 10, 0, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_EINVAL
+    assert ex(pg, -1, 10, 0, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_EINVAL
+    assert ex(pg, 1, 31, 0, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_EINVAL
+    assert ex(pg, 1, 10, 2, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_EINVAL
+    assert ex(pg, 1, 10, 0, FAKE + 4, FAKE + 4 * N, 1, None) == qse.FWT_EALIGN
+    assert ex(pg, 1, 10, 0, FAKE, FAKE, 1, None) == qse.FWT_EINVAL
+    assert ex(pg, 1, 10, 0, None, FAKE, 1, None) == qse.FWT_EINVAL
+    assert ex(oz, 1, 10, 0, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_EUNSUPPORTED
+    assert ex(mt, 1, 15, 0, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_EUNSUPPORTED
+    assert ex(pg, 0, 10, 0, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_OK
+    assert ex(qse.ABLATION_STAGEWISE, 0, 10, 0, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_OK
