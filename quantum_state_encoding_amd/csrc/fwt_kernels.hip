@@ -528,6 +528,48 @@ __device__ __forceinline__ void lane_stage(V* x, int lane)
     }
 }
 
+// The same stage, except that lane bits 4 and 5 are left exchanged with
+// register bits 0 and 1: the second swap of each pair is dropped.  After
+// it, lane bit 4 (5) holds the row bit register bit 0 (1) held, and
+// register bit 0 (1) holds the row bit of lane bit 4 (5); a caller must
+// address the data with that relabelling (lx_thread_row_rl, lx_reg_row_rl).
+template <int LBIT, int E, typename V, typename T>
+__device__ __forceinline__ void lane_stage_nr(V* x, int lane)
+{
+    constexpr int W = sizeof(V) / sizeof(T);
+    if constexpr (LBIT < 4) {
+        lane_stage<LBIT, E, V, T>(x, lane);
+    } else {
+        constexpr int RB = LBIT - 4;   // register bit paired with the lane bit
+        static_assert(E >= 4, "lane bits 4 and 5 pair register bits 0 and 1");
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            if (j & (1 << RB))
+                continue;
+#pragma unroll
+            for (int c = 0; c < W; ++c) {
+                T a = x[j][c], b = x[j | (1 << RB)][c];
+                permlane_swap<LBIT>(a, b);
+                x[j][c] = a + b;
+                x[j | (1 << RB)][c] = a - b;
+            }
+        }
+    }
+}
+
+template <int B, int LB, int GB, int E, typename V, typename T>
+struct LaneStagesNR {
+    __device__ __forceinline__ static void run(V* x, int lane)
+    {
+        lane_stage_nr<GB + B, E, V, T>(x, lane);
+        LaneStagesNR<B + 1, LB, GB, E, V, T>::run(x, lane);
+    }
+};
+template <int LB, int GB, int E, typename V, typename T>
+struct LaneStagesNR<LB, LB, GB, E, V, T> {
+    __device__ __forceinline__ static void run(V*, int) {}
+};
+
 template <int B, int LB, int GB, int E, typename V, typename T>
 struct LaneStages {
     __device__ __forceinline__ static void run(V* x, int lane)
@@ -658,9 +700,30 @@ __device__ __forceinline__ uint32_t lx_thread_row(int lane_row, int wave)
     return r;
 }
 
+// The load layout after lane_stage_nr on lane bits 4 and 5 (both are
+// lane row bits, GB <= 4): lane bits 4, 5 hold the row bits of register
+// bits 0, 1 (LR + W, LR + W + 1), and register bits 0, 1 hold rows 4 - GB
+// and 5 - GB.
+template <int W, int EB, int LR, int GB>
+__device__ __forceinline__ constexpr uint32_t lx_reg_row_rl(int j)
+{
+    return lx_reg_row<W, EB, LR, 0>(j & ~3) | ((uint32_t)(j & 1) << (4 - GB)) |
+           ((uint32_t)((j >> 1) & 1) << (5 - GB));
+}
+template <int W, int EB, int LR, int GB>
+__device__ __forceinline__ uint32_t lx_thread_row_rl(int lane_row, int wave)
+{
+    const uint32_t lr = (uint32_t)lane_row;
+    const uint32_t keep = lr & ~((1u << (4 - GB)) | (1u << (5 - GB)));
+    return lx_thread_row<W, EB, LR, 0>((int)keep, wave) | (((lr >> (4 - GB)) & 1u) << (LR + W)) |
+           (((lr >> (5 - GB)) & 1u) << (LR + W + 1));
+}
+
 // Exchanges X + 1 .. NX: move the next wave bits into the low register
-// bits through LDS, then their stages.
-template <typename V, int KR, int GB, int W, int EB, int PHB, int X, int NX>
+// bits through LDS, then their stages.  RL: the data arrive in the
+// relabelled load layout of lane_stage_nr, which the first exchange's
+// writes undo (its reads, and everything after, use the plain layouts).
+template <typename V, int KR, int GB, int W, int EB, int PHB, int X, int NX, bool RL>
 struct LxRounds {
     __device__ __forceinline__ static void run(V* x, V* L, int lane_row, int g, int wave)
     {
@@ -669,8 +732,12 @@ struct LxRounds {
         constexpr int C = W - X * EB < EB ? W - X * EB : EB;   // wave bits moved
         constexpr int EP = E >> PHB;                           // registers per phase
         constexpr uint32_t MASK = (1u << (KR + GB - PHB)) - 1; // slot within a phase
+        constexpr bool R = RL && X == 0;
         static_assert(PHB == 0 || (NX == 1 && EB - C >= PHB), "phases keep their bits");
-        const uint32_t from = (lx_thread_row<W, EB, LR, X>(lane_row, wave) << GB) | (uint32_t)g;
+        static_assert(!RL || EB >= 2 + PHB, "relabelled register bits lie below the phase bits");
+        const uint32_t from = ((R ? lx_thread_row_rl<W, EB, LR, GB>(lane_row, wave)
+                                  : lx_thread_row<W, EB, LR, X>(lane_row, wave)) << GB) |
+                              (uint32_t)g;
         const uint32_t to = (lx_thread_row<W, EB, LR, X + 1>(lane_row, wave) << GB) | (uint32_t)g;
 #pragma unroll
         for (int ph = 0; ph < (1 << PHB); ++ph) {
@@ -678,18 +745,19 @@ struct LxRounds {
                 __syncthreads();   // the previous reads of this region are done
 #pragma unroll
             for (int j = ph * EP; j < (ph + 1) * EP; ++j)
-                L[(from + (lx_reg_row<W, EB, LR, X>(j) << GB)) & MASK] = x[j];
+                L[(from + ((R ? lx_reg_row_rl<W, EB, LR, GB>(j) : lx_reg_row<W, EB, LR, X>(j))
+                           << GB)) & MASK] = x[j];
             __syncthreads();
 #pragma unroll
             for (int j = ph * EP; j < (ph + 1) * EP; ++j)
                 x[j] = L[(to + (lx_reg_row<W, EB, LR, X + 1>(j) << GB)) & MASK];
         }
         register_stages<C, E>(x);
-        LxRounds<V, KR, GB, W, EB, PHB, X + 1, NX>::run(x, L, lane_row, g, wave);
+        LxRounds<V, KR, GB, W, EB, PHB, X + 1, NX, RL>::run(x, L, lane_row, g, wave);
     }
 };
-template <typename V, int KR, int GB, int W, int EB, int PHB, int NX>
-struct LxRounds<V, KR, GB, W, EB, PHB, NX, NX> {
+template <typename V, int KR, int GB, int W, int EB, int PHB, int NX, bool RL>
+struct LxRounds<V, KR, GB, W, EB, PHB, NX, NX, RL> {
     __device__ __forceinline__ static void run(V*, V*, int, int, int) {}
 };
 
@@ -757,8 +825,14 @@ __device__ __forceinline__ void lx_process(typename S::V* x, typename S::V* L, i
             in_vector(x[j]);
     }
     register_stages<S::EB, S::E>(x);
-    LaneStages<0, S::LR, S::GB, S::E, V, T>::run(x, lane);
-    LxRounds<V, S::KR, S::GB, S::W, S::EB, S::PHB, 0, S::NX>::run(x, L, lane_row, g, wave);
+    // Lane bits 4 and 5 leave their swaps in place when register bits 0 and
+    // 1 lie below the phase bits: the first exchange's writes relabel.
+    constexpr bool RL = S::EB >= 2 + S::PHB;
+    if constexpr (RL)
+        LaneStagesNR<0, S::LR, S::GB, S::E, V, T>::run(x, lane);
+    else
+        LaneStages<0, S::LR, S::GB, S::E, V, T>::run(x, lane);
+    LxRounds<V, S::KR, S::GB, S::W, S::EB, S::PHB, 0, S::NX, RL>::run(x, L, lane_row, g, wave);
     if (do_scale) {
         const T c = (T)scale;
 #pragma unroll
