@@ -84,7 +84,7 @@ enum {
 };
 
 /* Largest supported n (2^30 amplitudes per vector). */
-#define FWT_MAX_N 30   /* fp64 plans support n <= 29 (FWT_EUNSUPPORTED above) */
+#define FWT_MAX_N 30
 
 /* Create a plan for vectors of 2^n amplitudes of `dtype`.
  *  out    receives the plan (set to NULL on failure); must not be NULL.

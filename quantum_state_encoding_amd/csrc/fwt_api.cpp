@@ -154,18 +154,22 @@ int build_lx_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool r
                   const fwt_pass_tuning& t, bool multipass);
 
 // Largest 32-bit lane offset of a pass's tile group must fit (lanes address
-// from the workgroup's first tile).  Returns FWT_OK or FWT_EUNSUPPORTED.
-int check_offsets(const Pass& p, fwt_dtype dtype, bool row, int kr, int vb)
+// from the workgroup's first tile).  `split`: the kernel addresses the top
+// half of each tile's rows from a second base (lane-exchange tiles whose
+// top row bit stays a register bit), so offsets span half the rows.
+// Returns FWT_OK or FWT_EUNSUPPORTED.
+int check_offsets(const Pass& p, fwt_dtype dtype, bool row, int kr, int vb, bool split = false)
 {
     const int esize_bits = dtype == FWT_F64 ? 3 : 2;
     const uint64_t tmax = ((uint64_t)1 << p.tpw_bits) - 1;
+    const int krs = split ? kr - 1 : kr;   // row bits the lane offsets span
     uint64_t max_el;
     if (row) {
-        max_el = ((tmax + 1) << p.k) - 1;
+        max_el = split ? (((uint64_t)1 << (krs + vb)) - 1) : ((tmax + 1) << p.k) - 1;
     } else {
         const uint64_t mask = ((uint64_t)1 << p.nblk_bits) - 1;
         max_el = ((tmax >> p.nblk_bits) << (p.lo + kr)) + ((tmax & mask) << (p.gbits + vb)) +
-                 ((((uint64_t)1 << kr) - 1) << p.lo) + ((uint64_t)1 << (p.gbits + vb)) - 1;
+                 ((((uint64_t)1 << krs) - 1) << p.lo) + ((uint64_t)1 << (p.gbits + vb)) - 1;
     }
     if ((max_el << esize_bits) + ((uint64_t)1 << esize_bits) - 1 > 0xFFFFFFFFull)
         return FWT_EUNSUPPORTED;
@@ -456,7 +460,7 @@ int build_lx_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, int kr, bool r
     p.lds = (size_t)16 << (kr + gbits - phb);
     p.store_back = 0;
     p.tiles_bits = row ? n - k : (n - lo - k) + p.nblk_bits;
-    return check_offsets(p, dtype, row, kr, vb);
+    return check_offsets(p, dtype, row, kr, vb, w < eb);
 }
 
 // Default Kronecker split (bit counts, lowest bits first), from sweeps of
@@ -853,7 +857,8 @@ int fwt_plan_create(fwt_plan_t* out, int n, fwt_dtype dtype, fwt_path path)
         return FWT_EINVAL;
     if (path == FWT_PATH_MFMA_ABLATION) {
         // the default split, with the row pass on the matrix-core kernel
-        if (n < kMfmaRowMin)
+        // (measured and tested up to n = 29 for fp64)
+        if (n < kMfmaRowMin || (dtype == FWT_F64 && n > 29))
             return FWT_EUNSUPPORTED;
         int bits[kMaxPasses] = {0, 0, 0, 0};
         const int np = default_split(n, dtype, FWT_PATH_AUTO, bits);

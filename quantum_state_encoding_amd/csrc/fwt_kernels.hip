@@ -772,6 +772,7 @@ struct LxShape {
     static constexpr int E = 1 << EB;
     static constexpr int LR = 6 - GB;              // row bits held by lanes
     static constexpr int NX = (W + EB - 1) / EB;   // exchanges
+    static constexpr bool SPLIT = W < EB;          // top row bit stays a register bit
     static_assert(KR == EB + LR + W && EB >= 1 && W >= 1 && W <= 4, "lane-exchange tile");
     static_assert(!ROW || GB == 0, "row passes have one column group");
 };
@@ -794,19 +795,41 @@ __device__ __forceinline__ unsigned char* lx_tile_base(T* buf, const TileArgs& a
     return reinterpret_cast<unsigned char*>(buf + base);
 }
 
+// When the exchange moves fewer wave bits than there are register bits
+// (W < EB), the top row bit is the top register bit in the load and the
+// store layout.  The registers with it set then address from a second base
+// half a tile further on, so 32-bit lane offsets need only span half the
+// tile: a column tile may span up to 8 GiB (fp64 n = 30, bits 20..29).
+// Which base a register uses is a compile-time choice.
+template <typename S, int X>
+__device__ __forceinline__ const unsigned char* lx_reg_base(int j, const unsigned char* p,
+                                                            const unsigned char* p_hi)
+{
+    return (S::SPLIT && ((j >> (S::EB - 1)) & 1)) ? p_hi : p;
+}
+template <typename S, int X>
+__device__ __forceinline__ constexpr uint32_t lx_reg_off_row(int j)
+{
+    const uint32_t r = lx_reg_row<S::W, S::EB, S::LR, X>(j);
+    return S::SPLIT ? (r & ~(1u << (S::KR - 1))) : r;
+}
+
 template <typename S>
-__device__ __forceinline__ void lx_load(typename S::V* x, const unsigned char* p, uint32_t gbase,
-                                        uint32_t rsh, uint32_t r0, int nt)
+__device__ __forceinline__ void lx_load(typename S::V* x, const unsigned char* p,
+                                        const unsigned char* p_hi, uint32_t gbase, uint32_t rsh,
+                                        uint32_t r0, int nt)
 {
     using V = typename S::V;
     if (nt) {
 #pragma unroll
         for (int j = 0; j < S::E; ++j)
-            x[j] = load16_nt<V>(p, gbase + ((r0 + lx_reg_row<S::W, S::EB, S::LR, 0>(j)) << rsh));
+            x[j] = load16_nt<V>(lx_reg_base<S, 0>(j, p, p_hi),
+                                gbase + ((r0 + lx_reg_off_row<S, 0>(j)) << rsh));
     } else {
 #pragma unroll
         for (int j = 0; j < S::E; ++j)
-            x[j] = load16<V>(p, gbase + ((r0 + lx_reg_row<S::W, S::EB, S::LR, 0>(j)) << rsh));
+            x[j] = load16<V>(lx_reg_base<S, 0>(j, p, p_hi),
+                             gbase + ((r0 + lx_reg_off_row<S, 0>(j)) << rsh));
     }
 }
 
@@ -842,19 +865,21 @@ __device__ __forceinline__ void lx_process(typename S::V* x, typename S::V* L, i
 }
 
 template <typename S>
-__device__ __forceinline__ void lx_store(const typename S::V* x, unsigned char* p, uint32_t gbase,
-                                         uint32_t rsh, uint32_t rf, int nt)
+__device__ __forceinline__ void lx_store(const typename S::V* x, unsigned char* p,
+                                         unsigned char* p_hi, uint32_t gbase, uint32_t rsh,
+                                         uint32_t rf, int nt)
 {
     using V = typename S::V;
     if (nt) {
 #pragma unroll
         for (int j = 0; j < S::E; ++j)
-            store16_nt<V>(p, gbase + ((rf + lx_reg_row<S::W, S::EB, S::LR, S::NX>(j)) << rsh),
-                          x[j]);
+            store16_nt<V>(const_cast<unsigned char*>(lx_reg_base<S, S::NX>(j, p, p_hi)),
+                          gbase + ((rf + lx_reg_off_row<S, S::NX>(j)) << rsh), x[j]);
     } else {
 #pragma unroll
         for (int j = 0; j < S::E; ++j)
-            store16<V>(p, gbase + ((rf + lx_reg_row<S::W, S::EB, S::LR, S::NX>(j)) << rsh), x[j]);
+            store16<V>(const_cast<unsigned char*>(lx_reg_base<S, S::NX>(j, p, p_hi)),
+                       gbase + ((rf + lx_reg_off_row<S, S::NX>(j)) << rsh), x[j]);
     }
 }
 
@@ -875,11 +900,13 @@ __global__ void __launch_bounds__(64 << W)
     const int lane_row = lane >> GB;
     uint32_t rsh;
     unsigned char* const p = lx_tile_base<S>(blockIdx.y ? im : re, a, t, &rsh);
+    unsigned char* const p_hi = p + ((uint64_t)1 << (KR - 1) << rsh);
     const uint32_t gbase = (uint32_t)g << 4;
     V x[S::E];
-    lx_load<S>(x, p, gbase, rsh, lx_thread_row<W, EB, S::LR, 0>(lane_row, wave), a.ld_nt);
+    lx_load<S>(x, p, p_hi, gbase, rsh, lx_thread_row<W, EB, S::LR, 0>(lane_row, wave), a.ld_nt);
     lx_process<S, T>(x, L, lane, lane_row, g, wave, a.do_scale, a.scale);
-    lx_store<S>(x, p, gbase, rsh, lx_thread_row<W, EB, S::LR, S::NX>(lane_row, wave), a.st_nt);
+    lx_store<S>(x, p, p_hi, gbase, rsh, lx_thread_row<W, EB, S::LR, S::NX>(lane_row, wave),
+                a.st_nt);
 }
 
 __global__ void __launch_bounds__(256)

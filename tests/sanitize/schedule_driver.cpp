@@ -236,7 +236,7 @@ int main()
     for (int d = 0; d <= 1; ++d) {
         const fwt_dtype dt = (fwt_dtype)d;
         const size_t esize = d ? 8 : 4;
-        const int nmax = d ? 29 : 30;
+        const int nmax = 30;
         for (int n = 2; n <= nmax; ++n) {
             std::vector<std::vector<int>> splits = {{}};   // {} = the default plan
             if (n % 5 == 2 && n >= 12) {

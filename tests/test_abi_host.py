@@ -59,7 +59,7 @@ def _split(lib, n, dtype, bits, eb=None, gbits=None, phases=None, pipe=None, wav
 
 @pytest.mark.parametrize("dtype", ["f32", "f64"])
 def test_default_plans_cover_all_bits(dtype, lib):
-    nmax = 30 if dtype == "f32" else 29
+    nmax = 30
     for n in range(0, nmax + 1):
         p = qse.Plan(n, dtype)
         bits = p.pass_bits
@@ -87,7 +87,7 @@ def test_default_splits(lib):
                     26: [15, 11], 27: [10, 9, 8], 30: [10, 10, 10]},
             "f64": {15: [9, 6], 18: [9, 9], 19: [11, 8], 20: [11, 9], 21: [12, 9],
                     22: [13, 9], 23: [14, 9], 24: [14, 10], 25: [14, 11], 26: [10, 8, 8],
-                    29: [10, 10, 9]}}
+                    29: [10, 10, 9], 30: [10, 10, 10]}}
     for dtype, table in want.items():
         for n, bits in table.items():
             assert qse.Plan(n, dtype).pass_bits == bits, (dtype, n)
@@ -111,6 +111,7 @@ def test_chunk_schedule(lib):
     assert p27.call_schedule(2, False) == (2, 19, 128)
     assert qse.Plan(26, "f64").call_schedule(2) == (2, 18, 64)
     assert qse.Plan(30, "f32").call_schedule(1) == (2, 20, 32)
+    assert qse.Plan(30, "f64").call_schedule(1) == (2, 20, 16)
     assert qse.Plan(28, "f32", split=(7, 7, 7, 7)).call_schedule(1) == (3, 21, 16)
     # two-pass plans with such vectors keep one vector per chunk
     assert qse.Plan(26, "f32").call_schedule(4) == (2, 26, 1)
@@ -133,7 +134,9 @@ def test_plan_create_errors(lib):
     assert _create(lib, 30, 1, qse.PATH_MFMA_ABLATION)[0] == qse.FWT_EUNSUPPORTED
     assert _create(lib, 16, 0, qse.PATH_SINGLE_BLOCK)[0] == qse.FWT_EUNSUPPORTED
     assert _create(lib, 15, 1, qse.PATH_SINGLE_BLOCK)[0] == qse.FWT_EUNSUPPORTED
-    assert _create(lib, 30, 1)[0] == qse.FWT_EUNSUPPORTED
+    st, h = _create(lib, 30, 1)      # fp64 n = 30: its top pass spans 8 GiB per tile
+    assert st == qse.FWT_OK
+    lib.fwt_plan_destroy(h)
     assert lib.fwt_plan_create(None, 10, 0, 0) == qse.FWT_EINVAL
 
 

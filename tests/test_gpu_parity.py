@@ -436,7 +436,7 @@ def _parity(t):
     return t & 1
 
 
-@pytest.mark.parametrize("dtype,n", [("f32", 30), ("f64", 29)])
+@pytest.mark.parametrize("dtype,n", [("f32", 30), ("f64", 29), ("f64", 30)])
 def test_largest_n_closed_form(dtype, n):
     """The largest n each dtype supports: x = e_j + 2 e_k (re) and e_k - e_j
     (im) transform to (-1)^popcount(i AND j) + 2 (-1)^popcount(i AND k) and
