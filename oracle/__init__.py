@@ -50,6 +50,8 @@ def _load():
         lib.oracle_fwt_threaded_f32.restype = i32
         lib.oracle_fwt_threaded_f64.argtypes = [pd, i64, i32, i32, i32]
         lib.oracle_fwt_threaded_f64.restype = i32
+        lib.oracle_fwt_ld.argtypes = [pd, pd, i64, i32, i32]
+        lib.oracle_fwt_ld.restype = i32
         lib.oracle_norm_constant_f64.argtypes = [i32]
         lib.oracle_norm_constant_f64.restype = ctypes.c_double
         lib.oracle_norm_constant_f32.argtypes = [i32]
@@ -108,6 +110,18 @@ def bruteforce(x, n, normalize=False):
     y = np.empty_like(a)
     _load().oracle_bruteforce_f64(_ptr(a, ctypes.c_double), _ptr(y, ctypes.c_double),
                                   nvec, n, int(bool(normalize)))
+    return y.reshape(np.shape(x))
+
+
+def fwt_ld(x, n, normalize=False):
+    """The textbook transform evaluated in long double (64-bit significand on
+    x86-64) and rounded to float64 once: a higher-precision cross-check of
+    the fp64 check mode."""
+    a, nvec = _as_rows(x, n, np.float64)
+    y = np.empty_like(a)
+    if _load().oracle_fwt_ld(_ptr(a, ctypes.c_double), _ptr(y, ctypes.c_double), nvec, n,
+                             int(bool(normalize))) != 0:
+        raise MemoryError("oracle_fwt_ld: allocation failed")
     return y.reshape(np.shape(x))
 
 

@@ -41,6 +41,10 @@
  *                           article, section "Kronecker block GEMM idea".
  *   oracle_fwt_threaded_*   the textbook transform run over the batch by a
  *                           pool of POSIX threads (CPU baseline timing).
+ *   oracle_fwt_ld           the same butterfly network in long double
+ *                           (x86-64: 64-bit significand), rounded to double
+ *                           once at the end: a higher-precision evaluation
+ *                           that bounds the rounding of the fp64 check mode.
  *
  * Normalisation constant (the pages do not state one; the plain reading of
  * "1/sqrt(2^n)-normalised" is used): c = 2^(-n/2), computed as
@@ -158,6 +162,38 @@ void oracle_fwt_f32(float* x, int64_t nvec, int n, int normalize)
             for (int64_t k = 0; k < N; ++k)
                 v[k] *= c;
     }
+}
+
+/* The textbook network in long double, one vector at a time, the result
+ * (times c in long double if normalize) rounded to double once.  x and y
+ * must not alias.  Returns 0, or -1 if the work vector cannot be
+ * allocated. */
+int oracle_fwt_ld(const double* x, double* y, int64_t nvec, int n, int normalize)
+{
+    const int64_t N = (int64_t)1 << n;
+    const long double c = n % 2 == 0 ? ldexpl(1.0L, -(n / 2))
+                                     : ldexpl(sqrtl(0.5L), -((n - 1) / 2));
+    long double* v = (long double*)malloc((size_t)N * sizeof(long double));
+    if (!v)
+        return -1;
+    for (int64_t b = 0; b < nvec; ++b) {
+        for (int64_t k = 0; k < N; ++k)
+            v[k] = (long double)x[b * N + k];
+        for (int64_t h = 1; h < N; h *= 2) {
+            for (int64_t i = 0; i < N; i += 2 * h) {
+                for (int64_t j = i; j < i + h; ++j) {
+                    const long double a = v[j];
+                    const long double d = v[j + h];
+                    v[j] = a + d;
+                    v[j + h] = a - d;
+                }
+            }
+        }
+        for (int64_t k = 0; k < N; ++k)
+            y[b * N + k] = (double)(normalize ? v[k] * c : v[k]);
+    }
+    free(v);
+    return 0;
 }
 
 /* Kronecker-composed transform: rows (n2 = n - n1 low bits) first, then

@@ -17,6 +17,7 @@ void oracle_fwt_f32(float* x, int64_t nvec, int n, int normalize);
 int oracle_fwt_kron_f64(double* x, int64_t nvec, int n, int n1, int normalize);
 int oracle_fwt_threaded_f32(float* x, int64_t nvec, int n, int normalize, int nthreads);
 int oracle_fwt_threaded_f64(double* x, int64_t nvec, int n, int normalize, int nthreads);
+int oracle_fwt_ld(const double* x, double* y, int64_t nvec, int n, int normalize);
 
 static uint64_t rng = 0x9E3779B97F4A7C15ull;
 static int next_int(void)   /* xorshift64, values in [-8, 8] */
@@ -59,6 +60,9 @@ int main(void)
             ++bad;
         for (int64_t i = 0; i < tot; ++i)
             bad += (double)wf[i] != brute[i];
+        if (oracle_fwt_ld(x, work, nvec, n, 0) != 0)
+            ++bad;
+        bad += memcmp(work, brute, sizeof(double) * tot) != 0;
         memcpy(work, x, sizeof(double) * tot);
         if (oracle_fwt_threaded_f64(work, nvec, n, 1, 3) < 1)
             ++bad;

@@ -306,3 +306,36 @@ def test_threaded_matches_serial_and_reports_threads():
     z = x.astype(np.float64)
     assert oracle.fwt_threaded_inplace(z, n, False, 3) == 3
     assert np.array_equal(z, oracle.fwt(x.astype(np.float64), n, False))
+
+
+@pytest.mark.parametrize("n", [0, 1, 3, 8, 10])
+def test_long_double_transform_equals_bruteforce_on_integers(n):
+    """The extended-precision network reaches the definition exactly on
+    integer inputs (every partial sum is an integer far below 2^53)."""
+    x = np.random.default_rng(500 + n).integers(-8, 9, size=(3, 1 << n)).astype(np.float64)
+    assert np.array_equal(oracle.fwt_ld(x, n, False), oracle.bruteforce(x, n, False))
+    if n % 2 == 0:
+        assert np.array_equal(oracle.fwt_ld(x, n, True), oracle.bruteforce(x, n, True))
+
+
+@pytest.mark.parametrize("n", [12, 13, 16, 17, 20])
+def test_fp64_check_mode_against_long_double(n):
+    """The fp64 check mode against the same network in long double: each of
+    the n stages rounds once (relative error 2^-53 per output; every stage
+    of the unnormalised network has norm sqrt(2), so the 2-norm of the
+    accumulated error stays within n * 2^-53 * 2^(n/2) * ||x||), the scale
+    rounds once more, and the long-double result is rounded to double once:
+    max |fp64 - long double| <= (n + 2) * 2^-53 * ||x|| after
+    normalisation.  That is at least 10^3 below the 1e-12 * ||x|| fp64
+    tolerance of the GPU comparisons."""
+    x = np.random.default_rng(600 + n).standard_normal((2, 1 << n))
+    y64 = oracle.fwt(x, n, True)
+    yld = oracle.fwt_ld(x, n, True)
+    for b in range(2):
+        nx = np.sqrt(np.sum(x[b] ** 2))
+        err = np.abs(y64[b] - yld[b]).max()
+        assert err <= (n + 2) * 2.0 ** -53 * nx, (b, err / nx)
+        assert err <= 1e-15 * nx
+    # and the long-double result keeps the norm to far better than fp64
+    nld = np.sqrt(np.sum(yld.astype(np.longdouble) ** 2, axis=1))
+    assert np.abs(nld - np.sqrt(np.sum(x.astype(np.longdouble) ** 2, axis=1))).max() <= 1e-14
