@@ -526,18 +526,24 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
         return out
     fetch, write = counters(fetch_dir), counters(write_dir)
 
-    # Calibration: the streaming copy of one component moves S/2 bytes each way.
+    # Calibration: the streaming copy of one component moves S/2 bytes each
+    # way (the launch with the largest grid; the bench also copies a 64 MiB
+    # buffer for its cache-resident ceiling).
     half_kib = w.state_bytes / 2 / 1024
-    cf = [v for (k, g), v in fetch.items() if "stream_copy_kernel" in k]
-    cw = [v for (k, g), v in write.items() if "stream_copy_kernel" in k]
-    f_scale = half_kib / float(np.mean(cf[0])) if cf else None
-    w_scale = half_kib / float(np.mean(cw[0])) if cw else None
+    cf = sorted(((g, v) for (k, g), v in fetch.items() if "stream_copy_kernel" in k),
+                key=lambda gv: -gv[0])
+    cw = sorted(((g, v) for (k, g), v in write.items() if "stream_copy_kernel" in k),
+                key=lambda gv: -gv[0])
+    f_scale = half_kib / float(np.mean(cf[0][1])) if cf else None
+    w_scale = half_kib / float(np.mean(cw[0][1])) if cw else None
     chunk = plan.chunk_vectors(w.batch, True) or w.batch
     chunk_bytes = w.state_bytes * chunk // w.batch
     lines = ["# rocprofv3 kernel trace: %s" % workload,
              "# command: " + command,
              "# kernel | grid (threads x, y) | dispatches | avg us | min us | max us"]
     for (name, gx, gy), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        if "at::native" in name:       # torch's input generation, not timed work
+            continue
         lines.append("%s | %d x %d | %d | %.2f | %.2f | %.2f" % (
             _short(name), gx, gy, len(d), np.mean(d) / 1e3, np.min(d) / 1e3, np.max(d) / 1e3))
     passes = {}
@@ -604,6 +610,8 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
                      "bank-conflict cycles | conflict / active | memory violations | "
                      "unaligned stalls"]
         for (name, grid), a in sorted(agg.items(), key=lambda kv: -kv[1].get("SQ_LDS_IDX_ACTIVE", 0)):
+            if "at::native" in name:
+                continue
             act = a.get("SQ_LDS_IDX_ACTIVE", 0.0)
             bc = a.get("SQ_LDS_BANK_CONFLICT", 0.0)
             lds_lines.append("%s | %d | %d | %.0f | %.0f | %.0f | %.4f | %.0f | %.0f" % (
@@ -714,7 +722,7 @@ def main():
     cache_copy = cache_copy_ceiling(torch)
 
     if args.ablations_only:
-        r = gpu_workload(torch, head, args.steps, args.warmup)
+        r = gpu_workload(torch, head, args.steps, args.warmup, split=None)   # default plan
         abl = bench_ablations(torch, head, r["ms"])
         print(json.dumps({"workload": head.name, "native_ms": r["ms"], "ablations": abl}),
               flush=True)
