@@ -261,10 +261,15 @@ def gpu_workload(torch, w, steps, warmup, split="configured", full=False, keep_o
         step()
     torch.cuda.synchronize()
     # Cache-resident workloads take microseconds per call: time at least
-    # 20 ms of them.
+    # 20 ms of them, after as many untimed calls (the GPU may have idled
+    # through the previous workload's CPU leg and must be back at speed).
     est = time_events(torch, stream, step, 3)
     k = max(steps, int(math.ceil(20.0 / max(est, 1e-3)))) if w.state_bytes < (256 << 20) \
         else steps
+    if k > steps:
+        for _ in range(k):
+            step()
+        torch.cuda.synchronize()
     log("timing %s: %d steps" % (w.name, k))
     t0 = time.perf_counter()
     ms = time_events(torch, stream, step, k)
