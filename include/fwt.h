@@ -148,9 +148,10 @@ typedef struct {
                     every field of the entry is -1: the wave-tile kernel
                     for a one-pass plan with 3 <= n <= 10; else the
                     lane-exchange kernel for a row pass of 8..13 row bits,
-                    except the row pass of a multi-pass plan with 11, and
-                    for a column pass of 8..11 bits whose rows hold at
-                    least 8 groups; else LDS tiles.  "Row bits" of a row
+                    except the row pass of a multi-pass plan with 11, for
+                    a column pass of 8..11 bits whose rows hold at least 8
+                    groups, and for a 7-bit column pass whose rows hold at
+                    least 16 groups (16 groups, eb = 2); else LDS tiles.  "Row bits" of a row
                     pass counts 16-byte vectors: the pass's bits less 2
                     (fp32) or 1 (fp64); of a column pass, the pass's
                     bits. */

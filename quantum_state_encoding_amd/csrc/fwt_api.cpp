@@ -255,6 +255,23 @@ int build_pass(Pass& p, int n, fwt_dtype dtype, int lo, int k, const fwt_pass_tu
         p.lo = lo;
         p.k = k;
     }
+    // 7-bit column passes with rows of at least 16 groups: the lane-exchange
+    // tile of 16 groups with eb = 2 (512 threads, one exchange) measured
+    // 0.1-3.7 % faster than the LDS tiles on every state tried (fp32 n = 14
+    // as 7|7 at 8-512 MiB, n = 17 at 16 MiB and 2 GiB, fp64 n = 16 at 16 MiB
+    // and 1 GiB).  (At 6 bits it was mixed: up to 11 % slower.)
+    if (all_default && !row && kr == 7 && lo - vec_bits(dtype) >= 4) {
+        fwt_pass_tuning t7 = t;
+        t7.eb = 2;
+        t7.gbits = 4;
+        t7.phases = 0;
+        const int rc = build_lx_pass(p, n, dtype, lo, k, kr, row, t7, multipass);
+        if (rc == FWT_OK)
+            return rc;
+        p = Pass{};
+        p.lo = lo;
+        p.k = k;
+    }
     const int eb = eb_req < 0 ? default_eb(kr, dtype, multipass, row) : eb_req;
     // A round of LDS tiles butterflies eb register bits, so a tile with row
     // bits needs eb >= 1 (rounds_of divides by eb).

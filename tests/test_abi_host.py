@@ -372,8 +372,8 @@ def test_default_kernel_choice(lib):
     """One-pass plans of 3 <= n <= 10 default to the wave-tile kernel; other
     row passes of 8..13 vector bits to the lane-exchange kernel (except a
     multi-pass row pass of 11), and so do column passes of 8..11 bits with
-    rows of at least 8 groups; the rest, and entries with any field forced,
-    use the LDS tiles."""
+    rows of at least 8 groups and of 7 bits with rows of at least 16 groups;
+    the rest, and entries with any field forced, use the LDS tiles."""
     for dtype, vb in (("f32", 2), ("f64", 1)):
         for n in range(2, 15 if dtype == "f32" else 14):
             want = 1 if 3 <= n <= 10 else (2 if n - vb >= 8 else 0)
@@ -389,7 +389,8 @@ def test_default_kernel_choice(lib):
                 if i == 0:
                     want.append(2 if b - vb >= 8 and b - vb != 11 else 0)
                 else:
-                    want.append(2 if 8 <= b <= 11 and lo - vb >= 3 else 0)
+                    want.append(2 if (8 <= b <= 11 and lo - vb >= 3) or (b == 7 and lo - vb >= 4)
+                                else 0)
                 lo += b
             assert [p.pass_config(i)["wave"] for i in range(p.num_passes)] == want, split
     for (dtype, n), (bits, wave) in {
@@ -402,6 +403,9 @@ def test_default_kernel_choice(lib):
         p = qse.Plan(n, dtype)
         assert p.pass_bits == bits, (dtype, n)
         assert [p.pass_config(i)["wave"] for i in range(2)] == wave, (dtype, n)
+    # 7 column bits: 16 groups, eb = 2 (the configured n = 14 split 7|7)
+    assert qse.Plan(14, "f32", split=(7, 7)).kernel_name(1) == "lx_kernel<float, 7, 2, 3, 0, 4, false>"
+    assert qse.Plan(17, "f32").kernel_name(1) == "lx_kernel<float, 7, 2, 3, 0, 4, false>"
     # column passes: eb = 4, two exchange phases, 16 groups up to 9 bits
     assert qse.Plan(20, "f32").kernel_name(1) == "lx_kernel<float, 8, 4, 2, 1, 4, false>"
     assert qse.Plan(24, "f64").kernel_name(1) == "lx_kernel<double, 10, 4, 3, 1, 3, false>"
