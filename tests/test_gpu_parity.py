@@ -949,6 +949,33 @@ def test_bound_call_keeps_its_plan_alive():
     assert_exact(tre.cpu().numpy(), re, n, False)
 
 
+def test_bound_call_keeps_its_tensors_alive():
+    """The callable holds the bound tensors: when the caller drops its own
+    references, torch's caching allocator cannot hand their memory to a new
+    tensor, so a later call transforms the bound data and nothing else."""
+    say("bind keeps tensors")
+    import gc
+    import weakref
+    n = 10
+    re = ints((4, 1 << n), 6, np.float32)
+    im = ints((4, 1 << n), 7, np.float32)
+    tre, tim = to_dev(re), to_dev(im)
+    step = qse.Plan(n, "f32").bind(tre, tim, normalize=False)
+    ref_re, ref_im = weakref.ref(tre), weakref.ref(tim)
+    del tre, tim
+    gc.collect()
+    assert ref_re() is not None and ref_im() is not None
+    other = torch.full((4, 1 << n), 3.0, device="cuda")   # same size, allocated after
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(other, torch.full_like(other, 3.0))
+    assert_exact(ref_re().cpu().numpy(), re, n, False)
+    assert_exact(ref_im().cpu().numpy(), im, n, False)
+    del step
+    gc.collect()
+    assert ref_re() is None and ref_im() is None          # released with the callable
+
+
 def test_stream_copy():
     say("stream copy")
     src = torch.randn(3 * 2**20 + 12, device="cuda")
