@@ -650,10 +650,14 @@ __global__ void __launch_bounds__(256)
 // the register, lane and (row passes) in-vector stages, each exchange
 // through LDS swaps the next min(EB, bits left) wave bits with the low
 // register bits, whose stages then run in registers: ceil(W / EB)
-// exchanges in all.  Lane bits never move, so the lanes of a wave always
+// exchanges in all.  Lane bits keep their rows, so the lanes of a wave
 // touch 64 consecutive 16-byte LDS slots (slot = row * 2^GB + group): the
-// exchanges need no padding.  In memory a wave covers 2^LR rows of 2^GB
-// consecutive 16-byte groups (1 KiB for row passes).
+// exchanges need no padding.  (With EB >= 2 + PHB, lane bits 4 and 5 stay
+// exchanged with register bits 0 and 1 after their stages, lane_stage_nr;
+// the first exchange's writes then cover four runs of 16 consecutive slots
+// per wave, still conflict-free, and its reads restore the plain layout.)
+// In memory a wave covers 2^LR rows of 2^GB consecutive 16-byte groups
+// (1 KiB for row passes).
 //
 // With PHB > 0 (one exchange, W < EB) the exchange runs in 2^PHB phases:
 // the top PHB register bits do not move, they are the top row bits in both
