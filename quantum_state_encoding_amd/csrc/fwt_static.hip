@@ -58,7 +58,8 @@ extern "C" int fwt_ablation_execute_static(int kind, int64_t batch, int n, fwt_d
     const size_t need = qse::ablation_workspace_size(kind, batch, n, (int)dtype, im ? 1 : 0);
     if (need > (size_t)FWT_STATIC_SCRATCH_BYTES)
         return FWT_ESCRATCH;
-    // Every argument check runs before the first HIP call.
+    // Every argument check (the device-memory range queries included) runs
+    // before the scratch lookup and before anything is enqueued.
     int rc = qse::ablation_validate(kind, batch, n, (int)dtype, re, im);
     if (rc != FWT_OK || batch == 0)
         return rc;
