@@ -1,0 +1,129 @@
+"""Host-side checks of bench.py's accounting (no GPU): the roofline is one
+read plus one write of a chunk's state over the summed durations of that
+chunk's pass kernels, the per-workload records carry the measurement
+fields, and the rocprofv3 summaries calibrate the counters on the
+state-sized streaming copy."""
+import csv
+import json
+import os
+
+import pytest
+
+import bench
+import workloads
+
+
+def _measured(w, per_pass_ms, chunk, pass_bits):
+    return {"ms": sum(per_pass_ms) * w.batch / chunk, "steps": 10, "wall_ms": 1.0,
+            "passes": len(per_pass_ms), "pass_bits": list(pass_bits),
+            "per_pass_ms": per_pass_ms, "copy_ms": 0.79, "S": w.state_bytes, "chunk": chunk,
+            "check": None, "reps_ms": [1.27, 1.28, 1.29],
+            "kernel_names": ["row", "col"][:len(per_pass_ms)], "output": None, "inputs": None}
+
+
+def test_roofline_counts_one_read_and_write_per_transform(monkeypatch):
+    monkeypatch.setattr(bench, "traffic_record", lambda name: None)
+    w = workloads.WORKLOADS["n20_b256_f32"]
+    r = _measured(w, [0.0807, 0.0775], 32, (12, 8))
+    rl = bench.roofline(w, r, {"gbps": 6650.0})
+    chunk_bytes = w.state_bytes * 32 // w.batch
+    assert rl["algorithmic_bytes"] == 2 * chunk_bytes == 512 << 20
+    assert rl["achieved"] == pytest.approx(2 * chunk_bytes / (0.1582e-3) / 1e9)
+    assert rl["frac"] == pytest.approx(rl["achieved"] / 8000.0)
+    assert 0.42 < rl["frac"] < 0.43
+    assert rl["peak"] == 8000.0 and rl["unit"] == "GB/s" and rl["bound"] == "hbm"
+    assert rl["traffic"] is None            # no counter record for this source
+    assert rl["launches_per_step"] == 2 * 8
+    # per pass: the rate at which it moves its chunk
+    assert rl["passes"][0]["pass_fabric_gbps"] == pytest.approx(2 * chunk_bytes / 0.0807e-3 / 1e9)
+
+
+def test_roofline_sums_the_counter_bytes_of_every_pass(monkeypatch):
+    w = workloads.WORKLOADS["n24_b16_f64"]
+    rec = {"fetch_scale": 2.0, "write_scale": 1.0,
+           "passes": {"0": {"bytes_per_launch": 5.0e8, "fetch_kib": 1000.0, "write_kib": 2000.0,
+                            "kernel": "k0"},
+                      "1": {"bytes_per_launch": 6.0e8, "fetch_kib": 3000.0, "write_kib": 4000.0,
+                            "kernel": "k1"}}}
+    monkeypatch.setattr(bench, "traffic_record", lambda name: rec)
+    monkeypatch.setattr(bench, "lds_conflicts", lambda name, kernel: None)
+    rl = bench.roofline(w, _measured(w, [0.090, 0.081], 1, (14, 10)), {"gbps": 6650.0})
+    assert rl["traffic"] == pytest.approx(1.1e9)
+    assert rl["fetch_bytes"] == pytest.approx((1000.0 + 3000.0) * 2.0 * 1024)
+    assert rl["write_bytes"] == pytest.approx((2000.0 + 4000.0) * 1.0 * 1024)
+
+
+def test_config_record_carries_the_measurement_fields():
+    w = workloads.WORKLOADS["n24_b16_f64"]
+    r = _measured(w, [0.090, 0.081], 1, (14, 10))
+    cpu = {"cores": 16, "ms": 575.0, "value": 4.7e8, "single_thread_ms_per_real_vector": 127.0,
+           "oracle_check": {"max_err_over_norm": 4e-19, "exact": False, "within_tolerance": True,
+                            "vectors": 16}}
+    rec = bench.config_record(5, w, r, cpu, "as configured")
+    for key in ("cfg", "n", "batch", "dtype", "path", "passes", "t_ms_median", "t_ms_min",
+                "amps_per_s", "gbps_accounted", "pct_peak_accounted", "pct_peak_algorithmic",
+                "copy_gbps", "max_err_over_norm", "exact", "cpu_cores", "cpu_ms",
+                "cpu_amps_per_s", "seed", "cpu_single_thread_ms_per_real_vector"):
+        assert key in rec, key
+    assert rec["pct_peak_algorithmic"] == pytest.approx(
+        100 * 2 * w.state_bytes / (r["ms"] * 1e-3) / 1e9 / 8000.0)
+    assert rec["gbps_accounted"] == pytest.approx(2 * rec["gbps_algorithmic"])
+    assert rec["path"] == "split 10|14"
+
+
+def _write_csv(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=list(rows[0].keys()))
+        wr.writeheader()
+        wr.writerows(rows)
+
+
+def test_profile_summary_calibrates_on_the_state_copy(tmp_path, monkeypatch, lib):
+    """bench.py runs a 64 MiB cache-resident copy before the state-sized
+    one; the counters must be scaled by the state-sized copy."""
+    import quantum_state_encoding_amd as qse
+    w = workloads.WORKLOADS["n20_b256_f32"]
+    plan = qse.Plan(w.n, w.dtype)
+    k0, k1 = plan.kernel_name(0, w.batch), plan.kernel_name(1, w.batch)
+    names = {"row": "void qse::(anonymous namespace)::%s(float*, float*, qse::TileArgs)" % k0,
+             "col": "void qse::(anonymous namespace)::%s(float*, float*, qse::TileArgs)" % k1,
+             "copy": "stream_copy_kernel(int4*, int4 const*, long)"}
+    grids = {"row": (2097152, 2), "col": (524288, 2), "copy_small": (524288, 1),
+             "copy_state": (8388608, 1)}
+    kt = []
+    for key, gkey, dur in (("row", "row", 80000), ("col", "col", 78000),
+                           ("copy", "copy_small", 20000), ("copy", "copy_state", 390000)):
+        for i in range(4):
+            kt.append({"Kernel_Name": names[key], "Grid_Size_X": grids[gkey][0],
+                       "Grid_Size_Y": grids[gkey][1], "Start_Timestamp": 1000 * i,
+                       "End_Timestamp": 1000 * i + dur})
+    _write_csv(str(tmp_path / "kt" / "x_kernel_trace.csv"), kt)
+    half_kib = w.state_bytes / 2 / 1024
+    chunk_kib = w.state_bytes * 32 // w.batch / 1024
+
+    def counters(name, small, state, row, col):
+        rows = []
+        for key, gkey, val in (("copy", "copy_small", small), ("copy", "copy_state", state),
+                               ("row", "row", row), ("col", "col", col)):
+            for i in range(2):
+                rows.append({"Kernel_Name": names[key],
+                             "Grid_Size": grids[gkey][0] * grids[gkey][1],
+                             "Counter_Name": name, "Counter_Value": val,
+                             "Dispatch_Id": "%s%d" % (gkey, i)})
+        return rows
+    # FETCH_SIZE reads half the bytes a copy moves, WRITE_SIZE all of them
+    _write_csv(str(tmp_path / "f" / "x_counter_collection.csv"),
+               counters("FETCH_SIZE", 64 * 1024 / 2, half_kib / 2, chunk_kib / 2, chunk_kib / 2))
+    _write_csv(str(tmp_path / "w" / "x_counter_collection.csv"),
+               counters("WRITE_SIZE", 64 * 1024, half_kib, chunk_kib, chunk_kib))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "profiles" / "traffic.json"))
+    bench.summarize_profile(w.name, str(tmp_path / "kt"), str(tmp_path / "f"),
+                            str(tmp_path / "w"), "rocprofv3 ...")
+    rec = json.load(open(tmp_path / "profiles" / "traffic.json"))["workloads"][w.name]
+    assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
+    for p in ("0", "1"):
+        assert rec["passes"][p]["bytes_per_launch"] == pytest.approx(2 * chunk_kib * 1024)
+    text = open(tmp_path / "profiles" / ("%s_traffic.txt" % w.name)).read()
+    assert "0.42" in text.splitlines()[-1] or "0.43" in text.splitlines()[-1]
