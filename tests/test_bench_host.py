@@ -17,7 +17,7 @@ def _measured(w, per_pass_ms, chunk, pass_bits):
     return {"ms": sum(per_pass_ms) * w.batch / chunk, "steps": 10, "wall_ms": 1.0,
             "passes": len(per_pass_ms), "pass_bits": list(pass_bits),
             "per_pass_ms": per_pass_ms, "copy_ms": 0.79, "S": w.state_bytes, "chunk": chunk,
-            "check": None, "reps_ms": [1.27, 1.28, 1.29],
+            "check": None, "reps_ms": [1.27, 1.28, 1.29, 1.30, 1.31],
             "kernel_names": ["row", "col"][:len(per_pass_ms)], "output": None, "inputs": None}
 
 
@@ -65,8 +65,11 @@ def test_config_record_carries_the_measurement_fields():
                 "copy_gbps", "max_err_over_norm", "exact", "cpu_cores", "cpu_ms",
                 "cpu_amps_per_s", "seed", "cpu_single_thread_ms_per_real_vector"):
         assert key in rec, key
+    blocks = sorted([r["ms"]] + r["reps_ms"])                # the six timed blocks
+    t_med = (blocks[2] + blocks[3]) / 2
+    assert rec["t_ms_median"] == pytest.approx(t_med)
     assert rec["pct_peak_algorithmic"] == pytest.approx(
-        100 * 2 * w.state_bytes / (r["ms"] * 1e-3) / 1e9 / 8000.0)
+        100 * 2 * w.state_bytes / (t_med * 1e-3) / 1e9 / 8000.0)
     assert rec["gbps_accounted"] == pytest.approx(2 * rec["gbps_algorithmic"])
     assert rec["path"] == "split 10|14"
 
