@@ -350,8 +350,10 @@ int fwt_ablation_execute(int kind, int64_t batch, int n, fwt_dtype dtype, void* 
  * hipMalloc.  Same kinds, arguments, layout and results as
  * fwt_ablation_execute, but the workspace is the library's static scratch
  * array on the current device (FWT_STATIC_SCRATCH_BYTES), so no workspace
- * is passed.  The call allocates no device memory and calls no allocating
- * routine.  The caller still provides re and im.
+ * is passed.  The call allocates no device memory and calls no device
+ * allocation routine.  (As with fwt_ablation_execute, the matrix-core kind
+ * builds its small host-side plan on its first call for each dtype and n,
+ * and keeps it for the process.)  The caller still provides re and im.
  *  - Returns FWT_ESCRATCH when fwt_ablation_workspace for the call exceeds
  *    FWT_STATIC_SCRATCH_BYTES (e.g. the popcount GEMM or the transposed
  *    matrix-core form beyond 32 MiB of state, the INT8 / CRT form beyond
