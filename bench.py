@@ -227,10 +227,12 @@ def cpu_leg(w, gpu_out=None, inputs=None, repeats=None):
     return rec
 
 
-def gpu_workload(torch, w, steps, warmup, split="configured", full=False, keep_output=False):
+def gpu_workload(torch, w, steps, warmup, split="configured", full=False, keep_output=False,
+                 graph=True):
     """GPU measurements of one workload: the timed steps, five short
-    repeats, and (full=True) per-kernel durations over the chunk schedule,
-    the involution self-check and a same-size streaming copy."""
+    repeats, the HIP-graph replay time of cache-resident workloads
+    (graph=True), and (full=True) per-kernel durations over the chunk
+    schedule, the involution self-check and a same-size streaming copy."""
     import quantum_state_encoding_amd as qse
     dev = torch.device("cuda:0")
     tdt = torch.float32 if w.dtype == "f32" else torch.float64
@@ -281,7 +283,7 @@ def gpu_workload(torch, w, steps, warmup, split="configured", full=False, keep_o
     # once into a HIP graph and replayed show the time without host
     # submission (reported beside the eager time, never as `value`).
     graph_ms = None
-    if w.state_bytes < (256 << 20):
+    if graph and w.state_bytes < (256 << 20):
         try:
             kg = min(k, 200)
             gs = torch.cuda.Stream()
@@ -414,6 +416,38 @@ def roofline(w, r, cache_copy):
             "passes": per_pass, "launches_per_step": launches}
 
 
+def counter_fields(w, label, r):
+    """The committed rocprofv3 counter record of this workload and plan
+    (profiles/traffic.json), per call: calibrated FETCH_SIZE and WRITE_SIZE
+    bytes summed over every launch of the call, their ratio to the
+    accounted bytes (one read and one write of the state per pass), and the
+    bank-conflict cycles per LDS-active cycle of each pass kernel.  Empty
+    when no record matches the current kernel source or the plan."""
+    trec = traffic_record(w.name)
+    if not trec:
+        return {}
+    prec = trec.get("plans", {}).get(label)
+    if prec is None and label == "as configured" and "plans" not in trec:
+        prec = trec
+    if not prec:
+        return {}
+    passes = prec.get("passes", {})
+    if len(passes) != r["passes"] or any("bytes_per_launch" not in p for p in passes.values()):
+        return {}
+    launches = -(-w.batch // (prec.get("chunk_vectors") or w.batch))
+    fetch = sum(p["fetch_kib"] for p in passes.values()) * trec["fetch_scale"] * 1024 * launches
+    write = sum(p["write_kib"] for p in passes.values()) * trec["write_scale"] * 1024 * launches
+    return {"fetch_bytes": fetch, "write_bytes": write,
+            "measured_over_accounted": (fetch + write) / (2.0 * w.state_bytes * r["passes"]),
+            "lds_bank_conflicts": {p["kernel"]: (lds_conflicts(w.name, p["kernel"]) or {}).get(
+                "conflict_per_active") for p in passes.values()},
+            "counters_note": "rocprofv3 FETCH_SIZE / WRITE_SIZE per call (L2-fabric bytes, "
+                             "Infinity-Cache hits included; lines an L2 still held from the "
+                             "previous call would not be counted), over one read and one "
+                             "write of the state per pass; LDS: bank-conflict cycles per "
+                             "LDS-active cycle"}
+
+
 def config_record(cfg, w, r, cpu, label):
     """Record of one configured workload.  Its rates use the median over
     the timed block and the five repeats after it (the minimum is reported
@@ -445,6 +479,7 @@ def config_record(cfg, w, r, cpu, label):
                         "overflow to infinities, which take the same add/sub path")
     if r["copy_ms"]:
         rec["copy_gbps"] = 2 * S / (r["copy_ms"] * 1e-3) / 1e9
+    rec.update(counter_fields(w, label, r))
     if r["check"]:
         rec["involution_check"] = r["check"]
     if cpu is not None:
@@ -541,12 +576,22 @@ def _short(name):
         "(double*")[0]
 
 
+def _profiled_plans(w):
+    """(label, split) of each plan bench.py times for a workload: as
+    configured, and the default plan where the configured records list it
+    too."""
+    out = [("as configured", w.split or None)]
+    if any(n == w.name and s is None for _, n, s in CONFIGS):
+        out.append(("default plan", None))
+    return out
+
+
 def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=None):
     """Turn rocprofv3 CSV output of this benchmark into the text summaries
-    under profiles/ and profiles/traffic.json (L2-fabric bytes per launch)."""
+    under profiles/ and profiles/traffic.json (L2-fabric bytes per launch,
+    per pass of each plan the benchmark times for the workload)."""
     import quantum_state_encoding_amd as qse
     w = workloads.WORKLOADS[workload]
-    plan = qse.Plan(w.n, w.dtype, split=w.split or None)
     trace = _read_csv(_find(kt_dir, "kernel_trace.csv"))
     groups = {}
     for r in trace:
@@ -561,18 +606,20 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
         return out
     fetch, write = counters(fetch_dir), counters(write_dir)
 
-    # Calibration: the streaming copy of one component moves S/2 bytes each
-    # way (the launch with the largest grid; the bench also copies a 64 MiB
-    # buffer for its cache-resident ceiling).
-    half_kib = w.state_bytes / 2 / 1024
-    cf = sorted(((g, v) for (k, g), v in fetch.items() if "stream_copy_kernel" in k),
-                key=lambda gv: -gv[0])
-    cw = sorted(((g, v) for (k, g), v in write.items() if "stream_copy_kernel" in k),
-                key=lambda gv: -gv[0])
-    f_scale = half_kib / float(np.mean(cf[0][1])) if cf else None
-    w_scale = half_kib / float(np.mean(cw[0][1])) if cw else None
-    chunk = plan.chunk_vectors(w.batch, True) or w.batch
-    chunk_bytes = w.state_bytes * chunk // w.batch
+    # Calibration on the streaming copy: a launch of G threads moves G x 128
+    # bytes each way (eight 16-byte vectors per thread).  The launch with
+    # the largest grid is used (the bench copies a 64 MiB buffer for its
+    # cache-resident ceiling and, for the large workloads, the state).
+    def calibration(cs):
+        c = sorted(((g, v) for (k, g), v in cs.items() if "stream_copy_kernel" in k),
+                   key=lambda gv: -gv[0])
+        if not c:
+            return None, None
+        g, v = c[0]
+        return g * 128 / 1024 / float(np.mean(v)), g * 128
+    f_scale, copy_bytes = calibration(fetch)
+    w_scale, _ = calibration(write)
+    resident = w.state_bytes < (256 << 20)
     lines = ["# rocprofv3 kernel trace: %s" % workload,
              "# command: " + command,
              "# kernel | grid (threads x, y) | dispatches | avg us | min us | max us"]
@@ -581,7 +628,6 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
             continue
         lines.append("%s | %d x %d | %d | %.2f | %.2f | %.2f" % (
             _short(name), gx, gy, len(d), np.mean(d) / 1e3, np.min(d) / 1e3, np.max(d) / 1e3))
-    passes = {}
 
     def run_command(counters, out_dir, out_name):
         # the recorded trace command, with the counter run's options and
@@ -593,37 +639,52 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
           "# commands: " + run_command("--pmc FETCH_SIZE", fetch_dir, "f"),
           "#           " + run_command("--pmc WRITE_SIZE", write_dir, "w"),
           "# calibration on fwt_stream_copy of %.0f KiB each way: FETCH_SIZE x %.4f, "
-          "WRITE_SIZE x %.4f" % (half_kib, f_scale or float("nan"), w_scale or float("nan")),
+          "WRITE_SIZE x %.4f" % ((copy_bytes or 0) / 1024, f_scale or float("nan"),
+                                 w_scale or float("nan")),
           "# FETCH_SIZE and WRITE_SIZE count bytes between the L2s and the fabric, "
           "Infinity-Cache hits included: HBM bytes only for a pass whose data is not "
-          "cache-resident",
-          "# pass | kernel | launches | FETCH KiB | WRITE KiB | scaled L2-fabric bytes/launch | "
-          "bytes one read + one write of the chunk moves | ratio | avg us (trace)"]
-    total_alg, total_us = 2 * chunk_bytes, 0.0
-    for i in range(plan.num_passes):
-        kname = plan.kernel_name(i, w.batch)
-        cand = [(k, v) for k, v in groups.items() if kname in k[0]]
-        if not cand:
-            continue
-        (name, gx, gy), d = max(cand, key=lambda kv: kv[0][1] * kv[0][2])
-        fv = fetch.get((name, gx * gy)) or fetch.get((name, gx))
-        wv = write.get((name, gx * gy)) or write.get((name, gx))
-        rec = {"kernel": _short(name), "grid": [gx, gy], "dispatches": len(d),
-               "avg_us": float(np.mean(d) / 1e3), "chunk_rw_bytes_per_launch": 2 * chunk_bytes}
-        total_us += rec["avg_us"]
-        if fv and wv and f_scale and w_scale:
-            b = (float(np.mean(fv)) * f_scale + float(np.mean(wv)) * w_scale) * 1024
-            rec.update({"fetch_kib": float(np.mean(fv)), "write_kib": float(np.mean(wv)),
-                        "bytes_per_launch": b})
-            tl.append("%d | %s | %d | %.1f | %.1f | %.4g | %.4g | %.4f | %.2f" % (
-                i, _short(name), len(fv), np.mean(fv), np.mean(wv), b, 2 * chunk_bytes,
-                b / (2 * chunk_bytes), rec["avg_us"]))
-        passes[str(i)] = rec
-    if total_us:
-        tl.append("# transform of one chunk: %d passes, %.2f us in all; algorithmic bytes "
-                  "(one read + one write of the chunk) %d -> %.1f GB/s, %.3f of 8 TB/s" % (
-                      len(passes), total_us, total_alg, total_alg / total_us / 1e3,
-                      total_alg / total_us / 1e3 / HBM_PEAK_GBS))
+          "cache-resident" + ("; this state stays in the Infinity Cache across calls (lines "
+                              "an L2 still held from the previous call would not be "
+                              "counted)" if resident else "")]
+    plans = {}
+    for label, split in _profiled_plans(w):
+        plan = qse.Plan(w.n, w.dtype, split=split)
+        chunk = plan.chunk_vectors(w.batch, True) or w.batch
+        chunk_bytes = w.state_bytes * chunk // w.batch
+        tl += ["# plan %s: %s, %d pass(es), chunks of %d vector(s)" % (
+                   label, "split " + "|".join(str(b) for b in plan.pass_bits[::-1]),
+                   plan.num_passes, chunk),
+               "# pass | kernel | launches | FETCH KiB | WRITE KiB | scaled L2-fabric "
+               "bytes/launch | bytes one read + one write of the chunk moves | ratio | "
+               "avg us (trace)"]
+        passes = {}
+        total_alg, total_us = 2 * chunk_bytes, 0.0
+        for i in range(plan.num_passes):
+            kname = plan.kernel_name(i, w.batch)
+            cand = [(k, v) for k, v in groups.items() if kname in k[0]]
+            if not cand:
+                continue
+            (name, gx, gy), d = max(cand, key=lambda kv: kv[0][1] * kv[0][2])
+            fv = fetch.get((name, gx * gy)) or fetch.get((name, gx))
+            wv = write.get((name, gx * gy)) or write.get((name, gx))
+            rec = {"kernel": _short(name), "grid": [gx, gy], "dispatches": len(d),
+                   "avg_us": float(np.mean(d) / 1e3),
+                   "chunk_rw_bytes_per_launch": 2 * chunk_bytes}
+            total_us += rec["avg_us"]
+            if fv and wv and f_scale and w_scale:
+                b = (float(np.mean(fv)) * f_scale + float(np.mean(wv)) * w_scale) * 1024
+                rec.update({"fetch_kib": float(np.mean(fv)), "write_kib": float(np.mean(wv)),
+                            "bytes_per_launch": b})
+                tl.append("%d | %s | %d | %.1f | %.1f | %.4g | %.4g | %.4f | %.2f" % (
+                    i, _short(name), len(fv), np.mean(fv), np.mean(wv), b, 2 * chunk_bytes,
+                    b / (2 * chunk_bytes), rec["avg_us"]))
+            passes[str(i)] = rec
+        if total_us:
+            tl.append("# transform of one chunk: %d passes, %.2f us in all; algorithmic bytes "
+                      "(one read + one write of the chunk) %d -> %.1f GB/s, %.3f of 8 TB/s" % (
+                          len(passes), total_us, total_alg, total_alg / total_us / 1e3,
+                          total_alg / total_us / 1e3 / HBM_PEAK_GBS))
+        plans[label] = {"chunk_vectors": chunk, "passes": passes}
     lds_lines = []
     if lds_dir:
         per = {}
@@ -666,9 +727,12 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
             allt = json.load(f)
     except (OSError, ValueError):
         allt = {"workloads": {}}
+    first = plans[_profiled_plans(w)[0][0]]
     allt["workloads"][workload] = {"kernel_source_sha256_16": kernel_source_hash(),
                                    "fetch_scale": f_scale, "write_scale": w_scale,
-                                   "chunk_vectors": chunk, "passes": passes}
+                                   "calibration_copy_bytes": copy_bytes,
+                                   "chunk_vectors": first["chunk_vectors"],
+                                   "passes": first["passes"], "plans": plans}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(allt, f, indent=1, sort_keys=True)
         f.write("\n")
@@ -716,7 +780,10 @@ def main():
     ap.add_argument("--workload", default="n20_b256_f32", choices=sorted(workloads.WORKLOADS),
                     help="the workload of the headline line")
     ap.add_argument("--only", action="store_true",
-                    help="measure the headline workload alone (no other configs, no ablations)")
+                    help="measure the headline workload alone, with each of its configured "
+                    "plans (no other workloads, no ablations)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing of cache-resident workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-ablations", action="store_true",
                     help="skip timing the pages' designs (stage-wise, popcount GEMM, "
@@ -767,6 +834,7 @@ def main():
     todo = [(c, n, s) for c, n, s in CONFIGS if n == head.name and s == "configured"]
     if not todo:
         todo = [(0, head.name, "configured")]
+    todo += [(c, n, s) for c, n, s in CONFIGS if n == head.name and (c, n, s) not in todo]
     if not args.only:
         todo += [(c, n, s) for c, n, s in CONFIGS if (c, n, s) not in todo]
     records, results, headline = [], {}, None
@@ -778,13 +846,15 @@ def main():
         r = gpu_workload(torch, w, args.steps if name == head.name else
                          (max(20, args.steps // 5) if name in LARGE else args.steps),
                          args.warmup, split=split, full=full,
-                         keep_output=not args.no_cpu)
+                         keep_output=not args.no_cpu, graph=not args.no_graph)
         cpu = None
         if not args.no_cpu:
             log("CPU oracle: %s" % name)
             cpu = cpu_leg(w, r["output"], r["inputs"])
         r["output"] = r["inputs"] = None
         rec = config_record(cfg, w, r, cpu, label)
+        rec["gpu_name"] = torch.cuda.get_device_name(0)
+        rec["rocm_version"] = rocm_version()
         if full and r["per_pass_ms"]:
             rec["roofline"] = roofline(w, r, cache_copy)
         records.append(rec)

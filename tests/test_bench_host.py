@@ -84,7 +84,8 @@ def _write_csv(path, rows):
 
 def test_profile_summary_calibrates_on_the_state_copy(tmp_path, monkeypatch, lib):
     """bench.py runs a 64 MiB cache-resident copy before the state-sized
-    one; the counters must be scaled by the state-sized copy."""
+    one; each copy launch of G threads moves G x 128 bytes each way, and
+    the counters are scaled by the largest one."""
     import quantum_state_encoding_amd as qse
     w = workloads.WORKLOADS["n20_b256_f32"]
     plan = qse.Plan(w.n, w.dtype)
@@ -130,3 +131,63 @@ def test_profile_summary_calibrates_on_the_state_copy(tmp_path, monkeypatch, lib
         assert rec["passes"][p]["bytes_per_launch"] == pytest.approx(2 * chunk_kib * 1024)
     text = open(tmp_path / "profiles" / ("%s_traffic.txt" % w.name)).read()
     assert "0.42" in text.splitlines()[-1] or "0.43" in text.splitlines()[-1]
+
+
+def test_profile_summary_of_a_cache_resident_workload_keeps_both_plans(tmp_path, monkeypatch,
+                                                                       lib):
+    """n=14 batch 64 is timed with its configured 7|7 split and with the
+    default one-pass plan: the summary keeps a counter record for each, and
+    each configured record reads its own plan's bytes back per call."""
+    import quantum_state_encoding_amd as qse
+    w = workloads.WORKLOADS["n14_b64_f32"]
+    cfg = qse.Plan(w.n, w.dtype, split=w.split)
+    dflt = qse.Plan(w.n, w.dtype)
+    kernels = {("cfg", i): cfg.kernel_name(i, w.batch) for i in range(cfg.num_passes)}
+    kernels[("dflt", 0)] = dflt.kernel_name(0, w.batch)
+    full = {k: "void qse::(anonymous namespace)::%s(float*, float*, qse::TileArgs)" % v
+            for k, v in kernels.items()}
+    full["copy"] = "stream_copy_kernel(int4*, int4 const*, long)"
+    grid = {("cfg", 0): 65536, ("cfg", 1): 32768, ("dflt", 0): 65536, "copy": 524288}
+    kt = [{"Kernel_Name": full[k], "Grid_Size_X": grid[k], "Grid_Size_Y": 2,
+           "Start_Timestamp": 0, "End_Timestamp": 5000} for k in full for _ in range(3)]
+    _write_csv(str(tmp_path / "kt" / "x_kernel_trace.csv"), kt)
+    half = w.state_bytes / 1024 / 2          # KiB of half the state
+
+    def counters(name, per_kernel, copy):
+        rows = []
+        for k in full:
+            v = copy if k == "copy" else per_kernel[k]
+            g = grid[k] * (1 if k == "copy" else 2)
+            rows += [{"Kernel_Name": full[k], "Grid_Size": g, "Counter_Name": name,
+                      "Counter_Value": v, "Dispatch_Id": str(i)} for i in range(2)]
+        return rows
+    # Synthetic counters: FETCH_SIZE reads half the bytes it stands for (the
+    # copy: 64 MiB / 2), and the passes move different amounts so that the
+    # plans can be told apart.
+    fetch = {("cfg", 0): half / 4 / 2, ("cfg", 1): half / 2, ("dflt", 0): half / 2}
+    write = {("cfg", 0): half, ("cfg", 1): half, ("dflt", 0): half}
+    _write_csv(str(tmp_path / "f" / "x_counter_collection.csv"),
+               counters("FETCH_SIZE", fetch, 64 * 1024 / 2))
+    _write_csv(str(tmp_path / "w" / "x_counter_collection.csv"),
+               counters("WRITE_SIZE", write, 64 * 1024))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "profiles" / "traffic.json"))
+    bench.summarize_profile(w.name, str(tmp_path / "kt"), str(tmp_path / "f"),
+                            str(tmp_path / "w"), "rocprofv3 ...")
+    rec = json.load(open(tmp_path / "profiles" / "traffic.json"))["workloads"][w.name]
+    assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
+    assert rec["calibration_copy_bytes"] == 64 << 20
+    assert set(rec["plans"]) == {"as configured", "default plan"}
+    assert len(rec["plans"]["as configured"]["passes"]) == 2
+    assert len(rec["plans"]["default plan"]["passes"]) == 1
+    monkeypatch.setattr(bench, "traffic_record", lambda name: rec)
+    monkeypatch.setattr(bench, "lds_conflicts", lambda name, kernel: None)
+    S = w.state_bytes
+    c = bench.counter_fields(w, "as configured", {"passes": 2})
+    assert c["fetch_bytes"] == pytest.approx(S / 4 / 2 + S / 2)
+    assert c["write_bytes"] == pytest.approx(2 * S / 2)
+    assert c["measured_over_accounted"] == pytest.approx((S / 8 + S / 2 + S) / (4 * S))
+    d = bench.counter_fields(w, "default plan", {"passes": 1})
+    assert d["fetch_bytes"] == pytest.approx(S / 2) and d["write_bytes"] == pytest.approx(S / 2)
+    assert d["measured_over_accounted"] == pytest.approx(0.5)
+    assert bench.counter_fields(w, "default plan", {"passes": 2}) == {}
