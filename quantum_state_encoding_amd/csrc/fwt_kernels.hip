@@ -421,7 +421,9 @@ __global__ void __launch_bounds__(512)
 // bit with a register bit so the stage becomes a register butterfly (and
 // a second swap restores the layout).  Lanes keep their own half of each
 // pair with y = partner + s * x, s = +1 for the lower index and -1 for the
-// upper: one rounding, exactly the sum or difference.
+// upper: one rounding, exactly the sum or difference.  (fp32 stages on lane
+// bits 0 and 1 keep x + s * partner instead, the difference negated, and
+// the kernel's final multiply removes the sign: fmac_dpp_regs.)
 
 template <int LBIT>
 __device__ __forceinline__ unsigned lane_partner_u32(unsigned v)
@@ -494,12 +496,143 @@ __device__ __forceinline__ void permlane_swap(double& a, double& b)
     b = __longlong_as_double((long long)(((unsigned long long)bhi << 32) | blo));
 }
 
+// fp32 stages on lane bits 0 and 1: one vector-ALU instruction per value,
+// v_fmac_f32 with a quad permutation on its first source, so each lane
+// keeps x + s * partner (s = -1 on the upper lane of each pair).  The
+// upper lane then holds the difference negated.  The negation is exact and
+// carries through every later stage unchanged (a stage's two operands come
+// from lanes with equal bits 0 and 1, so they carry the same sign), and
+// the kernel removes it with its final multiply (dpp_sign_lanes).  Each
+// asm block begins with five wait states: a DPP read of a VGPR needs two
+// after a vector-ALU write of it, and a DPP instruction five after a write
+// of EXEC; the compiler cannot see the DPP inside the block.
+#define QSE_FMAC_DPP(Q, R, S) "v_fmac_f32_dpp %" #R ", %" #R ", %" #S " quad_perm:" Q \
+                              " row_mask:0xf bank_mask:0xf\n\t"
+#define QSE_FMAC_DPP8(Q) "s_nop 4\n\t" \
+    QSE_FMAC_DPP(Q, 0, 8) \
+    QSE_FMAC_DPP(Q, 1, 8) \
+    QSE_FMAC_DPP(Q, 2, 8) \
+    QSE_FMAC_DPP(Q, 3, 8) \
+    QSE_FMAC_DPP(Q, 4, 8) \
+    QSE_FMAC_DPP(Q, 5, 8) \
+    QSE_FMAC_DPP(Q, 6, 8) \
+    QSE_FMAC_DPP(Q, 7, 8)
+#define QSE_FMAC_DPP16(Q) "s_nop 4\n\t" \
+    QSE_FMAC_DPP(Q, 0, 16) \
+    QSE_FMAC_DPP(Q, 1, 16) \
+    QSE_FMAC_DPP(Q, 2, 16) \
+    QSE_FMAC_DPP(Q, 3, 16) \
+    QSE_FMAC_DPP(Q, 4, 16) \
+    QSE_FMAC_DPP(Q, 5, 16) \
+    QSE_FMAC_DPP(Q, 6, 16) \
+    QSE_FMAC_DPP(Q, 7, 16) \
+    QSE_FMAC_DPP(Q, 8, 16) \
+    QSE_FMAC_DPP(Q, 9, 16) \
+    QSE_FMAC_DPP(Q, 10, 16) \
+    QSE_FMAC_DPP(Q, 11, 16) \
+    QSE_FMAC_DPP(Q, 12, 16) \
+    QSE_FMAC_DPP(Q, 13, 16) \
+    QSE_FMAC_DPP(Q, 14, 16) \
+    QSE_FMAC_DPP(Q, 15, 16)
+#define QSE_FMAC_DPP32(Q) "s_nop 4\n\t" \
+    QSE_FMAC_DPP(Q, 0, 32) \
+    QSE_FMAC_DPP(Q, 1, 32) \
+    QSE_FMAC_DPP(Q, 2, 32) \
+    QSE_FMAC_DPP(Q, 3, 32) \
+    QSE_FMAC_DPP(Q, 4, 32) \
+    QSE_FMAC_DPP(Q, 5, 32) \
+    QSE_FMAC_DPP(Q, 6, 32) \
+    QSE_FMAC_DPP(Q, 7, 32) \
+    QSE_FMAC_DPP(Q, 8, 32) \
+    QSE_FMAC_DPP(Q, 9, 32) \
+    QSE_FMAC_DPP(Q, 10, 32) \
+    QSE_FMAC_DPP(Q, 11, 32) \
+    QSE_FMAC_DPP(Q, 12, 32) \
+    QSE_FMAC_DPP(Q, 13, 32) \
+    QSE_FMAC_DPP(Q, 14, 32) \
+    QSE_FMAC_DPP(Q, 15, 32) \
+    QSE_FMAC_DPP(Q, 16, 32) \
+    QSE_FMAC_DPP(Q, 17, 32) \
+    QSE_FMAC_DPP(Q, 18, 32) \
+    QSE_FMAC_DPP(Q, 19, 32) \
+    QSE_FMAC_DPP(Q, 20, 32) \
+    QSE_FMAC_DPP(Q, 21, 32) \
+    QSE_FMAC_DPP(Q, 22, 32) \
+    QSE_FMAC_DPP(Q, 23, 32) \
+    QSE_FMAC_DPP(Q, 24, 32) \
+    QSE_FMAC_DPP(Q, 25, 32) \
+    QSE_FMAC_DPP(Q, 26, 32) \
+    QSE_FMAC_DPP(Q, 27, 32) \
+    QSE_FMAC_DPP(Q, 28, 32) \
+    QSE_FMAC_DPP(Q, 29, 32) \
+    QSE_FMAC_DPP(Q, 30, 32) \
+    QSE_FMAC_DPP(Q, 31, 32)
+
+// One stage on lane bit LBIT over the NR = 2, 4 or 8 fp32 registers at x.
+template <int LBIT, int NR>
+__device__ __forceinline__ void fmac_dpp_regs(Vec<float>::type* x, float s)
+{
+    static_assert(LBIT == 0 || LBIT == 1, "quad permutations pair lane bits 0 and 1");
+    static_assert(NR == 2 || NR == 4 || NR == 8, "blocks of 2, 4 or 8 registers");
+    float v[4 * NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            v[4 * j + c] = x[j][c];
+    if constexpr (NR == 2 && LBIT == 0)
+        asm(QSE_FMAC_DPP8("[1,0,3,2]")
+            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+            : "v"(s));
+    if constexpr (NR == 2 && LBIT == 1)
+        asm(QSE_FMAC_DPP8("[2,3,0,1]")
+            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+            : "v"(s));
+    if constexpr (NR == 4 && LBIT == 0)
+        asm(QSE_FMAC_DPP16("[1,0,3,2]")
+            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+            : "v"(s));
+    if constexpr (NR == 4 && LBIT == 1)
+        asm(QSE_FMAC_DPP16("[2,3,0,1]")
+            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+            : "v"(s));
+    if constexpr (NR == 8 && LBIT == 0)
+        asm(QSE_FMAC_DPP32("[1,0,3,2]")
+            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]), "+v"(v[16]), "+v"(v[17]), "+v"(v[18]), "+v"(v[19]), "+v"(v[20]), "+v"(v[21]), "+v"(v[22]), "+v"(v[23]), "+v"(v[24]), "+v"(v[25]), "+v"(v[26]), "+v"(v[27]), "+v"(v[28]), "+v"(v[29]), "+v"(v[30]), "+v"(v[31])
+            : "v"(s));
+    if constexpr (NR == 8 && LBIT == 1)
+        asm(QSE_FMAC_DPP32("[2,3,0,1]")
+            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]), "+v"(v[16]), "+v"(v[17]), "+v"(v[18]), "+v"(v[19]), "+v"(v[20]), "+v"(v[21]), "+v"(v[22]), "+v"(v[23]), "+v"(v[24]), "+v"(v[25]), "+v"(v[26]), "+v"(v[27]), "+v"(v[28]), "+v"(v[29]), "+v"(v[30]), "+v"(v[31])
+            : "v"(s));
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+        x[j] = Vec<float>::type{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+}
+#undef QSE_FMAC_DPP32
+#undef QSE_FMAC_DPP16
+#undef QSE_FMAC_DPP8
+#undef QSE_FMAC_DPP
+
+// Lane bits among 0 and 1 whose fp32 stages leave a sign (those in
+// [gb, gb + lb), the lane row bits of a tile); a lane's outputs carry
+// (-1)^popcount(lane & mask).
+__host__ __device__ constexpr unsigned dpp_sign_lanes(int gb, int lb)
+{
+    return (gb <= 0 && lb > 0 ? 1u : 0u) | (gb <= 1 && gb + lb > 1 ? 2u : 0u);
+}
+
 // Stage on lane bit LBIT for all E registers.
 template <int LBIT, int E, typename V, typename T>
 __device__ __forceinline__ void lane_stage(V* x, int lane)
 {
     constexpr int W = sizeof(V) / sizeof(T);
-    if constexpr (LBIT < 4) {
+    if constexpr (LBIT < 2 && sizeof(T) == 4 && E >= 2) {
+        const float s = ((lane >> LBIT) & 1) ? -1.f : 1.f;
+        constexpr int NR = E < 8 ? E : 8;
+#pragma unroll
+        for (int j = 0; j < E; j += NR)
+            fmac_dpp_regs<LBIT, NR>(x + j, s);
+    } else if constexpr (LBIT < 4) {
         const T s = ((lane >> LBIT) & 1) ? T(-1) : T(1);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -622,8 +755,12 @@ __global__ void __launch_bounds__(256)
     }
     register_stages<EB, E>(x);
     LaneStages<0, LB, GB, E, V, T>::run(x, lane);
-    if (a.do_scale) {
-        const T c = (T)a.scale;
+    // The scale, times the sign the fp32 stages on lane bits 0 and 1 leave.
+    constexpr unsigned SM = (sizeof(T) == 4 && E >= 2) ? dpp_sign_lanes(GB, LB) : 0u;
+    if (SM || a.do_scale) {
+        T c = a.do_scale ? (T)a.scale : T(1);
+        if (SM && (__popc((unsigned)lane & SM) & 1))
+            c = -c;
 #pragma unroll
         for (int j = 0; j < E; ++j)
             x[j] *= c;
@@ -860,8 +997,13 @@ __device__ __forceinline__ void lx_process(typename S::V* x, typename S::V* L, i
     else
         LaneStages<0, S::LR, S::GB, S::E, V, T>::run(x, lane);
     LxRounds<V, S::KR, S::GB, S::W, S::EB, S::PHB, 0, S::NX, RL>::run(x, L, lane_row, g, wave);
-    if (do_scale) {
-        const T c = (T)scale;
+    // The scale, times the sign the fp32 stages on lane bits 0 and 1 leave
+    // (lanes keep their lane bits through the exchanges).
+    constexpr unsigned SM = sizeof(T) == 4 ? dpp_sign_lanes(S::GB, S::LR) : 0u;
+    if (SM || do_scale) {
+        T c = do_scale ? (T)scale : T(1);
+        if (SM && (__popc((unsigned)lane & SM) & 1))
+            c = -c;
 #pragma unroll
         for (int j = 0; j < S::E; ++j)
             x[j] *= c;
