@@ -52,6 +52,15 @@ struct Vec<double> {
     static constexpr int WB = 1;
 };
 
+__device__ __forceinline__ float fma_sign(float x, float s, float p)
+{
+    return __builtin_fmaf(x, s, p);
+}
+__device__ __forceinline__ double fma_sign(double x, double s, double p)
+{
+    return __builtin_fma(x, s, p);
+}
+
 template <typename V>
 __device__ __forceinline__ void butterfly(V& a, V& b)
 {
@@ -59,6 +68,23 @@ __device__ __forceinline__ void butterfly(V& a, V& b)
     const V d = a - b;
     a = s;
     b = d;
+}
+
+// The butterfly times c: (c (a + b), c (a - b)) as t = c b, fma(a, c, +-t):
+// three operations for two outputs instead of four.  When c is a power of
+// two (or +-1), c b is exact and the results equal, bit for bit, the
+// butterfly followed by the multiply.
+template <typename V, typename T>
+__device__ __forceinline__ void butterfly_scaled(V& a, V& b, T c)
+{
+    constexpr int W = sizeof(V) / sizeof(T);
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const T t = b[k] * c;
+        const T u = a[k];
+        a[k] = fma_sign(u, c, t);
+        b[k] = fma_sign(u, c, -t);
+    }
 }
 
 // Stages on the vb index bits inside one vector (row passes only).
@@ -423,7 +449,7 @@ __global__ void __launch_bounds__(512)
 // pair with y = partner + s * x, s = +1 for the lower index and -1 for the
 // upper: one rounding, exactly the sum or difference.  (fp32 stages on lane
 // bits 0 and 1 keep x + s * partner instead, the difference negated, and
-// the kernel's final multiply removes the sign: fmac_dpp_regs.)
+// the kernel's final scaling removes the sign: fmac_dpp_regs.)
 
 template <int LBIT>
 __device__ __forceinline__ unsigned lane_partner_u32(unsigned v)
@@ -450,15 +476,6 @@ __device__ __forceinline__ double lane_partner(double v)
     const unsigned lo = lane_partner_u32<LBIT>((unsigned)u);
     const unsigned hi = lane_partner_u32<LBIT>((unsigned)(u >> 32));
     return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-
-__device__ __forceinline__ float fma_sign(float x, float s, float p)
-{
-    return __builtin_fmaf(x, s, p);
-}
-__device__ __forceinline__ double fma_sign(double x, double s, double p)
-{
-    return __builtin_fma(x, s, p);
 }
 
 // Swap lane bit 4 (LBIT = 4) or 5 with the register pair (a, b).
@@ -502,7 +519,7 @@ __device__ __forceinline__ void permlane_swap(double& a, double& b)
 // upper lane then holds the difference negated.  The negation is exact and
 // carries through every later stage unchanged (a stage's two operands come
 // from lanes with equal bits 0 and 1, so they carry the same sign), and
-// the kernel removes it with its final multiply (dpp_sign_lanes).  Each
+// the kernel removes it with its final scaling (dpp_sign_lanes).  Each
 // asm block begins with five wait states: a DPP read of a VGPR needs two
 // after a vector-ALU write of it, and a DPP instruction five after a write
 // of EXEC; the compiler cannot see the DPP inside the block.
@@ -864,6 +881,8 @@ __device__ __forceinline__ uint32_t lx_thread_row_rl(int lane_row, int wave)
 // bits through LDS, then their stages.  RL: the data arrive in the
 // relabelled load layout of lane_stage_nr, which the first exchange's
 // writes undo (its reads, and everything after, use the plain layouts).
+// The stage on the top register bit the last exchange moves is left to the
+// caller (lx_last_bit), which fuses it with the scale.
 template <typename V, int KR, int GB, int W, int EB, int PHB, int X, int NX, bool RL>
 struct LxRounds {
     __device__ __forceinline__ static void run(V* x, V* L, int lane_row, int g, int wave)
@@ -893,7 +912,7 @@ struct LxRounds {
             for (int j = ph * EP; j < (ph + 1) * EP; ++j)
                 x[j] = L[(to + (lx_reg_row<W, EB, LR, X + 1>(j) << GB)) & MASK];
         }
-        register_stages<C, E>(x);
+        register_stages<X + 1 == NX ? C - 1 : C, E>(x);
         LxRounds<V, KR, GB, W, EB, PHB, X + 1, NX, RL>::run(x, L, lane_row, g, wave);
     }
 };
@@ -913,6 +932,8 @@ struct LxShape {
     static constexpr int E = 1 << EB;
     static constexpr int LR = 6 - GB;              // row bits held by lanes
     static constexpr int NX = (W + EB - 1) / EB;   // exchanges
+    // register bit of the last stage, the top one the last exchange moves
+    static constexpr int LAST = (W - (NX - 1) * EB < EB ? W - (NX - 1) * EB : EB) - 1;
     static constexpr bool SPLIT = W < EB;          // top row bit stays a register bit
     static_assert(KR == EB + LR + W && EB >= 1 && W >= 1 && W <= 4, "lane-exchange tile");
     static_assert(!ROW || GB == 0, "row passes have one column group");
@@ -997,16 +1018,34 @@ __device__ __forceinline__ void lx_process(typename S::V* x, typename S::V* L, i
     else
         LaneStages<0, S::LR, S::GB, S::E, V, T>::run(x, lane);
     LxRounds<V, S::KR, S::GB, S::W, S::EB, S::PHB, 0, S::NX, RL>::run(x, L, lane_row, g, wave);
-    // The scale, times the sign the fp32 stages on lane bits 0 and 1 leave
-    // (lanes keep their lane bits through the exchanges).
+    // The last stage.  Where the fp32 stages on lane bits 0 and 1 leave a
+    // sign (lanes keep their lane bits through the exchanges), it is fused
+    // with the scale times that sign: for a scale that is a power of two
+    // (even n) or +-1 the fused form gives the same bits as the butterfly
+    // and then the multiply; for odd n it rounds c b first, within one unit
+    // of the other order.  Elsewhere the multiply follows the butterfly (a
+    // fused form behind a run-time branch costs these kernels 30 VGPRs).
     constexpr unsigned SM = sizeof(T) == 4 ? dpp_sign_lanes(S::GB, S::LR) : 0u;
-    if (SM || do_scale) {
+    constexpr int LB = 1 << S::LAST;
+    if constexpr (SM != 0) {
         T c = do_scale ? (T)scale : T(1);
-        if (SM && (__popc((unsigned)lane & SM) & 1))
+        if (__popc((unsigned)lane & SM) & 1)
             c = -c;
 #pragma unroll
         for (int j = 0; j < S::E; ++j)
-            x[j] *= c;
+            if (!(j & LB))
+                butterfly_scaled(x[j], x[j | LB], c);
+    } else {
+#pragma unroll
+        for (int j = 0; j < S::E; ++j)
+            if (!(j & LB))
+                butterfly(x[j], x[j | LB]);
+        if (do_scale) {
+            const T c = (T)scale;
+#pragma unroll
+            for (int j = 0; j < S::E; ++j)
+                x[j] *= c;
+        }
     }
 }
 
