@@ -739,6 +739,37 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
     print("\n".join(lines + [""] + tl + [""] + lds_lines))
 
 
+def summarize_counters(workload, counter_dir, command, tag):
+    """Per-kernel averages per dispatch of every counter in a rocprofv3
+    --pmc run of this benchmark into profiles/<workload>_<tag>.txt (the
+    workload's own pass kernels and the streaming copy)."""
+    import quantum_state_encoding_amd as qse
+    w = workloads.WORKLOADS[workload]
+    mine = ["stream_copy_kernel"]
+    for _, sp in _profiled_plans(w):
+        plan = qse.Plan(w.n, w.dtype, split=sp)
+        mine += [plan.kernel_name(i, w.batch) for i in range(plan.num_passes)]
+    per = {}
+    for r in _read_csv(_find(counter_dir, "counter_collection.csv")):
+        if not any(m in r["Kernel_Name"] for m in mine):
+            continue
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+        per.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
+    names = sorted({c for cs in per.values() for c in cs})
+    lines = ["# rocprofv3 counters: %s (average per dispatch)" % workload,
+             "# command: " + command,
+             "# kernel | grid | dispatches | " + " | ".join(names)]
+    for (name, grid), cs in sorted(per.items(), key=lambda kv: kv[0]):
+        lines.append("%s | %d | %d | %s" % (name, grid, max(len(v) for v in cs.values()),
+                                            " | ".join("%.4g" % np.mean(cs[c]) if c in cs else "-"
+                                                       for c in names)))
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "%s_%s.txt" % (workload, tag)), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_ablations(workload, kt_dir, command):
     """Per-kernel durations of everything in the trace that is neither a pass
     of the workload's default or configured plan nor the streaming copy
@@ -796,6 +827,9 @@ def main():
     ap.add_argument("--summarize-ablations", metavar="KT_DIR",
                     help="write profiles/<workload>_ablations_kernel_trace.txt from a rocprofv3 "
                     "kernel trace of this benchmark")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("DIR", "TAG"),
+                    help="write profiles/<workload>_<TAG>.txt: per-kernel averages of the "
+                    "counters of a rocprofv3 --pmc run of this benchmark")
     ap.add_argument("--profile-command", default="",
                     help="the rocprofv3 command line recorded in the summaries")
     args = ap.parse_args()
@@ -805,6 +839,10 @@ def main():
             ap.error("--summarize-profile takes 3 or 4 directories")
         summarize_profile(args.workload, d[0], d[1], d[2], args.profile_command,
                           d[3] if len(d) == 4 else None)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.workload, args.summarize_counters[0], args.profile_command,
+                           args.summarize_counters[1])
         return
     if args.summarize_ablations:
         summarize_ablations(args.workload, args.summarize_ablations, args.profile_command)
