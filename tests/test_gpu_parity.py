@@ -209,6 +209,21 @@ def test_integer_lane_exchange_kernels(dtype, n, split, eb, wave, batch):
         assert_exact(gim, im, n, True)
 
 
+@pytest.mark.parametrize("dtype,n,split,eb,wave,batch",
+                         [c for c in LX_CASES if c[1] % 2 == 1])
+def test_gaussian_lane_exchange_kernels_odd_n(dtype, n, split, eb, wave, batch):
+    """The lane-exchange kernels at odd n, normalised: the scale is not a
+    power of two there, and fp32 row tiles fuse it with their last
+    butterfly (a different rounding from a separate multiply), so these
+    are compared within the tolerance, on Gaussian states."""
+    say("lx gauss %s n=%d split=%s eb=%s wave=%s batch=%d" % (dtype, n, split, eb, wave, batch))
+    plan = qse.Plan(n, dtype, split=split, eb=eb, wave=wave)
+    w = workloads.custom(n, batch, dtype, "gauss", True, seed=91_000 + n)
+    re, im = workloads.gen(w)
+    gre, gim = run(plan, re, im, True)
+    assert_close(dtype, n, re, im, gre, gim)
+
+
 @pytest.mark.parametrize("dtype,n,split,eb,batch", LX_PHASE_CASES)
 def test_integer_lane_exchange_phases(dtype, n, split, eb, batch):
     """The lane-exchange kernel with its exchange in two phases through
