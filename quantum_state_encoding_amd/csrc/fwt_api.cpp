@@ -46,6 +46,9 @@ constexpr int kColTwoPassMax = 11;     // widest column factor of a default two-
 constexpr size_t kLdsMax = 160 * 1024; // per workgroup on gfx950
 constexpr size_t kPhaseLdsTarget = 68 * 1024;  // two tiles per CU
 constexpr size_t kChunkBytes = (size_t)256 << 20;  // Infinity Cache capacity
+// States up to this size get XCD-affine workgroup placement: at most
+// 2 MiB of each XCD's 4 MB L2.
+constexpr size_t kXcdAffineBytes = (size_t)16 << 20;
 constexpr int kTargetThreads = 256;    // workgroup size aimed for when packing tiles
 
 struct Pass {
@@ -851,6 +854,15 @@ int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, vo
             const int64_t per_cu = p.lds ? (int64_t)(kLdsMax / p.lds) : 1;
             const int64_t total = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
             a.grid = total / ncomp > 0 ? total / ncomp : 1;
+            // States that fit the L2s: each vector component's workgroups
+            // on one XCD, the same in every pass and call (xcd_group).
+            const int kb = p.tiles_bits - p.tpw_bits;   // log2 workgroups per component
+            a.xcd_bits = -1;
+            if (!p.key.pipe && sub_bits == 0 && kb >= 1 && kb < 30 &&
+                (size_t)batch * ((size_t)1 << n) * (plan->dtype == FWT_F64 ? 8 : 4) *
+                        (size_t)ncomp <= kXcdAffineBytes &&
+                a.wg_count % ((int64_t)8 << kb) == 0 && a.wg_count <= ((int64_t)1 << 30))
+                a.xcd_bits = kb;
             e = qse::launch_tile_pass(p.key, re, im, ncomp, a, p.block, p.lds, stream,
                                       i == first ? start : nullptr,
                                       i == last - 1 ? stop : nullptr);

@@ -23,6 +23,8 @@ struct TileArgs {
     int nblk_bits;       // log2 of column blocks per outer index (col passes)
     int tpw_bits;        // log2 of tiles per workgroup
     int tt_bits;         // log2 of threads per tile
+    int xcd_bits;        // >= 0: the 2^xcd_bits workgroups of each vector
+                         // component share an XCD (xcd_group); -1: launch order
     int do_scale;        // multiply by `scale` before the final store
     int ld_nt;           // nontemporal loads (input not reused by this call)
     int st_nt;           // nontemporal stores (output not reused by this call)
@@ -62,6 +64,20 @@ __host__ __device__ constexpr bool store_back(int kr, int eb, int gb)
                128 &&
            (16 << (gb + kr - eb)) >
                (16 << (gb + (kr - eb * rounds_of(kr, eb) > 0 ? kr - eb * rounds_of(kr, eb) : 0)));
+}
+
+// The tile group of workgroup w of a launch.  The dispatcher hands
+// consecutive workgroups to the eight XCDs in turn (workgroup w on XCD
+// w mod 8).  With xb >= 0 the 2^xb workgroups of vector component v are
+// the ones with w mod 8 = v mod 8, so every pass of a call, and every call,
+// runs v on the same XCD and finds in its L2 what the previous launch wrote
+// there.  A bijection of [0, wg_count) when wg_count is a multiple of
+// 2^(xb + 3); xb < 0 keeps the launch order.
+__host__ __device__ constexpr int64_t xcd_group(int64_t w, int xb)
+{
+    return xb < 0 ? w
+                  : ((((w & 7) + (((w >> 3) >> xb) << 3)) << xb) |
+                     ((w >> 3) & (((int64_t)1 << xb) - 1)));
 }
 
 // True if the variant is compiled into this library.

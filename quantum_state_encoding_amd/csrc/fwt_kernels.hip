@@ -382,7 +382,8 @@ __global__ void __launch_bounds__(EB >= 5 ? 512 : 1024)
     const int tau = tt >> GB;                         // row-thread index
     V* const L = reinterpret_cast<V*>(lds_raw) + tl * S::TILE_LDS;
 
-    const TileAddr ta = tile_addr<S>(blockIdx.y ? im : re, a, blockIdx.x, tl, g);
+    const TileAddr ta =
+        tile_addr<S>(blockIdx.y ? im : re, a, xcd_group(blockIdx.x, a.xcd_bits), tl, g);
     V x[S::E];
     load_tile<S>(x, ta, tau, a.ld_nt);
     process_tile<S>(x, L, tau, g, a.do_scale, a.scale);
@@ -749,7 +750,8 @@ __global__ void __launch_bounds__(256)
     const int rl = (lane >> GB) & ((1 << LB) - 1);
     const int tl = (wave << SUB) | (lane >> (GB + LB));
 
-    const TileAddr ta = tile_addr<S>(blockIdx.y ? im : re, a, blockIdx.x, tl, g);
+    const TileAddr ta =
+        tile_addr<S>(blockIdx.y ? im : re, a, xcd_group(blockIdx.x, a.xcd_bits), tl, g);
     const GlobalLayout<LB, EB> gl(ta.lane_bytes, rl, ta.row_bytes);
     V x[E];
     if (ta.active && a.ld_nt) {
@@ -1076,7 +1078,7 @@ __global__ void __launch_bounds__(64 << W)
     using V = typename S::V;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     V* const L = reinterpret_cast<V*>(lds_raw);
-    const int64_t t = a.tile0 + blockIdx.x;
+    const int64_t t = a.tile0 + xcd_group(blockIdx.x, a.xcd_bits);
     if (t >= a.tiles)
         return;   // uniform across the workgroup
     const int lane = threadIdx.x & 63;

@@ -12,7 +12,10 @@
 //  * scale only in the last pass, and use nontemporal loads only in the
 //    first pass and nontemporal stores only in the last one of a
 //    multi-pass plan;
-//  * put re and im at the same offset of their buffers.
+//  * put re and im at the same offset of their buffers;
+//  * place workgroups by XCD only on states that fit the L2s, through a
+//    permutation of the launch's workgroups that keeps every vector
+//    component on one XCD.
 // Nothing is dereferenced: the buffers are address ranges only.
 #include <hip/hip_runtime_api.h>
 
@@ -85,6 +88,7 @@ hipError_t record(const qse::KernelKey& key, void* re, void* im, int ncomp,
 
 int g_bad = 0;
 int g_vector_chunked = 0, g_block_chunked = 0;   // cases of each schedule kind
+int g_xcd_launches = 0;                           // launches with XCD-affine placement
 #define EXPECT(c, ...)                                                           \
     do {                                                                         \
         if (!(c)) {                                                              \
@@ -188,6 +192,32 @@ void check_case(fwt_plan_t plan, int n, fwt_dtype dt, int64_t batch, bool with_i
         EXPECT(L.a.tile0 == 0 && L.a.tiles > 0, "tiles");
         EXPECT(L.a.wg_count == (L.a.tiles + ((int64_t)1 << L.a.tpw_bits) - 1) >> L.a.tpw_bits,
                "workgroups");
+        // XCD-affine placement: only on states that fit the L2s, with whole
+        // vector components per workgroup group, and a permutation of the
+        // launch's workgroups that keeps each component on one XCD.
+        if (L.a.xcd_bits >= 0) {
+            ++g_xcd_launches;
+            const int xb = L.a.xcd_bits;
+            EXPECT(bytes * (with_im ? 2 : 1) <= ((size_t)16 << 20), "xcd placement on %zu B",
+                   bytes * (with_im ? 2 : 1));
+            EXPECT(!L.key.pipe && xb < 30 && L.a.wg_count % ((int64_t)8 << xb) == 0 &&
+                       ((L.a.tiles >> L.a.tpw_bits) << L.a.tpw_bits) == L.a.tiles,
+                   "xcd placement shape");
+            if (L.a.wg_count % ((int64_t)8 << xb) == 0 && L.a.wg_count <= ((int64_t)1 << 22)) {
+                const int64_t tpv = total[i] / batch;   // tiles per vector component
+                std::vector<char> seen((size_t)L.a.wg_count, 0);
+                for (int64_t w = 0; w < L.a.wg_count; ++w) {
+                    const int64_t g = qse::xcd_group(w, xb);
+                    EXPECT(g >= 0 && g < L.a.wg_count && !seen[(size_t)g], "xcd map w=%lld",
+                           (long long)w);
+                    if (g >= 0 && g < L.a.wg_count)
+                        seen[(size_t)g] = 1;
+                    const int64_t v = (g << L.a.tpw_bits) / tpv;   // its vector component
+                    EXPECT(w % 8 == v % 8, "xcd map: w=%lld holds component %lld", (long long)w,
+                           (long long)v);
+                }
+            }
+        }
         // the chunk this launch may touch
         int64_t lo_e = 0, hi_e = batch * N;
         if (i < chunked) {
@@ -251,8 +281,9 @@ int main()
                 if (rc != FWT_OK)
                     continue;   // a split outside the per-pass limits
                 const size_t vec = ((size_t)1 << n) * esize * 2;
-                // small, ragged, and past the cache (when the tile count stays small)
-                std::vector<int64_t> batches = {1, 3};
+                // small, ragged, a multiple of the 8 XCDs, and past the cache
+                // (when the tile count stays small)
+                std::vector<int64_t> batches = {1, 3, 8};
                 const int64_t big = (int64_t)(2 * cache / vec) + 3;
                 if (big > 3 && big <= ((int64_t)1 << 12))
                     batches.push_back(big);
@@ -270,7 +301,9 @@ int main()
     // both kinds of chunking must have been exercised
     EXPECT(g_vector_chunked >= 10 && g_block_chunked >= 10, "chunked cases: %d by vectors, %d by "
            "blocks", g_vector_chunked, g_block_chunked);
-    std::printf("schedule driver: %d cases (%d chunked by vectors, %d by blocks), %d failures%s\n",
-                cases, g_vector_chunked, g_block_chunked, g_bad, g_bad ? "" : " ok");
+    EXPECT(g_xcd_launches >= 10, "XCD-affine launches: %d", g_xcd_launches);
+    std::printf("schedule driver: %d cases (%d chunked by vectors, %d by blocks, %d launches "
+                "placed by XCD), %d failures%s\n", cases, g_vector_chunked, g_block_chunked,
+                g_xcd_launches, g_bad, g_bad ? "" : " ok");
     return g_bad ? 1 : 0;
 }

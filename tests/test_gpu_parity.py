@@ -224,6 +224,33 @@ def test_gaussian_lane_exchange_kernels_odd_n(dtype, n, split, eb, wave, batch):
     assert_close(dtype, n, re, im, gre, gim)
 
 
+# (dtype, n, split, batch, wave): multi-pass plans on states of at most
+# 16 MiB with a multiple of 8 vectors, whose launches place each vector
+# component's workgroups on one XCD, in each kernel family
+XCD_CASES = [("f32", 14, (7, 7), 64, None), ("f32", 14, (7, 7), 8, (1, 1)),
+             ("f32", 14, (7, 7), 16, (0, 0)), ("f32", 12, (6, 6), 64, None),
+             ("f32", 16, (9, 7), 16, None), ("f32", 18, (11, 7), 8, None),
+             ("f32", 15, (5, 5, 5), 64, None), ("f32", 16, (10, 6), 24, None),
+             ("f64", 14, (7, 7), 32, None), ("f64", 16, (8, 8), 8, None),
+             ("f64", 13, (7, 6), 64, (1, 1))]
+
+
+@pytest.mark.parametrize("dtype,n,split,batch,wave", XCD_CASES)
+def test_integer_xcd_placed_passes(dtype, n, split, batch, wave):
+    """Small multi-pass states, where each pass runs every vector
+    component's workgroups on one XCD (a permutation of the launch's
+    workgroups): exact against the oracle, unnormalised and normalised."""
+    say("xcd %s n=%d split=%s batch=%d wave=%s" % (dtype, n, split, batch, wave))
+    npd = np.float32 if dtype == "f32" else np.float64
+    plan = qse.Plan(n, dtype, split=split, wave=wave) if wave else qse.Plan(n, dtype, split=split)
+    re = ints((batch, 1 << n), 93_000 + n, npd)
+    im = ints((batch, 1 << n), 94_000 + n, npd)
+    for normalize in ((False, True) if n % 2 == 0 else (False,)):
+        gre, gim = run(plan, re, im, normalize)
+        assert_exact(gre, re, n, normalize)
+        assert_exact(gim, im, n, normalize)
+
+
 @pytest.mark.parametrize("dtype,n,split,eb,batch", LX_PHASE_CASES)
 def test_integer_lane_exchange_phases(dtype, n, split, eb, batch):
     """The lane-exchange kernel with its exchange in two phases through
