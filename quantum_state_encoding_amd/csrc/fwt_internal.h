@@ -66,18 +66,20 @@ __host__ __device__ constexpr bool store_back(int kr, int eb, int gb)
                (16 << (gb + (kr - eb * rounds_of(kr, eb) > 0 ? kr - eb * rounds_of(kr, eb) : 0)));
 }
 
-// The tile group of workgroup w of a launch.  The dispatcher hands
-// consecutive workgroups to the eight XCDs in turn (workgroup w on XCD
-// w mod 8).  With xb >= 0 the 2^xb workgroups of vector component v are
-// the ones with w mod 8 = v mod 8, so every pass of a call, and every call,
-// runs v on the same XCD and finds in its L2 what the previous launch wrote
-// there.  A bijection of [0, wg_count) when wg_count is a multiple of
-// 2^(xb + 3); xb < 0 keeps the launch order.
-__host__ __device__ constexpr int64_t xcd_group(int64_t w, int xb)
+// The tile group of workgroup w of a launch of wg workgroups.  The
+// dispatcher hands consecutive workgroups to the eight XCDs in turn
+// (workgroup w on XCD w mod 8).  With xb >= 0 the 2^xb workgroups of
+// vector component v are the ones with w mod 8 = v mod 8, so every pass of
+// a call, and every call, runs v on the same XCD and finds in its L2 what
+// the previous launch wrote there.  That covers the largest multiple of
+// 2^(xb + 3) workgroups; the rest keep the launch order.  A bijection of
+// [0, wg); xb < 0 keeps the launch order throughout.
+__host__ __device__ constexpr int64_t xcd_group(int64_t w, int xb, int64_t wg)
 {
-    return xb < 0 ? w
-                  : ((((w & 7) + (((w >> 3) >> xb) << 3)) << xb) |
-                     ((w >> 3) & (((int64_t)1 << xb) - 1)));
+    return (xb < 0 || w >= (wg & ~(((int64_t)8 << xb) - 1)))
+               ? w
+               : ((((w & 7) + (((w >> 3) >> xb) << 3)) << xb) |
+                  ((w >> 3) & (((int64_t)1 << xb) - 1)));
 }
 
 // True if the variant is compiled into this library.

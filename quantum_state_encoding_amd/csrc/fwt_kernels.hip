@@ -383,7 +383,8 @@ __global__ void __launch_bounds__(EB >= 5 ? 512 : 1024)
     V* const L = reinterpret_cast<V*>(lds_raw) + tl * S::TILE_LDS;
 
     const TileAddr ta =
-        tile_addr<S>(blockIdx.y ? im : re, a, xcd_group(blockIdx.x, a.xcd_bits), tl, g);
+        tile_addr<S>(blockIdx.y ? im : re, a, xcd_group(blockIdx.x, a.xcd_bits, a.wg_count), tl,
+                     g);
     V x[S::E];
     load_tile<S>(x, ta, tau, a.ld_nt);
     process_tile<S>(x, L, tau, g, a.do_scale, a.scale);
@@ -751,7 +752,8 @@ __global__ void __launch_bounds__(256)
     const int tl = (wave << SUB) | (lane >> (GB + LB));
 
     const TileAddr ta =
-        tile_addr<S>(blockIdx.y ? im : re, a, xcd_group(blockIdx.x, a.xcd_bits), tl, g);
+        tile_addr<S>(blockIdx.y ? im : re, a, xcd_group(blockIdx.x, a.xcd_bits, a.wg_count), tl,
+                     g);
     const GlobalLayout<LB, EB> gl(ta.lane_bytes, rl, ta.row_bytes);
     V x[E];
     if (ta.active && a.ld_nt) {
@@ -1078,7 +1080,7 @@ __global__ void __launch_bounds__(64 << W)
     using V = typename S::V;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     V* const L = reinterpret_cast<V*>(lds_raw);
-    const int64_t t = a.tile0 + xcd_group(blockIdx.x, a.xcd_bits);
+    const int64_t t = a.tile0 + xcd_group(blockIdx.x, a.xcd_bits, a.wg_count);
     if (t >= a.tiles)
         return;   // uniform across the workgroup
     const int lane = threadIdx.x & 63;

@@ -13,9 +13,9 @@
 //    first pass and nontemporal stores only in the last one of a
 //    multi-pass plan;
 //  * put re and im at the same offset of their buffers;
-//  * place workgroups by XCD only on states that fit the L2s, through a
-//    permutation of the launch's workgroups that keeps every vector
-//    component on one XCD.
+//  * place workgroups by XCD only on launches over less than the 256 MiB
+//    Infinity Cache, through a permutation of the launch's workgroups
+//    that keeps every vector component on one XCD.
 // Nothing is dereferenced: the buffers are address ranges only.
 #include <hip/hip_runtime_api.h>
 
@@ -198,23 +198,27 @@ void check_case(fwt_plan_t plan, int n, fwt_dtype dt, int64_t batch, bool with_i
         if (L.a.xcd_bits >= 0) {
             ++g_xcd_launches;
             const int xb = L.a.xcd_bits;
-            EXPECT(bytes * (with_im ? 2 : 1) <= ((size_t)16 << 20), "xcd placement on %zu B",
-                   bytes * (with_im ? 2 : 1));
-            EXPECT(!L.key.pipe && xb < 30 && L.a.wg_count % ((int64_t)8 << xb) == 0 &&
+            // the launch's own vectors, below the Infinity Cache's 256 MiB
+            const int64_t lb = L.a.tiles / (total[i] / batch);
+            EXPECT((size_t)lb * (size_t)N * esize * (with_im ? 2 : 1) < ((size_t)256 << 20),
+                   "xcd placement on a launch of %lld vectors", (long long)lb);
+            EXPECT(!L.key.pipe && xb < 30 && L.a.wg_count >= ((int64_t)8 << xb) &&
                        ((L.a.tiles >> L.a.tpw_bits) << L.a.tpw_bits) == L.a.tiles,
                    "xcd placement shape");
-            if (L.a.wg_count % ((int64_t)8 << xb) == 0 && L.a.wg_count <= ((int64_t)1 << 22)) {
+            if (L.a.wg_count <= ((int64_t)1 << 22)) {
                 const int64_t tpv = total[i] / batch;   // tiles per vector component
+                const int64_t span = L.a.wg_count & ~(((int64_t)8 << xb) - 1);
                 std::vector<char> seen((size_t)L.a.wg_count, 0);
                 for (int64_t w = 0; w < L.a.wg_count; ++w) {
-                    const int64_t g = qse::xcd_group(w, xb);
+                    const int64_t g = qse::xcd_group(w, xb, L.a.wg_count);
                     EXPECT(g >= 0 && g < L.a.wg_count && !seen[(size_t)g], "xcd map w=%lld",
                            (long long)w);
                     if (g >= 0 && g < L.a.wg_count)
                         seen[(size_t)g] = 1;
                     const int64_t v = (g << L.a.tpw_bits) / tpv;   // its vector component
-                    EXPECT(w % 8 == v % 8, "xcd map: w=%lld holds component %lld", (long long)w,
-                           (long long)v);
+                    EXPECT(w >= span || w % 8 == v % 8, "xcd map: w=%lld holds component %lld",
+                           (long long)w, (long long)v);
+                    EXPECT(w < span || g == w, "xcd map: tail w=%lld moved", (long long)w);
                 }
             }
         }
@@ -281,9 +285,14 @@ int main()
                 if (rc != FWT_OK)
                     continue;   // a split outside the per-pass limits
                 const size_t vec = ((size_t)1 << n) * esize * 2;
-                // small, ragged, a multiple of the 8 XCDs, and past the cache
-                // (when the tile count stays small)
-                std::vector<int64_t> batches = {1, 3, 8};
+                // small, ragged, past the cache (when the tile count stays
+                // small), and for states below the cache a multiple of the 8
+                // XCDs and a batch just past one
+                std::vector<int64_t> batches = {1, 3};
+                if (vec * 11 < ((size_t)256 << 20)) {
+                    batches.push_back(8);
+                    batches.push_back(11);
+                }
                 const int64_t big = (int64_t)(2 * cache / vec) + 3;
                 if (big > 3 && big <= ((int64_t)1 << 12))
                     batches.push_back(big);

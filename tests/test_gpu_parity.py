@@ -224,15 +224,17 @@ def test_gaussian_lane_exchange_kernels_odd_n(dtype, n, split, eb, wave, batch):
     assert_close(dtype, n, re, im, gre, gim)
 
 
-# (dtype, n, split, batch, wave): multi-pass plans on states of at most
-# 16 MiB with a multiple of 8 vectors, whose launches place each vector
-# component's workgroups on one XCD, in each kernel family
+# (dtype, n, split, batch, wave): multi-pass plans on states below 256 MiB
+# with at least 8 vectors, whose launches place each vector component's
+# workgroups on one XCD (all of them, or the first multiple of 8), in each
+# kernel family
 XCD_CASES = [("f32", 14, (7, 7), 64, None), ("f32", 14, (7, 7), 8, (1, 1)),
              ("f32", 14, (7, 7), 16, (0, 0)), ("f32", 12, (6, 6), 64, None),
              ("f32", 16, (9, 7), 16, None), ("f32", 18, (11, 7), 8, None),
              ("f32", 15, (5, 5, 5), 64, None), ("f32", 16, (10, 6), 24, None),
              ("f64", 14, (7, 7), 32, None), ("f64", 16, (8, 8), 8, None),
-             ("f64", 13, (7, 6), 64, (1, 1))]
+             ("f64", 13, (7, 6), 64, (1, 1)), ("f32", 16, (10, 6), 13, None),
+             ("f32", 20, (12, 8), 12, None)]
 
 
 @pytest.mark.parametrize("dtype,n,split,batch,wave", XCD_CASES)

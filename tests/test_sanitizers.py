@@ -68,8 +68,9 @@ def test_launch_schedule_covers_every_tile_once(workdir):
     once, chunked passes stay inside their chunks, launches come in the
     order fwt_plan_call_schedule states, the scale and nontemporal flags
     sit on the right passes, and the XCD-affine workgroup placement of
-    small states permutes each launch's workgroups so that every vector
-    component stays on one XCD (tests/sanitize/schedule_driver.cpp)."""
+    states below the Infinity Cache's size permutes each launch's
+    workgroups so that every vector component stays on one XCD
+    (tests/sanitize/schedule_driver.cpp)."""
     if shutil.which("g++") is None:
         pytest.skip("g++ not found")
     exe = os.path.join(workdir, "schedule_driver")
