@@ -133,7 +133,10 @@ LX_COLUMN_CASES = _lx_column_cases()
 RANDOM_MODES = ("default", "lds", "wave", "lx")
 
 
-def random_plan_cases(valid, count=80, seed=20_261_202):
+def random_plan_cases(valid, count=80, seed=20_261_202, batches=None):
+    """`count` random (dtype, n, split, tuning, batch, modes) cases that
+    `valid` accepts: batches of 1-5 vectors, or one of `batches` (cases
+    whose state would pass 2^22 elements per component are skipped then)."""
     import numpy as np
     rng = np.random.default_rng(seed)
 
@@ -178,6 +181,11 @@ def random_plan_cases(valid, count=80, seed=20_261_202):
         kw = {f: tuple(vals) for f, vals in fields.items()}
         if not valid(dtype, n, split, kw):
             continue
-        batch = max(1, min(int(rng.integers(1, 6)), (1 << 22) >> n))
+        if batches is None:
+            batch = max(1, min(int(rng.integers(1, 6)), (1 << 22) >> n))
+        else:
+            batch = int(rng.choice(batches))
+            if batch > (1 << 22) >> n:
+                continue
         out.append((dtype, n, split, kw, batch, tuple(modes)))
     return out

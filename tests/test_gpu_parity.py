@@ -309,13 +309,19 @@ def _planner_accepts(dtype, n, split, kw):
 
 
 RANDOM_CASES = random_plan_cases(_planner_accepts)
+# the same with 8-24 vectors, so that multi-pass launches place their
+# workgroups by XCD (all of them, or the first multiple of 8)
+RANDOM_XCD_CASES = random_plan_cases(_planner_accepts, count=40, seed=20_261_203,
+                                     batches=(8, 11, 16, 24))
 
 
-@pytest.mark.parametrize("dtype,n,split,kw,batch,modes", RANDOM_CASES,
+@pytest.mark.parametrize("dtype,n,split,kw,batch,modes", RANDOM_CASES + RANDOM_XCD_CASES,
                          ids=["r%02d-%s-n%d-%s" % (i, c[0], c[1], "-".join(c[5]))
-                              for i, c in enumerate(RANDOM_CASES)])
+                              for i, c in enumerate(RANDOM_CASES)] +
+                             ["x%02d-%s-n%d-b%d-%s" % (i, c[0], c[1], c[4], "-".join(c[5]))
+                              for i, c in enumerate(RANDOM_XCD_CASES)])
 def test_integer_random_plans(dtype, n, split, kw, batch, modes):
-    """Seeded random plans (1-3 factors, each pass on its default kernel
+    """Seeded random plans (1-4 factors, each pass on its default kernel
     or with a kernel family and random tiling fields forced), exactly
     against the oracle."""
     say("random plan %s n=%d split=%s %s batch=%d" % (dtype, n, split, kw, batch))
