@@ -527,65 +527,39 @@ __device__ __forceinline__ void permlane_swap(double& a, double& b)
 // of EXEC; the compiler cannot see the DPP inside the block.
 #define QSE_FMAC_DPP(Q, R, S) "v_fmac_f32_dpp %" #R ", %" #R ", %" #S " quad_perm:" Q \
                               " row_mask:0xf bank_mask:0xf\n\t"
-#define QSE_FMAC_DPP8(Q) "s_nop 4\n\t" \
-    QSE_FMAC_DPP(Q, 0, 8) \
-    QSE_FMAC_DPP(Q, 1, 8) \
-    QSE_FMAC_DPP(Q, 2, 8) \
-    QSE_FMAC_DPP(Q, 3, 8) \
-    QSE_FMAC_DPP(Q, 4, 8) \
-    QSE_FMAC_DPP(Q, 5, 8) \
-    QSE_FMAC_DPP(Q, 6, 8) \
-    QSE_FMAC_DPP(Q, 7, 8)
-#define QSE_FMAC_DPP16(Q) "s_nop 4\n\t" \
-    QSE_FMAC_DPP(Q, 0, 16) \
-    QSE_FMAC_DPP(Q, 1, 16) \
-    QSE_FMAC_DPP(Q, 2, 16) \
-    QSE_FMAC_DPP(Q, 3, 16) \
-    QSE_FMAC_DPP(Q, 4, 16) \
-    QSE_FMAC_DPP(Q, 5, 16) \
-    QSE_FMAC_DPP(Q, 6, 16) \
-    QSE_FMAC_DPP(Q, 7, 16) \
-    QSE_FMAC_DPP(Q, 8, 16) \
-    QSE_FMAC_DPP(Q, 9, 16) \
-    QSE_FMAC_DPP(Q, 10, 16) \
-    QSE_FMAC_DPP(Q, 11, 16) \
-    QSE_FMAC_DPP(Q, 12, 16) \
-    QSE_FMAC_DPP(Q, 13, 16) \
-    QSE_FMAC_DPP(Q, 14, 16) \
-    QSE_FMAC_DPP(Q, 15, 16)
-#define QSE_FMAC_DPP32(Q) "s_nop 4\n\t" \
-    QSE_FMAC_DPP(Q, 0, 32) \
-    QSE_FMAC_DPP(Q, 1, 32) \
-    QSE_FMAC_DPP(Q, 2, 32) \
-    QSE_FMAC_DPP(Q, 3, 32) \
-    QSE_FMAC_DPP(Q, 4, 32) \
-    QSE_FMAC_DPP(Q, 5, 32) \
-    QSE_FMAC_DPP(Q, 6, 32) \
-    QSE_FMAC_DPP(Q, 7, 32) \
-    QSE_FMAC_DPP(Q, 8, 32) \
-    QSE_FMAC_DPP(Q, 9, 32) \
-    QSE_FMAC_DPP(Q, 10, 32) \
-    QSE_FMAC_DPP(Q, 11, 32) \
-    QSE_FMAC_DPP(Q, 12, 32) \
-    QSE_FMAC_DPP(Q, 13, 32) \
-    QSE_FMAC_DPP(Q, 14, 32) \
-    QSE_FMAC_DPP(Q, 15, 32) \
-    QSE_FMAC_DPP(Q, 16, 32) \
-    QSE_FMAC_DPP(Q, 17, 32) \
-    QSE_FMAC_DPP(Q, 18, 32) \
-    QSE_FMAC_DPP(Q, 19, 32) \
-    QSE_FMAC_DPP(Q, 20, 32) \
-    QSE_FMAC_DPP(Q, 21, 32) \
-    QSE_FMAC_DPP(Q, 22, 32) \
-    QSE_FMAC_DPP(Q, 23, 32) \
-    QSE_FMAC_DPP(Q, 24, 32) \
-    QSE_FMAC_DPP(Q, 25, 32) \
-    QSE_FMAC_DPP(Q, 26, 32) \
-    QSE_FMAC_DPP(Q, 27, 32) \
-    QSE_FMAC_DPP(Q, 28, 32) \
-    QSE_FMAC_DPP(Q, 29, 32) \
-    QSE_FMAC_DPP(Q, 30, 32) \
-    QSE_FMAC_DPP(Q, 31, 32)
+#define QSE_FMAC_DPP_0(Q, S)                                                           \
+    QSE_FMAC_DPP(Q, 0, S) QSE_FMAC_DPP(Q, 1, S) QSE_FMAC_DPP(Q, 2, S) QSE_FMAC_DPP(Q, 3, S) \
+        QSE_FMAC_DPP(Q, 4, S) QSE_FMAC_DPP(Q, 5, S) QSE_FMAC_DPP(Q, 6, S) QSE_FMAC_DPP(Q, 7, S)
+#define QSE_FMAC_DPP_8(Q, S)                                                             \
+    QSE_FMAC_DPP(Q, 8, S) QSE_FMAC_DPP(Q, 9, S) QSE_FMAC_DPP(Q, 10, S) QSE_FMAC_DPP(Q, 11, S) \
+        QSE_FMAC_DPP(Q, 12, S) QSE_FMAC_DPP(Q, 13, S) QSE_FMAC_DPP(Q, 14, S)                \
+            QSE_FMAC_DPP(Q, 15, S)
+#define QSE_FMAC_DPP_16(Q, S)                                                               \
+    QSE_FMAC_DPP(Q, 16, S) QSE_FMAC_DPP(Q, 17, S) QSE_FMAC_DPP(Q, 18, S) QSE_FMAC_DPP(Q, 19, S) \
+        QSE_FMAC_DPP(Q, 20, S) QSE_FMAC_DPP(Q, 21, S) QSE_FMAC_DPP(Q, 22, S)                  \
+            QSE_FMAC_DPP(Q, 23, S)
+#define QSE_FMAC_DPP_24(Q, S)                                                               \
+    QSE_FMAC_DPP(Q, 24, S) QSE_FMAC_DPP(Q, 25, S) QSE_FMAC_DPP(Q, 26, S) QSE_FMAC_DPP(Q, 27, S) \
+        QSE_FMAC_DPP(Q, 28, S) QSE_FMAC_DPP(Q, 29, S) QSE_FMAC_DPP(Q, 30, S)                  \
+            QSE_FMAC_DPP(Q, 31, S)
+// Eight in-out operands v[b .. b + 7].
+#define QSE_OPS8(b)                                                                       \
+    "+v"(v[b]), "+v"(v[b + 1]), "+v"(v[b + 2]), "+v"(v[b + 3]), "+v"(v[b + 4]), "+v"(v[b + 5]), \
+        "+v"(v[b + 6]), "+v"(v[b + 7])
+// The stage on 8, 16 or 32 values with quad permutation Q; s is the last
+// operand.
+#define QSE_DPP_STAGE(Q)                                                                     \
+    if constexpr (NR == 2)                                                                   \
+        asm("s_nop 4\n\t" QSE_FMAC_DPP_0(Q, 8) : QSE_OPS8(0) : "v"(s));                       \
+    else if constexpr (NR == 4)                                                              \
+        asm("s_nop 4\n\t" QSE_FMAC_DPP_0(Q, 16) QSE_FMAC_DPP_8(Q, 16)                          \
+            : QSE_OPS8(0), QSE_OPS8(8)                                                        \
+            : "v"(s));                                                                        \
+    else                                                                                     \
+        asm("s_nop 4\n\t" QSE_FMAC_DPP_0(Q, 32) QSE_FMAC_DPP_8(Q, 32) QSE_FMAC_DPP_16(Q, 32)   \
+                QSE_FMAC_DPP_24(Q, 32)                                                        \
+            : QSE_OPS8(0), QSE_OPS8(8), QSE_OPS8(16), QSE_OPS8(24)                            \
+            : "v"(s));
 
 // One stage on lane bit LBIT over the NR = 2, 4 or 8 fp32 registers at x.
 template <int LBIT, int NR>
@@ -599,37 +573,21 @@ __device__ __forceinline__ void fmac_dpp_regs(Vec<float>::type* x, float s)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             v[4 * j + c] = x[j][c];
-    if constexpr (NR == 2 && LBIT == 0)
-        asm(QSE_FMAC_DPP8("[1,0,3,2]")
-            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
-            : "v"(s));
-    if constexpr (NR == 2 && LBIT == 1)
-        asm(QSE_FMAC_DPP8("[2,3,0,1]")
-            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
-            : "v"(s));
-    if constexpr (NR == 4 && LBIT == 0)
-        asm(QSE_FMAC_DPP16("[1,0,3,2]")
-            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
-            : "v"(s));
-    if constexpr (NR == 4 && LBIT == 1)
-        asm(QSE_FMAC_DPP16("[2,3,0,1]")
-            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
-            : "v"(s));
-    if constexpr (NR == 8 && LBIT == 0)
-        asm(QSE_FMAC_DPP32("[1,0,3,2]")
-            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]), "+v"(v[16]), "+v"(v[17]), "+v"(v[18]), "+v"(v[19]), "+v"(v[20]), "+v"(v[21]), "+v"(v[22]), "+v"(v[23]), "+v"(v[24]), "+v"(v[25]), "+v"(v[26]), "+v"(v[27]), "+v"(v[28]), "+v"(v[29]), "+v"(v[30]), "+v"(v[31])
-            : "v"(s));
-    if constexpr (NR == 8 && LBIT == 1)
-        asm(QSE_FMAC_DPP32("[2,3,0,1]")
-            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]), "+v"(v[16]), "+v"(v[17]), "+v"(v[18]), "+v"(v[19]), "+v"(v[20]), "+v"(v[21]), "+v"(v[22]), "+v"(v[23]), "+v"(v[24]), "+v"(v[25]), "+v"(v[26]), "+v"(v[27]), "+v"(v[28]), "+v"(v[29]), "+v"(v[30]), "+v"(v[31])
-            : "v"(s));
+    if constexpr (LBIT == 0) {
+        QSE_DPP_STAGE("[1,0,3,2]")
+    } else {
+        QSE_DPP_STAGE("[2,3,0,1]")
+    }
 #pragma unroll
     for (int j = 0; j < NR; ++j)
         x[j] = Vec<float>::type{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
 }
-#undef QSE_FMAC_DPP32
-#undef QSE_FMAC_DPP16
-#undef QSE_FMAC_DPP8
+#undef QSE_DPP_STAGE
+#undef QSE_OPS8
+#undef QSE_FMAC_DPP_24
+#undef QSE_FMAC_DPP_16
+#undef QSE_FMAC_DPP_8
+#undef QSE_FMAC_DPP_0
 #undef QSE_FMAC_DPP
 
 // Lane bits among 0 and 1 whose fp32 stages leave a sign (those in
