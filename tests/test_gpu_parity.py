@@ -600,6 +600,30 @@ def test_non_default_stream_and_determinism():
     assert_close("f32", n, re, im, a_re.cpu().numpy(), a_im.cpu().numpy())
 
 
+@pytest.mark.parametrize("n,batch", [(10, 256), (12, 256), (14, 256), (20, 4)])
+def test_repeated_calls_bit_identical(n, batch):
+    """The fp32 lane stages on lane bits 0 and 1 are hand-written DPP
+    multiply-adds whose wait states are set by hand.  Twenty calls on the
+    same Gaussian input, with many waves resident, must give the same bits
+    every time (a missed wait state would show as a timing-dependent
+    result), and the first must match the oracle."""
+    say("repeat n=%d batch=%d" % (n, batch))
+    w = workloads.custom(n, batch, "f32", "gauss", True, seed=12_000 + n)
+    re, im = workloads.gen(w)
+    plan = qse.Plan(n, "f32")
+    src_re, src_im = to_dev(re), to_dev(im)
+    first = None
+    for rep in range(20):
+        t_re, t_im = src_re.clone(), src_im.clone()
+        plan.execute(t_re, t_im, normalize=True)
+        if first is None:
+            torch.cuda.synchronize()
+            first = (t_re, t_im)
+            assert_close("f32", n, re, im, t_re.cpu().numpy(), t_im.cpu().numpy())
+        else:
+            assert torch.equal(t_re, first[0]) and torch.equal(t_im, first[1]), "call %d" % rep
+
+
 def test_one_plan_from_several_threads_and_streams():
     """One plan used at once from four host threads, each on its own
     stream and buffers (ctypes releases the GIL during the call): every
