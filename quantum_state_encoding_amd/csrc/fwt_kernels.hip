@@ -445,13 +445,14 @@ __global__ void __launch_bounds__(512)
 // butterflied in registers; lane bits cross lanes (the single-block design
 // of the iThome article's introduction, registers plus warp shuffle, on
 // wave64): lane bits 0 and 1 with DPP quad permutes, 2 and 3 with
-// ds_swizzle, and 4 and 5 with v_permlane16/32_swap, which exchange a lane
+// ds_swizzle (bit 3 in fp32 with a DPP row rotation instead), and 4 and 5
+// with v_permlane16/32_swap, which exchange a lane
 // bit with a register bit so the stage becomes a register butterfly (and
 // a second swap restores the layout).  Lanes keep their own half of each
 // pair with y = partner + s * x, s = +1 for the lower index and -1 for the
 // upper: one rounding, exactly the sum or difference.  (fp32 stages on lane
-// bits 0 and 1 keep x + s * partner instead, the difference negated, and
-// the kernel's final scaling removes the sign: fmac_dpp_regs.)
+// bits 0, 1 and 3 keep x + s * partner instead, the difference negated,
+// and the kernel's final scaling removes the sign: fmac_dpp_regs.)
 
 template <int LBIT>
 __device__ __forceinline__ unsigned lane_partner_u32(unsigned v)
@@ -515,17 +516,19 @@ __device__ __forceinline__ void permlane_swap(double& a, double& b)
     b = __longlong_as_double((long long)(((unsigned long long)bhi << 32) | blo));
 }
 
-// fp32 stages on lane bits 0 and 1: one vector-ALU instruction per value,
-// v_fmac_f32 with a quad permutation on its first source, so each lane
-// keeps x + s * partner (s = -1 on the upper lane of each pair).  The
-// upper lane then holds the difference negated.  The negation is exact and
-// carries through every later stage unchanged (a stage's two operands come
-// from lanes with equal bits 0 and 1, so they carry the same sign), and
-// the kernel removes it with its final scaling (dpp_sign_lanes).  Each
+// fp32 stages on lane bits 0, 1 and 3: one vector-ALU instruction per
+// value, v_fmac_f32 with a DPP lane permutation on its first source (quad
+// permutations for bits 0 and 1; for bit 3 a rotation of each 16-lane row
+// by 8, which is lane xor 8), so each lane keeps x + s * partner (s = -1 on
+// the upper lane of each pair).  The upper lane then holds the difference
+// negated.  The negation is exact and carries through every later stage
+// unchanged (a stage's two operands come from lanes with equal bits 0, 1
+// and 3, so they carry the same sign), and the kernel removes it with its
+// final scaling (dpp_sign_lanes).  Each
 // asm block begins with five wait states: a DPP read of a VGPR needs two
 // after a vector-ALU write of it, and a DPP instruction five after a write
 // of EXEC; the compiler cannot see the DPP inside the block.
-#define QSE_FMAC_DPP(Q, R, S) "v_fmac_f32_dpp %" #R ", %" #R ", %" #S " quad_perm:" Q \
+#define QSE_FMAC_DPP(Q, R, S) "v_fmac_f32_dpp %" #R ", %" #R ", %" #S " " Q \
                               " row_mask:0xf bank_mask:0xf\n\t"
 #define QSE_FMAC_DPP_0(Q, S)                                                           \
     QSE_FMAC_DPP(Q, 0, S) QSE_FMAC_DPP(Q, 1, S) QSE_FMAC_DPP(Q, 2, S) QSE_FMAC_DPP(Q, 3, S) \
@@ -546,7 +549,7 @@ __device__ __forceinline__ void permlane_swap(double& a, double& b)
 #define QSE_OPS8(b)                                                                       \
     "+v"(v[b]), "+v"(v[b + 1]), "+v"(v[b + 2]), "+v"(v[b + 3]), "+v"(v[b + 4]), "+v"(v[b + 5]), \
         "+v"(v[b + 6]), "+v"(v[b + 7])
-// The stage on 8, 16 or 32 values with quad permutation Q; s is the last
+// The stage on 8, 16 or 32 values with DPP control Q; s is the last
 // operand.
 #define QSE_DPP_STAGE(Q)                                                                     \
     if constexpr (NR == 2)                                                                   \
@@ -565,7 +568,7 @@ __device__ __forceinline__ void permlane_swap(double& a, double& b)
 template <int LBIT, int NR>
 __device__ __forceinline__ void fmac_dpp_regs(Vec<float>::type* x, float s)
 {
-    static_assert(LBIT == 0 || LBIT == 1, "quad permutations pair lane bits 0 and 1");
+    static_assert(LBIT == 0 || LBIT == 1 || LBIT == 3, "DPP pairs lane bits 0, 1 and 3");
     static_assert(NR == 2 || NR == 4 || NR == 8, "blocks of 2, 4 or 8 registers");
     float v[4 * NR];
 #pragma unroll
@@ -574,9 +577,11 @@ __device__ __forceinline__ void fmac_dpp_regs(Vec<float>::type* x, float s)
         for (int c = 0; c < 4; ++c)
             v[4 * j + c] = x[j][c];
     if constexpr (LBIT == 0) {
-        QSE_DPP_STAGE("[1,0,3,2]")
+        QSE_DPP_STAGE("quad_perm:[1,0,3,2]")
+    } else if constexpr (LBIT == 1) {
+        QSE_DPP_STAGE("quad_perm:[2,3,0,1]")
     } else {
-        QSE_DPP_STAGE("[2,3,0,1]")
+        QSE_DPP_STAGE("row_ror:8")
     }
 #pragma unroll
     for (int j = 0; j < NR; ++j)
@@ -590,12 +595,13 @@ __device__ __forceinline__ void fmac_dpp_regs(Vec<float>::type* x, float s)
 #undef QSE_FMAC_DPP_0
 #undef QSE_FMAC_DPP
 
-// Lane bits among 0 and 1 whose fp32 stages leave a sign (those in
+// Lane bits among 0, 1 and 3 whose fp32 stages leave a sign (those in
 // [gb, gb + lb), the lane row bits of a tile); a lane's outputs carry
 // (-1)^popcount(lane & mask).
 __host__ __device__ constexpr unsigned dpp_sign_lanes(int gb, int lb)
 {
-    return (gb <= 0 && lb > 0 ? 1u : 0u) | (gb <= 1 && gb + lb > 1 ? 2u : 0u);
+    return (gb <= 0 && lb > 0 ? 1u : 0u) | (gb <= 1 && gb + lb > 1 ? 2u : 0u) |
+           (gb <= 3 && gb + lb > 3 ? 8u : 0u);
 }
 
 // Stage on lane bit LBIT for all E registers.
@@ -603,7 +609,7 @@ template <int LBIT, int E, typename V, typename T>
 __device__ __forceinline__ void lane_stage(V* x, int lane)
 {
     constexpr int W = sizeof(V) / sizeof(T);
-    if constexpr (LBIT < 2 && sizeof(T) == 4 && E >= 2) {
+    if constexpr ((LBIT < 2 || LBIT == 3) && sizeof(T) == 4 && E >= 2) {
         const float s = ((lane >> LBIT) & 1) ? -1.f : 1.f;
         constexpr int NR = E < 8 ? E : 8;
 #pragma unroll
@@ -734,7 +740,7 @@ __global__ void __launch_bounds__(256)
     }
     register_stages<EB, E>(x);
     LaneStages<0, LB, GB, E, V, T>::run(x, lane);
-    // The scale, times the sign the fp32 stages on lane bits 0 and 1 leave.
+    // The scale, times the sign the fp32 DPP lane stages leave.
     constexpr unsigned SM = (sizeof(T) == 4 && E >= 2) ? dpp_sign_lanes(GB, LB) : 0u;
     if (SM || a.do_scale) {
         T c = a.do_scale ? (T)a.scale : T(1);
@@ -980,7 +986,7 @@ __device__ __forceinline__ void lx_process(typename S::V* x, typename S::V* L, i
     else
         LaneStages<0, S::LR, S::GB, S::E, V, T>::run(x, lane);
     LxRounds<V, S::KR, S::GB, S::W, S::EB, S::PHB, 0, S::NX, RL>::run(x, L, lane_row, g, wave);
-    // The last stage.  Where the fp32 stages on lane bits 0 and 1 leave a
+    // The last stage.  Where the fp32 DPP lane stages (bits 0, 1, 3) leave a
     // sign (lanes keep their lane bits through the exchanges), it is fused
     // with the scale times that sign: for a scale that is a power of two
     // (even n) or +-1 the fused form gives the same bits as the butterfly
