@@ -568,7 +568,7 @@ __device__ __forceinline__ void permlane_swap(double& a, double& b)
 template <int LBIT, int NR>
 __device__ __forceinline__ void fmac_dpp_regs(Vec<float>::type* x, float s)
 {
-    static_assert(LBIT == 0 || LBIT == 1 || LBIT == 3, "DPP pairs lane bits 0, 1 and 3");
+    static_assert(LBIT >= 0 && LBIT <= 3, "DPP pairs lanes within a row of 16");
     static_assert(NR == 2 || NR == 4 || NR == 8, "blocks of 2, 4 or 8 registers");
     float v[4 * NR];
 #pragma unroll
@@ -580,6 +580,8 @@ __device__ __forceinline__ void fmac_dpp_regs(Vec<float>::type* x, float s)
         QSE_DPP_STAGE("quad_perm:[1,0,3,2]")
     } else if constexpr (LBIT == 1) {
         QSE_DPP_STAGE("quad_perm:[2,3,0,1]")
+    } else if constexpr (LBIT == 2) {
+        QSE_DPP_STAGE("row_half_mirror")
     } else {
         QSE_DPP_STAGE("row_ror:8")
     }
@@ -595,21 +597,32 @@ __device__ __forceinline__ void fmac_dpp_regs(Vec<float>::type* x, float s)
 #undef QSE_FMAC_DPP_0
 #undef QSE_FMAC_DPP
 
-// Lane bits among 0, 1 and 3 whose fp32 stages leave a sign (those in
-// [gb, gb + lb), the lane row bits of a tile); a lane's outputs carry
-// (-1)^popcount(lane & mask).
-__host__ __device__ constexpr unsigned dpp_sign_lanes(int gb, int lb)
+// Lane bits among 0, 1, 3 (and 2 with the mirrored lane order below) whose
+// fp32 stages leave a sign (those in [gb, gb + lb), the lane row bits of a
+// tile); a lane's outputs carry (-1)^popcount(logical lane & mask).
+__host__ __device__ constexpr unsigned dpp_sign_lanes(int gb, int lb, bool mirror = false)
 {
     return (gb <= 0 && lb > 0 ? 1u : 0u) | (gb <= 1 && gb + lb > 1 ? 2u : 0u) |
-           (gb <= 3 && gb + lb > 3 ? 8u : 0u);
+           (mirror && gb <= 2 && gb + lb > 2 ? 4u : 0u) | (gb <= 3 && gb + lb > 3 ? 8u : 0u);
 }
 
-// Stage on lane bit LBIT for all E registers.
-template <int LBIT, int E, typename V, typename T>
+// Mirrored lane order: in each group of 8 lanes the upper 4 hold their rows
+// in reverse (logical lane = lane ^ 3 when lane bit 2 is set).  Lane xor 4
+// on logical lanes is then DPP row_half_mirror on physical ones (lane ->
+// 7 - lane in each group of 8), while xor 1, 2 and 8 stay the quad
+// permutations and the row rotation: they leave bit 2 alone.
+__device__ __forceinline__ int mirrored_lane(int lane)
+{
+    return lane ^ (((lane >> 2) & 1) * 3);
+}
+
+// Stage on lane bit LBIT for all E registers; `lane` is the logical lane
+// (mirrored_lane when MI).
+template <int LBIT, int E, typename V, typename T, bool MI = false>
 __device__ __forceinline__ void lane_stage(V* x, int lane)
 {
     constexpr int W = sizeof(V) / sizeof(T);
-    if constexpr ((LBIT < 2 || LBIT == 3) && sizeof(T) == 4 && E >= 2) {
+    if constexpr ((LBIT < 2 || LBIT == 3 || (MI && LBIT == 2)) && sizeof(T) == 4 && E >= 2) {
         const float s = ((lane >> LBIT) & 1) ? -1.f : 1.f;
         constexpr int NR = E < 8 ? E : 8;
 #pragma unroll
@@ -649,12 +662,12 @@ __device__ __forceinline__ void lane_stage(V* x, int lane)
 // it, lane bit 4 (5) holds the row bit register bit 0 (1) held, and
 // register bit 0 (1) holds the row bit of lane bit 4 (5); a caller must
 // address the data with that relabelling (lx_thread_row_rl, lx_reg_row_rl).
-template <int LBIT, int E, typename V, typename T>
+template <int LBIT, int E, typename V, typename T, bool MI = false>
 __device__ __forceinline__ void lane_stage_nr(V* x, int lane)
 {
     constexpr int W = sizeof(V) / sizeof(T);
     if constexpr (LBIT < 4) {
-        lane_stage<LBIT, E, V, T>(x, lane);
+        lane_stage<LBIT, E, V, T, MI>(x, lane);
     } else {
         constexpr int RB = LBIT - 4;   // register bit paired with the lane bit
         static_assert(E >= 4, "lane bits 4 and 5 pair register bits 0 and 1");
@@ -673,29 +686,29 @@ __device__ __forceinline__ void lane_stage_nr(V* x, int lane)
     }
 }
 
-template <int B, int LB, int GB, int E, typename V, typename T>
+template <int B, int LB, int GB, int E, typename V, typename T, bool MI = false>
 struct LaneStagesNR {
     __device__ __forceinline__ static void run(V* x, int lane)
     {
-        lane_stage_nr<GB + B, E, V, T>(x, lane);
-        LaneStagesNR<B + 1, LB, GB, E, V, T>::run(x, lane);
+        lane_stage_nr<GB + B, E, V, T, MI>(x, lane);
+        LaneStagesNR<B + 1, LB, GB, E, V, T, MI>::run(x, lane);
     }
 };
-template <int LB, int GB, int E, typename V, typename T>
-struct LaneStagesNR<LB, LB, GB, E, V, T> {
+template <int LB, int GB, int E, typename V, typename T, bool MI>
+struct LaneStagesNR<LB, LB, GB, E, V, T, MI> {
     __device__ __forceinline__ static void run(V*, int) {}
 };
 
-template <int B, int LB, int GB, int E, typename V, typename T>
+template <int B, int LB, int GB, int E, typename V, typename T, bool MI = false>
 struct LaneStages {
     __device__ __forceinline__ static void run(V* x, int lane)
     {
-        lane_stage<GB + B, E, V, T>(x, lane);
-        LaneStages<B + 1, LB, GB, E, V, T>::run(x, lane);
+        lane_stage<GB + B, E, V, T, MI>(x, lane);
+        LaneStages<B + 1, LB, GB, E, V, T, MI>::run(x, lane);
     }
 };
-template <int LB, int GB, int E, typename V, typename T>
-struct LaneStages<LB, LB, GB, E, V, T> {
+template <int LB, int GB, int E, typename V, typename T, bool MI>
+struct LaneStages<LB, LB, GB, E, V, T, MI> {
     __device__ __forceinline__ static void run(V*, int) {}
 };
 
@@ -903,6 +916,12 @@ struct LxShape {
     // register bit of the last stage, the top one the last exchange moves
     static constexpr int LAST = (W - (NX - 1) * EB < EB ? W - (NX - 1) * EB : EB) - 1;
     static constexpr bool SPLIT = W < EB;          // top row bit stays a register bit
+    // fp32 row tiles of 8 or more registers per lane use the mirrored lane
+    // order (mirrored_lane), so that lane bit 2 is a DPP stage too.  (With 2
+    // or 4 registers the fixed wait states of each DPP stage cost more than
+    // the swizzles they replace: n = 13 +1.7 %, n = 20 +0.13 %, against
+    // n = 14 -4.8 %, n = 15 -2.7 % with 8.)
+    static constexpr bool MI = sizeof(T) == 4 && GB == 0 && EB >= 3;
     static_assert(KR == EB + LR + W && EB >= 1 && W >= 1 && W <= 4, "lane-exchange tile");
     static_assert(!ROW || GB == 0, "row passes have one column group");
 };
@@ -982,9 +1001,9 @@ __device__ __forceinline__ void lx_process(typename S::V* x, typename S::V* L, i
     // 1 lie below the phase bits: the first exchange's writes relabel.
     constexpr bool RL = S::EB >= 2 + S::PHB;
     if constexpr (RL)
-        LaneStagesNR<0, S::LR, S::GB, S::E, V, T>::run(x, lane);
+        LaneStagesNR<0, S::LR, S::GB, S::E, V, T, S::MI>::run(x, lane);
     else
-        LaneStages<0, S::LR, S::GB, S::E, V, T>::run(x, lane);
+        LaneStages<0, S::LR, S::GB, S::E, V, T, S::MI>::run(x, lane);
     LxRounds<V, S::KR, S::GB, S::W, S::EB, S::PHB, 0, S::NX, RL>::run(x, L, lane_row, g, wave);
     // The last stage.  Where the fp32 DPP lane stages (bits 0, 1, 3) leave a
     // sign (lanes keep their lane bits through the exchanges), it is fused
@@ -993,7 +1012,7 @@ __device__ __forceinline__ void lx_process(typename S::V* x, typename S::V* L, i
     // and then the multiply; for odd n it rounds c b first, within one unit
     // of the other order.  Elsewhere the multiply follows the butterfly (a
     // fused form behind a run-time branch costs these kernels 30 VGPRs).
-    constexpr unsigned SM = sizeof(T) == 4 ? dpp_sign_lanes(S::GB, S::LR) : 0u;
+    constexpr unsigned SM = sizeof(T) == 4 ? dpp_sign_lanes(S::GB, S::LR, S::MI) : 0u;
     constexpr int LB = 1 << S::LAST;
     if constexpr (SM != 0) {
         T c = do_scale ? (T)scale : T(1);
@@ -1047,7 +1066,9 @@ __global__ void __launch_bounds__(64 << W)
     const int64_t t = a.tile0 + xcd_group(blockIdx.x, a.xcd_bits, a.wg_count);
     if (t >= a.tiles)
         return;   // uniform across the workgroup
-    const int lane = threadIdx.x & 63;
+    // The logical lane: which rows this lane holds (mirrored_lane for fp32
+    // row tiles); addresses, LDS slots and stage signs all follow it.
+    const int lane = S::MI ? mirrored_lane(threadIdx.x & 63) : (threadIdx.x & 63);
     const int wave = threadIdx.x >> 6;
     const int g = lane & ((1 << GB) - 1);
     const int lane_row = lane >> GB;
