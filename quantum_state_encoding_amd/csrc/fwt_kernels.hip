@@ -445,8 +445,9 @@ __global__ void __launch_bounds__(512)
 // butterflied in registers; lane bits cross lanes (the single-block design
 // of the iThome article's introduction, registers plus warp shuffle, on
 // wave64): lane bits 0 and 1 with DPP quad permutes, 2 and 3 with
-// ds_swizzle (bit 3 in fp32 with a DPP row rotation instead), and 4 and 5
-// with v_permlane16/32_swap, which exchange a lane
+// ds_swizzle (bit 3 with a DPP row rotation instead, and bit 2 with a DPP
+// row half-mirror in mirrored row tiles), and 4 and 5 with
+// v_permlane16/32_swap, which exchange a lane
 // bit with a register bit so the stage becomes a register butterfly (and
 // a second swap restores the layout).  Lanes keep their own half of each
 // pair with y = partner + s * x, s = +1 for the lower index and -1 for the
@@ -454,30 +455,32 @@ __global__ void __launch_bounds__(512)
 // bits 0, 1 and 3 keep x + s * partner instead, the difference negated,
 // and the kernel's final scaling removes the sign: fmac_dpp_regs.)
 
-template <int LBIT>
+template <int LBIT, bool MI = false>
 __device__ __forceinline__ unsigned lane_partner_u32(unsigned v)
 {
     if constexpr (LBIT == 0)
         return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // quad [1,0,3,2]
     else if constexpr (LBIT == 1)
         return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad [2,3,0,1]
+    else if constexpr (LBIT == 2 && MI)
+        return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true); // row_half_mirror
     else if constexpr (LBIT == 2)
         return (unsigned)__builtin_amdgcn_ds_swizzle((int)v, (4 << 10) | 0x1F);   // xor 4
     else
-        return (unsigned)__builtin_amdgcn_ds_swizzle((int)v, (8 << 10) | 0x1F);   // xor 8
+        return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true); // row_ror:8
 }
 
-template <int LBIT>
+template <int LBIT, bool MI = false>
 __device__ __forceinline__ float lane_partner(float v)
 {
-    return __uint_as_float(lane_partner_u32<LBIT>(__float_as_uint(v)));
+    return __uint_as_float(lane_partner_u32<LBIT, MI>(__float_as_uint(v)));
 }
-template <int LBIT>
+template <int LBIT, bool MI = false>
 __device__ __forceinline__ double lane_partner(double v)
 {
     const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-    const unsigned lo = lane_partner_u32<LBIT>((unsigned)u);
-    const unsigned hi = lane_partner_u32<LBIT>((unsigned)(u >> 32));
+    const unsigned lo = lane_partner_u32<LBIT, MI>((unsigned)u);
+    const unsigned hi = lane_partner_u32<LBIT, MI>((unsigned)(u >> 32));
     return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
@@ -635,7 +638,7 @@ __device__ __forceinline__ void lane_stage(V* x, int lane)
 #pragma unroll
             for (int c = 0; c < W; ++c) {
                 const T v = x[j][c];
-                x[j][c] = fma_sign(v, s, lane_partner<LBIT>(v));
+                x[j][c] = fma_sign(v, s, lane_partner<LBIT, MI>(v));
             }
         }
     } else {
@@ -916,12 +919,14 @@ struct LxShape {
     // register bit of the last stage, the top one the last exchange moves
     static constexpr int LAST = (W - (NX - 1) * EB < EB ? W - (NX - 1) * EB : EB) - 1;
     static constexpr bool SPLIT = W < EB;          // top row bit stays a register bit
-    // fp32 row tiles of 8 or more registers per lane use the mirrored lane
-    // order (mirrored_lane), so that lane bit 2 is a DPP stage too.  (With 2
-    // or 4 registers the fixed wait states of each DPP stage cost more than
-    // the swizzles they replace: n = 13 +1.7 %, n = 20 +0.13 %, against
-    // n = 14 -4.8 %, n = 15 -2.7 % with 8.)
-    static constexpr bool MI = sizeof(T) == 4 && GB == 0 && EB >= 3;
+    // Row tiles of 8 or more registers per lane use the mirrored lane order
+    // (mirrored_lane), so that lane bit 2 is a DPP stage too: a DPP
+    // multiply-add in fp32, two DPP moves and a multiply-add in fp64.
+    // (With 2 or 4 fp32 registers the fixed wait states of each DPP stage
+    // cost more than the swizzles they replace: n = 13 +1.7 %, n = 20
+    // +0.13 %, against n = 14 -4.8 %, n = 15 -2.7 % with 8; fp64 n = 13
+    // -4.5 %, n = 24 -0.4 %.)
+    static constexpr bool MI = GB == 0 && EB >= 3;
     static_assert(KR == EB + LR + W && EB >= 1 && W >= 1 && W <= 4, "lane-exchange tile");
     static_assert(!ROW || GB == 0, "row passes have one column group");
 };
