@@ -27,8 +27,16 @@ struct TileArgs {
                          // component share an XCD (xcd_group); -1: launch order
     int do_scale;        // multiply by `scale` before the final store
     int ld_nt;           // nontemporal loads (input not reused by this call)
-    int st_nt;           // nontemporal stores (output not reused by this call)
+    int st_policy;       // cache policy of the stores (StorePolicy)
     double scale;        // 2^(-n/2) rounded to the element type
+};
+
+// Cache policy of a pass's stores.
+enum StorePolicy : int {
+    kStorePlain = 0,          // write-back L2: the next launch may hit it
+    kStoreNontemporal = 1,    // streaming: this call does not read it again
+    kStoreWriteThrough = 2,   // device-scope stores (sc1): intermediate
+                              // results of states of 256 MiB and more
 };
 
 // Kernel variant: element type, row bits KR, register-round bits EB,

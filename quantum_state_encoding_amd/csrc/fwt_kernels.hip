@@ -32,6 +32,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
 #include <vector>
 
 #include "fwt_internal.h"
@@ -235,15 +236,57 @@ __device__ __forceinline__ V load16_nt(const unsigned char* p, uint32_t off)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const V*>(p + off));
 }
-template <typename V>
+// A 16-byte store with cache policy POL (StorePolicy).  The write-through
+// form is a buffer store with the device-scope bit (sc1) set: the resource
+// spans 2^32 bytes from the workgroup-uniform base p (its third word is
+// gfx9's 32-bit data format), so it lives in scalar registers and the lane
+// offset is the store's 32-bit VGPR offset.
+template <int POL, typename V>
 __device__ __forceinline__ void store16(unsigned char* p, uint32_t off, const V& v)
 {
-    *reinterpret_cast<V*>(p + off) = v;
+    if constexpr (POL == kStoreNontemporal) {
+        __builtin_nontemporal_store(v, reinterpret_cast<V*>(p + off));
+    } else if constexpr (POL == kStoreWriteThrough) {
+        typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+        constexpr int kFormatWord = 0x00020000;
+        constexpr int kScopeDevice = 16;   // the sc1 bit of the cache-policy operand
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(p, (short)0, -1, kFormatWord);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, (int)off, 0,
+                                               kScopeDevice);
+    } else {
+        *reinterpret_cast<V*>(p + off) = v;
+    }
 }
-template <typename V>
-__device__ __forceinline__ void store16_nt(unsigned char* p, uint32_t off, const V& v)
+
+// Runs f(std::integral_constant<int, POL>) for the run-time policy pol, so
+// that each policy's stores are unrolled with a compile-time form.
+template <typename F>
+__device__ __forceinline__ void with_store_policy(int pol, F&& f)
 {
-    __builtin_nontemporal_store(v, reinterpret_cast<V*>(p + off));
+    if (__builtin_expect(pol == kStorePlain, 1))
+        f(std::integral_constant<int, kStorePlain>{});
+    else if (pol == kStoreNontemporal)
+        f(std::integral_constant<int, kStoreNontemporal>{});
+    else
+        f(std::integral_constant<int, kStoreWriteThrough>{});
+}
+
+// The arguments a tile uses only after its stages, read together with the
+// ones it uses first.  Left to the scheduler, their scalar load can still
+// be in flight during the lane stages, and since LDS operations and scalar
+// loads share one wait counter, every ds_swizzle wait then drains to zero
+// (up to 4 % per pass).  The asm pins the values in scalar registers here.
+struct LateArgs {
+    int do_scale;
+    int st_policy;
+    double scale;
+};
+__device__ __forceinline__ LateArgs late_args(const TileArgs& a)
+{
+    LateArgs r{a.do_scale, a.st_policy, a.scale};
+    asm volatile("" : "+s"(r.do_scale), "+s"(r.st_policy), "+s"(r.scale));
+    return r;
 }
 
 // Compile-time shape of a tile kernel.
@@ -352,19 +395,17 @@ __device__ __forceinline__ void process_tile(typename S::V* x, typename S::V* L,
 
 template <typename S>
 __device__ __forceinline__ void store_tile(const typename S::V* x, const TileAddr& ta, int tau,
-                                           int nt)
+                                           int pol)
 {
     using V = typename S::V;
     const GlobalLayout<S::AF, S::EB> gl(ta.lane_bytes, tau, ta.row_bytes);
-    if (ta.active && nt) {
+    if (!ta.active)
+        return;
+    with_store_policy(pol, [&](auto P) {
 #pragma unroll
         for (int j = 0; j < S::E; ++j)
-            store16_nt<V>(ta.p, gl.base + (uint32_t)j * gl.jstride, x[j]);
-    } else if (ta.active) {
-#pragma unroll
-        for (int j = 0; j < S::E; ++j)
-            store16<V>(ta.p, gl.base + (uint32_t)j * gl.jstride, x[j]);
-    }
+            store16<decltype(P)::value, V>(ta.p, gl.base + (uint32_t)j * gl.jstride, x[j]);
+    });
 }
 
 // One workgroup per tile group: load, transform, store.
@@ -385,10 +426,11 @@ __global__ void __launch_bounds__(EB >= 5 ? 512 : 1024)
     const TileAddr ta =
         tile_addr<S>(blockIdx.y ? im : re, a, xcd_group(blockIdx.x, a.xcd_bits, a.wg_count), tl,
                      g);
+    const LateArgs la = late_args(a);
     V x[S::E];
     load_tile<S>(x, ta, tau, a.ld_nt);
-    process_tile<S>(x, L, tau, g, a.do_scale, a.scale);
-    store_tile<S>(x, ta, tau, a.st_nt);
+    process_tile<S>(x, L, tau, g, la.do_scale, la.scale);
+    store_tile<S>(x, ta, tau, la.st_policy);
 }
 
 // Persistent, software-pipelined form for tiles so large that a CU holds
@@ -414,6 +456,7 @@ __global__ void __launch_bounds__(512)
     int64_t w = blockIdx.x;
     if (w >= a.wg_count)
         return;   // uniform across the workgroup
+    const LateArgs la = late_args(a);
     V nx[S::E];
     TileAddr na = tile_addr<S>(buf, a, w, tl, g);
     load_tile<S>(nx, na, tau, a.ld_nt);
@@ -429,8 +472,8 @@ __global__ void __launch_bounds__(512)
             na = tile_addr<S>(buf, a, wn, tl, g);
             load_tile<S>(nx, na, tau, a.ld_nt);
         }
-        process_tile<S>(x, L, tau, g, a.do_scale, a.scale);
-        store_tile<S>(x, ca, tau, a.st_nt);
+        process_tile<S>(x, L, tau, g, la.do_scale, la.scale);
+        store_tile<S>(x, ca, tau, la.st_policy);
         if (!more)
             break;
         w = wn;
@@ -734,6 +777,7 @@ __global__ void __launch_bounds__(256)
     const TileAddr ta =
         tile_addr<S>(blockIdx.y ? im : re, a, xcd_group(blockIdx.x, a.xcd_bits, a.wg_count), tl,
                      g);
+    const LateArgs la = late_args(a);
     const GlobalLayout<LB, EB> gl(ta.lane_bytes, rl, ta.row_bytes);
     V x[E];
     if (ta.active && a.ld_nt) {
@@ -758,22 +802,20 @@ __global__ void __launch_bounds__(256)
     LaneStages<0, LB, GB, E, V, T>::run(x, lane);
     // The scale, times the sign the fp32 DPP lane stages leave.
     constexpr unsigned SM = (sizeof(T) == 4 && E >= 2) ? dpp_sign_lanes(GB, LB) : 0u;
-    if (SM || a.do_scale) {
-        T c = a.do_scale ? (T)a.scale : T(1);
+    if (SM || la.do_scale) {
+        T c = la.do_scale ? (T)la.scale : T(1);
         if (SM && (__popc((unsigned)lane & SM) & 1))
             c = -c;
 #pragma unroll
         for (int j = 0; j < E; ++j)
             x[j] *= c;
     }
-    if (ta.active && a.st_nt) {
+    if (ta.active) {
+        with_store_policy(la.st_policy, [&](auto P) {
 #pragma unroll
-        for (int j = 0; j < E; ++j)
-            store16_nt<V>(ta.p, gl.base + (uint32_t)j * gl.jstride, x[j]);
-    } else if (ta.active) {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            store16<V>(ta.p, gl.base + (uint32_t)j * gl.jstride, x[j]);
+            for (int j = 0; j < E; ++j)
+                store16<decltype(P)::value, V>(ta.p, gl.base + (uint32_t)j * gl.jstride, x[j]);
+        });
     }
 }
 
@@ -1044,20 +1086,16 @@ __device__ __forceinline__ void lx_process(typename S::V* x, typename S::V* L, i
 template <typename S>
 __device__ __forceinline__ void lx_store(const typename S::V* x, unsigned char* p,
                                          unsigned char* p_hi, uint32_t gbase, uint32_t rsh,
-                                         uint32_t rf, int nt)
+                                         uint32_t rf, int pol)
 {
     using V = typename S::V;
-    if (nt) {
+    with_store_policy(pol, [&](auto P) {
 #pragma unroll
         for (int j = 0; j < S::E; ++j)
-            store16_nt<V>(const_cast<unsigned char*>(lx_reg_base<S, S::NX>(j, p, p_hi)),
-                          gbase + ((rf + lx_reg_off_row<S, S::NX>(j)) << rsh), x[j]);
-    } else {
-#pragma unroll
-        for (int j = 0; j < S::E; ++j)
-            store16<V>(const_cast<unsigned char*>(lx_reg_base<S, S::NX>(j, p, p_hi)),
-                       gbase + ((rf + lx_reg_off_row<S, S::NX>(j)) << rsh), x[j]);
-    }
+            store16<decltype(P)::value, V>(
+                const_cast<unsigned char*>(lx_reg_base<S, S::NX>(j, p, p_hi)),
+                gbase + ((rf + lx_reg_off_row<S, S::NX>(j)) << rsh), x[j]);
+    });
 }
 
 template <typename T, int KR, int EB, int W, int PHB, int GB, bool ROW>
@@ -1071,6 +1109,7 @@ __global__ void __launch_bounds__(64 << W)
     const int64_t t = a.tile0 + xcd_group(blockIdx.x, a.xcd_bits, a.wg_count);
     if (t >= a.tiles)
         return;   // uniform across the workgroup
+    const LateArgs la = late_args(a);
     // The logical lane: which rows this lane holds (mirrored_lane for fp32
     // row tiles); addresses, LDS slots and stage signs all follow it.
     const int lane = S::MI ? mirrored_lane(threadIdx.x & 63) : (threadIdx.x & 63);
@@ -1083,9 +1122,9 @@ __global__ void __launch_bounds__(64 << W)
     const uint32_t gbase = (uint32_t)g << 4;
     V x[S::E];
     lx_load<S>(x, p, p_hi, gbase, rsh, lx_thread_row<W, EB, S::LR, 0>(lane_row, wave), a.ld_nt);
-    lx_process<S, T>(x, L, lane, lane_row, g, wave, a.do_scale, a.scale);
+    lx_process<S, T>(x, L, lane, lane_row, g, wave, la.do_scale, la.scale);
     lx_store<S>(x, p, p_hi, gbase, rsh, lx_thread_row<W, EB, S::LR, S::NX>(lane_row, wave),
-                a.st_nt);
+                la.st_policy);
 }
 
 __global__ void __launch_bounds__(256)

@@ -89,6 +89,8 @@ hipError_t record(const qse::KernelKey& key, void* re, void* im, int ncomp,
 int g_bad = 0;
 int g_vector_chunked = 0, g_block_chunked = 0;   // cases of each schedule kind
 int g_xcd_launches = 0;                           // launches with XCD-affine placement
+int g_wt_launches = 0;                            // launches with device-scope stores
+int g_nt_launches = 0;                            // launches with nontemporal stores
 #define EXPECT(c, ...)                                                           \
     do {                                                                         \
         if (!(c)) {                                                              \
@@ -188,7 +190,19 @@ void check_case(fwt_plan_t plan, int n, fwt_dtype dt, int64_t batch, bool with_i
             EXPECT(L.a.scale == want_c, "scale value n=%d", n);
         }
         EXPECT(L.a.ld_nt == (np > 1 && i == 0 ? 1 : 0), "nontemporal loads, pass %d", i);
-        EXPECT(L.a.st_nt == (np > 1 && last ? 1 : 0), "nontemporal stores, pass %d", i);
+        // Stores of a multi-pass plan: the last pass nontemporal once the
+        // call's state exceeds 256 MiB; earlier passes with device scope
+        // once it exceeds 32 MiB, if their tiles have at most 2^10 slots.
+        const size_t bytes = (size_t)batch * (size_t)N * esize * (with_im ? 2 : 1);
+        const int want_st =
+            np < 2 ? qse::kStorePlain
+            : last ? (bytes > ((size_t)256 << 20) ? qse::kStoreNontemporal : qse::kStorePlain)
+                   : (bytes > ((size_t)32 << 20) && p.kr + p.gbits <= 10 ? qse::kStoreWriteThrough
+                                                                        : qse::kStorePlain);
+        EXPECT(L.a.st_policy == want_st, "store policy %d, want %d, pass %d", L.a.st_policy,
+               want_st, i);
+        g_wt_launches += L.a.st_policy == qse::kStoreWriteThrough;
+        g_nt_launches += L.a.st_policy == qse::kStoreNontemporal;
         EXPECT(L.a.tile0 == 0 && L.a.tiles > 0, "tiles");
         EXPECT(L.a.wg_count == (L.a.tiles + ((int64_t)1 << L.a.tpw_bits) - 1) >> L.a.tpw_bits,
                "workgroups");
@@ -311,8 +325,11 @@ int main()
     EXPECT(g_vector_chunked >= 10 && g_block_chunked >= 10, "chunked cases: %d by vectors, %d by "
            "blocks", g_vector_chunked, g_block_chunked);
     EXPECT(g_xcd_launches >= 10, "XCD-affine launches: %d", g_xcd_launches);
+    EXPECT(g_wt_launches >= 10 && g_nt_launches >= 10,
+           "device-scope store launches: %d, nontemporal: %d", g_wt_launches, g_nt_launches);
     std::printf("schedule driver: %d cases (%d chunked by vectors, %d by blocks, %d launches "
-                "placed by XCD), %d failures%s\n", cases, g_vector_chunked, g_block_chunked,
-                g_xcd_launches, g_bad, g_bad ? "" : " ok");
+                "placed by XCD, %d with device-scope and %d with nontemporal stores), %d "
+                "failures%s\n", cases, g_vector_chunked, g_block_chunked, g_xcd_launches,
+                g_wt_launches, g_nt_launches, g_bad, g_bad ? "" : " ok");
     return g_bad ? 1 : 0;
 }

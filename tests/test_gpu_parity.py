@@ -369,6 +369,40 @@ def test_integer_chunked_schedule(dtype, n, batch):
         assert_exact(gim[b], im[b], n, False)
 
 
+# Multi-pass calls whose stores leave the plain form: passes before the last
+# store with device scope on states past the L2s (32 MiB) when their tiles
+# have at most 2^10 16-byte slots, and the last pass stores nontemporally on
+# states past the Infinity Cache (256 MiB).  The cases put every kernel
+# family in such a pass.
+STORE_CASES = [
+    ("f32", 18, (9, 9), 40, dict(wave=(0, 0))),       # LDS-tile row: device scope
+    ("f32", 18, (7, 11), 40, dict(wave=(1, 0))),      # wave-tile row: device scope
+    ("f32", 20, (10, 10), 40, dict(wave=(1, 0))),     # LDS-tile column: nontemporal
+    ("f32", 20, (12, 8), 40, dict(wave=(0, 1))),      # wave-tile column: nontemporal
+    ("f64", 18, (9, 9), 72, dict(wave=(0, 0))),       # both, fp64
+    ("f64", 20, (11, 9), 40, {}),                     # lane-exchange row and column
+    ("f64", 20, (8, 12), 20, dict(pipe=(0, 1), wave=(0, 0))),   # pipelined column
+    ("f32", 24, (8, 8, 8), 5, {}),                    # three passes on block chunks
+]
+
+
+@pytest.mark.parametrize("dtype,n,split,batch,kw", STORE_CASES)
+def test_integer_store_policies(dtype, n, split, batch, kw):
+    """Device-scope and nontemporal stores in every kernel family: each
+    vector exact against the oracle."""
+    say("stores %s n=%d split=%s batch=%d %s" % (dtype, n, split, batch, kw))
+    npd = np.float32 if dtype == "f32" else np.float64
+    plan = qse.Plan(n, dtype, split=split, **kw)
+    # fp32 results stay exact integers while |x| 2^n <= 2^24
+    lim = min(8, 1 << max(0, 24 - n)) if dtype == "f32" else 8
+    re = np.random.default_rng(87_000 + n).integers(-lim, lim + 1, (batch, 1 << n)).astype(npd)
+    im = np.random.default_rng(88_000 + n).integers(-lim, lim + 1, (batch, 1 << n)).astype(npd)
+    gre, gim = run(plan, re, im, False)
+    for b in range(batch):
+        assert_exact(gre[b], re[b], n, False)
+        assert_exact(gim[b], im[b], n, False)
+
+
 # ---- floating point, odd n and the normalisation -----------------------------
 
 @pytest.mark.parametrize("dtype,n", [("f32", n) for n in (3, 5, 11, 13, 15, 17, 19, 21, 23)] +
