@@ -184,7 +184,12 @@ int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
  * are then undefined).  Faults during execution surface at the caller's
  * next synchronisation of the stream.  The call only enqueues kernel
  * launches (no memsets, no allocation, no synchronisation), so it may be
- * captured into a HIP graph. */
+ * captured into a HIP graph.
+ * Cache hints (they change speed, never results): in a multi-pass plan the
+ * first pass loads nontemporally; the last pass stores nontemporally when
+ * the call's state exceeds 256 MiB (the chunked schedules); earlier passes
+ * store with device scope when the state exceeds 32 MiB and their tiles
+ * hold at most 2^10 16-byte slots; all other stores are plain. */
 int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im,
                 int normalize, hipStream_t stream);
 
@@ -222,7 +227,10 @@ int fwt_plan_call_schedule(fwt_plan_t plan, int64_t batch, int with_im, int* chu
  * in order on the same buffers and stream is exactly fwt_execute; the
  * factors commute, so any order gives the same transform up to rounding.
  * `normalize` takes effect only in the last pass.  Meant for per-kernel
- * timing and for interleaving passes with other work.  Returns as
+ * timing and for interleaving passes with other work.  The cache hints
+ * are fwt_execute's, with a state of 256 MiB or more taken as one chunk of
+ * a chunked call: running fwt_execute's chunk schedule pass by pass
+ * launches the same kernels with the same hints.  Returns as
  * fwt_execute, plus FWT_EINVAL for a pass index out of range. */
 int fwt_execute_pass(fwt_plan_t plan, int pass, int64_t batch, int n, void* re,
                      void* im, int normalize, hipStream_t stream);

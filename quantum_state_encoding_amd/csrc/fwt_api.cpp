@@ -792,25 +792,27 @@ size_t state_bytes(const fwt_plan_s* plan, int64_t batch, int ncomp)
            (size_t)ncomp;
 }
 
-// Cache policy of the stores of pass p in a call on a state of `bytes`.
-// Multi-pass plans only (one-pass plans store plainly).  From A/B timings
-// of the four combinations on 26 workloads from 8 MiB to 4 GiB:
-//  - the last pass stores nontemporally once the state exceeds the
-//    Infinity Cache (so a chunk's results leave room for the next chunk):
-//    -0.1 to -3.8 % per call; on smaller states the plain stores leave the
-//    results cached for the next call, and nontemporal ones cost 2-5 %;
+// Cache policy of the stores of pass p, in a call on a state of `bytes`
+// whose schedule is chunked or not.  Multi-pass plans only (one-pass plans
+// store plainly).  From A/B timings of the four combinations on 26
+// workloads from 8 MiB to 4 GiB:
+//  - the last pass stores nontemporally in chunked schedules (states past
+//    the Infinity Cache), so that a chunk's results leave room for the
+//    next chunk: -0.1 to -3.8 % per call; on smaller states the plain
+//    stores leave the results cached for the next call, and nontemporal
+//    ones cost 2-5 %;
 //  - an earlier pass stores with device scope once the state exceeds the
 //    L2s, when its tiles are at most 2^10 16-byte slots (the small row
 //    tiles, several per CU): 64-256 MiB states -0.8 to -8.7 %, 2 GiB
 //    states with such row tiles a further -1.1 to -1.6 %.  Within the L2s
 //    it costs 4-12 %, and with larger tiles (one or two per CU) it is
 //    0.5-2.5 % slower than plain stores.
-int store_policy(const Pass& p, bool multi, bool final_pass, size_t bytes)
+int store_policy(const Pass& p, bool multi, bool final_pass, size_t bytes, bool chunked)
 {
     if (!multi)
         return qse::kStorePlain;
     if (final_pass)
-        return bytes > kChunkBytes ? qse::kStoreNontemporal : qse::kStorePlain;
+        return chunked ? qse::kStoreNontemporal : qse::kStorePlain;
     return bytes > kL2Bytes && p.key.kr + p.gbits <= 10 ? qse::kStoreWriteThrough
                                                         : qse::kStorePlain;
 }
@@ -821,9 +823,9 @@ int store_policy(const Pass& p, bool multi, bool final_pass, size_t bytes)
 // first pass reads and the last pass writes with nontemporal hints: their
 // data is not reused by this call, while the intermediate data between
 // passes should stay in the caches.  The stores follow store_policy for
-// the call's whole state of call_bytes.
+// the call's whole state of call_bytes, in a chunked schedule or not.
 int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, void* re, void* im,
-                  int normalize, size_t call_bytes, hipStream_t stream,
+                  int normalize, size_t call_bytes, bool chunked, hipStream_t stream,
                   hipEvent_t start = nullptr, hipEvent_t stop = nullptr, int sub_bits = 0)
 {
     int cus = 1;
@@ -877,7 +879,7 @@ int launch_passes(fwt_plan_t plan, int first, int last, int64_t batch, int n, vo
             a.tt_bits = p.tt_bits;
             a.do_scale = do_scale;
             a.ld_nt = (multi && i == 0) ? 1 : 0;
-            a.st_policy = store_policy(p, multi, final_pass, call_bytes);
+            a.st_policy = store_policy(p, multi, final_pass, call_bytes, chunked);
             a.scale = plan->dtype == FWT_F64 ? c : (double)(float)c;
             // Persistent kernels: as many workgroups as the CUs hold at once.
             const int64_t per_cu = p.lds ? (int64_t)(kLdsMax / p.lds) : 1;
@@ -966,7 +968,8 @@ int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im, int n
     const Schedule s = call_schedule(plan, batch, im ? 2 : 1);
     const size_t bytes = state_bytes(plan, batch, im ? 2 : 1);
     if (s.chunked == 0)
-        return launch_passes(plan, 0, plan->npasses, batch, n, re, im, normalize, bytes, stream);
+        return launch_passes(plan, 0, plan->npasses, batch, n, re, im, normalize, bytes, false,
+                             stream);
     const int sub = n - s.block_bits;
     const int64_t blocks = batch << sub;
     const size_t block_bytes = ((size_t)1 << s.block_bits) * (plan->dtype == FWT_F64 ? 8 : 4);
@@ -974,14 +977,14 @@ int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im, int n
         const int64_t nb = blocks - b0 < s.blocks ? blocks - b0 : s.blocks;
         void* cre = (char*)re + (size_t)b0 * block_bytes;
         void* cim = im ? (char*)im + (size_t)b0 * block_bytes : nullptr;
-        const int r = launch_passes(plan, 0, s.chunked, nb, n, cre, cim, normalize, bytes,
+        const int r = launch_passes(plan, 0, s.chunked, nb, n, cre, cim, normalize, bytes, true,
                                     stream, nullptr, nullptr, sub);
         if (r != FWT_OK)
             return r;
     }
     if (s.chunked < plan->npasses)
         return launch_passes(plan, s.chunked, plan->npasses, batch, n, re, im, normalize, bytes,
-                             stream);
+                             true, stream);
     return FWT_OK;
 }
 
@@ -994,8 +997,9 @@ int fwt_execute_pass(fwt_plan_t plan, int pass, int64_t batch, int n, void* re, 
     const int rc = validate(plan, batch, n, re, im, &nothing);
     if (rc != FWT_OK || nothing)
         return rc;
-    return launch_passes(plan, pass, pass + 1, batch, n, re, im, normalize,
-                         state_bytes(plan, batch, im ? 2 : 1), stream);
+    const size_t bytes = state_bytes(plan, batch, im ? 2 : 1);
+    return launch_passes(plan, pass, pass + 1, batch, n, re, im, normalize, bytes,
+                         bytes >= kChunkBytes, stream);
 }
 
 int fwt_execute_pass_timed(fwt_plan_t plan, int pass, int64_t batch, int n, void* re, void* im,
@@ -1007,8 +1011,9 @@ int fwt_execute_pass_timed(fwt_plan_t plan, int pass, int64_t batch, int n, void
     const int rc = validate(plan, batch, n, re, im, &nothing);
     if (rc != FWT_OK || nothing)
         return rc == FWT_OK ? FWT_EINVAL : rc;   // nothing to time
-    return launch_passes(plan, pass, pass + 1, batch, n, re, im, normalize,
-                         state_bytes(plan, batch, im ? 2 : 1), stream, start, stop);
+    const size_t bytes = state_bytes(plan, batch, im ? 2 : 1);
+    return launch_passes(plan, pass, pass + 1, batch, n, re, im, normalize, bytes,
+                         bytes >= kChunkBytes, stream, start, stop);
 }
 
 int fwt_plan_chunk_vectors(fwt_plan_t plan, int64_t batch, int with_im, int64_t* out)

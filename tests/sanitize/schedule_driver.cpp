@@ -190,13 +190,16 @@ void check_case(fwt_plan_t plan, int n, fwt_dtype dt, int64_t batch, bool with_i
             EXPECT(L.a.scale == want_c, "scale value n=%d", n);
         }
         EXPECT(L.a.ld_nt == (np > 1 && i == 0 ? 1 : 0), "nontemporal loads, pass %d", i);
-        // Stores of a multi-pass plan: the last pass nontemporal once the
-        // call's state exceeds 256 MiB; earlier passes with device scope
-        // once it exceeds 32 MiB, if their tiles have at most 2^10 slots.
+        // Stores of a multi-pass plan: the last pass nontemporal in chunked
+        // schedules (states past 256 MiB); earlier passes with device scope
+        // once the state exceeds 32 MiB, if their tiles have at most 2^10
+        // slots.
         const size_t bytes = (size_t)batch * (size_t)N * esize * (with_im ? 2 : 1);
+        EXPECT(np < 2 || (chunked != 0) == (bytes > ((size_t)256 << 20)),
+               "multi-pass calls chunked past 256 MiB");
         const int want_st =
             np < 2 ? qse::kStorePlain
-            : last ? (bytes > ((size_t)256 << 20) ? qse::kStoreNontemporal : qse::kStorePlain)
+            : last ? (chunked ? qse::kStoreNontemporal : qse::kStorePlain)
                    : (bytes > ((size_t)32 << 20) && p.kr + p.gbits <= 10 ? qse::kStoreWriteThrough
                                                                         : qse::kStorePlain);
         EXPECT(L.a.st_policy == want_st, "store policy %d, want %d, pass %d", L.a.st_policy,
@@ -274,11 +277,58 @@ void check_case(fwt_plan_t plan, int n, fwt_dtype dt, int64_t batch, bool with_i
     }
 }
 
+// The cache hints of single-pass calls: fwt_execute's, with a state of
+// 256 MiB or more taken as one chunk of a chunked call.
+void check_pass_hints()
+{
+    fwt_plan_t plan = nullptr;
+    EXPECT(fwt_plan_create(&plan, 20, FWT_F32, FWT_PATH_AUTO) == FWT_OK, "plan n=20");
+    int np = 0;
+    fwt_plan_num_passes(plan, &np);
+    EXPECT(np == 2, "n=20 passes %d", np);
+    const size_t vec = (size_t)4 << 20;   // one fp32 component of 2^20
+    const uintptr_t A = (uintptr_t)1 << 44, B = A + 32 * vec + 4096;
+    g_ranges.assign({Range{A, 32 * vec}, Range{B, 32 * vec}});
+    hipEvent_t ev = reinterpret_cast<hipEvent_t>(&g_bad);   // never dereferenced
+    struct Want {
+        int pass;
+        int64_t batch;
+        bool timed;
+        int policy;
+    } const wants[] = {
+        {1, 32, false, qse::kStoreNontemporal},   // 256 MiB: a chunk of a larger call
+        {1, 32, true, qse::kStoreNontemporal},
+        {1, 31, false, qse::kStorePlain},
+        {0, 32, true, qse::kStoreWriteThrough},   // 12-bit row tiles of 2^10 slots
+        {0, 2, false, qse::kStorePlain},          // 16 MiB: within the L2s
+    };
+    for (const Want& w : wants) {
+        g_launches.clear();
+        const int rc = w.timed ? fwt_execute_pass_timed(plan, w.pass, w.batch, 20, (void*)A,
+                                                        (void*)B, 1, nullptr, ev, ev)
+                               : fwt_execute_pass(plan, w.pass, w.batch, 20, (void*)A, (void*)B,
+                                                  1, nullptr);
+        EXPECT(rc == FWT_OK && g_launches.size() == 1, "pass %d batch %lld rc %d", w.pass,
+               (long long)w.batch, rc);
+        if (rc == FWT_OK && g_launches.size() == 1)
+            EXPECT(g_launches[0].a.st_policy == w.policy, "pass %d batch %lld policy %d, want %d",
+                   w.pass, (long long)w.batch, g_launches[0].a.st_policy, w.policy);
+    }
+    // the whole 256 MiB call is not chunked: its last pass stores plainly
+    g_launches.clear();
+    EXPECT(fwt_execute(plan, 32, 20, (void*)A, (void*)B, 1, nullptr) == FWT_OK &&
+               g_launches.size() == 2 && g_launches[1].a.st_policy == qse::kStorePlain &&
+               g_launches[0].a.st_policy == qse::kStoreWriteThrough,
+           "fwt_execute on 256 MiB");
+    fwt_plan_destroy(plan);
+}
+
 }  // namespace
 
 int main()
 {
     qse::g_tile_launch_hook = record;
+    check_pass_hints();
     int cases = 0;
     const size_t cache = (size_t)256 << 20;
     for (int d = 0; d <= 1; ++d) {
