@@ -193,6 +193,60 @@ int fwt_plan_create_tuned(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses,
 int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im,
                 int normalize, hipStream_t stream);
 
+/* ---- One HBM pass on a caller's workspace --------------------------------
+ * The Kronecker split H_20 = H_5 (x) H_15 (the pull request's sections "Why"
+ * and "How"; the iThome article's "Kronecker block GEMM idea") done in a
+ * single read and write of the state: each vector component (4 MiB) is
+ * transformed by a group of 32 workgroups on one XCD, one per CU, which
+ * apply the 15-bit factor to the rows they hold in registers, exchange the
+ * rows through a ring buffer that stays in the XCD's 4 MB L2, and apply the
+ * 5-bit factor to the columns.  It serves default (FWT_PATH_AUTO) fp32
+ * n = 20 plans on a device of 8 XCDs x 32 CUs (MI355X) where two of its
+ * workgroups fit one CU; every other call runs fwt_execute's passes.
+ *
+ * fwt_workspace_size: *bytes = the workspace a call of `plan` on `batch`
+ * vectors (with_im != 0: both components) needs for the one-pass kernel
+ * (about 16 MiB), or 0 when such a call runs fwt_execute's passes (another
+ * plan, batch 0, an unsupported device).  Returns FWT_OK, FWT_EINVAL (null
+ * argument, batch < 0) or FWT_EHIP (the device could not be queried).
+ *
+ * fwt_execute_ws: the transform of fwt_execute, same arguments and
+ * validation, with `ws` a device buffer of `ws_bytes` (caller-owned,
+ * 256-byte aligned, inside one device allocation, overlapping neither re
+ * nor im).  When fwt_workspace_size is 0, `ws` is ignored (it may be NULL)
+ * and this is exactly fwt_execute.  Otherwise it enqueues two kernels: one
+ * workgroup that clears the workspace's 8 KiB header (a kernel, not a
+ * memset, so the call may be captured into a HIP graph), and the
+ * transform.  Statuses as fwt_execute, plus FWT_EINVAL for a missing or too
+ * small workspace or one that overlaps the state, FWT_EALIGN for a
+ * misaligned one.  Results equal fwt_execute's within rounding (bit for
+ * bit on small-integer inputs; the sums are associated differently).  Two
+ * calls that share a workspace must not run at the same time (each call
+ * uses all of it); calls on different workspaces may.  The kernel needs
+ * all of its 512 workgroups resident together: a concurrent kernel that
+ * holds CUs delays it, and its waits are bounded (about a second), after
+ * which it records an error and the result is undefined.
+ *
+ * fwt_execute_ws_timed: fwt_execute_ws with `start` and `stop` recorded by
+ * the dispatch of the transform kernel itself (its duration without launch
+ * gaps).  FWT_EINVAL for null events or a call that would not run the
+ * one-pass kernel.
+ *
+ * fwt_workspace_status: *bits = the error bits the last one-pass call on
+ * `ws` recorded (0: none; 1: a wait for the group's progress ran out,
+ * 2: an XCD received more workgroups than its two groups hold, 4: a wait
+ * for the next component's index ran out; any of them means the result is
+ * undefined).  Reads device memory synchronously: call it after the
+ * stream that ran the call has been synchronised.  Returns FWT_OK,
+ * FWT_EINVAL (null argument) or FWT_EHIP. */
+int fwt_workspace_size(fwt_plan_t plan, int64_t batch, int with_im, size_t* bytes);
+int fwt_execute_ws(fwt_plan_t plan, int64_t batch, int n, void* re, void* im, int normalize,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+int fwt_execute_ws_timed(fwt_plan_t plan, int64_t batch, int n, void* re, void* im,
+                         int normalize, void* ws, size_t ws_bytes, hipStream_t stream,
+                         hipEvent_t start, hipEvent_t stop);
+int fwt_workspace_status(const void* ws, int* bits);
+
 /* Vectors per chunk that fwt_execute uses for a call on `batch` vectors
  * (with_im != 0: both components): a multi-pass call whose state exceeds
  * the 256 MiB Infinity Cache runs every pass on one chunk of vectors before

@@ -22,7 +22,7 @@ __all__ = ["Plan", "FwtError", "execute", "stream_copy", "library_path", "load_l
            "PATH_AUTO", "PATH_SINGLE_BLOCK", "PATH_MULTIPASS", "PATH_MFMA_ABLATION",
            "FWT_OK", "FWT_EINVAL", "FWT_EALIGN", "FWT_EUNSUPPORTED", "FWT_EHIP",
            "FWT_ENOMEM", "FWT_ESCRATCH", "STATIC_SCRATCH_BYTES", "ablation_execute_static",
-           "EXPORTED_SYMBOLS"]
+           "EXPORTED_SYMBOLS", "workspace_status"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfwt.so")
@@ -36,7 +36,8 @@ _DTYPES = {"f32": 0, "f64": 1}
 # Every symbol include/fwt.h declares.
 EXPORTED_SYMBOLS = ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create_tuned",
                     "fwt_execute", "fwt_execute_pass", "fwt_execute_pass_timed",
-                    "fwt_execute_check",
+                    "fwt_execute_check", "fwt_workspace_size", "fwt_execute_ws",
+                    "fwt_execute_ws_timed", "fwt_workspace_status",
                     "fwt_plan_num_passes", "fwt_plan_pass_config", "fwt_plan_call_pass_config",
                     "fwt_plan_pass_bits",
                     "fwt_plan_destroy", "fwt_strerror", "fwt_last_hip_error",
@@ -103,7 +104,13 @@ def load_library():
     lib.fwt_ablation_workspace.argtypes = [i32, i64, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.fwt_ablation_execute.argtypes = [i32, i64, i32, i32, vp, vp, i32, vp, ctypes.c_size_t, vp]
     lib.fwt_ablation_execute_static.argtypes = [i32, i64, i32, i32, vp, vp, i32, vp]
-    for name in ("fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create_tuned",
+    lib.fwt_workspace_size.argtypes = [vp, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fwt_execute_ws.argtypes = [vp, i64, i32, vp, vp, i32, vp, ctypes.c_size_t, vp]
+    lib.fwt_execute_ws_timed.argtypes = [vp, i64, i32, vp, vp, i32, vp, ctypes.c_size_t, vp,
+                                         vp, vp]
+    lib.fwt_workspace_status.argtypes = [vp, pi]
+    for name in ("fwt_workspace_size", "fwt_execute_ws", "fwt_execute_ws_timed",
+                 "fwt_workspace_status", "fwt_plan_create", "fwt_plan_create_split", "fwt_plan_create_tuned",
                  "fwt_execute", "fwt_execute_pass", "fwt_execute_pass_timed",
                  "fwt_execute_check", "fwt_plan_num_passes", "fwt_plan_pass_bits",
                  "fwt_plan_pass_config", "fwt_plan_call_pass_config", "fwt_plan_destroy",
@@ -249,6 +256,72 @@ class Plan:
             raise FwtError(st, "fwt_execute")
         return re, im
 
+    def workspace_size(self, batch, with_im=True):
+        """Bytes of workspace execute_ws needs for `batch` vectors: 0 when
+        the call runs fwt_execute's passes (see fwt_workspace_size)."""
+        out = ctypes.c_size_t()
+        st = load_library().fwt_workspace_size(self._h, int(batch), 1 if with_im else 0,
+                                                ctypes.byref(out))
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_workspace_size")
+        return out.value
+
+    def execute_ws(self, re, im=None, normalize=True, workspace=None, stream=None):
+        """fwt_execute_ws on torch tensors: the one-pass kernel on a device
+        workspace (a uint8 tensor of workspace_size bytes) where it applies,
+        otherwise fwt_execute."""
+        batch = self._check_tensors(re, im)
+        wp, wb = _workspace_args(workspace)
+        st = load_library().fwt_execute_ws(
+            self._h, batch, self.n, ctypes.c_void_p(re.data_ptr()),
+            ctypes.c_void_p(im.data_ptr() if im is not None else None), 1 if normalize else 0,
+            wp, wb, _stream_handle(stream))
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_execute_ws")
+        return re, im
+
+    def execute_ws_timed(self, re, im, workspace, start, stop, normalize=True, stream=None):
+        """execute_ws with torch events recorded by the transform kernel's
+        dispatch (see fwt_execute_ws_timed)."""
+        import torch
+        batch = self._check_tensors(re, im)
+        s = torch.cuda.current_stream() if stream is None else stream
+        for ev in (start, stop):
+            if not ev.cuda_event:
+                ev.record(s)
+        wp, wb = _workspace_args(workspace)
+        st = load_library().fwt_execute_ws_timed(
+            self._h, batch, self.n, ctypes.c_void_p(re.data_ptr()),
+            ctypes.c_void_p(im.data_ptr() if im is not None else None), 1 if normalize else 0,
+            wp, wb, ctypes.c_void_p(s.cuda_stream), ctypes.c_void_p(start.cuda_event),
+            ctypes.c_void_p(stop.cuda_event))
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_execute_ws_timed")
+
+    def bind_ws(self, re, im=None, normalize=True, workspace=None, stream=None):
+        """bind() for execute_ws: a zero-argument callable with the
+        arguments marshalled once; it keeps the plan, the tensors and the
+        workspace alive."""
+        batch = self._check_tensors(re, im)
+        lib = load_library()
+        rp = ctypes.c_void_p(re.data_ptr())
+        ip = ctypes.c_void_p(im.data_ptr() if im is not None else None)
+        st = lib.fwt_execute_check(self._h, batch, self.n, rp, ip)
+        if st != FWT_OK:
+            raise FwtError(st, "fwt_execute_check")
+        wp, wb = _workspace_args(workspace)
+        fn = lib.fwt_execute_ws
+        args = (self._h, batch, self.n, rp, ip, 1 if normalize else 0, wp, wb,
+                _stream_handle(stream))
+
+        def call():
+            st = fn(*args)
+            if st != FWT_OK:
+                raise FwtError(st, "fwt_execute_ws")
+        call.plan = self
+        call.tensors = (re, im, workspace)
+        return call
+
     def chunk_vectors(self, batch, with_im=True):
         """Vectors per chunk fwt_execute uses for `batch` vectors (0 = none)."""
         out = ctypes.c_int64()
@@ -344,6 +417,27 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def _workspace_args(workspace):
+    """(pointer, bytes) of a workspace tensor, or (NULL, 0) for None."""
+    if workspace is None:
+        return ctypes.c_void_p(None), 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("the workspace must be a contiguous device tensor")
+    return (ctypes.c_void_p(workspace.data_ptr()),
+            workspace.numel() * workspace.element_size())
+
+
+def workspace_status(workspace):
+    """Error bits the last one-pass call on `workspace` recorded (0: none);
+    synchronise the stream that ran it first (see fwt_workspace_status)."""
+    out = ctypes.c_int()
+    st = load_library().fwt_workspace_status(ctypes.c_void_p(workspace.data_ptr()),
+                                             ctypes.byref(out))
+    if st != FWT_OK:
+        raise FwtError(st, "fwt_workspace_status")
+    return out.value
 
 
 def execute(re, im=None, n=None, normalize=True, stream=None, path=PATH_AUTO):

@@ -78,6 +78,9 @@ struct fwt_plan_s {
     // call's state fits the Infinity Cache (has_small != 0).
     int has_small;
     Pass small;
+    // Default fp32 n = 20 plans: fwt_execute_ws may run the whole transform
+    // as one HBM pass (the group-of-workgroups kernel) on a workspace.
+    int onepass;
 };
 
 namespace {
@@ -586,6 +589,7 @@ int make_plan(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* b
     // 6.28 us), equal at 256 MiB, and 4-5 % slower at 384-512 MiB, where the
     // extra threads keep more HBM reads in flight.
     p->has_small = 0;
+    p->onepass = 0;
     const bool pass0_default =
         !tuning || (tuning[0].eb < 0 && tuning[0].gbits < 0 && tuning[0].phases < 0 &&
                     tuning[0].pipe < 0 && tuning[0].wave < 0);
@@ -622,6 +626,7 @@ constexpr int kMaxDevices = 64;
 std::mutex g_init_mutex;
 std::atomic<uint64_t> g_init_devices{0};
 int g_cu_count[kMaxDevices];
+int g_onepass_ok[kMaxDevices];
 
 // Once per device: kernel attributes and the compute-unit count.  Returns
 // the CU count of the current device in *cus.
@@ -644,11 +649,29 @@ int ensure_device_init(int* cus)
             if (e != hipSuccess)
                 return hip_fail(e);
             g_cu_count[dev] = n > 0 ? n : 1;
+            // The one-pass kernel needs all kOpGroups * kOpMembers workgroups
+            // resident at once: 8 XCDs of 32 CUs, two workgroups per CU.
+            int per_cu = 0;
+            e = qse::onepass_occupancy(&per_cu);
+            if (e != hipSuccess)
+                return hip_fail(e);
+            g_onepass_ok[dev] = (n == qse::kOpXcds * qse::kOpMembers &&
+                                 per_cu >= qse::kOpGroupsPerXcd) ? 1 : 0;
             g_init_devices.fetch_or((uint64_t)1 << dev, std::memory_order_release);
         }
     }
     *cus = g_cu_count[dev];
     return FWT_OK;
+}
+
+// Whether the one-pass kernel can run on the current device (after
+// ensure_device_init).
+bool onepass_device_ok()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return false;
+    return g_onepass_ok[dev] != 0;
 }
 
 // The buffer must be device-visible memory holding [ptr, ptr + bytes).
@@ -938,7 +961,10 @@ int fwt_plan_create(fwt_plan_t* out, int n, fwt_dtype dtype, fwt_path path)
     const int np = default_split(n, dtype, path, bits);
     if (np < 0)
         return FWT_EUNSUPPORTED;
-    return make_plan(out, n, dtype, np, bits, nullptr);
+    const int rc = make_plan(out, n, dtype, np, bits, nullptr);
+    if (rc == FWT_OK && path == FWT_PATH_AUTO && n == qse::kOpN && dtype == FWT_F32)
+        (*out)->onepass = 1;
+    return rc;
 }
 
 int fwt_plan_create_split(fwt_plan_t* out, int n, fwt_dtype dtype, int npasses, const int* bits)
@@ -1014,6 +1040,106 @@ int fwt_execute_pass_timed(fwt_plan_t plan, int pass, int64_t batch, int n, void
     const size_t bytes = state_bytes(plan, batch, im ? 2 : 1);
     return launch_passes(plan, pass, pass + 1, batch, n, re, im, normalize, bytes,
                          bytes >= kChunkBytes, stream, start, stop);
+}
+
+// ---- one HBM pass on a workspace (fp32 n = 20) -------------------------------
+
+namespace {
+
+// Workspace bytes a call of `plan` on `batch` vectors needs for the one-pass
+// kernel, or 0 when the call runs fwt_execute's passes.  *rc receives an
+// FWT_* status (FWT_EHIP when the device cannot be queried).
+size_t onepass_bytes(fwt_plan_t plan, int64_t batch, int with_im, int* rc)
+{
+    *rc = FWT_OK;
+    if (!plan->onepass || batch <= 0)
+        return 0;
+    const int64_t ncomp = batch * (with_im ? 2 : 1);
+    if (ncomp >= ((int64_t)1 << 30))
+        return 0;
+    int cus = 0;
+    *rc = ensure_device_init(&cus);
+    if (*rc != FWT_OK || !onepass_device_ok())
+        return 0;
+    return qse::kOpWorkspaceBytes;
+}
+
+int execute_ws(fwt_plan_t plan, int64_t batch, int n, void* re, void* im, int normalize,
+               void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t start,
+               hipEvent_t stop)
+{
+    bool nothing = false;
+    int rc = validate(plan, batch, n, re, im, &nothing);
+    if (rc != FWT_OK || nothing)
+        return rc;
+    const size_t need = onepass_bytes(plan, batch, im != nullptr, &rc);
+    if (rc != FWT_OK)
+        return rc;
+    if (need == 0)
+        return fwt_execute(plan, batch, n, re, im, normalize, stream);
+    if (!ws || ws_bytes < need)
+        return FWT_EINVAL;
+    if ((uintptr_t)ws & 255u)
+        return FWT_EALIGN;
+    const size_t bytes = (size_t)batch << (n + 2);
+    const uintptr_t w = (uintptr_t)ws;
+    for (const void* b : {(const void*)re, (const void*)im}) {
+        const uintptr_t a = (uintptr_t)b;
+        if (b && ((a <= w && w - a < bytes) || (w < a && a - w < need)))
+            return FWT_EINVAL;
+    }
+    rc = check_range(ws, need);
+    if (rc != FWT_OK)
+        return rc;
+    const int ncomp = (int)(batch * (im ? 2 : 1));
+    const float scale = normalize ? (float)norm_constant(n) : 1.0f;
+    const hipError_t e = qse::launch_onepass((float*)re, (float*)im, ncomp, ws, scale, stream,
+                                             start, stop);
+    return e == hipSuccess ? FWT_OK : hip_fail(e);
+}
+
+}  // namespace
+
+int fwt_workspace_size(fwt_plan_t plan, int64_t batch, int with_im, size_t* bytes)
+{
+    if (!valid_plan(plan) || !bytes || batch < 0)
+        return FWT_EINVAL;
+    *bytes = 0;
+    int rc = FWT_OK;
+    *bytes = onepass_bytes(plan, batch, with_im, &rc);
+    return rc;
+}
+
+int fwt_execute_ws(fwt_plan_t plan, int64_t batch, int n, void* re, void* im, int normalize,
+                   void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    return execute_ws(plan, batch, n, re, im, normalize, ws, ws_bytes, stream, nullptr,
+                      nullptr);
+}
+
+int fwt_execute_ws_timed(fwt_plan_t plan, int64_t batch, int n, void* re, void* im,
+                         int normalize, void* ws, size_t ws_bytes, hipStream_t stream,
+                         hipEvent_t start, hipEvent_t stop)
+{
+    if (!start || !stop || !valid_plan(plan))
+        return FWT_EINVAL;
+    int rc = FWT_OK;
+    const size_t need = onepass_bytes(plan, batch, im != nullptr, &rc);
+    if (rc != FWT_OK)
+        return rc;
+    if (need == 0)
+        return FWT_EINVAL;   // only the one-pass kernel is timed here
+    return execute_ws(plan, batch, n, re, im, normalize, ws, ws_bytes, stream, start, stop);
+}
+
+int fwt_workspace_status(const void* ws, int* bits)
+{
+    if (!ws || !bits)
+        return FWT_EINVAL;
+    *bits = 0;
+    const hipError_t e = hipMemcpy(bits, (const unsigned char*)ws + qse::kOpErrOff, sizeof(int),
+                                   hipMemcpyDeviceToHost);
+    return e == hipSuccess ? FWT_OK : hip_fail(e);
 }
 
 int fwt_plan_chunk_vectors(fwt_plan_t plan, int64_t batch, int with_im, int64_t* out)

@@ -179,4 +179,48 @@ int hip_status(hipError_t e);
 // Workspace bytes ablation `kind` needs (0 if none).
 size_t ablation_workspace_size(int kind, int64_t batch, int n, int dtype, int with_im);
 
+// ---- One-pass transform of fp32 n = 20 states (fwt_kernels.hip) ----
+// Each vector component (2^20 floats, 4 MiB) is transformed by one group
+// of 32 workgroups on one XCD, one workgroup per CU, with the state read
+// from and written to HBM once.  Each workgroup holds a 2^15-element row
+// block in registers and applies the factor on the 15 low bits; the group
+// then exchanges the blocks through a ring in its XCD's L2 (kOpSlices
+// slices, kOpRingSlots slots) and each workgroup applies the factor on the
+// 5 high bits to its 2^10-column slice.  Two groups share each XCD and take
+// components from a per-XCD queue.  The caller's workspace holds the ring
+// and the synchronisation words; the first 32-bit word collects error bits
+// (kOpErr*) of the call.
+constexpr int kOpN = 20;
+constexpr int kOpXcds = 8;
+constexpr int kOpMembers = 32;          // workgroups per group (CUs per XCD)
+constexpr int kOpGroupsPerXcd = 2;
+constexpr int kOpGroups = kOpXcds * kOpGroupsPerXcd;
+constexpr int kOpThreads = 512;
+constexpr int kOpSlices = 8;
+constexpr int kOpRingSlots = 2;
+constexpr size_t kOpSlotBytes = ((size_t)4 << 20) / kOpSlices;   // one slice of a component
+constexpr size_t kOpErrOff = 0;          // int: error bits
+constexpr size_t kOpQueueOff = 256;      // int[kOpXcds]: components taken per XCD
+constexpr size_t kOpArriveOff = 384;     // int[kOpXcds]: workgroups that found themselves on each XCD
+constexpr size_t kOpNextOff = 512;       // uint64[kOpGroups][2]: (sequence << 32) | next index
+constexpr size_t kOpFlagOff = 1024;      // int[kOpGroups][64]: slices written, slices read
+constexpr size_t kOpHeaderBytes = 8192;  // the words above, cleared by each call
+constexpr size_t kOpWorkspaceBytes =
+    kOpHeaderBytes + (size_t)kOpGroups * kOpRingSlots * kOpSlotBytes;
+constexpr size_t kOpLdsBytes = 64 * 1024;
+enum : int {
+    kOpErrTimeout = 1,     // a wait for the group's progress words ran out
+    kOpErrPlacement = 2,   // more workgroups on one XCD than its groups hold
+    kOpErrQueue = 4,       // a wait for the next component's index ran out
+};
+// Workgroups of the one-pass kernel that fit one CU at once (0 if it cannot
+// run on the current device).
+hipError_t onepass_occupancy(int* blocks_per_cu);
+// Enqueue a call: clear the workspace header, then the transform of
+// `ncomp` components (re: components 0, 2, 4, ... when im is given, else
+// 0, 1, 2, ...).  start/stop (may be null) are recorded at the transform
+// kernel's start and end by the dispatch itself.
+hipError_t launch_onepass(float* re, float* im, int ncomp, void* ws, float scale,
+                          hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 }  // namespace qse

@@ -595,3 +595,36 @@ def test_static_ablation_validation_before_any_hip_call(lib):
     assert ex(mt, 1, 15, 0, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_EUNSUPPORTED
     assert ex(pg, 0, 10, 0, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_OK
     assert ex(qse.ABLATION_STAGEWISE, 0, 10, 0, FAKE, FAKE + 4 * N, 1, None) == qse.FWT_OK
+
+
+def test_workspace_entry_points_reject_before_any_hip_call(lib, plan10):
+    """The one-pass entry points check their arguments before touching the
+    device: null plan or workspace pointers, negative batches, null events
+    and the base validation of fwt_execute all fail without a GPU."""
+    import ctypes
+    N = 1 << 10
+    out = ctypes.c_size_t(7)
+    bits = ctypes.c_int(3)
+    h = plan10.handle
+    assert lib.fwt_workspace_size(None, 1, 1, ctypes.byref(out)) == qse.FWT_EINVAL
+    assert lib.fwt_workspace_size(h, -1, 1, ctypes.byref(out)) == qse.FWT_EINVAL
+    assert lib.fwt_workspace_size(h, 1, 1, None) == qse.FWT_EINVAL
+    # a plan other than fp32 n = 20 never uses a workspace; no device query
+    assert lib.fwt_workspace_size(h, 4, 1, ctypes.byref(out)) == qse.FWT_OK
+    assert out.value == 0
+    p20 = qse.Plan(20, "f32", split=(10, 10))
+    assert lib.fwt_workspace_size(p20.handle, 4, 1, ctypes.byref(out)) == qse.FWT_OK
+    assert out.value == 0
+    for dt in ("f64",):
+        p = qse.Plan(20, dt)
+        assert lib.fwt_workspace_size(p.handle, 4, 1, ctypes.byref(out)) == qse.FWT_OK
+        assert out.value == 0
+    ws = lambda *a: lib.fwt_execute_ws(*a)
+    assert ws(None, 1, 10, FAKE, FAKE + 4 * N, 1, FAKE + (1 << 20), 1 << 24, None) == qse.FWT_EINVAL
+    assert ws(h, 1, 10, FAKE + 4, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EALIGN
+    assert ws(h, 2, 10, FAKE, FAKE + 4 * N, 1, None, 0, None) == qse.FWT_EINVAL   # overlap
+    assert ws(h, 0, 10, FAKE, FAKE + 16, 1, None, 0, None) == qse.FWT_OK          # no-op
+    timed = lib.fwt_execute_ws_timed
+    assert timed(h, 1, 10, FAKE, FAKE + 4 * N, 1, None, 0, None, None, None) == qse.FWT_EINVAL
+    assert lib.fwt_workspace_status(None, ctypes.byref(bits)) == qse.FWT_EINVAL
+    assert lib.fwt_workspace_status(FAKE, None) == qse.FWT_EINVAL
