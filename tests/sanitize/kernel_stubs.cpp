@@ -59,5 +59,14 @@ hipError_t ablation_mfma_row(int, void*, void*, int64_t, int, int, int, double, 
 {
     return hipErrorNotSupported;
 }
+hipError_t onepass_occupancy(int* blocks_per_cu)
+{
+    *blocks_per_cu = 2;
+    return hipSuccess;
+}
+hipError_t launch_onepass(float*, float*, int, void*, float, hipStream_t, hipEvent_t, hipEvent_t)
+{
+    return hipErrorNotSupported;
+}
 
 }  // namespace qse

@@ -55,6 +55,7 @@ hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* d)
 }
 hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
 hipError_t hipGetLastError(void) { return hipSuccess; }
+hipError_t hipMemcpy(void*, const void*, size_t, hipMemcpyKind) { return hipErrorNotSupported; }
 hipError_t hipMemGetAddressRange(hipDeviceptr_t* base, size_t* size, hipDeviceptr_t p)
 {
     const uintptr_t a = (uintptr_t)p;
