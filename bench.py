@@ -39,6 +39,7 @@ CONFIGS = ((1, "n10_b8_f32_int", "configured"),
            (3, "n14_b64_f32", "configured"),
            (3, "n14_b64_f32", None),
            (4, "n20_b256_f32", "configured"),
+           (4, "n20_b256_f32", "two-pass"),
            (5, "n24_b16_f64", "configured"))
 LARGE = ("n20_b256_f32", "n24_b16_f64")      # HBM-sized states: full per-pass record
 TOL = {"f32": 1e-5, "f64": 1e-12}            # max |err| / ||x||_2 against the fp64 oracle
@@ -242,23 +243,41 @@ def gpu_workload(torch, w, steps, warmup, split="configured", full=False, keep_o
     workloads.gen(w, hre.numpy(), him.numpy())
     re = hre.to(dev)
     im = him.to(dev)
-    sp = (w.split or None) if split == "configured" else split
+    two_pass = split == "two-pass"
+    sp = (w.split or None) if split == "configured" else (None if two_pass else split)
     plan = qse.Plan(w.n, w.dtype, split=sp)
     stream = torch.cuda.current_stream()
-    passes = plan.num_passes
+    # The default fp32 n = 20 plan runs as one HBM pass on a workspace
+    # (fwt_execute_ws); "two-pass" times fwt_execute's passes instead.
+    ws_bytes = 0 if two_pass else plan.workspace_size(w.batch)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    passes = 1 if ws is not None else plan.num_passes
+
+    def bind(stream=None):
+        if ws is not None:
+            return plan.bind_ws(re, im, normalize=w.normalize, workspace=ws, stream=stream)
+        return plan.bind(re, im, normalize=w.normalize, stream=stream)
+
+    def check_ws():
+        if ws is not None:
+            torch.cuda.synchronize()
+            bits = qse.workspace_status(ws)
+            if bits:
+                raise RuntimeError("one-pass kernel recorded error bits %d" % bits)
 
     # The GPU's output of one call from the pristine input (for the
     # oracle comparison of the CPU leg).
     output = inputs = None
     if keep_output:
-        plan.execute(re, im, normalize=w.normalize)
+        bind()()
         torch.cuda.synchronize()
+        check_ws()
         output = (re.cpu().numpy(), im.cpu().numpy())
         inputs = (hre.numpy(), him.numpy())
         re.copy_(hre)
         im.copy_(him)
 
-    step = plan.bind(re, im, normalize=w.normalize)
+    step = bind()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -289,7 +308,7 @@ def gpu_workload(torch, w, steps, warmup, split="configured", full=False, keep_o
             gs = torch.cuda.Stream()
             gs.wait_stream(stream)
             with torch.cuda.stream(gs):
-                gstep = plan.bind(re, im, normalize=w.normalize, stream=gs)
+                gstep = bind(stream=gs)
                 gstep()
                 gs.synchronize()
                 graph = torch.cuda.CUDAGraph()
@@ -304,14 +323,27 @@ def gpu_workload(torch, w, steps, warmup, split="configured", full=False, keep_o
         except RuntimeError as e:        # supplementary figure: report and go on
             log("graph replay timing of %s skipped: %s" % (w.name, e))
             torch.cuda.synchronize()
-    per_pass, chunk, check, copy_ms = [], plan.chunk_vectors(w.batch, True) or w.batch, None, None
+    check_ws()
+    chunk = w.batch if ws is not None else (plan.chunk_vectors(w.batch, True) or w.batch)
+    per_pass, check, copy_ms = [], None, None
+    if full and ws is not None:
+        # The one-pass kernel timed by the events its own dispatch records.
+        evs = []
+        for _ in range(min(k, 50)):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            plan.execute_ws_timed(re, im, ws, a, b, normalize=w.normalize)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        check_ws()
+        per_pass = [sum(a.elapsed_time(b) for a, b in evs) / len(evs)]
     if full:
         # Per-kernel durations: the schedule fwt_execute runs (all passes of
         # one chunk of vectors, chunk after chunk), each kernel timed by HIP
         # events that its own dispatch records at its start and end;
         # averaged per pass.
         evs = []
-        for _ in range(min(k, 50)):
+        for _ in range(min(k, 50) if ws is None else 0):
             for c0 in range(0, w.batch, chunk):
                 sl = slice(c0, min(w.batch, c0 + chunk))
                 for i in range(passes):
@@ -320,11 +352,12 @@ def gpu_workload(torch, w, steps, warmup, split="configured", full=False, keep_o
                     plan.execute_pass_timed(i, re[sl], im[sl], a, b, normalize=w.normalize)
                     evs.append((i, a, b))
         torch.cuda.synchronize()
-        tot, cnt = [0.0] * passes, [0] * passes
-        for i, a, b in evs:
-            tot[i] += a.elapsed_time(b)
-            cnt[i] += 1
-        per_pass = [tot[i] / cnt[i] for i in range(passes)]
+        if ws is None:
+            tot, cnt = [0.0] * passes, [0] * passes
+            for i, a, b in evs:
+                tot[i] += a.elapsed_time(b)
+                cnt[i] += 1
+            per_pass = [tot[i] / cnt[i] for i in range(passes)]
         # Self-check without the oracle: H is its own inverse up to 2^n
         # (H H = 2^n I), so two calls from the original input must give the
         # input back (normalised) or 2^n times it (unnormalised, exact for
@@ -334,6 +367,7 @@ def gpu_workload(torch, w, steps, warmup, split="configured", full=False, keep_o
         step()
         step()
         torch.cuda.synchronize()
+        check_ws()
         scale = 1.0 if w.normalize else float(2 ** w.n)
         rows = sorted(set(int(r) for r in np.linspace(0, w.batch - 1, min(8, w.batch))))
         worst, exact = 0.0, True
@@ -360,23 +394,33 @@ def gpu_workload(torch, w, steps, warmup, split="configured", full=False, keep_o
     del re, im
     torch.cuda.empty_cache()
     return {"ms": ms, "steps": k, "wall_ms": wall_ms, "passes": passes,
-            "pass_bits": plan.pass_bits, "per_pass_ms": per_pass, "copy_ms": copy_ms,
+            "pass_bits": [w.n] if ws is not None else plan.pass_bits, "per_pass_ms": per_pass, "copy_ms": copy_ms,
             "S": w.state_bytes, "chunk": chunk, "check": check, "reps_ms": reps,
-            "kernel_names": [plan.kernel_name(i, w.batch) for i in range(passes)],
+            "kernel_names": (["onepass_kernel"] if ws is not None else
+                             [plan.kernel_name(i, w.batch) for i in range(passes)]),
+            "onepass": ws is not None, "workspace_bytes": ws_bytes,
             "output": output, "inputs": inputs, "graph_ms": graph_ms}
 
 
-def roofline(w, r, cache_copy):
+def roofline(w, r, cache_copy, label="as configured"):
     """The transform's algorithmic roofline: one read and one write of a
     chunk's state (2 x chunk bytes) over the sum of the average durations of
     that chunk's pass kernels, against the 8 TB/s HBM peak.  Per pass, the
     rate at which it moves its chunk (each pass reads and writes it once;
-    after the first, the chunk is served from the Infinity Cache)."""
+    after the first, the chunk is served from the Infinity Cache).  A
+    one-pass call is one launch over the whole state (chunk = batch)."""
     chunk_bytes = w.state_bytes * r["chunk"] // w.batch
     alg = 2 * chunk_bytes
     t_ms = sum(r["per_pass_ms"])
     achieved = alg / (t_ms * 1e-3) / 1e9
     trec = traffic_record(w.name)
+    prec = None
+    if trec:
+        prec = trec.get("plans", {}).get(label)
+        if prec is None and label == "as configured":
+            prec = {"passes": trec.get("passes", {})}
+        if prec is None or bool(prec.get("onepass")) != bool(r.get("onepass")):
+            trec = prec = None
     per_pass = []
     traffic = 0.0 if trec else None
     fetch = write = 0.0
@@ -384,7 +428,7 @@ def roofline(w, r, cache_copy):
         p = {"pass": i, "bits": r["pass_bits"][i], "kernel": r["kernel_names"][i],
              "avg_us": ms * 1e3, "pass_fabric_gbps": alg / (ms * 1e-3) / 1e9,
              "frac_of_cache_copy": alg / (ms * 1e-3) / 1e9 / cache_copy["gbps"]}
-        pr = trec.get("passes", {}).get(str(i)) if trec else None
+        pr = prec.get("passes", {}).get(str(i)) if prec else None
         if pr is not None and "bytes_per_launch" in pr:
             p["l2_fabric_bytes_per_launch"] = pr["bytes_per_launch"]
             p["lds_bank_conflicts"] = lds_conflicts(w.name, pr.get("kernel", ""))
@@ -397,6 +441,24 @@ def roofline(w, r, cache_copy):
     if traffic is None:
         fetch = write = None
     launches = r["passes"] * (-(-w.batch // r["chunk"]))
+    if r.get("onepass"):
+        return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "kernel": "onepass_kernel: the whole state in one launch (factors 15|5 on "
+                          "chip, the row-to-column exchange through each XCD's L2)",
+                "algorithmic_bytes": alg,
+                "algorithmic_bytes_note": "one read and one write of the state: %d vectors "
+                                          "x 2 components x 2^%d x %d B, x 2"
+                                          % (w.batch, w.n, w.itemsize),
+                "duration_us": t_ms * 1e3,
+                "traffic_note": "rocprofv3 FETCH_SIZE + WRITE_SIZE of the kernel, calibrated "
+                                "on a streaming copy: bytes between the L2s and the fabric "
+                                "(the in-L2 exchange would show here if its lines left the "
+                                "L2s)",
+                "fetch_bytes": fetch, "write_bytes": write,
+                "limiter": "HBM streaming (one read and one write of the state) overlapped "
+                           "with the groups' exchange and synchronisation chain",
+                "passes": per_pass, "launches_per_step": 1}
     return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
             "kernel": "the transform of one chunk: %s (%d launches, one per pass)" % (
@@ -458,8 +520,11 @@ def config_record(cfg, w, r, cpu, label):
     galg = 2 * S / t / 1e9
     rec = {"cfg": cfg, "workload": w.name, "plan": label, "n": w.n, "batch": w.batch,
            "dtype": w.dtype, "values": w.values, "normalize": w.normalize,
-           "path": "default" if label == "default plan" else
-                   ("split " + "|".join(str(b) for b in r["pass_bits"][::-1])),
+           "path": ("one HBM pass on a workspace (fwt_execute_ws): factors 15|5 on chip, "
+                    "the row-to-column exchange in each XCD's L2") if r.get("onepass") else
+                   ("default" if label == "default plan" else
+                    ("fwt_execute, " if label == "two-pass" else "") +
+                    "split " + "|".join(str(b) for b in r["pass_bits"][::-1])),
            "passes": r["passes"], "pass_bits_low_first": r["pass_bits"],
            "kernels": r["kernel_names"], "steps": r["steps"],
            "t_ms_timed_block": r["ms"],
@@ -578,11 +643,14 @@ def _short(name):
 
 def _profiled_plans(w):
     """(label, split) of each plan bench.py times for a workload: as
-    configured, and the default plan where the configured records list it
-    too."""
+    configured, the default plan where the configured records list it too,
+    and fwt_execute's passes where the configured plan runs as one HBM pass
+    on a workspace ("two-pass")."""
     out = [("as configured", w.split or None)]
     if any(n == w.name and s is None for _, n, s in CONFIGS):
         out.append(("default plan", None))
+    if any(n == w.name and s == "two-pass" for _, n, s in CONFIGS):
+        out.append(("two-pass", None))
     return out
 
 
@@ -647,20 +715,26 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
                               "an L2 still held from the previous call would not be "
                               "counted)" if resident else "")]
     plans = {}
+    onepass_traced = any("onepass_kernel" in k[0] for k in groups)
     for label, split in _profiled_plans(w):
         plan = qse.Plan(w.n, w.dtype, split=split)
-        chunk = plan.chunk_vectors(w.batch, True) or w.batch
+        # the configured default plan of a workload the one-pass kernel
+        # serves ran as one launch over the whole state
+        onepass = label == "as configured" and split is None and onepass_traced
+        chunk = w.batch if onepass else (plan.chunk_vectors(w.batch, True) or w.batch)
         chunk_bytes = w.state_bytes * chunk // w.batch
+        npass = 1 if onepass else plan.num_passes
         tl += ["# plan %s: %s, %d pass(es), chunks of %d vector(s)" % (
-                   label, "split " + "|".join(str(b) for b in plan.pass_bits[::-1]),
-                   plan.num_passes, chunk),
+                   label, "one HBM pass (onepass_kernel, factors 15|5 on chip)" if onepass else
+                   "split " + "|".join(str(b) for b in plan.pass_bits[::-1]),
+                   npass, chunk),
                "# pass | kernel | launches | FETCH KiB | WRITE KiB | scaled L2-fabric "
                "bytes/launch | bytes one read + one write of the chunk moves | ratio | "
                "avg us (trace)"]
         passes = {}
         total_alg, total_us = 2 * chunk_bytes, 0.0
-        for i in range(plan.num_passes):
-            kname = plan.kernel_name(i, w.batch)
+        for i in range(npass):
+            kname = "onepass_kernel" if onepass else plan.kernel_name(i, w.batch)
             cand = [(k, v) for k, v in groups.items() if kname in k[0]]
             if not cand:
                 continue
@@ -684,7 +758,7 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
                       "(one read + one write of the chunk) %d -> %.1f GB/s, %.3f of 8 TB/s" % (
                           len(passes), total_us, total_alg, total_alg / total_us / 1e3,
                           total_alg / total_us / 1e3 / HBM_PEAK_GBS))
-        plans[label] = {"chunk_vectors": chunk, "passes": passes}
+        plans[label] = {"chunk_vectors": chunk, "passes": passes, "onepass": onepass}
     lds_lines = []
     if lds_dir:
         per = {}
@@ -880,7 +954,7 @@ def main():
     for cfg, name, split in todo:
         w = workloads.WORKLOADS[name]
         full = name in LARGE or name == head.name
-        label = "default plan" if split is None else "as configured"
+        label = {None: "default plan", "two-pass": "two-pass"}.get(split, "as configured")
         r = gpu_workload(torch, w, args.steps if name == head.name else
                          (max(20, args.steps // 5) if name in LARGE else args.steps),
                          args.warmup, split=split, full=full,
@@ -894,7 +968,7 @@ def main():
         rec["gpu_name"] = torch.cuda.get_device_name(0)
         rec["rocm_version"] = rocm_version()
         if full and r["per_pass_ms"]:
-            rec["roofline"] = roofline(w, r, cache_copy)
+            rec["roofline"] = roofline(w, r, cache_copy, label)
         records.append(rec)
         if split == ("configured" if name != "n14_b64_f32" else None):
             native[name] = r["ms"]
@@ -939,7 +1013,9 @@ def main():
                 if w.values == "gauss" else "synthetic: seeded integers in [-8, 8]",
         "config": {"workload": w.name, "n": w.n, "batch": w.batch, "normalize": w.normalize,
                    "layout": "planar re/im", "passes": r["passes"],
-                   "pass_bits_low_first": r["pass_bits"], "chunk_vectors": r["chunk"]},
+                   "pass_bits_low_first": r["pass_bits"], "chunk_vectors": r["chunk"],
+                   "entry_point": "fwt_execute_ws" if r.get("onepass") else "fwt_execute",
+                   "workspace_bytes": r.get("workspace_bytes", 0)},
         "gbps_algorithmic": gbps_alg,
         "pct_peak_algorithmic": 100 * gbps_alg / HBM_PEAK_GBS,
         "gbps_accounted": gbps_accounted,

@@ -201,16 +201,17 @@ constexpr int kOpRingSlots = 2;
 constexpr size_t kOpSlotBytes = ((size_t)4 << 20) / kOpSlices;   // one slice of a component
 constexpr size_t kOpErrOff = 0;          // int: error bits
 constexpr size_t kOpQueueOff = 256;      // int[kOpXcds]: components taken per XCD
-constexpr size_t kOpArriveOff = 384;     // int[kOpXcds]: workgroups that found themselves on each XCD
+constexpr size_t kOpMemberOff = 384;     // int[kOpXcds][kOpGroupsPerXcd]: members that joined
 constexpr size_t kOpNextOff = 512;       // uint64[kOpGroups][2]: (sequence << 32) | next index
 constexpr size_t kOpFlagOff = 1024;      // int[kOpGroups][64]: slices written, slices read
-constexpr size_t kOpHeaderBytes = 8192;  // the words above, cleared by each call
+constexpr size_t kOpCuOff = 8192;        // int[kOpXcds][256]: workgroups seen per CU
+constexpr size_t kOpHeaderBytes = 16384; // the words above, cleared by each call
 constexpr size_t kOpWorkspaceBytes =
     kOpHeaderBytes + (size_t)kOpGroups * kOpRingSlots * kOpSlotBytes;
 constexpr size_t kOpLdsBytes = 64 * 1024;
 enum : int {
     kOpErrTimeout = 1,     // a wait for the group's progress words ran out
-    kOpErrPlacement = 2,   // more workgroups on one XCD than its groups hold
+    kOpErrPlacement = 2,   // a CU or an XCD received more workgroups than planned
     kOpErrQueue = 4,       // a wait for the next component's index ran out
 };
 // Workgroups of the one-pass kernel that fit one CU at once (0 if it cannot

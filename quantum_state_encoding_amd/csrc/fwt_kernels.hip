@@ -1219,10 +1219,12 @@ __global__ void __launch_bounds__(256)
 // only when a member is behind.  The slice loads are device-scope too: a
 // plain load can return a line the CU's L1 kept from the slot's previous
 // use.  Every member of a group runs on the same XCD: a workgroup reads its
-// XCD from the XCC_ID register and takes a rank among that XCD's
-// workgroups with one atomic add (the dispatcher deals the 512 workgroups
-// to the 8 XCDs in turn, 64 each, but the first one it serves varies), so
-// one L2 serves the group.  All 2 x 256 workgroups are resident together
+// XCD and CU from the XCC_ID and HW_ID registers and joins a group with two
+// atomic adds (the dispatcher deals the 512 workgroups to the 8 XCDs in
+// turn, 64 each, two per CU, but the first XCD it serves varies), so one L2
+// serves the group, and the two workgroups of a CU belong to different
+// groups (two members of one group on one CU would halve that pair's
+// share of the CU, and the whole group waits for them).  All 2 x 256 workgroups are resident together
 // (at most 128 VGPRs and 64 KiB of LDS each), so every wait ends; the spin
 // bounds are only a guard, recorded in the workspace's error word.
 //
@@ -1304,21 +1306,30 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
     __shared__ int sh_next, sh_broken, sh_xcd, sh_rank;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     int* const err = reinterpret_cast<int*>(a.ws + kOpErrOff);
-    // The workgroup's XCD, from the hardware, and its rank among the
-    // workgroups there (the dispatcher deals workgroups to the XCDs in turn,
-    // but not always starting from the first one, e.g. in graph replays).
+    // The workgroup's XCD and CU, from the hardware (the dispatcher deals
+    // workgroups to the XCDs in turn, but not always starting from the
+    // first one, e.g. in graph replays).  The two workgroups of a CU join
+    // different groups (the first to arrive group 0), and take member
+    // ranks in their group by arrival, so every group spans 32 CUs.
     if (t == 0) {
         const int x = xcc_id();
-        int r = -1;
+        int hw;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+        const int cu = (hw >> 8) & 0xff;   // CU, shader array and engine of the XCD
+        int grp = -1, r = -1;
         if (x < kOpXcds)
-            r = __hip_atomic_fetch_add(reinterpret_cast<int*>(a.ws + kOpArriveOff) + x, 1,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (r < 0 || r >= kOpGroupsPerXcd * kOpMembers) {
+            grp = __hip_atomic_fetch_add(reinterpret_cast<int*>(a.ws + kOpCuOff) + 256 * x + cu, 1,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (grp >= 0 && grp < kOpGroupsPerXcd)
+            r = __hip_atomic_fetch_add(reinterpret_cast<int*>(a.ws + kOpMemberOff) +
+                                           kOpGroupsPerXcd * x + grp,
+                                       1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (r < 0 || r >= kOpMembers) {
             atomicOr(err, kOpErrPlacement);
             r = -1;
         }
         sh_xcd = x;
-        sh_rank = r;
+        sh_rank = r < 0 ? -1 : grp * kOpMembers + r;
     }
     __syncthreads();
     if (sh_rank < 0)
