@@ -36,88 +36,12 @@
 #include <vector>
 
 #include "fwt_internal.h"
+#include "fwt_device.h"
 
 namespace qse {
 namespace {
 
-template <typename T>
-struct Vec;
-template <>
-struct Vec<float> {
-    typedef float type __attribute__((ext_vector_type(4)));
-    static constexpr int WB = 2;  // log2 elements per 16-byte vector
-};
-template <>
-struct Vec<double> {
-    typedef double type __attribute__((ext_vector_type(2)));
-    static constexpr int WB = 1;
-};
-
-__device__ __forceinline__ float fma_sign(float x, float s, float p)
-{
-    return __builtin_fmaf(x, s, p);
-}
-__device__ __forceinline__ double fma_sign(double x, double s, double p)
-{
-    return __builtin_fma(x, s, p);
-}
-
-template <typename V>
-__device__ __forceinline__ void butterfly(V& a, V& b)
-{
-    const V s = a + b;
-    const V d = a - b;
-    a = s;
-    b = d;
-}
-
-// The butterfly times c: (c (a + b), c (a - b)) as t = c b, fma(a, c, +-t):
-// three operations for two outputs instead of four.  When c is a power of
-// two (or +-1), c b is exact and the results equal, bit for bit, the
-// butterfly followed by the multiply.
-template <typename V, typename T>
-__device__ __forceinline__ void butterfly_scaled(V& a, V& b, T c)
-{
-    constexpr int W = sizeof(V) / sizeof(T);
-#pragma unroll
-    for (int k = 0; k < W; ++k) {
-        const T t = b[k] * c;
-        const T u = a[k];
-        a[k] = fma_sign(u, c, t);
-        b[k] = fma_sign(u, c, -t);
-    }
-}
-
-// Stages on the vb index bits inside one vector (row passes only).
-__device__ __forceinline__ void in_vector(Vec<float>::type& v)
-{
-    const float s0 = v.x + v.y, d0 = v.x - v.y;   // bit 0: (0,1), (2,3)
-    const float s1 = v.z + v.w, d1 = v.z - v.w;
-    v.x = s0 + s1;                                // bit 1: (0,2), (1,3)
-    v.z = s0 - s1;
-    v.y = d0 + d1;
-    v.w = d0 - d1;
-}
-__device__ __forceinline__ void in_vector(Vec<double>::type& v)
-{
-    const double s = v.x + v.y, d = v.x - v.y;
-    v.x = s;
-    v.y = d;
-}
-
-// Butterflies on register bits [0, NB) of x[0..E).
-template <int NB, int E, typename V>
-__device__ __forceinline__ void register_stages(V* x)
-{
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-            if (!(j & (1 << b)))
-                butterfly(x[j], x[j | (1 << b)]);
-        }
-    }
-}
+// Vector types, butterflies and lane stages: fwt_device.h.
 
 // Row held by thread tau in register j when the register bits are the EB
 // row bits starting at A: the low A row bits come from tau's low bits, the
@@ -498,265 +422,6 @@ __global__ void __launch_bounds__(512)
 // bits 0, 1 and 3 keep x + s * partner instead, the difference negated,
 // and the kernel's final scaling removes the sign: fmac_dpp_regs.)
 
-template <int LBIT, bool MI = false>
-__device__ __forceinline__ unsigned lane_partner_u32(unsigned v)
-{
-    if constexpr (LBIT == 0)
-        return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // quad [1,0,3,2]
-    else if constexpr (LBIT == 1)
-        return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad [2,3,0,1]
-    else if constexpr (LBIT == 2 && MI)
-        return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true); // row_half_mirror
-    else if constexpr (LBIT == 2)
-        return (unsigned)__builtin_amdgcn_ds_swizzle((int)v, (4 << 10) | 0x1F);   // xor 4
-    else
-        return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true); // row_ror:8
-}
-
-template <int LBIT, bool MI = false>
-__device__ __forceinline__ float lane_partner(float v)
-{
-    return __uint_as_float(lane_partner_u32<LBIT, MI>(__float_as_uint(v)));
-}
-template <int LBIT, bool MI = false>
-__device__ __forceinline__ double lane_partner(double v)
-{
-    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-    const unsigned lo = lane_partner_u32<LBIT, MI>((unsigned)u);
-    const unsigned hi = lane_partner_u32<LBIT, MI>((unsigned)(u >> 32));
-    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-
-// Swap lane bit 4 (LBIT = 4) or 5 with the register pair (a, b).
-template <int LBIT>
-__device__ __forceinline__ void permlane_swap_u32(unsigned& a, unsigned& b)
-{
-    if constexpr (LBIT == 4) {
-        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-        a = r[0];
-        b = r[1];
-    } else {
-        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-        a = r[0];
-        b = r[1];
-    }
-}
-template <int LBIT>
-__device__ __forceinline__ void permlane_swap(float& a, float& b)
-{
-    unsigned ua = __float_as_uint(a), ub = __float_as_uint(b);
-    permlane_swap_u32<LBIT>(ua, ub);
-    a = __uint_as_float(ua);
-    b = __uint_as_float(ub);
-}
-template <int LBIT>
-__device__ __forceinline__ void permlane_swap(double& a, double& b)
-{
-    const unsigned long long ua = (unsigned long long)__double_as_longlong(a);
-    const unsigned long long ub = (unsigned long long)__double_as_longlong(b);
-    unsigned alo = (unsigned)ua, ahi = (unsigned)(ua >> 32);
-    unsigned blo = (unsigned)ub, bhi = (unsigned)(ub >> 32);
-    permlane_swap_u32<LBIT>(alo, blo);
-    permlane_swap_u32<LBIT>(ahi, bhi);
-    a = __longlong_as_double((long long)(((unsigned long long)ahi << 32) | alo));
-    b = __longlong_as_double((long long)(((unsigned long long)bhi << 32) | blo));
-}
-
-// fp32 stages on lane bits 0, 1 and 3: one vector-ALU instruction per
-// value, v_fmac_f32 with a DPP lane permutation on its first source (quad
-// permutations for bits 0 and 1; for bit 3 a rotation of each 16-lane row
-// by 8, which is lane xor 8), so each lane keeps x + s * partner (s = -1 on
-// the upper lane of each pair).  The upper lane then holds the difference
-// negated.  The negation is exact and carries through every later stage
-// unchanged (a stage's two operands come from lanes with equal bits 0, 1
-// and 3, so they carry the same sign), and the kernel removes it with its
-// final scaling (dpp_sign_lanes).  Each
-// asm block begins with five wait states: a DPP read of a VGPR needs two
-// after a vector-ALU write of it, and a DPP instruction five after a write
-// of EXEC; the compiler cannot see the DPP inside the block.
-#define QSE_FMAC_DPP(Q, R, S) "v_fmac_f32_dpp %" #R ", %" #R ", %" #S " " Q \
-                              " row_mask:0xf bank_mask:0xf\n\t"
-#define QSE_FMAC_DPP_0(Q, S)                                                           \
-    QSE_FMAC_DPP(Q, 0, S) QSE_FMAC_DPP(Q, 1, S) QSE_FMAC_DPP(Q, 2, S) QSE_FMAC_DPP(Q, 3, S) \
-        QSE_FMAC_DPP(Q, 4, S) QSE_FMAC_DPP(Q, 5, S) QSE_FMAC_DPP(Q, 6, S) QSE_FMAC_DPP(Q, 7, S)
-#define QSE_FMAC_DPP_8(Q, S)                                                             \
-    QSE_FMAC_DPP(Q, 8, S) QSE_FMAC_DPP(Q, 9, S) QSE_FMAC_DPP(Q, 10, S) QSE_FMAC_DPP(Q, 11, S) \
-        QSE_FMAC_DPP(Q, 12, S) QSE_FMAC_DPP(Q, 13, S) QSE_FMAC_DPP(Q, 14, S)                \
-            QSE_FMAC_DPP(Q, 15, S)
-#define QSE_FMAC_DPP_16(Q, S)                                                               \
-    QSE_FMAC_DPP(Q, 16, S) QSE_FMAC_DPP(Q, 17, S) QSE_FMAC_DPP(Q, 18, S) QSE_FMAC_DPP(Q, 19, S) \
-        QSE_FMAC_DPP(Q, 20, S) QSE_FMAC_DPP(Q, 21, S) QSE_FMAC_DPP(Q, 22, S)                  \
-            QSE_FMAC_DPP(Q, 23, S)
-#define QSE_FMAC_DPP_24(Q, S)                                                               \
-    QSE_FMAC_DPP(Q, 24, S) QSE_FMAC_DPP(Q, 25, S) QSE_FMAC_DPP(Q, 26, S) QSE_FMAC_DPP(Q, 27, S) \
-        QSE_FMAC_DPP(Q, 28, S) QSE_FMAC_DPP(Q, 29, S) QSE_FMAC_DPP(Q, 30, S)                  \
-            QSE_FMAC_DPP(Q, 31, S)
-// Eight in-out operands v[b .. b + 7].
-#define QSE_OPS8(b)                                                                       \
-    "+v"(v[b]), "+v"(v[b + 1]), "+v"(v[b + 2]), "+v"(v[b + 3]), "+v"(v[b + 4]), "+v"(v[b + 5]), \
-        "+v"(v[b + 6]), "+v"(v[b + 7])
-// The stage on 8, 16 or 32 values with DPP control Q; s is the last
-// operand.
-#define QSE_DPP_STAGE(Q)                                                                     \
-    if constexpr (NR == 2)                                                                   \
-        asm("s_nop 4\n\t" QSE_FMAC_DPP_0(Q, 8) : QSE_OPS8(0) : "v"(s));                       \
-    else if constexpr (NR == 4)                                                              \
-        asm("s_nop 4\n\t" QSE_FMAC_DPP_0(Q, 16) QSE_FMAC_DPP_8(Q, 16)                          \
-            : QSE_OPS8(0), QSE_OPS8(8)                                                        \
-            : "v"(s));                                                                        \
-    else                                                                                     \
-        asm("s_nop 4\n\t" QSE_FMAC_DPP_0(Q, 32) QSE_FMAC_DPP_8(Q, 32) QSE_FMAC_DPP_16(Q, 32)   \
-                QSE_FMAC_DPP_24(Q, 32)                                                        \
-            : QSE_OPS8(0), QSE_OPS8(8), QSE_OPS8(16), QSE_OPS8(24)                            \
-            : "v"(s));
-
-// One stage on lane bit LBIT over the NR = 2, 4 or 8 fp32 registers at x.
-template <int LBIT, int NR>
-__device__ __forceinline__ void fmac_dpp_regs(Vec<float>::type* x, float s)
-{
-    static_assert(LBIT >= 0 && LBIT <= 3, "DPP pairs lanes within a row of 16");
-    static_assert(NR == 2 || NR == 4 || NR == 8, "blocks of 2, 4 or 8 registers");
-    float v[4 * NR];
-#pragma unroll
-    for (int j = 0; j < NR; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            v[4 * j + c] = x[j][c];
-    if constexpr (LBIT == 0) {
-        QSE_DPP_STAGE("quad_perm:[1,0,3,2]")
-    } else if constexpr (LBIT == 1) {
-        QSE_DPP_STAGE("quad_perm:[2,3,0,1]")
-    } else if constexpr (LBIT == 2) {
-        QSE_DPP_STAGE("row_half_mirror")
-    } else {
-        QSE_DPP_STAGE("row_ror:8")
-    }
-#pragma unroll
-    for (int j = 0; j < NR; ++j)
-        x[j] = Vec<float>::type{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
-}
-#undef QSE_DPP_STAGE
-#undef QSE_OPS8
-#undef QSE_FMAC_DPP_24
-#undef QSE_FMAC_DPP_16
-#undef QSE_FMAC_DPP_8
-#undef QSE_FMAC_DPP_0
-#undef QSE_FMAC_DPP
-
-// Lane bits among 0, 1, 3 (and 2 with the mirrored lane order below) whose
-// fp32 stages leave a sign (those in [gb, gb + lb), the lane row bits of a
-// tile); a lane's outputs carry (-1)^popcount(logical lane & mask).
-__host__ __device__ constexpr unsigned dpp_sign_lanes(int gb, int lb, bool mirror = false)
-{
-    return (gb <= 0 && lb > 0 ? 1u : 0u) | (gb <= 1 && gb + lb > 1 ? 2u : 0u) |
-           (mirror && gb <= 2 && gb + lb > 2 ? 4u : 0u) | (gb <= 3 && gb + lb > 3 ? 8u : 0u);
-}
-
-// Mirrored lane order: in each group of 8 lanes the upper 4 hold their rows
-// in reverse (logical lane = lane ^ 3 when lane bit 2 is set).  Lane xor 4
-// on logical lanes is then DPP row_half_mirror on physical ones (lane ->
-// 7 - lane in each group of 8), while xor 1, 2 and 8 stay the quad
-// permutations and the row rotation: they leave bit 2 alone.
-__device__ __forceinline__ int mirrored_lane(int lane)
-{
-    return lane ^ (((lane >> 2) & 1) * 3);
-}
-
-// Stage on lane bit LBIT for all E registers; `lane` is the logical lane
-// (mirrored_lane when MI).
-template <int LBIT, int E, typename V, typename T, bool MI = false>
-__device__ __forceinline__ void lane_stage(V* x, int lane)
-{
-    constexpr int W = sizeof(V) / sizeof(T);
-    if constexpr ((LBIT < 2 || LBIT == 3 || (MI && LBIT == 2)) && sizeof(T) == 4 && E >= 2) {
-        const float s = ((lane >> LBIT) & 1) ? -1.f : 1.f;
-        constexpr int NR = E < 8 ? E : 8;
-#pragma unroll
-        for (int j = 0; j < E; j += NR)
-            fmac_dpp_regs<LBIT, NR>(x + j, s);
-    } else if constexpr (LBIT < 4) {
-        const T s = ((lane >> LBIT) & 1) ? T(-1) : T(1);
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-#pragma unroll
-            for (int c = 0; c < W; ++c) {
-                const T v = x[j][c];
-                x[j][c] = fma_sign(v, s, lane_partner<LBIT, MI>(v));
-            }
-        }
-    } else {
-        static_assert(E >= 2, "lane bits 4 and 5 pair registers");
-#pragma unroll
-        for (int j = 0; j < E; j += 2) {
-#pragma unroll
-            for (int c = 0; c < W; ++c) {
-                T a = x[j][c], b = x[j + 1][c];
-                permlane_swap<LBIT>(a, b);
-                const T sum = a + b, dif = a - b;
-                a = sum;
-                b = dif;
-                permlane_swap<LBIT>(a, b);
-                x[j][c] = a;
-                x[j + 1][c] = b;
-            }
-        }
-    }
-}
-
-// The same stage, except that lane bits 4 and 5 are left exchanged with
-// register bits 0 and 1: the second swap of each pair is dropped.  After
-// it, lane bit 4 (5) holds the row bit register bit 0 (1) held, and
-// register bit 0 (1) holds the row bit of lane bit 4 (5); a caller must
-// address the data with that relabelling (lx_thread_row_rl, lx_reg_row_rl).
-template <int LBIT, int E, typename V, typename T, bool MI = false>
-__device__ __forceinline__ void lane_stage_nr(V* x, int lane)
-{
-    constexpr int W = sizeof(V) / sizeof(T);
-    if constexpr (LBIT < 4) {
-        lane_stage<LBIT, E, V, T, MI>(x, lane);
-    } else {
-        constexpr int RB = LBIT - 4;   // register bit paired with the lane bit
-        static_assert(E >= 4, "lane bits 4 and 5 pair register bits 0 and 1");
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-            if (j & (1 << RB))
-                continue;
-#pragma unroll
-            for (int c = 0; c < W; ++c) {
-                T a = x[j][c], b = x[j | (1 << RB)][c];
-                permlane_swap<LBIT>(a, b);
-                x[j][c] = a + b;
-                x[j | (1 << RB)][c] = a - b;
-            }
-        }
-    }
-}
-
-template <int B, int LB, int GB, int E, typename V, typename T, bool MI = false>
-struct LaneStagesNR {
-    __device__ __forceinline__ static void run(V* x, int lane)
-    {
-        lane_stage_nr<GB + B, E, V, T, MI>(x, lane);
-        LaneStagesNR<B + 1, LB, GB, E, V, T, MI>::run(x, lane);
-    }
-};
-template <int LB, int GB, int E, typename V, typename T, bool MI>
-struct LaneStagesNR<LB, LB, GB, E, V, T, MI> {
-    __device__ __forceinline__ static void run(V*, int) {}
-};
-
-template <int B, int LB, int GB, int E, typename V, typename T, bool MI = false>
-struct LaneStages {
-    __device__ __forceinline__ static void run(V* x, int lane)
-    {
-        lane_stage<GB + B, E, V, T, MI>(x, lane);
-        LaneStages<B + 1, LB, GB, E, V, T, MI>::run(x, lane);
-    }
-};
-template <int LB, int GB, int E, typename V, typename T, bool MI>
-struct LaneStages<LB, LB, GB, E, V, T, MI> {
-    __device__ __forceinline__ static void run(V*, int) {}
-};
 
 template <typename T, int KR, int EB, int GB, bool ROW>
 __global__ void __launch_bounds__(256)
@@ -1173,343 +838,6 @@ __global__ void __launch_bounds__(256)
     }
 }
 
-// ---- one HBM pass for fp32 n = 20: groups of workgroups on one XCD -----
-//
-// The Kronecker split H_20 = H_5 (x) H_15 (Apache Mahout pull request
-// "[QDP] [feature] Pr4 kronecker fwt", sections "Why" and "How"; iThome
-// "Day 18" article, "Kronecker block GEMM idea") without a second pass
-// over HBM.  A vector component is a 32 x 2^15 matrix: row m is the
-// 2^15-element block whose element bits 15..19 equal m.  Workgroup m of a
-// group (32 workgroups, one per CU of one XCD) loads row m into its
-// registers and applies H_15 to it (the row factor); the group then moves
-// the matrix through a ring buffer that stays in the XCD's L2, so that
-// workgroup m ends up holding the 1024-column slice m of all 32 rows, and
-// applies H_5 down the columns (the column factor) before storing.  HBM
-// sees one read and one write of the state; the intermediate only crosses
-// the L2.
-//
-// Layouts (element bits of a row block; lanes l = 0..63, waves w = 0..7,
-// 16 float4 registers j per thread; bits 0-1 lie inside a float4):
-//  load L0:  lanes 0-4 = bits 2-6, lane 5 = bit 10, waves = bits 7-9,
-//            registers j = bit 14 << 3 | bits 11-13;
-//  row L1:   after one LDS exchange, waves = bits 11-13 and registers
-//            j = bit 14 << 3 | bits 7-9.  Element bits 10-14 are then the
-//            destination column slice (lane 5, waves, register bit 3), and
-//            register bits 0-2 (element bits 7-9) the ring slice s.
-//  column R0 (as read from the ring): lanes 0-4 = bits 2-6 as before,
-//            lane 5 = row bit 0, waves = row bits 1-3, registers
-//            j = row bit 4 << 3 | s;
-//  store R1: after one LDS exchange, waves = s and registers j = row bit 4
-//            << 3 | row bits 1-3.
-// Lanes 0-4 keep element bits 2-6 throughout, so the sign that the fp32
-// DPP lane stages leave on lanes with odd popcount(lane & 0xB) is still
-// attached to the same lanes at the end and is removed with the scale.
-//
-// The ring exchange, per slice s (8 per component, 512 KiB each, ring of 2
-// slots per group): each workgroup stores its registers of slice s (the
-// values for all 32 destinations), then loads slice s - 1 as written by
-// every member, waits for both with one s_waitcnt, and publishes "slices
-// written" and "slices read" in its two progress words (plain stores: they
-// land in the XCD's L2).  Before storing into a slot it needs every member
-// to have read the slice that last used it; before loading a slice, every
-// member to have written it.  Wave 0 reads the group's 64 progress words
-// with device-scope loads (sc1: they miss the CU's L1 and hit the L2; a
-// device-scope atomic would leave the L2 and take about 1.2 us here) in
-// the same round trip as the slice's data, so a wait costs a round trip
-// only when a member is behind.  The slice loads are device-scope too: a
-// plain load can return a line the CU's L1 kept from the slot's previous
-// use.  Every member of a group runs on the same XCD: a workgroup reads its
-// XCD and CU from the XCC_ID and HW_ID registers and joins a group with two
-// atomic adds (the dispatcher deals the 512 workgroups to the 8 XCDs in
-// turn, 64 each, two per CU, but the first XCD it serves varies), so one L2
-// serves the group, and the two workgroups of a CU belong to different
-// groups (two members of one group on one CU would halve that pair's
-// share of the CU, and the whole group waits for them).  All 2 x 256 workgroups are resident together
-// (at most 128 VGPRs and 64 KiB of LDS each), so every wait ends; the spin
-// bounds are only a guard, recorded in the workspace's error word.
-//
-// Components are spread over the XCDs by index (c = xcd + 8 i) and over
-// an XCD's two groups by a queue: the group's first workgroup takes the
-// index of the group's next component with one atomic add while its loads
-// are in flight, and publishes it for the group (double-buffered by the
-// parity of the group's component count, so a fast leader cannot
-// overwrite a value a slow member has not read).  The second workgroup on
-// a CU issues later than the first, so a static split ended 20 % later.
-
-constexpr int kOpSpin = 1 << 20;
-constexpr int kOpRegs = 16;        // float4 per thread: a 2^15-element row block
-constexpr int kOpRowF4 = 8192;     // float4 per row block
-
-struct OnepassArgs {
-    float* re;
-    float* im;        // null: components are consecutive vectors of re
-    unsigned char* ws;
-    int ncomp;
-    float scale;
-};
-
-__device__ __forceinline__ int xcc_id()
-{
-    int x;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
-    return x & 15;
-}
-
-typedef unsigned int op_u4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t op_rsrc(const void* p)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, -1, 0x00020000);
-}
-// 16-byte buffer accesses with a cache-policy operand: 2 = nontemporal,
-// 16 = device scope (sc1), 0 = plain.
-template <int AUX>
-__device__ __forceinline__ Vec<float>::type op_load(__amdgpu_buffer_rsrc_t r, uint32_t voff,
-                                                    uint32_t soff)
-{
-    return __builtin_bit_cast(Vec<float>::type,
-                              __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
-}
-template <int AUX>
-__device__ __forceinline__ void op_store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                         const Vec<float>::type& v)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(op_u4, v), r, (int)voff, (int)soff,
-                                           AUX);
-}
-constexpr int kOpNt = 2, kOpDevice = 16;
-
-// Keeps the compiler from sinking the stages into their consumers (which
-// keeps their inputs alive and spills).
-__device__ __forceinline__ void op_pin(Vec<float>::type (&x)[kOpRegs])
-{
-#pragma unroll
-    for (int j = 0; j < kOpRegs; ++j)
-        asm volatile("" : "+v"(x[j]));
-}
-
-__global__ void __launch_bounds__(kOpThreads)
-    onepass_reset_kernel(unsigned char* ws)
-{
-    for (int i = threadIdx.x; i < (int)(kOpHeaderBytes / 16); i += blockDim.x)
-        reinterpret_cast<int4*>(ws)[i] = int4{0, 0, 0, 0};
-}
-
-__global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu(4)))
-    onepass_kernel(OnepassArgs a)
-{
-    using V = Vec<float>::type;
-    constexpr int S = kOpSlices, R = kOpRingSlots, UL = 256 / S;
-    static_assert(S == 8 && kOpRegs == 2 * S, "slice s is registers s and 8 + s");
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    V* const L = reinterpret_cast<V*>(lds_raw);
-    __shared__ int sh_min[2][2];   // cached minima of the progress words, by parity
-    __shared__ int sh_next, sh_broken, sh_xcd, sh_rank;
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    int* const err = reinterpret_cast<int*>(a.ws + kOpErrOff);
-    // The workgroup's XCD and CU, from the hardware (the dispatcher deals
-    // workgroups to the XCDs in turn, but not always starting from the
-    // first one, e.g. in graph replays).  The two workgroups of a CU join
-    // different groups (the first to arrive group 0), and take member
-    // ranks in their group by arrival, so every group spans 32 CUs.
-    if (t == 0) {
-        const int x = xcc_id();
-        int hw;
-        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
-        const int cu = (hw >> 8) & 0xff;   // CU, shader array and engine of the XCD
-        int grp = -1, r = -1;
-        if (x < kOpXcds)
-            grp = __hip_atomic_fetch_add(reinterpret_cast<int*>(a.ws + kOpCuOff) + 256 * x + cu, 1,
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (grp >= 0 && grp < kOpGroupsPerXcd)
-            r = __hip_atomic_fetch_add(reinterpret_cast<int*>(a.ws + kOpMemberOff) +
-                                           kOpGroupsPerXcd * x + grp,
-                                       1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (r < 0 || r >= kOpMembers) {
-            atomicOr(err, kOpErrPlacement);
-            r = -1;
-        }
-        sh_xcd = x;
-        sh_rank = r < 0 ? -1 : grp * kOpMembers + r;
-    }
-    __syncthreads();
-    if (sh_rank < 0)
-        return;   // uniform across the workgroup
-    const int xcd = sh_xcd, rank = sh_rank;
-    const int gi = rank / kOpMembers, m = rank % kOpMembers;
-    const int g = gi * kOpXcds + xcd;
-    int* const queue = reinterpret_cast<int*>(a.ws + kOpQueueOff);
-    unsigned long long* const nxt = reinterpret_cast<unsigned long long*>(a.ws + kOpNextOff) + 2 * g;
-    int* const prog = reinterpret_cast<int*>(a.ws + kOpFlagOff) + 64 * g;
-    const __amdgpu_buffer_rsrc_t ring =
-        op_rsrc(a.ws + kOpHeaderBytes + (size_t)g * R * kOpSlotBytes);
-    if (t == 0) {
-        sh_min[0][0] = sh_min[0][1] = sh_min[1][0] = sh_min[1][1] = 0;
-        sh_broken = 0;
-    }
-    __syncthreads();
-    const int ul = lane & 31, lh = lane >> 5;
-    // Thread parts of the byte offsets (the register parts are constants).
-    const uint32_t ld_v = ((uint32_t)m * kOpRowF4 + ul + (wv << 5) + (lh << 8)) * 16;
-    const uint32_t xw_v = ((uint32_t)((lh | (wv << 1)) * 32 + m) * UL + ul) * 16;
-    const uint32_t xr_v = ((uint32_t)(m * 32 + (lh | (wv << 1))) * UL + ul) * 16;
-    const uint32_t st_v = ((uint32_t)lh * kOpRowF4 + m * 256 + (wv << 5) + ul) * 16;
-    float cs = a.scale;
-    if (__popc((unsigned)lane & dpp_sign_lanes(0, 6)) & 1)
-        cs = -cs;
-
-    // Wave 0 waits until every member has written >= need_w slices and read
-    // >= need_r; the decision to call this is the same in every wave.
-    auto wait_flags = [&](int need_w, int need_r) {
-        __syncthreads();
-        if (t < 64 && !sh_broken) {
-            bool ok = false;
-            for (int i = 0; i < kOpSpin; ++i) {
-                const int v = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-                if (__ballot(v < (lane < 32 ? need_w : need_r)) == 0) {
-                    ok = true;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            if (t == 0 && !ok) {
-                sh_broken = 1;
-                atomicOr(err, kOpErrTimeout);
-            }
-        }
-        __syncthreads();
-    };
-
-    const int cx = (a.ncomp - xcd + kOpXcds - 1) / kOpXcds;   // components c = xcd + 8 i
-    int q = 0;                                                // slices so far
-    int seq = 0;                                              // components so far
-    V x[kOpRegs];
-    for (int i = gi; i < cx;) {
-        const int c = xcd + kOpXcds * i;
-        float* const base = a.im ? ((c & 1) ? a.im : a.re) + ((size_t)(c >> 1) << kOpN)
-                                 : a.re + ((size_t)c << kOpN);
-        const __amdgpu_buffer_rsrc_t comp = op_rsrc(base);
-#pragma unroll
-        for (int j = 0; j < kOpRegs; ++j)
-            x[j] = op_load<kOpNt>(comp, ld_v, (((j & 7) << 9) | ((j >> 3) << 12)) * 16);
-        if (m == 0 && t == 0) {
-            const int nx = __hip_atomic_fetch_add(queue + xcd, 1, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT) + kOpGroupsPerXcd;
-            __hip_atomic_store(nxt + ((seq + 1) & 1),
-                               ((unsigned long long)(seq + 1) << 32) | (unsigned)nx,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-        op_pin(x);
-        // Row factor H_15: in-vector bits 0-1, register bits 11-14, lane bits
-        // 2-6 and 10, then the exchange to L1 and register bits 7-9.
-#pragma unroll
-        for (int j = 0; j < kOpRegs; ++j)
-            in_vector(x[j]);
-        register_stages<4, kOpRegs>(x);
-        LaneStages<0, 6, 0, kOpRegs, V, float, false>::run(x, lane);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            __syncthreads();
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                L[ul | (wv << 5) | (lh << 8) | (r << 9)] = x[(p << 3) | r];
-            __syncthreads();
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                x[(p << 3) | s] = L[ul | (s << 5) | (lh << 8) | (wv << 9)];
-        }
-        register_stages<3, kOpRegs>(x);
-        op_pin(x);
-        // The ring exchange: iteration s stores slice s and loads slice s - 1.
-#pragma unroll
-        for (int s = 0; s <= S; ++s) {
-            const int qw = q + s, qr = q + s - 1;
-            const int need_w = s >= 1 ? qr + 1 : 0;
-            const int need_r = s < S ? qw - R + 1 : 0;
-            const int cb = qw & 1;
-            if (!(sh_min[cb][0] >= need_w && sh_min[cb][1] >= need_r))
-                wait_flags(need_w, need_r);
-            if (s < S) {
-                const uint32_t so = (uint32_t)(qw % R) * (uint32_t)kOpSlotBytes;
-                op_store<0>(ring, xw_v, so, x[s]);
-                op_store<0>(ring, xw_v, so + 16u * 16 * 32 * UL, x[8 + s]);
-            }
-            if (s >= 1) {
-                const uint32_t so = (uint32_t)(qr % R) * (uint32_t)kOpSlotBytes;
-                x[s - 1] = op_load<kOpDevice>(ring, xr_v, so);
-                x[8 + s - 1] = op_load<kOpDevice>(ring, xr_v, so + 16u * 16 * UL);
-            }
-            int pv = 0;
-            if (t < 64)
-                pv = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (t < 64) {
-                for (int o = 16; o >= 1; o >>= 1)
-                    pv = min(pv, __shfl_xor(pv, o));
-                const int mw = __shfl(pv, 0), mr = __shfl(pv, 32);
-                if (t == 0) {
-                    sh_min[cb ^ 1][0] = mw;
-                    sh_min[cb ^ 1][1] = mr;
-                }
-            }
-            __syncthreads();
-            if (t == 0) {
-                if (s < S)
-                    __hip_atomic_store(prog + m, qw + 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-                if (s >= 1)
-                    __hip_atomic_store(prog + 32 + m, qr + 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-        }
-        q += S;
-        op_pin(x);
-        // Column factor H_5: row bit 4 in registers, row bit 0 on lane 5,
-        // then the exchange to R1 and row bits 1-3 in registers.
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            butterfly(x[j], x[j | 8]);
-        lane_stage<5, kOpRegs, V, float>(x, lane);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            __syncthreads();
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                L[ul | (s << 5) | (lh << 8) | (wv << 9)] = x[(p << 3) | s];
-            __syncthreads();
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                x[(p << 3) | k] = L[ul | (wv << 5) | (lh << 8) | (k << 9)];
-        }
-        register_stages<3, kOpRegs>(x);
-#pragma unroll
-        for (int j = 0; j < kOpRegs; ++j)
-            x[j] *= cs;
-#pragma unroll
-        for (int j = 0; j < kOpRegs; ++j)
-            op_store<kOpNt>(comp, st_v, ((((j & 7) << 1) | ((j >> 3) << 4)) * kOpRowF4) * 16, x[j]);
-        // The group's next component.
-        if (t == 0) {
-            unsigned long long v = 0;
-            for (int k = 0; k < kOpSpin; ++k) {
-                v = __hip_atomic_load(nxt + ((seq + 1) & 1), __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-                if ((int)(v >> 32) == seq + 1)
-                    break;
-                __builtin_amdgcn_s_sleep(1);
-            }
-            if ((int)(v >> 32) != seq + 1) {
-                atomicOr(err, kOpErrQueue);
-                v = 0x7fffffffu;
-            }
-            sh_next = (int)(unsigned)v;
-        }
-        __syncthreads();
-        i = sh_next;
-        ++seq;
-    }
-}
-
 struct Entry {
     KernelKey key;
     const void* fn;
@@ -1752,34 +1080,5 @@ hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStre
     return hipGetLastError();
 }
 
-hipError_t onepass_occupancy(int* blocks_per_cu)
-{
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&onepass_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kOpLdsBytes);
-    if (e != hipSuccess)
-        return e;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, reinterpret_cast<const void*>(&onepass_kernel), kOpThreads, kOpLdsBytes);
-}
-
-hipError_t launch_onepass(float* re, float* im, int ncomp, void* ws, float scale,
-                          hipStream_t stream, hipEvent_t start, hipEvent_t stop)
-{
-    unsigned char* const w = reinterpret_cast<unsigned char*>(ws);
-    hipLaunchKernelGGL(onepass_reset_kernel, dim3(1), dim3(kOpThreads), 0, stream, w);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    OnepassArgs a{re, im, w, ncomp, scale};
-    void* kargs[] = {&a};
-    const dim3 grid(kOpGroups * kOpMembers, 1, 1);
-    if (start || stop)
-        return hipExtLaunchKernel(reinterpret_cast<const void*>(&onepass_kernel), grid,
-                                  dim3(kOpThreads, 1, 1), kargs, kOpLdsBytes, stream, start, stop,
-                                  0);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&onepass_kernel), grid,
-                           dim3(kOpThreads, 1, 1), kargs, kOpLdsBytes, stream);
-}
 
 }  // namespace qse

@@ -1,0 +1,381 @@
+// One HBM pass for the fp32 n = 20 transform: groups of workgroups on one
+// XCD exchange the Kronecker factors' intermediate through the XCD's L2.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include "fwt_device.h"
+#include "fwt_internal.h"
+
+namespace qse {
+namespace {
+
+// ---- one HBM pass for fp32 n = 20: groups of workgroups on one XCD -----
+//
+// The Kronecker split H_20 = H_5 (x) H_15 (Apache Mahout pull request
+// "[QDP] [feature] Pr4 kronecker fwt", sections "Why" and "How"; iThome
+// "Day 18" article, "Kronecker block GEMM idea") without a second pass
+// over HBM.  A vector component is a 32 x 2^15 matrix: row m is the
+// 2^15-element block whose element bits 15..19 equal m.  Workgroup m of a
+// group (32 workgroups, one per CU of one XCD) loads row m into its
+// registers and applies H_15 to it (the row factor); the group then moves
+// the matrix through a ring buffer that stays in the XCD's L2, so that
+// workgroup m ends up holding the 1024-column slice m of all 32 rows, and
+// applies H_5 down the columns (the column factor) before storing.  HBM
+// sees one read and one write of the state; the intermediate only crosses
+// the L2.
+//
+// Layouts (element bits of a row block; lanes l = 0..63, waves w = 0..7,
+// 16 float4 registers j per thread; bits 0-1 lie inside a float4):
+//  load L0:  lanes 0-4 = bits 2-6, lane 5 = bit 10, waves = bits 7-9,
+//            registers j = bit 14 << 3 | bits 11-13;
+//  row L1:   after one LDS exchange, waves = bits 11-13 and registers
+//            j = bit 14 << 3 | bits 7-9.  Element bits 10-14 are then the
+//            destination column slice (lane 5, waves, register bit 3), and
+//            register bits 0-2 (element bits 7-9) the ring slice s.
+//  column R0 (as read from the ring): lanes 0-4 = bits 2-6 as before,
+//            lane 5 = row bit 0, waves = row bits 1-3, registers
+//            j = row bit 4 << 3 | s;
+//  store R1: after one LDS exchange, waves = s and registers j = row bit 4
+//            << 3 | row bits 1-3.
+// Lanes 0-4 keep element bits 2-6 throughout, so the sign that the fp32
+// DPP lane stages leave on lanes with odd popcount(lane & 0xB) is still
+// attached to the same lanes at the end and is removed with the scale.
+//
+// The ring exchange, per slice s (8 per component, 512 KiB each, ring of 2
+// slots per group): each workgroup stores its registers of slice s (the
+// values for all 32 destinations), then loads slice s - 1 as written by
+// every member, waits for both with one s_waitcnt, and publishes "slices
+// written" and "slices read" in its two progress words (plain stores: they
+// land in the XCD's L2).  Before storing into a slot it needs every member
+// to have read the slice that last used it; before loading a slice, every
+// member to have written it.  Wave 0 reads the group's 64 progress words
+// with device-scope loads (sc1: they miss the CU's L1 and hit the L2; a
+// device-scope atomic would leave the L2 and take about 1.2 us here) in
+// the same round trip as the slice's data, so a wait costs a round trip
+// only when a member is behind.  The slice loads are device-scope too: a
+// plain load can return a line the CU's L1 kept from the slot's previous
+// use.  Every member of a group runs on the same XCD: a workgroup reads its
+// XCD and CU from the XCC_ID and HW_ID registers and joins a group with two
+// atomic adds (the dispatcher deals the 512 workgroups to the 8 XCDs in
+// turn, 64 each, two per CU, but the first XCD it serves varies), so one L2
+// serves the group, and the two workgroups of a CU belong to different
+// groups (two members of one group on one CU would halve that pair's
+// share of the CU, and the whole group waits for them).  All 2 x 256 workgroups are resident together
+// (at most 128 VGPRs and 64 KiB of LDS each), so every wait ends; the spin
+// bounds are only a guard, recorded in the workspace's error word.
+//
+// Components are spread over the XCDs by index (c = xcd + 8 i) and over
+// an XCD's two groups by a queue: the group's first workgroup takes the
+// index of the group's next component with one atomic add while its loads
+// are in flight, and publishes it for the group (double-buffered by the
+// parity of the group's component count, so a fast leader cannot
+// overwrite a value a slow member has not read).  The second workgroup on
+// a CU issues later than the first, so a static split ended 20 % later.
+
+constexpr int kOpSpin = 1 << 20;
+constexpr int kOpRegs = 16;        // float4 per thread: a 2^15-element row block
+constexpr int kOpRowF4 = 8192;     // float4 per row block
+
+struct OnepassArgs {
+    float* re;
+    float* im;        // null: components are consecutive vectors of re
+    unsigned char* ws;
+    int ncomp;
+    float scale;
+};
+
+__device__ __forceinline__ int xcc_id()
+{
+    int x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    return x & 15;
+}
+
+typedef unsigned int op_u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t op_rsrc(const void* p)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, -1, 0x00020000);
+}
+// 16-byte buffer accesses with a cache-policy operand: 2 = nontemporal,
+// 16 = device scope (sc1), 0 = plain.
+template <int AUX>
+__device__ __forceinline__ Vec<float>::type op_load(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                    uint32_t soff)
+{
+    return __builtin_bit_cast(Vec<float>::type,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ void op_store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                         const Vec<float>::type& v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(op_u4, v), r, (int)voff, (int)soff,
+                                           AUX);
+}
+constexpr int kOpNt = 2, kOpDevice = 16;
+
+// Keeps the compiler from sinking the stages into their consumers (which
+// keeps their inputs alive and spills).
+__device__ __forceinline__ void op_pin(Vec<float>::type (&x)[kOpRegs])
+{
+#pragma unroll
+    for (int j = 0; j < kOpRegs; ++j)
+        asm volatile("" : "+v"(x[j]));
+}
+
+__global__ void __launch_bounds__(kOpThreads)
+    onepass_reset_kernel(unsigned char* ws)
+{
+    for (int i = threadIdx.x; i < (int)(kOpHeaderBytes / 16); i += blockDim.x)
+        reinterpret_cast<int4*>(ws)[i] = int4{0, 0, 0, 0};
+}
+
+__global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu(4)))
+    onepass_kernel(OnepassArgs a)
+{
+    using V = Vec<float>::type;
+    constexpr int S = kOpSlices, R = kOpRingSlots, UL = 256 / S;
+    static_assert(S == 8 && kOpRegs == 2 * S, "slice s is registers s and 8 + s");
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    V* const L = reinterpret_cast<V*>(lds_raw);
+    __shared__ int sh_min[2][2];   // cached minima of the progress words, by parity
+    __shared__ int sh_next, sh_broken, sh_xcd, sh_rank;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    int* const err = reinterpret_cast<int*>(a.ws + kOpErrOff);
+    // The workgroup's XCD and CU, from the hardware (the dispatcher deals
+    // workgroups to the XCDs in turn, but not always starting from the
+    // first one, e.g. in graph replays).  The two workgroups of a CU join
+    // different groups (the first to arrive group 0), and take member
+    // ranks in their group by arrival, so every group spans 32 CUs.
+    if (t == 0) {
+        const int x = xcc_id();
+        int hw;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+        const int cu = (hw >> 8) & 0xff;   // CU, shader array and engine of the XCD
+        int grp = -1, r = -1;
+        if (x < kOpXcds)
+            grp = __hip_atomic_fetch_add(reinterpret_cast<int*>(a.ws + kOpCuOff) + 256 * x + cu, 1,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (grp >= 0 && grp < kOpGroupsPerXcd)
+            r = __hip_atomic_fetch_add(reinterpret_cast<int*>(a.ws + kOpMemberOff) +
+                                           kOpGroupsPerXcd * x + grp,
+                                       1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (r < 0 || r >= kOpMembers) {
+            atomicOr(err, kOpErrPlacement);
+            r = -1;
+        }
+        sh_xcd = x;
+        sh_rank = r < 0 ? -1 : grp * kOpMembers + r;
+    }
+    __syncthreads();
+    if (sh_rank < 0)
+        return;   // uniform across the workgroup
+    const int xcd = sh_xcd, rank = sh_rank;
+    const int gi = rank / kOpMembers, m = rank % kOpMembers;
+    const int g = gi * kOpXcds + xcd;
+    int* const queue = reinterpret_cast<int*>(a.ws + kOpQueueOff);
+    unsigned long long* const nxt = reinterpret_cast<unsigned long long*>(a.ws + kOpNextOff) + 2 * g;
+    int* const prog = reinterpret_cast<int*>(a.ws + kOpFlagOff) + 64 * g;
+    const __amdgpu_buffer_rsrc_t ring =
+        op_rsrc(a.ws + kOpHeaderBytes + (size_t)g * R * kOpSlotBytes);
+    if (t == 0) {
+        sh_min[0][0] = sh_min[0][1] = sh_min[1][0] = sh_min[1][1] = 0;
+        sh_broken = 0;
+    }
+    __syncthreads();
+    const int ul = lane & 31, lh = lane >> 5;
+    // Thread parts of the byte offsets (the register parts are constants).
+    const uint32_t ld_v = ((uint32_t)m * kOpRowF4 + ul + (wv << 5) + (lh << 8)) * 16;
+    const uint32_t xw_v = ((uint32_t)((lh | (wv << 1)) * 32 + m) * UL + ul) * 16;
+    const uint32_t xr_v = ((uint32_t)(m * 32 + (lh | (wv << 1))) * UL + ul) * 16;
+    const uint32_t st_v = ((uint32_t)lh * kOpRowF4 + m * 256 + (wv << 5) + ul) * 16;
+    float cs = a.scale;
+    if (__popc((unsigned)lane & dpp_sign_lanes(0, 6)) & 1)
+        cs = -cs;
+
+    // Wave 0 waits until every member has written >= need_w slices and read
+    // >= need_r; the decision to call this is the same in every wave.
+    auto wait_flags = [&](int need_w, int need_r) {
+        __syncthreads();
+        if (t < 64 && !sh_broken) {
+            bool ok = false;
+            for (int i = 0; i < kOpSpin; ++i) {
+                const int v = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+                if (__ballot(v < (lane < 32 ? need_w : need_r)) == 0) {
+                    ok = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (t == 0 && !ok) {
+                sh_broken = 1;
+                atomicOr(err, kOpErrTimeout);
+            }
+        }
+        __syncthreads();
+    };
+
+    const int cx = (a.ncomp - xcd + kOpXcds - 1) / kOpXcds;   // components c = xcd + 8 i
+    int q = 0;                                                // slices so far
+    int seq = 0;                                              // components so far
+    V x[kOpRegs];
+    for (int i = gi; i < cx;) {
+        const int c = xcd + kOpXcds * i;
+        float* const base = a.im ? ((c & 1) ? a.im : a.re) + ((size_t)(c >> 1) << kOpN)
+                                 : a.re + ((size_t)c << kOpN);
+        const __amdgpu_buffer_rsrc_t comp = op_rsrc(base);
+#pragma unroll
+        for (int j = 0; j < kOpRegs; ++j)
+            x[j] = op_load<kOpNt>(comp, ld_v, (((j & 7) << 9) | ((j >> 3) << 12)) * 16);
+        if (m == 0 && t == 0) {
+            const int nx = __hip_atomic_fetch_add(queue + xcd, 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT) + kOpGroupsPerXcd;
+            __hip_atomic_store(nxt + ((seq + 1) & 1),
+                               ((unsigned long long)(seq + 1) << 32) | (unsigned)nx,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        op_pin(x);
+        // Row factor H_15: in-vector bits 0-1, register bits 11-14, lane bits
+        // 2-6 and 10, then the exchange to L1 and register bits 7-9.
+#pragma unroll
+        for (int j = 0; j < kOpRegs; ++j)
+            in_vector(x[j]);
+        register_stages<4, kOpRegs>(x);
+        LaneStages<0, 6, 0, kOpRegs, V, float, false>::run(x, lane);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                L[ul | (wv << 5) | (lh << 8) | (r << 9)] = x[(p << 3) | r];
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                x[(p << 3) | s] = L[ul | (s << 5) | (lh << 8) | (wv << 9)];
+        }
+        register_stages<3, kOpRegs>(x);
+        op_pin(x);
+        // The ring exchange: iteration s stores slice s and loads slice s - 1.
+#pragma unroll
+        for (int s = 0; s <= S; ++s) {
+            const int qw = q + s, qr = q + s - 1;
+            const int need_w = s >= 1 ? qr + 1 : 0;
+            const int need_r = s < S ? qw - R + 1 : 0;
+            const int cb = qw & 1;
+            if (!(sh_min[cb][0] >= need_w && sh_min[cb][1] >= need_r))
+                wait_flags(need_w, need_r);
+            if (s < S) {
+                const uint32_t so = (uint32_t)(qw % R) * (uint32_t)kOpSlotBytes;
+                op_store<0>(ring, xw_v, so, x[s]);
+                op_store<0>(ring, xw_v, so + 16u * 16 * 32 * UL, x[8 + s]);
+            }
+            if (s >= 1) {
+                const uint32_t so = (uint32_t)(qr % R) * (uint32_t)kOpSlotBytes;
+                x[s - 1] = op_load<kOpDevice>(ring, xr_v, so);
+                x[8 + s - 1] = op_load<kOpDevice>(ring, xr_v, so + 16u * 16 * UL);
+            }
+            int pv = 0;
+            if (t < 64)
+                pv = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (t < 64) {
+                for (int o = 16; o >= 1; o >>= 1)
+                    pv = min(pv, __shfl_xor(pv, o));
+                const int mw = __shfl(pv, 0), mr = __shfl(pv, 32);
+                if (t == 0) {
+                    sh_min[cb ^ 1][0] = mw;
+                    sh_min[cb ^ 1][1] = mr;
+                }
+            }
+            __syncthreads();
+            if (t == 0) {
+                if (s < S)
+                    __hip_atomic_store(prog + m, qw + 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (s >= 1)
+                    __hip_atomic_store(prog + 32 + m, qr + 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+        q += S;
+        op_pin(x);
+        // Column factor H_5: row bit 4 in registers, row bit 0 on lane 5,
+        // then the exchange to R1 and row bits 1-3 in registers.
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            butterfly(x[j], x[j | 8]);
+        lane_stage<5, kOpRegs, V, float>(x, lane);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                L[ul | (s << 5) | (lh << 8) | (wv << 9)] = x[(p << 3) | s];
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                x[(p << 3) | k] = L[ul | (wv << 5) | (lh << 8) | (k << 9)];
+        }
+        register_stages<3, kOpRegs>(x);
+#pragma unroll
+        for (int j = 0; j < kOpRegs; ++j)
+            x[j] *= cs;
+#pragma unroll
+        for (int j = 0; j < kOpRegs; ++j)
+            op_store<kOpNt>(comp, st_v, ((((j & 7) << 1) | ((j >> 3) << 4)) * kOpRowF4) * 16, x[j]);
+        // The group's next component.
+        if (t == 0) {
+            unsigned long long v = 0;
+            for (int k = 0; k < kOpSpin; ++k) {
+                v = __hip_atomic_load(nxt + ((seq + 1) & 1), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+                if ((int)(v >> 32) == seq + 1)
+                    break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if ((int)(v >> 32) != seq + 1) {
+                atomicOr(err, kOpErrQueue);
+                v = 0x7fffffffu;
+            }
+            sh_next = (int)(unsigned)v;
+        }
+        __syncthreads();
+        i = sh_next;
+        ++seq;
+    }
+}
+
+}  // namespace
+
+hipError_t onepass_occupancy(int* blocks_per_cu)
+{
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&onepass_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kOpLdsBytes);
+    if (e != hipSuccess)
+        return e;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks_per_cu, reinterpret_cast<const void*>(&onepass_kernel), kOpThreads, kOpLdsBytes);
+}
+
+hipError_t launch_onepass(float* re, float* im, int ncomp, void* ws, float scale,
+                          hipStream_t stream, hipEvent_t start, hipEvent_t stop)
+{
+    unsigned char* const w = reinterpret_cast<unsigned char*>(ws);
+    hipLaunchKernelGGL(onepass_reset_kernel, dim3(1), dim3(kOpThreads), 0, stream, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    OnepassArgs a{re, im, w, ncomp, scale};
+    void* kargs[] = {&a};
+    const dim3 grid(kOpGroups * kOpMembers, 1, 1);
+    if (start || stop)
+        return hipExtLaunchKernel(reinterpret_cast<const void*>(&onepass_kernel), grid,
+                                  dim3(kOpThreads, 1, 1), kargs, kOpLdsBytes, stream, start, stop,
+                                  0);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&onepass_kernel), grid,
+                           dim3(kOpThreads, 1, 1), kargs, kOpLdsBytes, stream);
+}
+
+}  // namespace qse
