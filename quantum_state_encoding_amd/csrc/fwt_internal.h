@@ -198,6 +198,7 @@ constexpr int kOpGroups = kOpXcds * kOpGroupsPerXcd;
 constexpr int kOpThreads = 512;
 constexpr int kOpSlices = 8;
 constexpr int kOpRingSlots = 2;
+constexpr int kOpLag = 1;                // slices between a slice's store and its load
 constexpr size_t kOpSlotBytes = ((size_t)4 << 20) / kOpSlices;   // one slice of a component
 constexpr size_t kOpErrOff = 0;          // int: error bits
 constexpr size_t kOpQueueOff = 256;      // int[kOpXcds]: components taken per XCD

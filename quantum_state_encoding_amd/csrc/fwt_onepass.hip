@@ -46,7 +46,11 @@ namespace {
 // values for all 32 destinations), then loads slice s - 1 as written by
 // every member, waits for both with one s_waitcnt, and publishes "slices
 // written" and "slices read" in its two progress words (plain stores: they
-// land in the XCD's L2).  Before storing into a slot it needs every member
+// land in the XCD's L2).  The ring's size is set by the L2: two groups'
+// rings of 2 x 512 KiB share an XCD's 4 MB with the HBM streams; a third
+// slot (loads two slices behind the stores, so their progress words are
+// usually published before they are polled) made every ring round trip
+// about three times slower and the call 21 % slower.  Before storing into a slot it needs every member
 // to have read the slice that last used it; before loading a slice, every
 // member to have written it.  Wave 0 reads the group's 64 progress words
 // with device-scope loads (sc1: they miss the CU's L1 and hit the L2; a
@@ -134,13 +138,15 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
     onepass_kernel(OnepassArgs a)
 {
     using V = Vec<float>::type;
-    constexpr int S = kOpSlices, R = kOpRingSlots, UL = 256 / S;
+    constexpr int S = kOpSlices, R = kOpRingSlots, LAG = kOpLag, UL = 256 / S;
+    static_assert(LAG >= 1 && R > LAG, "a slot is rewritten only after its slice was read");
     static_assert(S == 8 && kOpRegs == 2 * S, "slice s is registers s and 8 + s");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     V* const L = reinterpret_cast<V*>(lds_raw);
     __shared__ int sh_min[2][2];   // cached minima of the progress words, by parity
     __shared__ int sh_next, sh_broken, sh_xcd, sh_rank;
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    // The logical lane: mirrored_lane order makes lane bit 2 a DPP stage.
+    const int t = threadIdx.x, lane = mirrored_lane(t & 63), wv = t >> 6;
     int* const err = reinterpret_cast<int*>(a.ws + kOpErrOff);
     // The workgroup's XCD and CU, from the hardware (the dispatcher deals
     // workgroups to the XCDs in turn, but not always starting from the
@@ -190,7 +196,7 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
     const uint32_t xr_v = ((uint32_t)(m * 32 + (lh | (wv << 1))) * UL + ul) * 16;
     const uint32_t st_v = ((uint32_t)lh * kOpRowF4 + m * 256 + (wv << 5) + ul) * 16;
     float cs = a.scale;
-    if (__popc((unsigned)lane & dpp_sign_lanes(0, 6)) & 1)
+    if (__popc((unsigned)lane & dpp_sign_lanes(0, 6, true)) & 1)
         cs = -cs;
 
     // Wave 0 waits until every member has written >= need_w slices and read
@@ -216,6 +222,7 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
         __syncthreads();
     };
 
+    unsigned long long spec_next = 0;                          // thread 0 only
     const int cx = (a.ncomp - xcd + kOpXcds - 1) / kOpXcds;   // components c = xcd + 8 i
     int q = 0;                                                // slices so far
     int seq = 0;                                              // components so far
@@ -242,7 +249,7 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
         for (int j = 0; j < kOpRegs; ++j)
             in_vector(x[j]);
         register_stages<4, kOpRegs>(x);
-        LaneStages<0, 6, 0, kOpRegs, V, float, false>::run(x, lane);
+        LaneStages<0, 6, 0, kOpRegs, V, float, true>::run(x, lane);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             __syncthreads();
@@ -256,11 +263,11 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
         }
         register_stages<3, kOpRegs>(x);
         op_pin(x);
-        // The ring exchange: iteration s stores slice s and loads slice s - 1.
+        // The ring exchange: iteration s stores slice s and loads slice s - LAG.
 #pragma unroll
-        for (int s = 0; s <= S; ++s) {
-            const int qw = q + s, qr = q + s - 1;
-            const int need_w = s >= 1 ? qr + 1 : 0;
+        for (int s = 0; s < S + LAG; ++s) {
+            const int qw = q + s, qr = q + s - LAG;
+            const int need_w = s >= LAG ? qr + 1 : 0;
             const int need_r = s < S ? qw - R + 1 : 0;
             const int cb = qw & 1;
             if (!(sh_min[cb][0] >= need_w && sh_min[cb][1] >= need_r))
@@ -270,14 +277,17 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
                 op_store<0>(ring, xw_v, so, x[s]);
                 op_store<0>(ring, xw_v, so + 16u * 16 * 32 * UL, x[8 + s]);
             }
-            if (s >= 1) {
+            if (s >= LAG) {
                 const uint32_t so = (uint32_t)(qr % R) * (uint32_t)kOpSlotBytes;
-                x[s - 1] = op_load<kOpDevice>(ring, xr_v, so);
-                x[8 + s - 1] = op_load<kOpDevice>(ring, xr_v, so + 16u * 16 * UL);
+                x[s - LAG] = op_load<kOpDevice>(ring, xr_v, so);
+                x[8 + s - LAG] = op_load<kOpDevice>(ring, xr_v, so + 16u * 16 * UL);
             }
             int pv = 0;
             if (t < 64)
                 pv = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (s == S + LAG - 1 && t == 0)   // the group's next component, published long ago
+                spec_next = __hip_atomic_load(nxt + ((seq + 1) & 1), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             if (t < 64) {
                 for (int o = 16; o >= 1; o >>= 1)
@@ -293,7 +303,7 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
                 if (s < S)
                     __hip_atomic_store(prog + m, qw + 1, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_WORKGROUP);
-                if (s >= 1)
+                if (s >= LAG)
                     __hip_atomic_store(prog + 32 + m, qr + 1, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_WORKGROUP);
             }
@@ -305,7 +315,7 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             butterfly(x[j], x[j | 8]);
-        lane_stage<5, kOpRegs, V, float>(x, lane);
+        lane_stage<5, kOpRegs, V, float, true>(x, lane);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             __syncthreads();
@@ -326,13 +336,11 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
             op_store<kOpNt>(comp, st_v, ((((j & 7) << 1) | ((j >> 3) << 4)) * kOpRowF4) * 16, x[j]);
         // The group's next component.
         if (t == 0) {
-            unsigned long long v = 0;
-            for (int k = 0; k < kOpSpin; ++k) {
+            unsigned long long v = spec_next;
+            for (int k = 0; k < kOpSpin && (int)(v >> 32) != seq + 1; ++k) {
+                __builtin_amdgcn_s_sleep(1);
                 v = __hip_atomic_load(nxt + ((seq + 1) & 1), __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
-                if ((int)(v >> 32) == seq + 1)
-                    break;
-                __builtin_amdgcn_s_sleep(1);
             }
             if ((int)(v >> 32) != seq + 1) {
                 atomicOr(err, kOpErrQueue);
