@@ -823,7 +823,7 @@ def summarize_counters(workload, counter_dir, command, tag):
     workload's own pass kernels and the streaming copy)."""
     import quantum_state_encoding_amd as qse
     w = workloads.WORKLOADS[workload]
-    mine = ["stream_copy_kernel"]
+    mine = ["stream_copy_kernel", "onepass_kernel"]
     for _, sp in _profiled_plans(w):
         plan = qse.Plan(w.n, w.dtype, split=sp)
         mine += [plan.kernel_name(i, w.batch) for i in range(plan.num_passes)]
