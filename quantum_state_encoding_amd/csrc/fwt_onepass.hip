@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     V* const L = reinterpret_cast<V*>(lds_raw);
     __shared__ int sh_min[2][2];   // cached minima of the progress words, by parity
-    __shared__ int sh_next, sh_broken, sh_xcd, sh_rank;
+    __shared__ int sh_next, sh_spec, sh_broken, sh_xcd, sh_rank;
     // The logical lane: mirrored_lane order makes lane bit 2 a DPP stage.
     const int t = threadIdx.x, lane = mirrored_lane(t & 63), wv = t >> 6;
     int* const err = reinterpret_cast<int*>(a.ws + kOpErrOff);
@@ -227,14 +227,24 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
     int q = 0;                                                // slices so far
     int seq = 0;                                              // components so far
     V x[kOpRegs];
-    for (int i = gi; i < cx;) {
+    auto comp_rsrc = [&](int i) {
         const int c = xcd + kOpXcds * i;
-        float* const base = a.im ? ((c & 1) ? a.im : a.re) + ((size_t)(c >> 1) << kOpN)
-                                 : a.re + ((size_t)c << kOpN);
-        const __amdgpu_buffer_rsrc_t comp = op_rsrc(base);
+        return op_rsrc(a.im ? ((c & 1) ? a.im : a.re) + ((size_t)(c >> 1) << kOpN)
+                            : a.re + ((size_t)c << kOpN));
+    };
+    auto load_offset = [](int j) -> uint32_t {
+        return (uint32_t)((((j & 7) << 9) | ((j >> 3) << 12)) * 16);
+    };
+    __amdgpu_buffer_rsrc_t comp = comp_rsrc(gi);
+    bool loaded = false;   // the component's loads were issued with the last stores
+    for (int i = gi; i < cx;) {
+        if (!loaded) {     // uniform across the workgroup
+            comp = comp_rsrc(i);
 #pragma unroll
-        for (int j = 0; j < kOpRegs; ++j)
-            x[j] = op_load<kOpNt>(comp, ld_v, (((j & 7) << 9) | ((j >> 3) << 12)) * 16);
+            for (int j = 0; j < kOpRegs; ++j)
+                x[j] = op_load<kOpNt>(comp, ld_v, load_offset(j));
+        }
+        loaded = false;
         if (m == 0 && t == 0) {
             const int nx = __hip_atomic_fetch_add(queue + xcd, 1, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT) + kOpGroupsPerXcd;
@@ -310,6 +320,8 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
         }
         q += S;
         op_pin(x);
+        if (t == 0)   // the group's next component, if the speculative load saw it
+            sh_spec = (int)(spec_next >> 32) == seq + 1 ? (int)(unsigned)spec_next : -1;
         // Column factor H_5: row bit 4 in registers, row bit 0 on lane 5,
         // then the exchange to R1 and row bits 1-3 in registers.
 #pragma unroll
@@ -331,6 +343,26 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int j = 0; j < kOpRegs; ++j)
             x[j] *= cs;
+        // Store; when the next component is known, each register's store is
+        // followed by its load for that component.  (sh_spec was written
+        // before the column exchange's barriers; uniform.)
+        const int spec = sh_spec;
+        if (spec >= 0) {
+            const bool more = spec < cx;
+            const __amdgpu_buffer_rsrc_t next = comp_rsrc(more ? spec : i);
+#pragma unroll
+            for (int j = 0; j < kOpRegs; ++j) {
+                op_store<kOpNt>(comp, st_v, ((((j & 7) << 1) | ((j >> 3) << 4)) * kOpRowF4) * 16,
+                                x[j]);
+                if (more)
+                    x[j] = op_load<kOpNt>(next, ld_v, load_offset(j));
+            }
+            comp = next;
+            loaded = more;
+            i = spec;
+            ++seq;
+            continue;
+        }
 #pragma unroll
         for (int j = 0; j < kOpRegs; ++j)
             op_store<kOpNt>(comp, st_v, ((((j & 7) << 1) | ((j >> 3) << 4)) * kOpRowF4) * 16, x[j]);
