@@ -6,7 +6,8 @@
 //   - two unnormalised calls map x to 2^n x exactly (zero-mean small
 //     integers: every partial sum stays an exact integer);
 //   - e_0 maps to 2^(-n/2) times the all-ones vector when normalised;
-// over one-, two- and three-pass default plans in fp32 and fp64.
+// over one-, two- and three-pass default plans in fp32 and fp64; and the
+// one-pass entry point (fwt_execute_ws) against fwt_execute at n = 20.
 // Prints "abi consumer: ok" and exits 0 on success.
 #include <hip/hip_runtime.h>
 
@@ -99,11 +100,70 @@ static int run_case(int n, fwt_dtype dtype, int64_t batch, hipStream_t stream, i
     return 0;
 }
 
+// The one-pass entry point on the default fp32 n = 20 plan: the workspace
+// query, then fwt_execute_ws against fwt_execute on the same small-integer
+// input (both exact, so equal bit for bit), a zero error word, and a
+// workspace one byte short rejected before anything runs.
+static int run_workspace_case(hipStream_t stream, int* bad)
+{
+    const int n = 20;
+    const int64_t batch = 3, N = (int64_t)1 << n, tot = batch * N;
+    std::vector<float> x(tot), a(tot), b(tot);
+    uint64_t s = 0x2545F4914F6CDD1Dull;
+    for (int64_t i = 0; i < tot; ++i) {
+        s = s * 6364136223846793005ull + 1442695040888963407ull;
+        x[i] = (float)((int)((s >> 33) % 17) - 8);
+    }
+    fwt_plan_t plan = nullptr;
+    if (fwt_plan_create(&plan, n, FWT_F32, FWT_PATH_AUTO) != FWT_OK) {
+        ++*bad;
+        return 0;
+    }
+    size_t need = 0;
+    if (fwt_workspace_size(plan, batch, 1, &need) != FWT_OK || need == 0) {
+        std::printf("one-pass kernel unavailable (workspace %zu)\n", need);
+        ++*bad;
+        fwt_plan_destroy(plan);
+        return 0;
+    }
+    float *d_a = nullptr, *d_b = nullptr, *d_ai = nullptr, *d_bi = nullptr;
+    void* ws = nullptr;
+    HIP_OK(hipMalloc(&d_a, sizeof(float) * tot));
+    HIP_OK(hipMalloc(&d_b, sizeof(float) * tot));
+    HIP_OK(hipMalloc(&d_ai, sizeof(float) * tot));
+    HIP_OK(hipMalloc(&d_bi, sizeof(float) * tot));
+    HIP_OK(hipMalloc(&ws, need));
+    for (float* d : {d_a, d_b, d_ai, d_bi})
+        HIP_OK(hipMemcpy(d, x.data(), sizeof(float) * tot, hipMemcpyHostToDevice));
+    *bad += fwt_execute_ws(plan, batch, n, d_a, d_ai, 1, ws, need - 1, stream) != FWT_EINVAL;
+    *bad += fwt_execute(plan, batch, n, d_a, d_ai, 1, stream) != FWT_OK;
+    *bad += fwt_execute_ws(plan, batch, n, d_b, d_bi, 1, ws, need, stream) != FWT_OK;
+    HIP_OK(hipStreamSynchronize(stream));
+    int bits = -1;
+    *bad += fwt_workspace_status(ws, &bits) != FWT_OK || bits != 0;
+    HIP_OK(hipMemcpy(a.data(), d_a, sizeof(float) * tot, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(b.data(), d_b, sizeof(float) * tot, hipMemcpyDeviceToHost));
+    for (int64_t i = 0; i < tot; ++i)
+        *bad += a[i] != b[i];
+    HIP_OK(hipMemcpy(a.data(), d_ai, sizeof(float) * tot, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(b.data(), d_bi, sizeof(float) * tot, hipMemcpyDeviceToHost));
+    for (int64_t i = 0; i < tot; ++i)
+        *bad += a[i] != b[i];
+    fwt_plan_destroy(plan);
+    for (void* d : {(void*)d_a, (void*)d_b, (void*)d_ai, (void*)d_bi, ws})
+        HIP_OK(hipFree(d));
+    std::printf("one-pass n=20 f32 batch=%lld workspace=%zu bytes error bits=%d\n",
+                (long long)batch, need, bits);
+    return 0;
+}
+
 int main()
 {
     hipStream_t stream;
     HIP_OK(hipStreamCreate(&stream));
     int bad = 0;
+    if (run_workspace_case(stream, &bad))
+        return 2;
     const int nf[] = {1, 5, 10, 12, 15, 16, 20, 22, 27};
     for (int n : nf)
         if (run_case<float>(n, FWT_F32, n <= 20 ? 3 : 1, stream, &bad))

@@ -1,7 +1,8 @@
 """The C ABI used from a plain C++ program (tests/c_abi/abi_consumer.cpp,
 built by __graft_entry__.build()): hipMalloc'd buffers and a stream of its
 own, no Python binding and no torch.  It checks closed forms of the
-transform over one-, two- and three-pass default plans in fp32 and fp64."""
+transform over one-, two- and three-pass default plans in fp32 and fp64,
+and the one-pass entry point (fwt_execute_ws) against fwt_execute."""
 import os
 import subprocess
 import sys
