@@ -53,6 +53,34 @@ def test_roofline_sums_the_counter_bytes_of_every_pass(monkeypatch):
     assert rl["write_bytes"] == pytest.approx((2000.0 + 4000.0) * 1.0 * 1024)
 
 
+def test_roofline_of_the_one_pass_kernel(monkeypatch):
+    """One launch over the whole state: algorithmic bytes 2 x S, achieved =
+    2 x S over the kernel's duration; the counter record of the configured
+    plan is used only when it, too, was taken on the one-pass kernel."""
+    w = workloads.WORKLOADS["n20_b256_f32"]
+    r = _measured(w, [1.100], w.batch, (20,))
+    r.update({"onepass": True, "kernel_names": ["onepass_kernel"]})
+    rec = {"fetch_scale": 2.0, "write_scale": 1.0,
+           "plans": {"as configured": {"onepass": True, "passes": {
+               "0": {"bytes_per_launch": 4.76e9, "fetch_kib": 1.05e6, "write_kib": 2.5e6,
+                     "kernel": "onepass_kernel(OnepassArgs)"}}},
+                     "two-pass": {"onepass": False, "passes": {}}}}
+    monkeypatch.setattr(bench, "traffic_record", lambda name: rec)
+    monkeypatch.setattr(bench, "lds_conflicts", lambda name, kernel: None)
+    rl = bench.roofline(w, r, {"gbps": 6650.0})
+    assert rl["algorithmic_bytes"] == 2 * w.state_bytes == 4 << 30
+    assert rl["achieved"] == pytest.approx(2 * w.state_bytes / 1.100e-3 / 1e9)
+    assert 0.48 < rl["frac"] < 0.49
+    assert rl["launches_per_step"] == 1 and "onepass_kernel" in rl["kernel"]
+    assert rl["traffic"] == pytest.approx(4.76e9)
+    # a record taken on fwt_execute's passes does not price the one-pass kernel
+    rec["plans"]["as configured"]["onepass"] = False
+    assert bench.roofline(w, r, {"gbps": 6650.0})["traffic"] is None
+    rec2 = bench.config_record(4, w, r, None, "as configured")
+    assert rec2["passes"] == 1 and rec2["path"].startswith("one HBM pass")
+    assert rec2["gbps_accounted"] == pytest.approx(rec2["gbps_algorithmic"])
+
+
 def test_config_record_carries_the_measurement_fields():
     w = workloads.WORKLOADS["n24_b16_f64"]
     r = _measured(w, [0.090, 0.081], 1, (14, 10))
