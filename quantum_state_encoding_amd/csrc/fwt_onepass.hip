@@ -192,11 +192,22 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
     const int ul = lane & 31, lh = lane >> 5;
     // Thread parts of the byte offsets (the register parts are constants).
     const uint32_t ld_v = ((uint32_t)m * kOpRowF4 + ul + (wv << 5) + (lh << 8)) * 16;
-    const uint32_t xw_v = ((uint32_t)((lh | (wv << 1)) * 32 + m) * UL + ul) * 16;
-    const uint32_t xr_v = ((uint32_t)(m * 32 + (lh | (wv << 1))) * UL + ul) * 16;
-    const uint32_t st_v = ((uint32_t)lh * kOpRowF4 + m * 256 + (wv << 5) + ul) * 16;
+    // Ring slot layout: float4 (destination d, source r, column u of the
+    // slice) at ((d * 8 + u / 4) * 32 + r) * 4 + u % 4, so that a reader's
+    // wave loads 1 KiB in one piece (lanes 0-1 = u % 4, lanes 2-5 = r % 16).
+    const uint32_t xw_v =
+        ((uint32_t)(((lh | (wv << 1)) * 8 + (ul >> 2)) * 32 + m) * 4 + (ul & 3)) * 16;
+    const uint32_t xr_v = ((uint32_t)((m * 8 + wv) * 32 + (lane >> 2)) * 4 + (lane & 3)) * 16;
+    // Column output: source row lane >> 2 (+ 16), column u = (lane & 3) |
+    // wv << 2 of the slice, in member m's 1024-column slice.
+    const uint32_t st_v =
+        ((uint32_t)(lane >> 2) * kOpRowF4 + m * 256 + (wv << 2) + (lane & 3)) * 16;
+    // The scale times the signs of the fp32 DPP lane stages: the row stages
+    // on lane bits 0-3 left them by element bits 2-5, now lane bits 0-1 and
+    // wave bits 0-1; the column stages on lane bits 2-3 leave them by
+    // those lanes.
     float cs = a.scale;
-    if (__popc((unsigned)lane & dpp_sign_lanes(0, 6, true)) & 1)
+    if ((__popc((unsigned)lane & 15u) + __popc((unsigned)wv & 3u)) & 1)
         cs = -cs;
 
     // Wave 0 waits until every member has written >= need_w slices and read
@@ -237,6 +248,22 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
     };
     __amdgpu_buffer_rsrc_t comp = comp_rsrc(gi);
     bool loaded = false;   // the component's loads were issued with the last stores
+    // Column factor H_5 on slice k as loaded from the ring: registers k and
+    // 8 + k hold source rows (lane >> 2) and 16 + (lane >> 2), columns
+    // (lane & 3) | wv << 2 of the slice: the source bits are register bit 3
+    // and lane bits 2-5, so the whole factor runs in registers and lanes.
+    auto column_slice = [&](int k) {
+        V y[2] = {x[k], x[8 + k]};
+        butterfly(y[0], y[1]);
+        lane_stage<2, 2, V, float, true>(y, lane);
+        lane_stage<3, 2, V, float, true>(y, lane);
+        lane_stage<4, 2, V, float, true>(y, lane);
+        lane_stage<5, 2, V, float, true>(y, lane);
+        y[0] *= cs;
+        y[1] *= cs;
+        op_store<kOpNt>(comp, st_v, (uint32_t)(k * UL) * 16, y[0]);
+        op_store<kOpNt>(comp, st_v, (uint32_t)(16 * kOpRowF4 + k * UL) * 16, y[1]);
+    };
     for (int i = gi; i < cx;) {
         if (!loaded) {     // uniform across the workgroup
             comp = comp_rsrc(i);
@@ -273,7 +300,11 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
         }
         register_stages<3, kOpRegs>(x);
         op_pin(x);
-        // The ring exchange: iteration s stores slice s and loads slice s - LAG.
+        // The ring exchange: iteration s stores slice s, loads slice s - LAG,
+        // and applies the column factor to slice s - LAG - 1 (loaded in the
+        // previous iteration) and stores it to HBM, while the slice loads
+        // and stores of this iteration are in flight.
+        static_assert(LAG == 1, "column work trails the loads by one iteration");
 #pragma unroll
         for (int s = 0; s < S + LAG; ++s) {
             const int qw = q + s, qr = q + s - LAG;
@@ -285,13 +316,15 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
             if (s < S) {
                 const uint32_t so = (uint32_t)(qw % R) * (uint32_t)kOpSlotBytes;
                 op_store<0>(ring, xw_v, so, x[s]);
-                op_store<0>(ring, xw_v, so + 16u * 16 * 32 * UL, x[8 + s]);
+                op_store<0>(ring, xw_v, so + 16u * 16 * 8 * 32 * 4, x[8 + s]);
             }
             if (s >= LAG) {
                 const uint32_t so = (uint32_t)(qr % R) * (uint32_t)kOpSlotBytes;
                 x[s - LAG] = op_load<kOpDevice>(ring, xr_v, so);
-                x[8 + s - LAG] = op_load<kOpDevice>(ring, xr_v, so + 16u * 16 * UL);
+                x[8 + s - LAG] = op_load<kOpDevice>(ring, xr_v, so + 16u * 16 * 4);
             }
+            if (s >= LAG + 1)
+                column_slice(s - LAG - 1);
             int pv = 0;
             if (t < 64)
                 pv = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -306,6 +339,9 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
                 if (t == 0) {
                     sh_min[cb ^ 1][0] = mw;
                     sh_min[cb ^ 1][1] = mr;
+                    if (s == S + LAG - 1)   // read by every thread after the barrier
+                        sh_spec = (int)(spec_next >> 32) == seq + 1 ? (int)(unsigned)spec_next
+                                                                    : -1;
                 }
             }
             __syncthreads();
@@ -319,53 +355,21 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
             }
         }
         q += S;
-        op_pin(x);
-        if (t == 0)   // the group's next component, if the speculative load saw it
-            sh_spec = (int)(spec_next >> 32) == seq + 1 ? (int)(unsigned)spec_next : -1;
-        // Column factor H_5: row bit 4 in registers, row bit 0 on lane 5,
-        // then the exchange to R1 and row bits 1-3 in registers.
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            butterfly(x[j], x[j | 8]);
-        lane_stage<5, kOpRegs, V, float, true>(x, lane);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            __syncthreads();
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                L[ul | (s << 5) | (lh << 8) | (wv << 9)] = x[(p << 3) | s];
-            __syncthreads();
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                x[(p << 3) | k] = L[ul | (wv << 5) | (lh << 8) | (k << 9)];
-        }
-        register_stages<3, kOpRegs>(x);
-#pragma unroll
-        for (int j = 0; j < kOpRegs; ++j)
-            x[j] *= cs;
-        // Store; when the next component is known, each register's store is
-        // followed by its load for that component.  (sh_spec was written
-        // before the column exchange's barriers; uniform.)
+        column_slice(S - 1);
+        // When the next component is known, its loads follow at once.
         const int spec = sh_spec;
         if (spec >= 0) {
-            const bool more = spec < cx;
-            const __amdgpu_buffer_rsrc_t next = comp_rsrc(more ? spec : i);
+            if (spec < cx) {
+                comp = comp_rsrc(spec);
 #pragma unroll
-            for (int j = 0; j < kOpRegs; ++j) {
-                op_store<kOpNt>(comp, st_v, ((((j & 7) << 1) | ((j >> 3) << 4)) * kOpRowF4) * 16,
-                                x[j]);
-                if (more)
-                    x[j] = op_load<kOpNt>(next, ld_v, load_offset(j));
+                for (int j = 0; j < kOpRegs; ++j)
+                    x[j] = op_load<kOpNt>(comp, ld_v, load_offset(j));
+                loaded = true;
             }
-            comp = next;
-            loaded = more;
             i = spec;
             ++seq;
             continue;
         }
-#pragma unroll
-        for (int j = 0; j < kOpRegs; ++j)
-            op_store<kOpNt>(comp, st_v, ((((j & 7) << 1) | ((j >> 3) << 4)) * kOpRowF4) * 16, x[j]);
         // The group's next component.
         if (t == 0) {
             unsigned long long v = spec_next;
