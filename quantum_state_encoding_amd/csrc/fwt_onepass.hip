@@ -32,41 +32,47 @@ namespace {
 //            j = bit 14 << 3 | bits 7-9.  Element bits 10-14 are then the
 //            destination column slice (lane 5, waves, register bit 3), and
 //            register bits 0-2 (element bits 7-9) the ring slice s.
-//  column R0 (as read from the ring): lanes 0-4 = bits 2-6 as before,
-//            lane 5 = row bit 0, waves = row bits 1-3, registers
-//            j = row bit 4 << 3 | s;
-//  store R1: after one LDS exchange, waves = s and registers j = row bit 4
-//            << 3 | row bits 1-3.
-// Lanes 0-4 keep element bits 2-6 throughout, so the sign that the fp32
-// DPP lane stages leave on lanes with odd popcount(lane & 0xB) is still
-// attached to the same lanes at the end and is removed with the scale.
+//  column:   slice s as read from the ring: registers s and 8 + s hold
+//            source rows (l >> 2) and 16 + (l >> 2), columns (l & 3) |
+//            w << 2 of the slice (element bits 2-6).  The five source bits
+//            are lane bits 2-5 and one register bit, so the column factor
+//            runs on the slice's two registers alone, inside the ring loop,
+//            and the slice goes to HBM while the next slice is exchanged.
+// The fp32 DPP lane stages leave a sign on some lanes: the row stages on
+// lane bits 0-3 by element bits 2-5 (in the column layout lane bits 0-1
+// and wave bits 0-1), the column stages on lane bits 2-3 by those lanes;
+// the scale removes both.
 //
 // The ring exchange, per slice s (8 per component, 512 KiB each, ring of 2
 // slots per group): each workgroup stores its registers of slice s (the
-// values for all 32 destinations), then loads slice s - 1 as written by
-// every member, waits for both with one s_waitcnt, and publishes "slices
-// written" and "slices read" in its two progress words (plain stores: they
-// land in the XCD's L2).  The ring's size is set by the L2: two groups'
+// values for all 32 destinations), loads slice s - 1 as written by every
+// member, applies the column factor to slice s - 2 and stores it to HBM,
+// waits for all of it with one s_waitcnt, and publishes "slices written"
+// and "slices read" in its two progress words (plain stores: they land in
+// the XCD's L2).  A slot holds float4 (destination d, source r, column u)
+// at ((d * 8 + u / 4) * 32 + r) * 4 + u % 4, so a reader's wave loads
+// 1 KiB in one piece.  The ring's size is set by the L2: two groups'
 // rings of 2 x 512 KiB share an XCD's 4 MB with the HBM streams; a third
 // slot (loads two slices behind the stores, so their progress words are
 // usually published before they are polled) made every ring round trip
-// about three times slower and the call 21 % slower.  Before storing into a slot it needs every member
-// to have read the slice that last used it; before loading a slice, every
-// member to have written it.  Wave 0 reads the group's 64 progress words
-// with device-scope loads (sc1: they miss the CU's L1 and hit the L2; a
-// device-scope atomic would leave the L2 and take about 1.2 us here) in
-// the same round trip as the slice's data, so a wait costs a round trip
-// only when a member is behind.  The slice loads are device-scope too: a
-// plain load can return a line the CU's L1 kept from the slot's previous
-// use.  Every member of a group runs on the same XCD: a workgroup reads its
-// XCD and CU from the XCC_ID and HW_ID registers and joins a group with two
-// atomic adds (the dispatcher deals the 512 workgroups to the 8 XCDs in
-// turn, 64 each, two per CU, but the first XCD it serves varies), so one L2
-// serves the group, and the two workgroups of a CU belong to different
-// groups (two members of one group on one CU would halve that pair's
-// share of the CU, and the whole group waits for them).  All 2 x 256 workgroups are resident together
-// (at most 128 VGPRs and 64 KiB of LDS each), so every wait ends; the spin
-// bounds are only a guard, recorded in the workspace's error word.
+// about three times slower and the call 21 % slower.  Before storing into
+// a slot a workgroup needs every member to have read the slice that last
+// used it; before loading a slice, every member to have written it.  Wave
+// 0 reads the group's 64 progress words with device-scope loads (sc1:
+// they miss the CU's L1 and hit the L2; a device-scope atomic would leave
+// the L2 and take about 1.2 us here) in the same round trip as the
+// slice's data, so a wait costs a round trip only when a member is behind.
+// The slice loads are device-scope too: a plain load can return a line the
+// CU's L1 kept from the slot's previous use.  Every member of a group runs
+// on the same XCD: a workgroup reads its XCD and CU from the XCC_ID and
+// HW_ID registers and joins a group with two atomic adds (the dispatcher
+// deals the 512 workgroups to the 8 XCDs in turn, 64 each, two per CU, but
+// the first XCD it serves varies), so one L2 serves the group, and the two
+// workgroups of a CU belong to different groups (two members of one group
+// on one CU would halve that pair's share of the CU, and the whole group
+// waits for them).  All 2 x 256 workgroups are resident together (at most
+// 128 VGPRs and 64 KiB of LDS each), so every wait ends; the spin bounds
+// are only a guard, recorded in the workspace's error word.
 //
 // Components are spread over the XCDs by index (c = xcd + 8 i) and over
 // an XCD's two groups by a queue: the group's first workgroup takes the
