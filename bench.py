@@ -65,13 +65,14 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    """Hash of the transform kernels' source code (the device helpers, the
-    pass kernels and the one-pass kernel): comments and whitespace are
-    dropped first, so that an edit of either keeps the counter record."""
+def kernel_source_hash(onepass=True):
+    """Hash of the source code of the kernels a counter record covers: the
+    device helpers and the pass kernels, and the one-pass kernel's source
+    when the record traced that kernel. Comments and whitespace are dropped
+    first, so that an edit of either keeps the record."""
     import re as _re
     src = ""
-    for path in KERNEL_SRC:
+    for path in KERNEL_SRC if onepass else KERNEL_SRC[:2]:
         with open(path) as f:
             src += f.read()
     src = _re.sub(r"/\*.*?\*/", "", src, flags=_re.S)
@@ -80,17 +81,22 @@ def kernel_source_hash():
     return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
+def _record_traces_onepass(rec):
+    return any(p.get("onepass") for p in rec.get("plans", {}).values())
+
+
 def traffic_record(workload):
     """The committed rocprofv3 counter record of a workload
-    (profiles/traffic.json), or None if absent or taken on an older kernel
-    source."""
+    (profiles/traffic.json), or None if absent or taken on an older source
+    of the kernels it traced."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     rec = t.get("workloads", {}).get(workload)
-    if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash(
+            _record_traces_onepass(rec)):
         return None
     return rec
 
@@ -806,7 +812,8 @@ def summarize_profile(workload, kt_dir, fetch_dir, write_dir, command, lds_dir=N
     except (OSError, ValueError):
         allt = {"workloads": {}}
     first = plans[_profiled_plans(w)[0][0]]
-    allt["workloads"][workload] = {"kernel_source_sha256_16": kernel_source_hash(),
+    allt["workloads"][workload] = {"kernel_source_sha256_16": kernel_source_hash(
+                                       any(p["onepass"] for p in plans.values())),
                                    "fetch_scale": f_scale, "write_scale": w_scale,
                                    "calibration_copy_bytes": copy_bytes,
                                    "chunk_vectors": first["chunk_vectors"],
