@@ -219,3 +219,33 @@ def test_profile_summary_of_a_cache_resident_workload_keeps_both_plans(tmp_path,
     assert d["fetch_bytes"] == pytest.approx(S / 2) and d["write_bytes"] == pytest.approx(S / 2)
     assert d["measured_over_accounted"] == pytest.approx(0.5)
     assert bench.counter_fields(w, "default plan", {"passes": 2}) == {}
+
+
+def test_counter_records_are_keyed_to_the_sources_of_the_kernels_they_traced(tmp_path,
+                                                                              monkeypatch):
+    # Three stand-in sources: helpers, pass kernels, the one-pass kernel.
+    srcs = []
+    for name, text in (("h.h", "int helper;"), ("k.hip", "int pass;"), ("o.hip", "int one;")):
+        p = tmp_path / name
+        p.write_text(text)
+        srcs.append(str(p))
+    monkeypatch.setattr(bench, "KERNEL_SRC", srcs)
+    traffic = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(traffic))
+    recs = {"passes_only": {"plans": {"as configured": {"onepass": False}}},
+            "with_onepass": {"plans": {"as configured": {"onepass": True},
+                                       "two-pass": {"onepass": False}}}}
+    recs["passes_only"]["kernel_source_sha256_16"] = bench.kernel_source_hash(False)
+    recs["with_onepass"]["kernel_source_sha256_16"] = bench.kernel_source_hash(True)
+    traffic.write_text(json.dumps({"workloads": recs}))
+    assert bench.traffic_record("passes_only") and bench.traffic_record("with_onepass")
+    # Comments and whitespace do not change the key.
+    (tmp_path / "o.hip").write_text("int  one; // a note\n")
+    assert bench.traffic_record("with_onepass")
+    # A code change in the one-pass kernel stales only the record that traced it.
+    (tmp_path / "o.hip").write_text("int one2;")
+    assert bench.traffic_record("passes_only")
+    assert bench.traffic_record("with_onepass") is None
+    # A code change in the pass kernels stales both.
+    (tmp_path / "k.hip").write_text("int pass2;")
+    assert bench.traffic_record("passes_only") is None
