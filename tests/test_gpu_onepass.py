@@ -140,6 +140,31 @@ def test_equals_two_pass_on_integers_and_repeats(plan):
         assert torch.equal(a_re, b_re) and torch.equal(a_im, b_im), "call %d" % rep
 
 
+def test_batch_past_the_benchmark_without_im(plan):
+    """300 vectors with no imaginary plane: 300 components, 37 or 38 per
+    XCD, so the groups' queues run past the benchmark's 32 components per
+    group and end unevenly.  Bit-for-bit equal to fwt_execute's two passes
+    on integers (|values| <= 8 * 2^20 stay exact in fp32), and sampled
+    vectors equal the oracle's transform."""
+    batch = 300
+    say("onepass batch=%d without im" % batch)
+    re = ints((batch, 1 << N20), 1300)
+    src = to_dev(re)
+    a = src.clone()
+    plan.execute(a, None, normalize=False)
+    ws = workspace(plan, batch, False)
+    b = src.clone()
+    plan.execute_ws(b, None, normalize=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert qse.workspace_status(ws) == 0
+    assert torch.equal(a, b)
+    for i in (0, 7, 8, 151, 299):
+        assert np.array_equal(b[i].cpu().numpy().astype(np.float64),
+                              oracle.fwt(re[i:i + 1], N20, False)[0]), "vector %d" % i
+    del src, a, b
+    torch.cuda.empty_cache()
+
+
 def test_involution_gaussian(plan):
     """Two normalised calls give back the input within tolerance."""
     say("onepass involution")
