@@ -215,7 +215,7 @@ int fwt_execute(fwt_plan_t plan, int64_t batch, int n, void* re, void* im,
  * 256-byte aligned, inside one device allocation, overlapping neither re
  * nor im).  When fwt_workspace_size is 0, `ws` is ignored (it may be NULL)
  * and this is exactly fwt_execute.  Otherwise it enqueues two kernels: one
- * workgroup that clears the workspace's 8 KiB header (a kernel, not a
+ * workgroup that clears the workspace's 16 KiB header (a kernel, not a
  * memset, so the call may be captured into a HIP graph), and the
  * transform.  Statuses as fwt_execute, plus FWT_EINVAL for a missing or too
  * small workspace or one that overlaps the state, FWT_EALIGN for a
