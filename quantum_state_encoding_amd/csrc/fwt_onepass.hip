@@ -286,6 +286,13 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         op_pin(x);
+        // Wave priority: the row factor runs at the lowest level, the ring
+        // exchange and everything up to the next row factor at a higher
+        // one.  The two workgroups of a CU belong to different groups, and
+        // a group's ring moves at the pace of its slowest member, so a CU
+        // serves the exchange first and fits the row factor around it
+        // (measured 3.7 % faster at n = 20, batch 256, than one level).
+        __builtin_amdgcn_s_setprio(0);
         // Row factor H_15: in-vector bits 0-1, register bits 11-14, lane bits
         // 2-6 and 10, then the exchange to L1 and register bits 7-9.
 #pragma unroll
@@ -311,6 +318,7 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
         // previous iteration) and stores it to HBM, while the slice loads
         // and stores of this iteration are in flight.
         static_assert(LAG == 1, "column work trails the loads by one iteration");
+        __builtin_amdgcn_s_setprio(2);   // until the next component's row factor
 #pragma unroll
         for (int s = 0; s < S + LAG; ++s) {
             const int qw = q + s, qr = q + s - LAG;
