@@ -149,7 +149,7 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
     static_assert(S == 8 && kOpRegs == 2 * S, "slice s is registers s and 8 + s");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     V* const L = reinterpret_cast<V*>(lds_raw);
-    __shared__ int sh_min[2][2];   // cached minima of the progress words, by parity
+    __shared__ int sh_ok[2];   // the last poll met the next iteration's needs, by parity
     __shared__ int sh_next, sh_spec, sh_broken, sh_xcd, sh_rank;
     // The logical lane: mirrored_lane order makes lane bit 2 a DPP stage.
     const int t = threadIdx.x, lane = mirrored_lane(t & 63), wv = t >> 6;
@@ -191,7 +191,8 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
     const __amdgpu_buffer_rsrc_t ring =
         op_rsrc(a.ws + kOpHeaderBytes + (size_t)g * R * kOpSlotBytes);
     if (t == 0) {
-        sh_min[0][0] = sh_min[0][1] = sh_min[1][0] = sh_min[1][1] = 0;
+        sh_ok[0] = 1;   // the first iteration needs nothing
+        sh_ok[1] = 0;
         sh_broken = 0;
     }
     __syncthreads();
@@ -258,8 +259,9 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
     // 8 + k hold source rows (lane >> 2) and 16 + (lane >> 2), columns
     // (lane & 3) | wv << 2 of the slice: the source bits are register bit 3
     // and lane bits 2-5, so the whole factor runs in registers and lanes.
-    auto column_slice = [&](int k) {
-        V y[2] = {x[k], x[8 + k]};
+    auto column_factor = [&](int k, V (&y)[2]) {
+        y[0] = x[k];
+        y[1] = x[8 + k];
         butterfly(y[0], y[1]);
         lane_stage<2, 2, V, float, true>(y, lane);
         lane_stage<3, 2, V, float, true>(y, lane);
@@ -267,8 +269,15 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
         lane_stage<5, 2, V, float, true>(y, lane);
         y[0] *= cs;
         y[1] *= cs;
-        op_store<kOpNt>(comp, st_v, (uint32_t)(k * UL) * 16, y[0]);
-        op_store<kOpNt>(comp, st_v, (uint32_t)(16 * kOpRowF4 + k * UL) * 16, y[1]);
+    };
+    auto column_store = [&](__amdgpu_buffer_rsrc_t dst, int k, const V (&y)[2]) {
+        op_store<kOpNt>(dst, st_v, (uint32_t)(k * UL) * 16, y[0]);
+        op_store<kOpNt>(dst, st_v, (uint32_t)(16 * kOpRowF4 + k * UL) * 16, y[1]);
+    };
+    auto column_slice = [&](int k) {
+        V y[2];
+        column_factor(k, y);
+        column_store(comp, k, y);
     };
     for (int i = gi; i < cx;) {
         if (!loaded) {     // uniform across the workgroup
@@ -290,8 +299,7 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
         // exchange and everything up to the next row factor at a higher
         // one.  The two workgroups of a CU belong to different groups, and
         // a group's ring moves at the pace of its slowest member, so a CU
-        // serves the exchange first and fits the row factor around it
-        // (measured 3.7 % faster at n = 20, batch 256, than one level).
+        // serves the exchange first and fits the row factor around it.
         __builtin_amdgcn_s_setprio(0);
         // Row factor H_15: in-vector bits 0-1, register bits 11-14, lane bits
         // 2-6 and 10, then the exchange to L1 and register bits 7-9.
@@ -318,14 +326,21 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
         // previous iteration) and stores it to HBM, while the slice loads
         // and stores of this iteration are in flight.
         static_assert(LAG == 1, "column work trails the loads by one iteration");
+        static_assert((S + LAG) % 2 == 1, "the flag's buffer parity counts components");
         __builtin_amdgcn_s_setprio(2);   // until the next component's row factor
 #pragma unroll
         for (int s = 0; s < S + LAG; ++s) {
             const int qw = q + s, qr = q + s - LAG;
             const int need_w = s >= LAG ? qr + 1 : 0;
             const int need_r = s < S ? qw - R + 1 : 0;
-            const int cb = qw & 1;
-            if (!(sh_min[cb][0] >= need_w && sh_min[cb][1] >= need_r))
+            // What the next iteration will need (the next component's first
+            // iteration after the last one).
+            const int next_w = s + 1 >= S + LAG ? 0 : s + 1 >= LAG ? qr + 2 : 0;
+            const int next_r = s + 1 >= S + LAG ? q + S - R + 1 : s + 1 < S ? qw - R + 2 : 0;
+            // Iterations alternate the flag's buffer; a component has an odd
+            // number of them, so the parity includes the component count.
+            const int cb = (s + seq) & 1;
+            if (!sh_ok[cb])
                 wait_flags(need_w, need_r);
             if (s < S) {
                 const uint32_t so = (uint32_t)(qw % R) * (uint32_t)kOpSlotBytes;
@@ -347,12 +362,9 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
                                               __HIP_MEMORY_SCOPE_AGENT);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             if (t < 64) {
-                for (int o = 16; o >= 1; o >>= 1)
-                    pv = min(pv, __shfl_xor(pv, o));
-                const int mw = __shfl(pv, 0), mr = __shfl(pv, 32);
+                const bool ok = __ballot(pv < (lane < 32 ? next_w : next_r)) == 0;
                 if (t == 0) {
-                    sh_min[cb ^ 1][0] = mw;
-                    sh_min[cb ^ 1][1] = mr;
+                    sh_ok[cb ^ 1] = ok;
                     if (s == S + LAG - 1)   // read by every thread after the barrier
                         sh_spec = (int)(spec_next >> 32) == seq + 1 ? (int)(unsigned)spec_next
                                                                     : -1;
@@ -369,8 +381,13 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
             }
         }
         q += S;
-        column_slice(S - 1);
-        // When the next component is known, its loads follow at once.
+        // The last slice's column factor.  When the next component is
+        // known, its loads are issued before this slice's stores: memory
+        // operations complete in issue order, so the row factor's wait for
+        // the loads does not also wait for the stores' acknowledgement.
+        V ylast[2];
+        column_factor(S - 1, ylast);
+        const __amdgpu_buffer_rsrc_t done_comp = comp;
         const int spec = sh_spec;
         if (spec >= 0) {
             if (spec < cx) {
@@ -380,10 +397,12 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
                     x[j] = op_load<kOpNt>(comp, ld_v, load_offset(j));
                 loaded = true;
             }
+            column_store(done_comp, S - 1, ylast);
             i = spec;
             ++seq;
             continue;
         }
+        column_store(done_comp, S - 1, ylast);
         // The group's next component.
         if (t == 0) {
             unsigned long long v = spec_next;
