@@ -218,9 +218,13 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
         cs = -cs;
 
     // Wave 0 waits until every member has written >= need_w slices and read
-    // >= need_r; the decision to call this is the same in every wave.
+    // >= need_r; the decision to call this is the same in every wave.  The
+    // iteration's closing barrier already ordered every wave before it, and
+    // only wave 0 touches the words it reads, so it starts at once.  Each
+    // poll waits for its own load's round trip through the L2 (about a
+    // microsecond), which paces the loop without a sleep and bounds the
+    // whole wait to about a second.
     auto wait_flags = [&](int need_w, int need_r) {
-        __syncthreads();
         if (t < 64 && !sh_broken) {
             bool ok = false;
             for (int i = 0; i < kOpSpin; ++i) {
@@ -230,7 +234,6 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
                     ok = true;
                     break;
                 }
-                __builtin_amdgcn_s_sleep(1);
             }
             if (t == 0 && !ok) {
                 sh_broken = 1;
