@@ -355,15 +355,21 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
                 x[s - LAG] = op_load<kOpDevice>(ring, xr_v, so);
                 x[8 + s - LAG] = op_load<kOpDevice>(ring, xr_v, so + 16u * 16 * 4);
             }
-            if (s >= LAG + 1)
-                column_slice(s - LAG - 1);
             int pv = 0;
             if (t < 64)
                 pv = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (s == S + LAG - 1 && t == 0)   // the group's next component, published long ago
                 spec_next = __hip_atomic_load(nxt + ((seq + 1) & 1), __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // The column slice's two HBM stores are issued last and left out
+            // of the wait (operations complete in issue order): the next
+            // iteration's wait covers them.
+            if (s >= LAG + 1) {
+                column_slice(s - LAG - 1);
+                asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
             if (t < 64) {
                 const bool ok = __ballot(pv < (lane < 32 ? next_w : next_r)) == 0;
                 if (t == 0) {
