@@ -47,9 +47,9 @@ namespace {
 // slots per group): each workgroup stores its registers of slice s (the
 // values for all 32 destinations), loads slice s - 1 as written by every
 // member, applies the column factor to slice s - 2 and stores it to HBM,
-// waits for all of it with one s_waitcnt, and publishes "slices written"
-// and "slices read" in its two progress words (plain stores: they land in
-// the XCD's L2).  A slot holds float4 (destination d, source r, column u)
+// waits for everything but those HBM stores with one s_waitcnt, and
+// publishes "slices written" and "slices read" in its two progress words
+// (plain stores: they land in the XCD's L2).  A slot holds float4 (destination d, source r, column u)
 // at ((d * 8 + u / 4) * 32 + r) * 4 + u % 4, so a reader's wave loads
 // 1 KiB in one piece.  The ring's size is set by the L2: two groups'
 // rings of 2 x 512 KiB share an XCD's 4 MB with the HBM streams; a third
