@@ -363,8 +363,9 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
                                               __HIP_MEMORY_SCOPE_AGENT);
             // The column slice's two HBM stores are issued last and left out
             // of the wait (operations complete in issue order): the next
-            // iteration's wait covers them.
-            if (s >= LAG + 1) {
+            // iteration's wait covers them.  The last iteration leaves its
+            // slice to the component's tail.
+            if (s >= LAG + 1 && s < S + LAG - 1) {
                 column_slice(s - LAG - 1);
                 asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
             } else {
@@ -390,11 +391,13 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
             }
         }
         q += S;
-        // The last slice's column factor.  When the next component is
-        // known, its loads are issued before this slice's stores: memory
-        // operations complete in issue order, so the row factor's wait for
-        // the loads does not also wait for the stores' acknowledgement.
-        V ylast[2];
+        // The last two slices' column factors (the last iteration leaves
+        // slice S - 2 here too).  When the next component is known, its
+        // loads are issued before these slices' stores: memory operations
+        // complete in issue order, so the row factor's wait for the loads
+        // does not also wait for the stores' acknowledgement.
+        V yprev[2], ylast[2];
+        column_factor(S - 2, yprev);
         column_factor(S - 1, ylast);
         const __amdgpu_buffer_rsrc_t done_comp = comp;
         const int spec = sh_spec;
@@ -406,11 +409,13 @@ __global__ void __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu
                     x[j] = op_load<kOpNt>(comp, ld_v, load_offset(j));
                 loaded = true;
             }
+            column_store(done_comp, S - 2, yprev);
             column_store(done_comp, S - 1, ylast);
             i = spec;
             ++seq;
             continue;
         }
+        column_store(done_comp, S - 2, yprev);
         column_store(done_comp, S - 1, ylast);
         // The group's next component.
         if (t == 0) {
