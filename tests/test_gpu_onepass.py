@@ -165,6 +165,30 @@ def test_batch_past_the_benchmark_without_im(plan):
     torch.cuda.empty_cache()
 
 
+def test_successive_batches_share_one_workspace(plan):
+    """Calls of different sizes in a row on one workspace (each call clears
+    its header; the queue and the next-index words start over): every call
+    equals fwt_execute's two passes bit for bit and leaves no error bits."""
+    ws = workspace(plan, 300)
+    for k, batch in enumerate((256, 1, 37, 300, 2, 256)):
+        say("onepass successive batch=%d" % batch)
+        re = ints((batch, 1 << N20), 2000 + k)
+        im = ints((batch, 1 << N20), 3000 + k) if batch % 2 == 0 else None
+        src_re = to_dev(re)
+        src_im = to_dev(im) if im is not None else None
+        a_re = src_re.clone()
+        a_im = src_im.clone() if src_im is not None else None
+        plan.execute(a_re, a_im, normalize=True)
+        plan.execute_ws(src_re, src_im, normalize=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert qse.workspace_status(ws) == 0, "batch %d" % batch
+        assert torch.equal(a_re, src_re), "batch %d" % batch
+        if im is not None:
+            assert torch.equal(a_im, src_im), "batch %d" % batch
+        del src_re, src_im, a_re, a_im
+    torch.cuda.empty_cache()
+
+
 def test_involution_gaussian(plan):
     """Two normalised calls give back the input within tolerance."""
     say("onepass involution")
